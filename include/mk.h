@@ -1,0 +1,171 @@
+/* mk.h -- C ABI of the persistent fused MoE decode-layer step for AMD MI355X (gfx950).
+ *
+ * One call of mk_layer_step() enqueues ONE kernel launch that runs a whole decoder layer
+ * for a batch-one speculative verify step, as the LMSYS / SGLang "Muse Spark Open"
+ * megakernel pages draw the fusion boundary (orcarouter.ai write-up, section "where the
+ * kernel boundary sits"; alphasignal.ai, "Launch boundaries leave hardware idle"): the
+ * launch starts with attention of layer L over the KV cache and ends with layer L+1's
+ * query/key/value projection and KV-cache write.  In between: output projection, pooler,
+ * top-k-of-E router, routed experts stored as NVFP4 (gate/up GEMM with SwiGLU, an fp4
+ * intermediate, down GEMM, combine), unpooler.
+ *
+ * Conventions (all entry points):
+ *  - Every pointer is a caller-owned DEVICE pointer unless marked [host].  The library
+ *    never allocates, frees or retains device memory; it keeps no pointer after a call.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls only
+ *    enqueue work; they return before it runs.
+ *  - Return value: MK_OK (0) or a negative mk_status.  Every argument, shape and alignment
+ *    check happens on the host BEFORE any HIP call, so a rejected call enqueues nothing.
+ *    Errors found while the kernel runs (a malformed tree, a bounded wait that expired) are
+ *    written to the status word in the workspace; read them with mk_read_status().
+ *  - Tensors are row-major; weight matrices use the PyTorch Linear layout [out][in].
+ *  - bf16 tensors are passed as void* (16-bit patterns).  Device pointers must be 16-byte
+ *    aligned unless stated otherwise.
+ *  - Thread safety: calls on distinct streams with distinct workspaces may run
+ *    concurrently from several host threads.  A mk_layer_step launch needs every CU of
+ *    the device (one workgroup per CU); a concurrent kernel on another stream delays it,
+ *    and if CUs stay occupied its bounded waits expire with MK_ETIMEOUT instead of hanging.
+ */
+#ifndef MK_H_
+#define MK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MK_OK = 0,
+  MK_EINVAL = -1,     /* NULL pointer where one is required, or a bad enum value          */
+  MK_ESHAPE = -2,     /* shape outside what the kernels support (see mk_layer_cfg)         */
+  MK_EALIGN = -3,     /* pointer not 16-byte aligned                                       */
+  MK_ECAPACITY = -4,  /* KV cache or workspace too small                                   */
+  MK_EHIP = -5,       /* a HIP runtime call failed (launch, copy, device query)            */
+  MK_ETIMEOUT = -6,   /* a bounded in-kernel wait expired (CUs not all available)          */
+  MK_EBADTREE = -7    /* tree_parent malformed: parent[0] != -1 or parent[i] not in [0,i)  */
+} mk_status;
+
+typedef enum { MK_W_BF16 = 0, MK_W_NVFP4 = 1 } mk_wfmt;
+
+/* Shapes of one GPU's share of a layer [host].  Supported: hidden, pooled multiples of 256;
+ * head_dim 64 or 128; n_q_heads a multiple of n_kv_heads with T*(n_q_heads/n_kv_heads) <= 128;
+ * n_experts <= 256 (multiple of 16); 1 <= top_k <= 8; expert_inter a multiple of 32;
+ * window 0 (global attention) or >= 16; T <= 16. */
+typedef struct {
+  int hidden, n_q_heads, n_kv_heads, head_dim;   /* H, Hq, Hkv, d                          */
+  int pooled, n_experts, top_k, expert_inter;    /* P, E, k, I (this GPU's share of I)     */
+  int window;                                    /* sliding window length, 0 = global      */
+  int expert_fmt;                                /* mk_wfmt of the routed experts           */
+  int kv_capacity;                               /* rows of each KV cache                   */
+} mk_layer_cfg;
+
+/* Weights of one layer [host struct of device pointers]. */
+typedef struct {
+  const void *w_o;         /* bf16 [H][Hq*d]          output projection                     */
+  const void *w_pool;      /* bf16 [P][H]             pooler                                */
+  const void *w_router;    /* bf16 [E][P]             router                                */
+  const void *w_unpool;    /* bf16 [H][P]             unpooler                              */
+  const void *w_qkv_next;  /* bf16 [(Hq+2Hkv)*d][H]   next layer's q, k, v rows, in that order */
+  const void *w1, *w2;     /* MK_W_BF16:  bf16 [E][2I][P] (rows [0,I) gate, [I,2I) up), [E][P][I] */
+  const uint8_t *w1_codes, *w1_scales;  /* MK_W_NVFP4: [E][2I][P/2], [E][2I][P/16] (mk_nvfp4_pack) */
+  const uint8_t *w2_codes, *w2_scales;  /*             [E][P][I/2],  [E][P][I/16]                  */
+  const float *w1_tscale, *w2_tscale;   /*             fp32 [E] tensor scales                      */
+} mk_layer_weights;
+
+/* Inputs and outputs of one step [host struct; pointers are device pointers]. */
+typedef struct {
+  int T;                       /* [host] tree nodes, 1..16                                  */
+  int ctx_len;                 /* [host] KV rows before the tree; ctx_len + T <= kv_capacity */
+  const int32_t *tree_parent;  /* [T]; parent[0] = -1, parent[i] in [0, i).  Node i sits at
+                                  position ctx_len + depth(i) and in KV slot ctx_len + i      */
+  const void *q_in;            /* bf16 [T][Hq*d]   this layer's queries (previous launch)     */
+  const void *h_in;            /* bf16 [T][H]      residual stream entering the layer         */
+  const void *k_cache, *v_cache;      /* bf16 [cap][Hkv][d]; rows [0, ctx_len+T) valid        */
+  void *k_cache_next, *v_cache_next;  /* bf16 [cap][Hkv][d]; rows ctx_len..ctx_len+T-1 written,
+                                         every other row left untouched                       */
+  void *h_out;                 /* bf16 [T][H]      residual stream leaving the layer          */
+  void *q_next;                /* bf16 [T][Hq*d]   next layer's queries                       */
+  int32_t *topk_idx;           /* [T][k] or NULL   experts per token, best first              */
+  float *topk_gate;            /* [T][k] or NULL   softmax over the k selected logits         */
+  float *router_logits;        /* [T][E] or NULL   fp32 logits (bias included)                */
+  float *attn_stats;           /* [T][Hq][2] or NULL: row max m of the scaled scores and
+                                  l = sum exp(score - m), natural-log units                   */
+  int32_t *expert_hist;        /* [E] or NULL      += number of (token, slot) pairs per expert */
+  const int32_t *prefetch_experts; /* [n_prefetch] or NULL: expert ids to pull into the
+                                  device-side cache at launch start (speculative prefetch)    */
+  int n_prefetch;              /* [host] 0..16                                              */
+  const float *router_bias;    /* [T][E] or NULL   added to the logits before top-k           */
+  void *workspace;             /* >= mk_workspace_bytes(); initialised once by
+                                  mk_workspace_init(); holds the status word, the
+                                  cross-workgroup flags and the stage hand-off buffers        */
+  size_t workspace_bytes;      /* [host]                                                    */
+  uint64_t *timestamps;        /* NULL, or [n_cu][MK_TS_EVENTS] wall-clock ticks (100 MHz)
+                                  written by lane 0 of every workgroup at phase boundaries;
+                                  when NULL the launched kernel contains no timing code       */
+  int spin_limit;              /* [host] 0 = default; else max polls of each in-kernel wait  */
+  int debug_skip_signal_wg;    /* [host] -1 normally; test hook: this workgroup never signals,
+                                  so the others' bounded waits must end in MK_ETIMEOUT        */
+} mk_step_io;
+
+#define MK_TS_EVENTS 16
+
+/* Stage hand-off buffers inside the workspace (byte offsets), for stage-local checks. */
+typedef struct {
+  size_t status;       /* int32 status word                                      */
+  size_t attn;         /* bf16 [T][Hq*d]   attention output                      */
+  size_t h1;           /* bf16 [T][H]      residual after the output projection  */
+  size_t xp;           /* bf16 [T][P]      pooler output                         */
+  size_t logits;       /* fp32 [T][E]      router logits (bias included)         */
+  size_t y;            /* bf16 [T][P]      combined expert output                */
+  size_t total;        /* bytes needed                                           */
+  int n_wg;            /* workgroups per launch (= CUs of the current device)    */
+  int attn_items;      /* attention work items (KV chunks)                       */
+} mk_workspace_layout;
+
+/* Workspace bytes for this config on the current device (0 on an unsupported config). */
+size_t mk_workspace_bytes(const mk_layer_cfg *cfg, int T);
+/* Offsets of the hand-off buffers; returns MK_OK or an mk_status. */
+int mk_workspace_query(const mk_layer_cfg *cfg, int T, mk_workspace_layout *out /* [host] */);
+/* Zero the workspace (a fill kernel, no hipMemset).  Call once before first use and after
+ * an MK_ETIMEOUT. */
+int mk_workspace_init(void *workspace, size_t bytes, void *stream);
+
+/* One fused decoder-layer step (see the file comment).  Enqueues one kernel. */
+int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
+                  const mk_step_io *io /* [host] */, void *stream);
+
+/* Copy n new rows into a KV cache pair at rows pos..pos+n-1 (the rest untouched).
+ * k_cache, v_cache: bf16 [capacity][n_kv_heads][head_dim]; k_new, v_new: bf16 [n][n_kv_heads][head_dim]. */
+int mk_kv_append(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int head_dim, int pos,
+                 const void *k_new, const void *v_new, int n, void *stream);
+
+/* Router on its own: logits = x . w_router^T (+ bias) in fp32, then the top-k experts per
+ * token ordered by (logit desc, index asc) and softmax gates over the k selected logits.
+ * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k];
+ * gate fp32 [T][k]; logits fp32 [T][E] or NULL.  T <= 64, E <= 256, k <= 8, P % 8 == 0. */
+int mk_route_topk(const void *x, const void *w_router, const float *bias, int T, int P, int E, int k,
+                  int32_t *idx, float *gate, float *logits, void *stream);
+
+/* NVFP4 quantisation of `batch` matrices w [batch][N][K] (bf16 when w_is_fp32 == 0, else
+ * fp32), K % 16 == 0.  Per matrix: tensor scale ts = fp32(amax) / 2688 (1 when amax = 0);
+ * per 16-element block: E4M3 scale s = RNE(amax_block / (6 ts)) saturating at 448;
+ * per element: E2M1 code = RNE(x / (s ts)) saturating at +-6, ties to the even code, a zero
+ * result stored as +0, all codes 0 when s = 0.  Rounding decisions are exact comparisons with
+ * grid midpoints.  Outputs: codes uint8 [batch][N][K/2] (element 2j in the low nibble),
+ * scales uint8 [batch][N][K/16], tensor_scale fp32 [batch]. */
+int mk_nvfp4_pack(const void *w, int w_is_fp32, int batch, int N, int K, uint8_t *codes,
+                  uint8_t *scales, float *tensor_scale, void *stream);
+
+/* Synchronise `stream` and return the status word of the last mk_layer_step on this
+ * workspace (MK_OK, MK_EBADTREE or MK_ETIMEOUT), or MK_EHIP if the copy failed. */
+int mk_read_status(const void *workspace, void *stream);
+
+/* Human-readable name of a status code. */
+const char *mk_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H_ */

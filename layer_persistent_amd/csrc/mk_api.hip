@@ -1,0 +1,264 @@
+// C ABI (include/mk.h): argument validation on the host, workspace layout, launches.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kLayerLds = 96 * 1024;       // > half of the 160 KB LDS: one workgroup per CU
+constexpr int kChunkKeys = 128;            // KV rows per attention work item
+constexpr int kDefaultSpin = 1 << 20;      // polls per wait before MK_ETIMEOUT
+
+std::mutex g_mu;
+int g_cu[kMaxDevices];                     // CU count per device (0 = not queried)
+bool g_attr[kMaxDevices];
+
+int device_cus(int* n_cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_EHIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_cu[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return MK_EHIP;
+    g_cu[dev] = n;
+  }
+  if (!g_attr[dev]) {
+    if (mk::set_layer_kernel_attrs(kLayerLds)) return MK_EHIP;
+    g_attr[dev] = true;
+  }
+  *n_cu = g_cu[dev];
+  return MK_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int check_cfg(const mk_layer_cfg* c, int T) {
+  if (!c) return MK_EINVAL;
+  if (c->expert_fmt != MK_W_BF16 && c->expert_fmt != MK_W_NVFP4) return MK_EINVAL;
+  if (T < 1 || T > 16) return MK_ESHAPE;
+  if (c->hidden <= 0 || c->hidden % 128) return MK_ESHAPE;
+  if (c->pooled <= 0 || c->pooled % 128) return MK_ESHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return MK_ESHAPE;
+  if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads) return MK_ESHAPE;
+  if (T * (c->n_q_heads / c->n_kv_heads) > 128) return MK_ESHAPE;
+  if (c->n_experts <= 0 || c->n_experts > 256 || c->n_experts % 16) return MK_ESHAPE;
+  if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MK_ESHAPE;
+  if (c->expert_inter <= 0 || c->expert_inter % 32) return MK_ESHAPE;
+  if (c->window < 0) return MK_ESHAPE;
+  if (c->kv_capacity <= 0) return MK_ESHAPE;
+  return MK_OK;
+}
+
+struct Layout {
+  size_t status, epoch, flags, part_o, part_ml, attn, h1, xp, logits, act, y, total;
+  int n_wg, items, chunks_per_head, attn_lo;
+};
+
+// attention work split: context rows [attn_lo, ctx) in chunks of kChunkKeys, plus one chunk
+// holding the tree's own slots, for each kv head
+void attn_split(const mk_layer_cfg* c, int ctx, int* lo, int* chunks) {
+  const int l = c->window > 0 ? (ctx - c->window + 1 > 0 ? ctx - c->window + 1 : 0) : 0;
+  *lo = l;
+  *chunks = (ctx - l + kChunkKeys - 1) / kChunkKeys + 1;
+}
+
+Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
+  Layout L;
+  memset(&L, 0, sizeof(L));
+  L.n_wg = n_wg;
+  attn_split(c, ctx, &L.attn_lo, &L.chunks_per_head);
+  L.items = c->n_kv_heads * L.chunks_per_head;
+  const int H = c->hidden, Hq = c->n_q_heads, d = c->head_dim, P = c->pooled, E = c->n_experts,
+            k = c->top_k, I = c->expert_inter;
+  size_t o = 0;
+  L.status = o; o = up256(o + 4);
+  L.epoch = o; o = up256(o + (size_t)n_wg * 64);
+  L.flags = o; o = up256(o + (size_t)n_wg * 64);
+  L.part_o = o; o = up256(o + (size_t)L.items * 128 * d * 4);
+  L.part_ml = o; o = up256(o + (size_t)L.items * 128 * 2 * 4);
+  L.attn = o; o = up256(o + (size_t)T * Hq * d * 2);
+  L.h1 = o; o = up256(o + (size_t)T * H * 2);
+  L.xp = o; o = up256(o + (size_t)T * P * 2);
+  L.logits = o; o = up256(o + (size_t)T * E * 4);
+  const size_t act_q = (size_t)T * k * (I / 16) * 16, act_b = (size_t)T * k * I * 2;
+  L.act = o; o = up256(o + (act_q > act_b ? act_q : act_b));
+  L.y = o; o = up256(o + (size_t)T * P * 2);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mk_strerror(int s) {
+  switch (s) {
+    case MK_OK: return "ok";
+    case MK_EINVAL: return "invalid argument";
+    case MK_ESHAPE: return "unsupported shape";
+    case MK_EALIGN: return "pointer not 16-byte aligned";
+    case MK_ECAPACITY: return "KV cache or workspace too small";
+    case MK_EHIP: return "HIP runtime error";
+    case MK_ETIMEOUT: return "in-kernel wait timed out";
+    case MK_EBADTREE: return "malformed tree_parent";
+    default: return "unknown status";
+  }
+}
+
+int mk_workspace_query(const mk_layer_cfg* cfg, int T, mk_workspace_layout* out) {
+  // the layout depends on ctx through the attention split; the query assumes the largest
+  // context the cache allows
+  int rc = check_cfg(cfg, T);
+  if (rc) return rc;
+  if (!out) return MK_EINVAL;
+  int n_wg = 0;
+  rc = device_cus(&n_wg);
+  if (rc) return rc;
+  Layout L = layout(cfg, T, cfg->kv_capacity - T > 0 ? cfg->kv_capacity - T : 0, n_wg);
+  out->status = L.status;
+  out->attn = L.attn;
+  out->h1 = L.h1;
+  out->xp = L.xp;
+  out->logits = L.logits;
+  out->y = L.y;
+  out->total = L.total;
+  out->n_wg = L.n_wg;
+  out->attn_items = L.items;
+  return MK_OK;
+}
+
+size_t mk_workspace_bytes(const mk_layer_cfg* cfg, int T) {
+  mk_workspace_layout l;
+  if (mk_workspace_query(cfg, T, &l)) return 0;
+  return l.total;
+}
+
+int mk_workspace_init(void* ws, size_t bytes, void* stream) {
+  if (!ws || bytes == 0) return MK_EINVAL;
+  if (!aligned16(ws)) return MK_EALIGN;
+  return mk::launch_fill_zero(ws, bytes, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
+int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, void* stream) {
+  if (!c || !w || !io) return MK_EINVAL;
+  int rc = check_cfg(c, io->T);
+  if (rc) return rc;
+  const int T = io->T, ctx = io->ctx_len;
+  if (ctx < 0 || ctx + T > c->kv_capacity) return MK_ECAPACITY;
+  const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next,
+                       io->v_cache_next, io->h_out, io->q_next, io->workspace, w->w_o, w->w_pool,
+                       w->w_router, w->w_unpool, w->w_qkv_next};
+  for (const void* p : req) if (!p) return MK_EINVAL;
+  if (c->expert_fmt == MK_W_BF16) {
+    if (!w->w1 || !w->w2) return MK_EINVAL;
+  } else {
+    if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales || !w->w1_tscale || !w->w2_tscale)
+      return MK_EINVAL;
+    if (c->pooled % 128) return MK_ESHAPE;
+  }
+  if (io->n_prefetch < 0 || io->n_prefetch > 16) return MK_ESHAPE;
+  if (io->n_prefetch > 0 && !io->prefetch_experts) return MK_EINVAL;
+  if (io->spin_limit < 0) return MK_EINVAL;
+  const void* al[] = {io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next, io->v_cache_next,
+                      io->h_out, io->q_next, io->workspace, io->topk_idx, io->topk_gate,
+                      io->router_logits, io->attn_stats, io->router_bias, w->w_o, w->w_pool,
+                      w->w_router, w->w_unpool, w->w_qkv_next, w->w1, w->w2, w->w1_codes,
+                      w->w1_scales, w->w2_codes, w->w2_scales};
+  for (const void* p : al) if (p && !aligned16(p)) return MK_EALIGN;
+  int n_wg = 0;
+  rc = device_cus(&n_wg);
+  if (rc) return rc;
+  // the workspace must cover the largest context this cache allows, so one workspace serves
+  // every step of a layer
+  Layout L = layout(c, T, c->kv_capacity - T, n_wg);
+  Layout Lc = layout(c, T, ctx, n_wg);
+  if (io->workspace_bytes < L.total) return MK_ECAPACITY;
+
+  mk::KArgs a;
+  memset(&a, 0, sizeof(a));
+  a.H = c->hidden; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.d = c->head_dim; a.P = c->pooled;
+  a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
+  a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
+  a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
+  a.attn_lo = Lc.attn_lo; a.ck = kChunkKeys;
+  a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
+  a.skip_wg = io->debug_skip_signal_wg;
+  a.parent = io->tree_parent;
+  a.q_in = (const uint16_t*)io->q_in; a.h_in = (const uint16_t*)io->h_in;
+  a.kc = (const uint16_t*)io->k_cache; a.vc = (const uint16_t*)io->v_cache;
+  a.kn = (uint16_t*)io->k_cache_next; a.vn = (uint16_t*)io->v_cache_next;
+  a.h_out = (uint16_t*)io->h_out; a.q_next = (uint16_t*)io->q_next;
+  a.topk_idx = io->topk_idx; a.topk_gate = io->topk_gate; a.router_logits = io->router_logits;
+  a.attn_stats = io->attn_stats; a.hist = io->expert_hist;
+  a.prefetch = io->prefetch_experts; a.n_prefetch = io->n_prefetch; a.bias = io->router_bias;
+  a.w_o = (const uint16_t*)w->w_o; a.w_pool = (const uint16_t*)w->w_pool;
+  a.w_router = (const uint16_t*)w->w_router; a.w_unpool = (const uint16_t*)w->w_unpool;
+  a.w_qkv = (const uint16_t*)w->w_qkv_next;
+  a.w1 = (const uint16_t*)w->w1; a.w2 = (const uint16_t*)w->w2;
+  a.w1_codes = w->w1_codes; a.w1_scales = w->w1_scales; a.w2_codes = w->w2_codes; a.w2_scales = w->w2_scales;
+  a.w1_ts = w->w1_tscale; a.w2_ts = w->w2_tscale;
+  char* ws = (char*)io->workspace;
+  a.status = (int32_t*)(ws + L.status);
+  a.epoch = (uint32_t*)(ws + L.epoch);
+  a.flags = (uint32_t*)(ws + L.flags);
+  a.part_o = (float*)(ws + L.part_o);
+  a.part_ml = (float*)(ws + L.part_ml);
+  a.attn = (uint16_t*)(ws + L.attn);
+  a.h1 = (uint16_t*)(ws + L.h1);
+  a.xp = (uint16_t*)(ws + L.xp);
+  a.logits = (float*)(ws + L.logits);
+  a.act_q = (uint32_t*)(ws + L.act);
+  a.act_bf = (uint16_t*)(ws + L.act);
+  a.y = (uint16_t*)(ws + L.y);
+  a.timestamps = io->timestamps;
+  return mk::launch_layer(a, kLayerLds, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
+int mk_kv_append(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int head_dim, int pos,
+                 const void* k_new, const void* v_new, int n, void* stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new) return MK_EINVAL;
+  if (n_kv_heads <= 0 || head_dim <= 0 || (n_kv_heads * head_dim) % 8 || n < 0 || capacity <= 0) return MK_ESHAPE;
+  if (pos < 0 || pos + n > capacity) return MK_ECAPACITY;
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new)) return MK_EALIGN;
+  if (n == 0) return MK_OK;
+  return mk::launch_kv_append((uint16_t*)k_cache, (uint16_t*)v_cache, n_kv_heads * head_dim, pos,
+                              (const uint16_t*)k_new, (const uint16_t*)v_new, n, (hipStream_t)stream)
+             ? MK_EHIP : MK_OK;
+}
+
+int mk_route_topk(const void* x, const void* w_router, const float* bias, int T, int P, int E, int k,
+                  int32_t* idx, float* gate, float* logits, void* stream) {
+  if (!x || !w_router || !idx || !gate) return MK_EINVAL;
+  if (T < 1 || T > 64 || P <= 0 || P % 8 || E <= 0 || E > 256 || k < 1 || k > 8 || k > E) return MK_ESHAPE;
+  if (!aligned16(x) || !aligned16(w_router)) return MK_EALIGN;
+  return mk::launch_route_topk((const uint16_t*)x, (const uint16_t*)w_router, bias, T, P, E, k, idx, gate,
+                               logits, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
+int mk_nvfp4_pack(const void* w, int w_is_fp32, int batch, int N, int K, uint8_t* codes, uint8_t* scales,
+                  float* tensor_scale, void* stream) {
+  if (!w || !codes || !scales || !tensor_scale) return MK_EINVAL;
+  if (w_is_fp32 != 0 && w_is_fp32 != 1) return MK_EINVAL;
+  if (batch < 1 || batch > 65535 || N < 1 || K < 16 || K % 16) return MK_ESHAPE;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || !aligned16(tensor_scale)) return MK_EALIGN;
+  return mk::launch_nvfp4_pack(w, w_is_fp32, batch, N, K, codes, scales, tensor_scale, (hipStream_t)stream)
+             ? MK_EHIP : MK_OK;
+}
+
+int mk_read_status(const void* workspace, void* stream) {
+  if (!workspace) return MK_EINVAL;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_EHIP;
+  int32_t st = 0;
+  if (hipMemcpy(&st, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return MK_EHIP;
+  return st;
+}
+
+}  // extern "C"

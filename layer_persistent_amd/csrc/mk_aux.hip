@@ -1,0 +1,219 @@
+// Small kernels behind the C ABI: workspace fill, KV-cache append, stand-alone router top-k,
+// and NVFP4 packing of weight matrices.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_device.h"
+#include "mk_internal.h"
+
+namespace mk {
+
+// ------------------------------------------------------------------ fill
+
+__global__ void fill_zero_kernel(u32x4* p, size_t n16, uint8_t* tail, size_t ntail) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = u32x4{0, 0, 0, 0};
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+  const size_t n16 = bytes / 16, ntail = bytes % 16;
+  int grid = (int)((n16 + 255) / 256);
+  if (grid < 1) grid = 1;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, (u32x4*)p, n16,
+                     (uint8_t*)p + n16 * 16, ntail);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ------------------------------------------------------------------ KV append
+
+// rows pos..pos+n-1 of both caches <- k_new / v_new; row_elems = n_kv_heads * head_dim (bf16)
+__global__ void kv_append_kernel(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,
+                                 const uint16_t* vn, int n) {
+  const int per_row = row_elems / 8;  // 16-byte pieces
+  const int total = n * per_row;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < total; i += gridDim.x * blockDim.x) {
+    const int r = i / per_row, c = (i % per_row) * 8;
+    *(u32x4*)(kc + (size_t)(pos + r) * row_elems + c) = *(const u32x4*)(kn + (size_t)r * row_elems + c);
+    *(u32x4*)(vc + (size_t)(pos + r) * row_elems + c) = *(const u32x4*)(vn + (size_t)r * row_elems + c);
+  }
+}
+
+int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,
+                     const uint16_t* vn, int n, hipStream_t stream) {
+  const int total = n * (row_elems / 8);
+  int grid = (total + 255) / 256;
+  if (grid < 1) grid = 1;
+  if (grid > 1024) grid = 1024;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(grid), dim3(256), 0, stream, kc, vc, row_elems, pos, kn, vn, n);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ------------------------------------------------------------------ router top-k
+
+// One workgroup (256 threads) per token: fp32 logits by per-expert dot products, then the
+// top-k by (value desc, index asc) in wave 0, softmax gates over the selected logits.
+__global__ void __launch_bounds__(256) route_topk_kernel(const uint16_t* x, const uint16_t* w,
+                                                         const float* bias, int P, int E, int k,
+                                                         int32_t* idx, float* gate, float* logits) {
+  __shared__ float lg[256];
+  const int t = blockIdx.x;
+  const uint16_t* xr = x + (size_t)t * P;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) {
+    const uint16_t* wr = w + (size_t)e * P;
+    float acc = 0.f;
+    for (int c = 0; c < P; c += 8) {
+      const u32x4 xv = *(const u32x4*)(xr + c), wv = *(const u32x4*)(wr + c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(bf2f(xv[j] & 0xFFFF), bf2f(wv[j] & 0xFFFF), acc);
+        acc = fmaf(bf2f(xv[j] >> 16), bf2f(wv[j] >> 16), acc);
+      }
+    }
+    if (bias) acc += bias[(size_t)t * E + e];
+    lg[e] = acc;
+    if (logits) logits[(size_t)t * E + e] = acc;
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    float v[4];
+    int ee[4];
+    bool taken[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ee[q] = lane + 64 * q;
+      taken[q] = ee[q] >= E;
+      v[q] = taken[q] ? -INFINITY : lg[ee[q]];
+    }
+    float zsel[8];
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (!taken[q] && (v[q] > bv || (v[q] == bv && ee[q] < be))) { bv = v[q]; be = ee[q]; }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oe = __shfl_xor(be, off);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) if (ee[q] == be) taken[q] = true;
+      zsel[j] = bv;
+      if (lane == 0) idx[(size_t)t * k + j] = be;
+    }
+    if (lane == 0) {
+      float s = 0.f, ex[8];
+      for (int j = 0; j < k; ++j) { ex[j] = __expf(zsel[j] - zsel[0]); s += ex[j]; }
+      for (int j = 0; j < k; ++j) gate[(size_t)t * k + j] = ex[j] / s;
+    }
+  }
+}
+
+int launch_route_topk(const uint16_t* x, const uint16_t* w, const float* bias, int T, int P, int E,
+                      int k, int32_t* idx, float* gate, float* logits, hipStream_t stream) {
+  hipLaunchKernelGGL(route_topk_kernel, dim3(T), dim3(256), 0, stream, x, w, bias, P, E, k, idx, gate, logits);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+// ------------------------------------------------------------------ NVFP4 packing
+
+__device__ __forceinline__ float load_w(const void* w, int is_fp32, size_t i) {
+  return is_fp32 ? ((const float*)w)[i] : bf2f(((const uint16_t*)w)[i]);
+}
+
+// pass 1: amax of each matrix, as the bit pattern of a non-negative float (monotone as uint)
+__global__ void amax_kernel(const void* w, int is_fp32, size_t per_mat, uint32_t* amax_bits) {
+  const int b = blockIdx.y;
+  float m = 0.f;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_mat; i += (size_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(load_w(w, is_fp32, (size_t)b * per_mat + i)));
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) atomicMax(amax_bits + b, __float_as_uint(m));
+}
+
+// pass 2: ts = fp32(amax) / 2688 (correctly rounded fp32 division), 1 when amax = 0
+__global__ void tscale_kernel(float* ts, int batch) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) {
+    const float amax = __uint_as_float(((const uint32_t*)ts)[b]);
+    ts[b] = amax > 0.f ? amax / 2688.0f : 1.0f;
+  }
+}
+
+// E4M3 byte -> value in fp64 (non-negative codes 0..126)
+__device__ __forceinline__ double e4m3_pos_f64(int c) {
+  const int E = c >> 3, M = c & 7;
+  return E == 0 ? (double)M * 0x1p-9 : (1.0 + M / 8.0) * ldexp(1.0, E - 7);
+}
+
+// pass 3: one thread per 16-element block.  Scale and code decisions are exact fp64
+// comparisons of the input with midpoint * 6 * ts and midpoint * s * ts (<= 31 significant bits).
+__global__ void pack_kernel(const void* w, int is_fp32, int N, int K, int batch, const float* ts,
+                            uint8_t* codes, uint8_t* scales) {
+  const size_t nblk_row = K / 16;
+  const size_t nblocks = (size_t)batch * N * nblk_row;
+  for (size_t blk = (size_t)blockIdx.x * blockDim.x + threadIdx.x; blk < nblocks;
+       blk += (size_t)gridDim.x * blockDim.x) {
+    const size_t b = blk / ((size_t)N * nblk_row);
+    const double t = (double)ts[b];
+    float x[16];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      x[j] = load_w(w, is_fp32, blk * 16 + j);
+      amax = fmaxf(amax, fabsf(x[j]));
+    }
+    // scale: number of midpoints passed, ties to the even code
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+      const int c = (lo + hi) >> 1;
+      const double thr = 6.0 * t * (0.5 * (e4m3_pos_f64(c) + e4m3_pos_f64(c + 1)));
+      const bool passed = (double)amax > thr || ((double)amax == thr && (c & 1));
+      if (passed) lo = c + 1; else hi = c;
+    }
+    const int sc = lo;
+    const double unit = e4m3_pos_f64(sc) * t;
+    uint32_t w0 = 0, w1 = 0;
+    if (unit > 0.0) {
+      const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const double ax = fabs((double)x[j]);
+        uint32_t c = 0;
+#pragma unroll
+        for (int i = 0; i < 7; ++i) {
+          const double thr = mids[i] * unit;
+          c += (ax > thr || (ax == thr && (i & 1))) ? 1u : 0u;
+        }
+        if (x[j] < 0.f && c) c |= 8u;
+        if (j < 8) w0 |= c << (4 * j); else w1 |= c << (4 * (j - 8));
+      }
+    }
+    *(u32x2*)(codes + blk * 8) = u32x2{w0, w1};
+    scales[blk] = (uint8_t)sc;
+  }
+}
+
+int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8_t* codes,
+                      uint8_t* scales, float* ts, hipStream_t stream) {
+  if (launch_fill_zero(ts, (size_t)batch * 4, stream)) return -5;
+  const size_t per_mat = (size_t)N * K;
+  int gx = (int)((per_mat + 255) / 256);
+  if (gx > 256) gx = 256;
+  if (gx < 1) gx = 1;
+  hipLaunchKernelGGL(amax_kernel, dim3(gx, batch), dim3(256), 0, stream, w, is_fp32, per_mat, (uint32_t*)ts);
+  if (hipGetLastError() != hipSuccess) return -5;
+  hipLaunchKernelGGL(tscale_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, ts, batch);
+  if (hipGetLastError() != hipSuccess) return -5;
+  const size_t nblocks = (size_t)batch * N * (K / 16);
+  size_t g = (nblocks + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)g), dim3(256), 0, stream, w, is_fp32, N, K, batch, ts, codes, scales);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+}  // namespace mk

@@ -1,0 +1,112 @@
+// Device helpers for the gfx950 (CDNA4) kernels: bf16 packing, MFMA fragments, NVFP4
+// dequantisation, coherent hand-off stores and wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+namespace mk {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
+// fp32 -> bf16, round to nearest even (finite inputs)
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+// v_mfma_f32_16x16x32_bf16.  Lane l supplies A[l%16][8*(l/16) + j] and B[8*(l/16) + j][l%16]
+// (j = 0..7, any common permutation of k is allowed); C lane l holds rows 4*(l/16)+r, col l%16.
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight E2M1 codes (one dword, element 2q in the low nibble of byte q) times an fp32 block
+// scale -> eight bf16 in MFMA operand order.  The hardware converter applies only the
+// exponent of its scale operand, so it decodes the bare codes (scale 1.0, exact) and the
+// E4M3 scale is applied by an fp32 multiply; e2m1 x e4m3 products have <= 6 significant
+// bits, so truncating the fp32 product to its upper half is exact.
+template <int Q>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t codes, float scale) {
+  f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, Q);
+  const uint32_t lo = __float_as_uint(v.x * scale), hi = __float_as_uint(v.y * scale);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+__device__ __forceinline__ u32x4 fp4x8_to_bf16(uint32_t codes, float scale) {
+  return u32x4{fp4x2_to_bf16x2<0>(codes, scale), fp4x2_to_bf16x2<1>(codes, scale),
+               fp4x2_to_bf16x2<2>(codes, scale), fp4x2_to_bf16x2<3>(codes, scale)};
+}
+
+// OCP E4M3 byte -> fp32 (gfx950 converts the OCP "FN" encoding).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Coherent (device-scope, write-through) stores for data another workgroup reads in the
+// same launch; plain loads see them because every hand-off buffer is written once per
+// launch before any workgroup of the launch first reads it.
+__device__ __forceinline__ void st_coh_u32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u64(void* p, uint64_t v) {
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u128(void* p, u32x4 v) {
+  st_coh_u64(p, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+  st_coh_u64((char*)p + 8, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+}
+__device__ __forceinline__ uint32_t ld_coh_u32(const uint32_t* p) {
+  return __hip_atomic_load((uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
+
+// max / sum across the 4 lanes {l, l^16, l^32, l^48} (the four k-groups of an MFMA column)
+__device__ __forceinline__ float xgroup_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float xgroup_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// E4M3 code of RNE(v / 6) for v >= 0 (fp32), saturating at 448, by binary search over the
+// exact thresholds 6*mid (a midpoint of two neighbouring E4M3 values has <= 5 significant
+// bits, so 6*mid is exact in fp32).  A tie goes to the even code.
+__device__ __forceinline__ uint32_t e4m3_code_of_amax_over6(float v) {
+  // passed(c): v lies above the midpoint between codes c and c+1 (or on it with c odd)
+  int lo = 0, hi = 126;  // answer in [0, 126] = number of thresholds passed
+  while (lo < hi) {
+    int c = (lo + hi) >> 1;  // test threshold between c and c+1
+    float mid = 0.5f * (e4m3_to_f32(c) + e4m3_to_f32(c + 1));
+    float thr = 6.0f * mid;
+    bool passed = v > thr || (v == thr && (c & 1));
+    if (passed) lo = c + 1; else hi = c;
+  }
+  return (uint32_t)lo;
+}
+
+// E2M1 code of RNE(x / s) (s > 0 an E4M3 value), ties to the even code, saturating at 6;
+// thresholds mid*s have <= 7 significant bits and are exact in fp32.
+__device__ __forceinline__ uint32_t e2m1_code(float x, float s) {
+  const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  float ax = fabsf(x);
+  uint32_t c = 0;
+#pragma unroll
+  for (int i = 0; i < 7; ++i) {
+    float thr = mids[i] * s;
+    c += (ax > thr || (ax == thr && (i & 1))) ? 1u : 0u;
+  }
+  return (x < 0.f && c) ? (c | 8u) : c;
+}
+
+}  // namespace mk

@@ -1,0 +1,57 @@
+// Internal interface between the C ABI (mk_api.hip) and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MK_TS_EVENTS_DEV 16
+#define MK_ETIMEOUT_DEV (-6)
+#define MK_EBADTREE_DEV (-7)
+
+namespace mk {
+
+// Kernel arguments of one fused layer launch (passed by value).
+struct KArgs {
+  // shapes
+  int H, Hq, Hkv, d, P, E, topk, I, window, fmt, cap, T, ctx;
+  // launch geometry
+  int n_wg, attn_items, attn_chunks_per_head, attn_lo, ck;
+  int spin_limit, skip_wg;
+  // step inputs / outputs
+  const int32_t* parent;
+  const uint16_t *q_in, *h_in, *kc, *vc;
+  uint16_t *kn, *vn, *h_out, *q_next;
+  int32_t* topk_idx;
+  float *topk_gate, *router_logits, *attn_stats;
+  int32_t* hist;
+  const int32_t* prefetch;
+  int n_prefetch;
+  const float* bias;
+  // weights
+  const uint16_t *w_o, *w_pool, *w_router, *w_unpool, *w_qkv, *w1, *w2;
+  const uint8_t *w1_codes, *w1_scales, *w2_codes, *w2_scales;
+  const float *w1_ts, *w2_ts;
+  // workspace
+  int32_t* status;
+  uint32_t *epoch, *flags;
+  float *part_o, *part_ml;
+  uint16_t *attn, *h1, *xp;
+  float* logits;
+  uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes lo, codes hi, scale byte, 0
+  uint16_t* act_bf;     // bf16 intermediate [T*k][I]
+  uint16_t* y;
+  uint64_t* timestamps;
+};
+
+int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream);
+int set_layer_kernel_attrs(int lds_bytes);
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,
+                     const uint16_t* vn, int n, hipStream_t stream);
+int launch_route_topk(const uint16_t* x, const uint16_t* w, const float* bias, int T, int P, int E,
+                      int k, int32_t* idx, float* gate, float* logits, hipStream_t stream);
+int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8_t* codes,
+                      uint8_t* scales, float* ts, hipStream_t stream);
+
+}  // namespace mk

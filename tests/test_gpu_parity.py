@@ -1,0 +1,234 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import layer_persistent_amd as mk
+    from layer_persistent_amd import tensors as dt
+
+from gpu_util import (assert_close_bf16, assert_stats, check_routing, fp32_dot_bound, log)
+
+SMALL_NVFP4 = synth.LayerShape("small-tree-swa-nvfp4", 256, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
+SMALL_GQA = synth.LayerShape("small-tree-gqa2-global-bf16", 256, 8, 2, 64, 128, 32, 3, 64, 0, 200, 16, False)
+SMALL_T5 = synth.LayerShape("small-t5-window-nvfp4", 256, 4, 1, 128, 256, 16, 2, 96, 40, 60, 5, True)
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_nvfp4_pack_bit_exact():
+    g = np.random.default_rng(21)
+    for is_fp32 in (0, 1):
+        B, N, K = 3, 40, 96
+        w = (g.standard_normal((B, N, K)) * 0.02).astype(np.float32)
+        w[1, 3, :16] = 0
+        w[2, 5, 7] = 1.5
+        if is_fp32:
+            wd = torch.from_numpy(w).cuda()
+            ref_w = w.astype(np.float64)
+        else:
+            bits = synth.bf16_bits_from_f32(w)
+            wd = dt.dev_u16(bits)
+            ref_w = oracle.bf16_to_f64(bits)
+        codes = torch.empty((B, N, K // 2), dtype=torch.uint8, device="cuda")
+        scales = torch.empty((B, N, K // 16), dtype=torch.uint8, device="cuda")
+        ts = torch.empty(B, dtype=torch.float32, device="cuda")
+        mk.mk_nvfp4_pack(wd, is_fp32, B, N, K, codes, scales, ts)
+        torch.cuda.synchronize()
+        for b in range(B):
+            rc, rs, rt = oracle.nvfp4_pack(ref_w[b])
+            assert np.array_equal(codes[b].cpu().numpy(), rc)
+            assert np.array_equal(scales[b].cpu().numpy(), rs)
+            assert ts[b].item() == rt
+    log("  nvfp4 pack: bit-exact (bf16 and fp32 inputs)")
+
+
+def test_kv_append_bit_exact_and_untouched_rows():
+    g = np.random.default_rng(22)
+    cap, Hkv, d, pos, n = 64, 2, 64, 17, 9
+    kc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+    vc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+    kn = synth.normal_bf16(g, (n, Hkv, d), 1.0)
+    vn = synth.normal_bf16(g, (n, Hkv, d), 1.0)
+    K, V, KN, VN = (dt.dev_u16(x) for x in (kc, vc, kn, vn))
+    mk.mk_kv_append(K, V, cap, Hkv, d, pos, KN, VN, n)
+    torch.cuda.synchronize()
+    ek, ev = kc.copy(), vc.copy()
+    ek[pos:pos + n] = kn
+    ev[pos:pos + n] = vn
+    assert np.array_equal(dt.host_u16(K), ek) and np.array_equal(dt.host_u16(V), ev)
+    assert mk.mk_kv_append(K, V, cap, Hkv, d, cap - 2, KN, VN, n, check=False) == mk.MK_ECAPACITY
+
+
+def test_route_topk_standalone():
+    g = np.random.default_rng(23)
+    T, P, E, k = 16, 2048, 256, 8
+    x = synth.normal_bf16(g, (T, P), 1.0)
+    w = synth.normal_bf16(g, (E, P), 0.02)
+    bias = np.zeros((T, E), np.float32)
+    bias[2, 77] = 8.0
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    gate = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    mk.mk_route_topk(dt.dev_u16(x), dt.dev_u16(w), torch.from_numpy(bias).cuda(), T, P, E, k, idx, gate, logits)
+    torch.cuda.synchronize()
+    l64, _, _, _ = oracle.router(x, w, None, k)
+    gl = logits.cpu().numpy()
+    bound = fp32_dot_bound(x, w)
+    assert np.all(np.abs(gl - bias - l64) <= bound + 1e-6)
+    check_routing(gl, idx.cpu().numpy(), gate.cpu().numpy(), l64, bias, k, float(bound.max()))
+    assert idx[2, 0].item() == 77
+
+
+def _run(inp, timestamps=False, st=None, dw=None):
+    dw = dw or dt.upload_weights(inp)
+    st = st or dt.make_step(inp, timestamps=timestamps)
+    dt.run_step(dw, st)
+    out = dt.outputs(st)
+    return dw, st, out
+
+
+def _check_layer(inp, out, n_sample_pairs=None):
+    """Stage-local parity (each stage's oracle fed the GPU's own stage inputs) and end-to-end."""
+    sh = inp.shape
+    T, ctx = sh.T, sh.ctx
+    assert out["status"] == 0, mk.mk_strerror(out["status"])
+    attn, stats = oracle.attention(inp.q_in, inp.k_cache, inp.v_cache, inp.parent, ctx, sh.window,
+                                   sh.n_q_heads, sh.n_kv_heads, sh.head_dim)
+    assert_close_bf16("attn", out["attn"], attn)
+    assert_stats("attn stats m", out["stats"][..., 0], stats[..., 0])
+    assert_stats("attn stats l", out["stats"][..., 1], stats[..., 1])
+    assert_close_bf16("h1 (anchored on gpu attn)", out["h1"], oracle.dense(out["attn"], inp.w_o, inp.h_in))
+    assert_close_bf16("xp (anchored on gpu h1)", out["xp"], oracle.dense(out["h1"], inp.w_pool))
+    l64, _, _, _ = oracle.router(out["xp"], inp.w_router, None, sh.top_k)
+    bias = inp.router_bias
+    bound = fp32_dot_bound(out["xp"], inp.w_router)
+    dl = np.abs(out["logits"] - (bias if bias is not None else 0) - l64)
+    log(f"  logits: max |gpu - fp64| {dl.max():.3e} (rigorous fp32 bound {bound.max():.3e})")
+    assert np.all(dl <= bound + 1e-6)
+    check_routing(out["logits"], out["idx"], out["gate"], l64, bias, sh.top_k, float(bound.max()))
+    hist = np.bincount(out["idx"].reshape(-1), minlength=sh.n_experts)
+    assert np.array_equal(out["hist"], hist)
+    used = sorted(set(np.unique(out["idx"]).tolist()))
+    ex = oracle.pack_experts(inp, used)
+    y_ref, _ = oracle.moe(out["xp"], out["idx"], out["gate"].astype(np.float64), ex, sh.expert_inter)
+    assert_close_bf16("y (anchored on gpu xp, routing)", out["y"], y_ref)
+    assert_close_bf16("h_out (anchored on gpu y, h1)", out["h_out"], oracle.dense(out["y"], inp.w_unpool, out["h1"]))
+    qkv = oracle.bf16_to_f64(out["h_out"]) @ oracle.bf16_to_f64(inp.w_qkv_next).T
+    qd, kd = sh.n_q_heads * sh.head_dim, sh.n_kv_heads * sh.head_dim
+    assert_close_bf16("q_next (anchored on gpu h_out)", out["q_next"], oracle.bf16_round(qkv[:, :qd]))
+    kn = out["k_cache_next"].reshape(sh.kv_capacity, -1)
+    vn = out["v_cache_next"].reshape(sh.kv_capacity, -1)
+    assert_close_bf16("k_new (anchored)", kn[ctx:ctx + T], oracle.bf16_round(qkv[:, qd:qd + kd]))
+    assert_close_bf16("v_new (anchored)", vn[ctx:ctx + T], oracle.bf16_round(qkv[:, qd + kd:]))
+    # every other row of the next layer's cache is untouched, bit for bit
+    k0 = inp.k_cache_next.reshape(sh.kv_capacity, -1)
+    v0 = inp.v_cache_next.reshape(sh.kv_capacity, -1)
+    assert np.array_equal(kn[:ctx], k0[:ctx]) and np.array_equal(kn[ctx + T:], k0[ctx + T:])
+    assert np.array_equal(vn[:ctx], v0[:ctx]) and np.array_equal(vn[ctx + T:], v0[ctx + T:])
+    # end to end, no anchoring
+    ref = oracle.layer_step_auto(inp)
+    assert_close_bf16("h_out end-to-end", out["h_out"], ref["h_out"])
+    assert_close_bf16("q_next end-to-end", out["q_next"], ref["q_next"])
+    assert_close_bf16("k_new end-to-end", kn[ctx:ctx + T], ref["k_new"].reshape(T, -1))
+    assert_close_bf16("v_new end-to-end", vn[ctx:ctx + T], ref["v_new"].reshape(T, -1))
+
+
+@pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83)])
+def test_layer_small_shapes(shape, cfg_id):
+    log(f"[layer parity] {shape.name}")
+    inp = synth.make_layer_inputs(shape, cfg_id)
+    _, _, out = _run(inp)
+    _check_layer(inp, out)
+
+
+@pytest.fixture(scope="module")
+def cfg2_inputs():
+    return synth.make_layer_inputs(synth.CFG2, 2)
+
+
+def test_layer_cfg2_full_size(cfg2_inputs):
+    log("[layer parity] cfg2 full size: SWA-2048 over ctx 8192, 16-token tree, NVFP4 experts")
+    dw, st, out = _run(cfg2_inputs)
+    _check_layer(cfg2_inputs, out)
+    log(f"  distinct experts: {len(np.unique(out['idx']))}")
+
+
+def test_layer_cfg3_full_size():
+    log("[layer parity] cfg3 full size: global over ctx 32768, Zipf routing")
+    inp = synth.make_layer_inputs(synth.CFG3, 3)
+    _, _, out = _run(inp)
+    _check_layer(inp, out)
+    log(f"  distinct experts: {len(np.unique(out['idx']))}")
+
+
+def test_deterministic_and_timing_build_identical():
+    inp = synth.make_layer_inputs(SMALL_NVFP4, 84)
+    dw = dt.upload_weights(inp)
+    outs = []
+    for ts in (False, False, True):
+        st = dt.make_step(inp, timestamps=ts)
+        dt.run_step(dw, st)
+        outs.append(dt.outputs(st))
+    for key in ("h_out", "q_next", "k_cache_next", "v_cache_next", "idx", "gate", "logits", "stats", "y", "xp"):
+        assert np.array_equal(outs[0][key], outs[1][key]), key
+        assert np.array_equal(outs[0][key], outs[2][key]), key
+
+
+def test_repeated_steps_on_one_workspace():
+    """Successive launches on one workspace (as layer after layer / step after step)."""
+    dw = None
+    st = None
+    for step in range(4):
+        inp = synth.make_layer_inputs(SMALL_NVFP4, 85, step=step)
+        if dw is None:
+            dw = dt.upload_weights(inp)
+            st = dt.make_step(inp)
+        else:
+            # refresh the step inputs in place, keep the workspace
+            st.q_in.copy_(dt.dev_u16(inp.q_in)); st.h_in.copy_(dt.dev_u16(inp.h_in))
+            st.k_cache.copy_(dt.dev_u16(inp.k_cache)); st.v_cache.copy_(dt.dev_u16(inp.v_cache))
+            st.parent.copy_(torch.from_numpy(inp.parent).cuda())
+            st.k_next.copy_(dt.dev_u16(inp.k_cache_next)); st.v_next.copy_(dt.dev_u16(inp.v_cache_next))
+            st.hist.zero_()
+        dt.run_step(dw, st)
+        out = dt.outputs(st)
+        ref = oracle.layer_step_auto(inp)
+        assert out["status"] == 0
+        assert_close_bf16(f"step {step} h_out", out["h_out"], ref["h_out"])
+        assert_close_bf16(f"step {step} q_next", out["q_next"], ref["q_next"])
+
+
+def test_bad_tree_reports_status():
+    inp = synth.make_layer_inputs(SMALL_NVFP4, 86)
+    inp.parent[5] = 9   # parent after child
+    dw = dt.upload_weights(inp)
+    st = dt.make_step(inp)
+    dt.run_step(dw, st)
+    assert mk.mk_read_status(st.workspace) == mk.MK_EBADTREE
+
+
+def test_stalled_workgroup_times_out_instead_of_hanging():
+    """A workgroup that never signals (host-set test hook) makes every bounded wait expire."""
+    inp = synth.make_layer_inputs(SMALL_NVFP4, 87)
+    dw = dt.upload_weights(inp)
+    st = dt.make_step(inp)
+    dt.run_step(dw, st, spin_limit=2000, skip_wg=5)
+    assert mk.mk_read_status(st.workspace) == mk.MK_ETIMEOUT
+    # after re-initialising the workspace a normal launch works
+    mk.mk_workspace_init(st.workspace, st.workspace.numel())
+    dt.run_step(dw, st)
+    out = dt.outputs(st)
+    assert out["status"] == 0
+    assert_close_bf16("h_out after recovery", out["h_out"], oracle.layer_step_auto(inp)["h_out"])
