@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused decode-layer step on one MI355X.
+
+One "step" is one launch of mk_layer_step: a whole decoder layer (16-token tree verify) of
+the sliding-window-2048 layer at one GPU's shard shape over a KV context of 8192 rows, NVFP4
+experts -- the workload the headline metric is quoted on.  Inputs are seeded synthetic
+tensors already resident in HBM.  To keep the 256 MB MALL from serving a layer's weights
+from an earlier launch, launches rotate over R full replicas of weights, KV and step inputs
+(R * ~120 MB read per launch between two uses of a replica).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(shape, n_active: int) -> dict:
+    """Compulsory HBM bytes of one layer launch: weights read once, KV rows the tree can see,
+    the step's activations in and out, the KV rows written."""
+    H, Hq, Hkv, d, P, E, I, T = (shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                                 shape.pooled, shape.n_experts, shape.expert_inter, shape.T)
+    lo = max(0, shape.ctx - shape.window + 1) if shape.window > 0 else 0
+    kv = (shape.ctx - lo + T) * Hkv * d * 2 * 2
+    dense = 2 * (H * Hq * d + P * H + E * P + H * P + shape.qkv_out * H)
+    per_expert = (2 * I * P // 2 + 2 * I * P // 16) + (P * I // 2 + P * I // 16)
+    experts = n_active * per_expert
+    acts = T * (2 * H + 2 * Hq * d) * 2
+    kv_write = T * 2 * Hkv * d * 2
+    return dict(kv=kv, dense=dense, experts=experts, per_expert=per_expert, acts=acts, kv_write=kv_write,
+                total=kv + dense + experts + acts + kv_write)
+
+
+def cpu_baseline(inp) -> dict:
+    """The oracle (fp64 NumPy) on the host: one full layer step of the same workload.  Expert
+    packing is weight preparation (the GPU side does it with mk_nvfp4_pack outside the timed
+    region) and is excluded here too."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    t0 = time.time()
+    ref0 = oracle.layer_step_auto(inp)            # routing + packing of the used experts
+    used = sorted(set(np.unique(ref0["idx"]).tolist()))
+    ex = oracle.pack_experts(inp, used)
+    prep = time.time() - t0
+    t1 = time.perf_counter()
+    oracle.layer_step(inp, ex)
+    dt = time.perf_counter() - t1
+    cores = len(os.sched_getaffinity(0))
+    log(f"cpu baseline: oracle layer step {dt:.2f} s (prep {prep:.1f} s), {cores} cores, BLAS threads {blas_threads}")
+    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": int(max(1, min(cores, blas_threads))),
+            "kind": "oracle",
+            "sample": "one full layer step of the same workload (SWA-2048 layer, ctx 8192, 16-token tree, "
+                      f"{len(used)} active NVFP4 experts), fp64 NumPy; expert packing excluded; "
+                      f"{cores} host cores visible, {blas_threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--config", type=int, default=2, help="workload id (2: SWA ctx 8192, 3: global ctx 32768)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-phases", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (the layer kernel needs no collectives); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import layer_persistent_amd as mk
+    from layer_persistent_amd import tensors as dt
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    shape = synth.CONFIGS[args.config]
+    log(f"workload {shape.name}: generating inputs")
+    t0 = time.time()
+    inp = synth.make_layer_inputs(shape, args.config)
+    log(f"  inputs ready in {time.time() - t0:.1f} s; uploading + packing {args.replicas} replicas")
+    reps = []
+    for r in range(args.replicas):
+        dw = dt.upload_weights(inp)
+        st = dt.make_step(inp)
+        reps.append((dw, st))
+    ts_step = dt.make_step(inp, timestamps=True)
+    stream = torch.cuda.current_stream()
+    lib = mk.lib()
+    import ctypes
+    # argument structs built once, kept alive for the whole run
+    structs = [(st.cfg, dw.struct(), st.struct()) for dw, st in reps]
+    sp = stream.cuda_stream
+
+    def launch(i):
+        c, w, io = structs[i % len(structs)]
+        rc = lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), sp)
+        if rc != 0:
+            raise RuntimeError(f"mk_layer_step: {mk.mk_strerror(rc)}")
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    for _, st in reps:
+        s = mk.mk_read_status(st.workspace)
+        if s != 0:
+            raise RuntimeError(f"in-kernel status {mk.mk_strerror(s)}")
+    out = dt.outputs(reps[0][1])
+    n_active = int(len(np.unique(out["idx"])))
+    ab = algorithmic_bytes(shape, n_active)
+
+    # timed region: K launches, an event pair around each on the launch stream
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    wall0 = torch.cuda.Event(enable_timing=True)
+    wall1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(args.warmup + i)
+        ev[i][1].record(stream)
+    wall1.record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])     # us per launch
+    wall_us = wall0.elapsed_time(wall1) * 1000.0
+    ms_per_step = wall_us / K / 1000.0
+    kern_us = float(np.mean(per))
+    med_us = float(np.median(per))
+    log(f"per-launch us: mean {kern_us:.2f} median {med_us:.2f} p10 {np.percentile(per, 10):.2f} "
+        f"p90 {np.percentile(per, 90):.2f}; wall per step {ms_per_step * 1000:.2f} us")
+    achieved = ab["total"] / (kern_us * 1e-6) / 1e9
+    log(f"algorithmic bytes {ab['total'] / 1e6:.2f} MB ({n_active} active experts) -> {achieved:.0f} GB/s "
+        f"= {achieved / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f} GB/s")
+
+    # achievable streaming-read bandwidth in this run (1 GiB sum, cold)
+    big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    big.fill_(1.0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    big.sum()
+    e0.record(stream)
+    for _ in range(5):
+        big.sum()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    read_gbs = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big
+    log(f"achievable streaming read (torch sum over 1 GiB): {read_gbs:.0f} GB/s")
+
+    phases = None
+    if not args.no_phases:
+        dw0 = reps[0][0]
+        for _ in range(3):
+            dt.run_step(dw0, ts_step)
+        torch.cuda.synchronize()
+        tsv = ts_step.timestamps.cpu().numpy().astype(np.int64)
+        names = ["attn", "merge", "oproj", "pool", "router", "route", "gemm1", "gemm2", "unpool", "qkv"]
+        t_start = tsv[:, 0].min()
+        ends = [(tsv[:, j + 1].max() - t_start) / 100.0 for j in range(len(names))]   # 100 MHz ticks -> us
+        phases = {n: round(e, 2) for n, e in zip(names, ends)}
+        log("phase end times (us after the first workgroup starts, timestamp build): " + json.dumps(phases))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp)
+
+    res = {
+        "metric": "us per fused decoder layer (16-token verify, 1 GPU)",
+        "value": round(kern_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": shape.name, "T": shape.T, "ctx": shape.ctx, "window": shape.window,
+                   "hidden": shape.hidden, "q_heads": shape.n_q_heads, "kv_heads": shape.n_kv_heads,
+                   "head_dim": shape.head_dim, "pooled": shape.pooled, "experts": shape.n_experts,
+                   "top_k": shape.top_k, "expert_inter": shape.expert_inter, "expert_format": "nvfp4",
+                   "active_experts": n_active, "replicas": args.replicas, "launches_per_layer": 1},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": ab["total"], "achievable_read_gbs": round(read_gbs, 1)},
+        "median_us": round(med_us, 2),
+        "p10_us": round(float(np.percentile(per, 10)), 2),
+        "p90_us": round(float(np.percentile(per, 90)), 2),
+        "phases_end_us": phases,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
