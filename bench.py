@@ -174,10 +174,43 @@ def main():
             dt.run_step(dw0, ts_step)
         torch.cuda.synchronize()
         tsv = ts_step.timestamps.cpu().numpy().astype(np.int64)
-        names = ["attn", "merge", "oproj", "pool", "router", "route", "gemm1", "gemm2", "unpool", "qkv"]
-        t_start = tsv[:, 0].min()
-        ends = [(tsv[:, j + 1].max() - t_start) / 100.0 for j in range(len(names))]   # 100 MHz ticks -> us
-        phases = {n: round(e, 2) for n, e in zip(names, ends)}
+        # events: 0 start, 1 setup done, 2p work of phase p done, 2p+1 its grid hand-off done
+        # (p = 1 attn, 2 merge, 3 oproj, 4 pool, 5 router, 6 gemm1, 7 gemm2, 8 unpool),
+        # 18 routing tables built, 19 qkv done; ticks of the 100 MHz wall clock
+        t0 = tsv[:, 0].min()
+        rel = lambda ev: float((tsv[:, ev].max() - t0) / 100.0)
+        names = ["attn", "merge", "oproj", "pool", "router", "gemm1", "gemm2", "unpool"]
+        phases = {"setup": round(rel(1), 2)}
+        for p, n in enumerate(names, start=1):
+            phases[n + "_work"] = round(rel(2 * p), 2)
+            phases[n + "_sync"] = round(rel(2 * p + 1), 2)
+        phases["route_tables"] = round(rel(18), 2)
+        phases["qkv_end"] = round(rel(19), 2)
+        for p, n in enumerate(names, start=1):
+            phases[n + "_poll_done"] = round(rel(20 + p), 2)
+            phases[n + "_loads_issued"] = round(rel(28 + p), 2)
+        starts = (tsv[:, 0] - t0) / 100.0
+        phases["wg_start_spread"] = round(float(starts.max()), 2)
+        items = tsv[:, 37] > 0
+        if items.any():
+            phases["attn_stage_us_max"] = round(float(((tsv[items, 37] - tsv[items, 1]) / 100.0).max()), 2)
+            phases["attn_compute_us_max"] = round(float(((tsv[items, 38] - tsv[items, 37]) / 100.0).max()), 2)
+            phases["attn_setup_end_max"] = round(float(((tsv[items, 1] - t0) / 100.0).max()), 2)
+            d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
+            phases["attn_q_arrived_after_stage"] = d(39, 37, items)
+            phases["attn_scores_after_q"] = d(40, 39, items)
+            phases["attn_pv_after_scores"] = d(41, 40, items)
+            phases["attn_stores_after_pv"] = d(38, 41, items)
+        g2 = tsv[:, 42] > 0
+        if g2.any():
+            d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
+            phases["gemm2_staged_after_sync"] = d(42, 13, g2)
+            phases["gemm2_experts_after_staged"] = d(43, 42, g2)
+        g1 = tsv[:, 45] > 0
+        if g1.any():
+            d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
+            phases["gemm1_xs_after_routes"] = d(44, 18, g1)
+            phases["gemm1_batch1_after_xs"] = d(45, 44, g1)
         log("phase end times (us after the first workgroup starts, timestamp build): " + json.dumps(phases))
 
     cpu = None

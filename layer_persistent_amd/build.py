@@ -24,7 +24,8 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into layer_persistent_amd/libmk.so; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", CSRC, "-o", tmp, *srcs]
+    extra = os.environ.get("MK_HIPCC_DEFINES", "").split()   # e.g. "-DMK_SYNC_MODE=0" for experiments
+    cmd = [HIPCC, *FLAGS, *extra, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

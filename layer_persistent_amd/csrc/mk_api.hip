@@ -11,7 +11,6 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kLayerLds = 96 * 1024;       // > half of the 160 KB LDS: one workgroup per CU
 constexpr int kChunkKeys = 128;            // KV rows per attention work item
 constexpr int kDefaultSpin = 1 << 20;      // polls per wait before MK_ETIMEOUT
 
@@ -26,10 +25,10 @@ int device_cus(int* n_cu) {
   if (!g_cu[dev]) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return MK_EHIP;
-    g_cu[dev] = n;
+    g_cu[dev] = n < 256 ? n : 256;   // the kernel's flag polling covers at most 256 workgroups
   }
   if (!g_attr[dev]) {
-    if (mk::set_layer_kernel_attrs(kLayerLds)) return MK_EHIP;
+    if (mk::set_layer_kernel_attrs(mk::layer_lds_bytes())) return MK_EHIP;
     g_attr[dev] = true;
   }
   *n_cu = g_cu[dev];
@@ -44,14 +43,15 @@ int check_cfg(const mk_layer_cfg* c, int T) {
   if (!c) return MK_EINVAL;
   if (c->expert_fmt != MK_W_BF16 && c->expert_fmt != MK_W_NVFP4) return MK_EINVAL;
   if (T < 1 || T > 16) return MK_ESHAPE;
-  if (c->hidden <= 0 || c->hidden % 128) return MK_ESHAPE;
-  if (c->pooled <= 0 || c->pooled % 128) return MK_ESHAPE;
+  if (c->hidden <= 0 || c->hidden % 128 || c->hidden > 4096) return MK_ESHAPE;
+  if (c->pooled <= 0 || c->pooled % 128 || c->pooled > 2048) return MK_ESHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return MK_ESHAPE;
   if (c->n_kv_heads <= 0 || c->n_q_heads <= 0 || c->n_q_heads % c->n_kv_heads) return MK_ESHAPE;
   if (T * (c->n_q_heads / c->n_kv_heads) > 128) return MK_ESHAPE;
+  if (c->n_q_heads * c->head_dim > 1024) return MK_ESHAPE;
   if (c->n_experts <= 0 || c->n_experts > 256 || c->n_experts % 16) return MK_ESHAPE;
   if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts) return MK_ESHAPE;
-  if (c->expert_inter <= 0 || c->expert_inter % 32) return MK_ESHAPE;
+  if (c->expert_inter <= 0 || c->expert_inter % 32 || c->expert_inter > 256) return MK_ESHAPE;
   if (c->window < 0) return MK_ESHAPE;
   if (c->kv_capacity <= 0) return MK_ESHAPE;
   return MK_OK;
@@ -219,7 +219,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.act_bf = (uint16_t*)(ws + L.act);
   a.y = (uint16_t*)(ws + L.y);
   a.timestamps = io->timestamps;
-  return mk::launch_layer(a, kLayerLds, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+  return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
 }
 
 int mk_kv_append(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int head_dim, int pos,

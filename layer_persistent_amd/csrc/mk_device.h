@@ -79,6 +79,23 @@ __device__ __forceinline__ float xgroup_sum(float v) {
   return v + __shfl_xor(v, 32);
 }
 
+// Maximum over the 64 lanes of a wave (all lanes active): DPP exchanges inside each row of
+// 16 lanes (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four row values.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));    // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));    // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));   // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));   // row_mirror
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
+}
+
 // E4M3 code of RNE(v / 6) for v >= 0 (fp32), saturating at 448, by binary search over the
 // exact thresholds 6*mid (a midpoint of two neighbouring E4M3 values has <= 5 significant
 // bits, so 6*mid is exact in fp32).  A tie goes to the even code.

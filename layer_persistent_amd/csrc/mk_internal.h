@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define MK_TS_EVENTS_DEV 16
+#define MK_TS_EVENTS_DEV 48
 #define MK_ETIMEOUT_DEV (-6)
 #define MK_EBADTREE_DEV (-7)
 
@@ -44,6 +44,7 @@ struct KArgs {
 };
 
 int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream);
+int layer_lds_bytes();
 int set_layer_kernel_attrs(int lds_bytes);
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);

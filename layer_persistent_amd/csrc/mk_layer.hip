@@ -8,24 +8,32 @@
 // device-side flags, the role the pages give to device-side counters (alphasignal.ai, "A
 // 12-warp pipeline takes over scheduling").
 //
-// Phases (each ends in a grid-wide hand-off):
-//   ATTN   tree-masked GQA attention over KV chunks -> per-chunk partial (m, l, o)
-//   MERGE  merge partials per (token, head) -> attn (bf16), stats (m, l)
-//   OPROJ  h1 = bf16(h_in + attn Wo^T)
-//   POOL   xp = bf16(h1 Wp^T)
-//   ROUTER logits = xp Wr^T (+ bias), fp32
-//   GEMM1  every workgroup: top-k, gates and dispatch from the logits (identical everywhere);
-//          then (expert, 16-column block) tasks: u = xp W1^T ts1, a = silu(u_gate) u_up,
-//          NVFP4 requantisation of a (bf16 for bf16 experts)
-//   GEMM2  per 8-column slice of P: every active expert's down projection, then the combine
-//          y = bf16(sum over the token's slots, in slot order, of gate * out)
-//   UNPOOL h_out = bf16(h1 + y Wu^T)
-//   QKV    [q; k; v] = h_out Wqkv^T -> q_next, KV rows of the next layer
+// Workgroup = 9 waves.  Waves 0..7 compute (MFMA, attention, routing, experts).  Wave 8 is
+// the control wave: it stores each dense phase's output tile, signals this workgroup's flag
+// and polls everyone else's.  Because compute waves never wait for their own global stores
+// at a hand-off, the weight loads they issue for a later phase stay in flight across the
+// grid-wide wait -- the pages' "weights do not depend on the previous output, so fetch the
+// next operation's weights while the current one runs" (alphasignal.ai, "Four mechanisms
+// keep work moving"), with the register file as the staging buffer.
 //
-// Cross-workgroup hand-off: a workgroup writes its outputs with device-coherent stores, waits
-// for them to complete, then stores its per-phase flag; consumers poll all flags with
-// coherent loads and read the data with ordinary loads.  Hand-off buffers are written once
-// per launch, before any workgroup of that launch reads them.
+// Phases (each ends in a grid-wide hand-off):
+//   1 ATTN   tree-masked GQA attention over KV chunks -> per-chunk partial (m, l, o)
+//   2 MERGE  merge partials per (token, head) -> attn (bf16), stats (m, l)
+//   3 OPROJ  h1 = bf16(h_in + attn Wo^T)
+//   4 POOL   xp = bf16(h1 Wp^T)
+//   5 ROUTER logits = xp Wr^T (+ bias), fp32
+//   6 GEMM1  every workgroup: top-k, gates and dispatch from the logits (identical everywhere);
+//            then (expert, 16-column block) tasks: u = xp W1^T ts1, a = silu(u_gate) u_up,
+//            NVFP4 requantisation of a (bf16 for bf16 experts)
+//   7 GEMM2  per 8-column slice of P: every active expert's down projection, then the combine
+//            y = bf16(sum over the token's slots, in slot order, of gate * out)
+//   8 UNPOOL h_out = bf16(h1 + y Wu^T)
+//     QKV    [q; k; v] = h_out Wqkv^T -> q_next, KV rows of the next layer
+//
+// Cross-workgroup hand-off: data is written with device-coherent (write-through) stores; the
+// writer waits for them, then stores its per-phase flag; readers poll all flags with coherent
+// loads and then read the data with ordinary loads.  Each hand-off buffer is written once per
+// launch before any workgroup of the launch first reads it, so no cache can hold a stale copy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -34,55 +42,47 @@
 
 namespace mk {
 
-// ------------------------------------------------------------------ sync
+constexpr int kThreads = 576;      // 8 compute waves + 1 control wave
+constexpr int kCompute = 512;
+constexpr int kCtl = 512;          // first thread of the control wave
 
-struct Sync {
-  uint32_t* flags;     // [n_wg] x 16 dwords
-  int32_t* status;
-  uint32_t base;       // epoch * 64
-  int spin_limit;
-  int skip_wg;
-  bool dead;           // a wait expired or the launch aborted: skip the remaining work
-};
+// per-wave MFMA k-steps (32 k each) held in registers for each dense phase
+constexpr int MAXS_O = 4;          // o-proj   K = Hq*d <= 1024
+constexpr int MAXS_P = 16;         // pooler   K = H    <= 4096
+constexpr int MAXS_R = 8;          // router   K = P    <= 2048
+constexpr int MAXS_U = 8;          // unpooler K = P    <= 2048
+constexpr int MAXS_Q = 16;         // qkv      K = H    <= 4096
+constexpr int MAXT = 4;            // GEMM1 tasks per batch
+#ifndef MK_SYNC_MODE
+#define MK_SYNC_MODE 0
+#endif
+constexpr int SYNC_MODE = MK_SYNC_MODE;   // grid hand-off: 1 sharded counters, 0 per-workgroup flags
 
-// Grid-wide hand-off after `phase` (1-based).  Every thread of every workgroup must call it.
-__device__ __noinline__ void grid_sync(Sync& s, int phase) {
-  // each thread's coherent stores must be complete before its workgroup signals
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const uint32_t target = s.base + (uint32_t)phase;
-  if (threadIdx.x == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
-  __shared__ int dead_flag;
-  if (threadIdx.x < kWave) {
-    bool dead = s.dead;
-    int polls = 0;
-    while (!dead) {
-      bool ok = true;
-      for (uint32_t w = threadIdx.x; w < gridDim.x; w += kWave) ok &= (int32_t)(ld_coh_u32(s.flags + w * 16) - target) >= 0;
-      if (__all(ok)) break;
-      if (++polls >= s.spin_limit) {
-        if (threadIdx.x == 0) {
-          __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        dead = true;
-      } else if ((polls & 63) == 0) {
-        dead = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
-      }
-    }
-    if (threadIdx.x == 0) dead_flag = dead;
-  }
-  __syncthreads();
-  s.dead = dead_flag;
+// dynamic LDS layout (byte offsets; phases reuse the same space)
+constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
+constexpr int G1_XS_BYTES = 16 * (2048 + 8) * 2;       // xp rows for GEMM1
+constexpr int G1_RED_FLOATS = MAXT * 2 * 8 * 16 * 17;  // per-task partial gate/up tiles
+constexpr int LDS_BYTES = 144 * 1024;                  // >= every phase's use (GEMM1: 136.5 KB)
+static_assert(G1_XS_BYTES + G1_RED_FLOATS * 4 + MAXT * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
+
+__device__ __forceinline__ void wg_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Timestamp event `ev` of this workgroup, written by thread `who` (timing build only).
+// Events: 0 start, 1 setup done, 2p work of phase p done, 2p+1 its hand-off done (p = 1..8),
+// 18 routing tables built, 19 end, 20+p control wave's wait for phase p done, 28+p compute
+// waves' loads for a later phase issued, 37 / 38 first attention item staged / computed.
 template <bool TS>
-__device__ __forceinline__ void stamp(uint64_t* ts, int ev) {
+__device__ __forceinline__ void stamp(uint64_t* ts, int ev, int who = kCtl) {
   if constexpr (TS) {
-    if (threadIdx.x == 0) ts[blockIdx.x * MK_TS_EVENTS_DEV + ev] = wall_clock64();
+    if ((int)threadIdx.x == who) ts[blockIdx.x * MK_TS_EVENTS_DEV + ev] = wall_clock64();
   }
 }
 
-// ------------------------------------------------------------------ shared layout
+// ------------------------------------------------------------------ shared state
 
 struct Route {            // routing tables, identical in every workgroup
   int32_t idx[16 * 8];    // [T][k]
@@ -94,6 +94,7 @@ struct Route {            // routing tables, identical in every workgroup
   int32_t pair_list[128]; // pair id t*k + slot, grouped by expert (ascending), then by pair id
   int32_t expert_cnt[256];
   int32_t expert_first[256];
+  uint32_t mask[256 * 4]; // per expert: bit p set when pair p routes there
 };
 
 struct Tree {
@@ -102,41 +103,196 @@ struct Tree {
   int32_t bad;
 };
 
-constexpr int kRedBytes = 8 * 16 * 17 * 4 * 2;   // two 16x16 fp32 tiles per wave, padded
-constexpr int kScratchOff = 0;
+struct Ctl {              // control-wave state shared through LDS
+  int32_t dead;           // a wait expired or the launch aborted
+};
+
+// ------------------------------------------------------------------ grid hand-off
+
+struct Sync {
+  uint32_t* flags;        // counters / flags of the grid hand-off (see ctl_signal_wait)
+  int32_t* status;
+  uint32_t base;          // epoch * 64
+  int spin_limit;
+  int skip_wg;
+};
+
+// Control wave only: signal this workgroup's flag for `phase`, then wait until every
+// workgroup's flag has reached it.  Four polls stay in flight so that a flag landing is
+// seen about a quarter of a round trip later.  Returns false when the wait expired or the
+// launch was aborted (status word set).
+__device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead) {
+  const int lane = threadIdx.x & 63;
+  const int n = gridDim.x;
+  __builtin_amdgcn_s_waitcnt(0);           // this wave's hand-off stores are complete
+  if constexpr (SYNC_MODE == 1) {
+    // Eight counters, one per XCD group (workgroup w adds to counter w % 8, 256 bytes
+    // apart); each add is fire-and-forget.  Counter j has grown by (epoch*8 + phase) * n_j
+    // once every member of group j has signalled `phase`, n_j = members of group j.
+    if (lane == 0 && (int)blockIdx.x != s.skip_wg)
+      __hip_atomic_fetch_add(s.flags + (blockIdx.x & 7) * 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dead) return false;
+    const int j = lane & 7;
+    const uint32_t members = (uint32_t)((n - j + 7) / 8);
+    const uint32_t target = (s.base / 64u * 8u + (uint32_t)phase) * members;
+    const uint32_t* f = s.flags + j * 64;
+    auto poll = [&]() -> uint32_t { return lane < 8 ? ld_coh_u32(f) : target; };
+    auto done = [&](uint32_t x) { return __all((int32_t)(x - target) >= 0); };
+    uint32_t a = poll(), b = poll();
+    int polls = 0;
+    while (true) {
+      if (done(a)) break;
+      a = poll();
+      if (done(b)) break;
+      b = poll();
+      polls += 2;
+      if (polls >= s.spin_limit) {
+        if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        return false;
+      }
+      if (polls > 16) __builtin_amdgcn_s_sleep(2);
+      if ((polls & 63) == 0) {
+        const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
+      }
+    }
+  } else {
+    // One flag per workgroup, 64 bytes apart; a poll reads all of them (4 loads per lane).
+    const uint32_t target = s.base + (uint32_t)phase;
+    if (lane == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
+    if (dead) return false;
+    const uint32_t* f = s.flags + lane * 16;
+    auto poll = [&]() -> u32x4 {
+      u32x4 x = {target, target, target, target};
+      if (lane < n) x[0] = ld_coh_u32(f);
+      if (lane + 64 < n) x[1] = ld_coh_u32(f + 64 * 16);
+      if (lane + 128 < n) x[2] = ld_coh_u32(f + 128 * 16);
+      if (lane + 192 < n) x[3] = ld_coh_u32(f + 192 * 16);
+      return x;
+    };
+    auto done = [&](u32x4 x) {
+      return __all((int32_t)(x[0] - target) >= 0 && (int32_t)(x[1] - target) >= 0 &&
+                   (int32_t)(x[2] - target) >= 0 && (int32_t)(x[3] - target) >= 0);
+    };
+    u32x4 a = poll(), b = poll();
+    int polls = 0;
+    while (true) {
+      if (done(a)) break;
+      a = poll();
+      if (done(b)) break;
+      b = poll();
+      polls += 2;
+      if (polls >= s.spin_limit) {
+        if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0);
+        return false;
+      }
+      if (polls > 8) __builtin_amdgcn_s_sleep(4);
+      if ((polls & 63) == 0) {
+        const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  return true;
+}
 
 // ------------------------------------------------------------------ dense tiles
 
-// Partial tile of C[16][16] = x[rows][K] . W[n0 .. n0+16][K]^T over this wave's k-steps.
-// Rows m >= T are zero.  K multiple of 32; the WG's 8 waves take k-steps round-robin.
-__device__ __forceinline__ f32x4 dense_partial(const uint16_t* __restrict__ x, int T, int K,
-                                               const uint16_t* __restrict__ W, int n0) {
+// Weight fragments of one wave for one 16-column tile of W [N][K]: MFMA k-steps
+// s = wave + 8j (j < MAXS) hold W[n0 + l%16][32 s + 8 (l/16) .. +8].
+template <int MAXS>
+struct WFrag {
+  u32x4 v[MAXS > 0 ? MAXS : 1];
+};
+
+template <int MAXS>
+__device__ __forceinline__ void wfrag_load(WFrag<MAXS>& f, const uint16_t* __restrict__ W, int K, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, g = lane >> 4;
-  const uint16_t* wrow = W + (size_t)(n0 + nl) * K + g * 8;
-  const uint16_t* xrow = x + (size_t)nl * K + g * 8;
-  const bool xv = nl < T;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + (lane >> 4) * 8;
   const int ksteps = K >> 5;
-  int s = wave;
-  for (; s + 24 < ksteps; s += 32) {
-    u32x4 b[4], a[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = ld16(wrow + (s + 8 * j) * 32);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) a[j] = xv ? ld16(xrow + (s + 8 * j) * 32) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma_bf16(a[j], b[j], acc);
+  for (int j = 0; j < MAXS; ++j) {
+    const int s = wave + 8 * j;
+    f.v[j] = s < ksteps ? ld16(row + s * 32) : u32x4{0, 0, 0, 0};
   }
-  for (; s < ksteps; s += 8) {
-    u32x4 b = ld16(wrow + s * 32);
-    u32x4 a = xv ? ld16(xrow + s * 32) : u32x4{0, 0, 0, 0};
-    acc = mfma_bf16(a, b, acc);
+}
+
+// Pull a tile's weight rows into the cache hierarchy without holding them in registers: each
+// lane reads one dword of a different 128-byte line (a 16 x K tile is 16 * 2K bytes, covered
+// by 16 * 2K / 8K loads per wave over the 8 compute waves).  The values are folded into one
+// word that the caller keeps alive, so the loads are not dropped.
+template <int NT>
+__device__ __forceinline__ uint32_t touch_tile(const uint16_t* __restrict__ W, int K, int n0) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const char* base = (const char*)(W + (size_t)n0 * K);
+  const int lines = 16 * K * 2 / 128;
+  uint32_t v[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int l = (wave + 8 * j) * 64 + lane;
+    v[j] = l < lines ? *(const uint32_t*)(base + (size_t)l * 128) : 0u;
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) x ^= v[j];
+  return x;
+}
+
+// This wave's partial of the tile: x [rows][K] (rows >= T are zero) times the fragments.
+template <int MAXS>
+__device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t* __restrict__ x, int T, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
+  const bool xv = nl < T;
+  const int ksteps = K >> 5;
+  constexpr int XB = MAXS < 8 ? MAXS : 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j0 = 0; j0 < MAXS; j0 += XB) {
+    u32x4 xa[XB];
+#pragma unroll
+    for (int j = 0; j < XB; ++j) {
+      const int s = wave + 8 * (j0 + j);
+      xa[j] = (xv && s < ksteps) ? ld16(xrow + s * 32) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < XB; ++j)
+      if (wave + 8 * (j0 + j) < ksteps) acc = mfma_bf16(xa[j], f.v[j0 + j], acc);
   }
   return acc;
 }
 
-// Store a wave's partial tile into LDS red[wave][row][col] (row stride 17 floats).
+// This wave's partial of a tile whose weights are read now (typically from L2 after a touch
+// prefetch): weights and x of 8 k-steps are loaded together, then multiplied.
+__device__ __forceinline__ f32x4 stream_mma(const uint16_t* __restrict__ W, int K, int n0,
+                                           const uint16_t* __restrict__ x, int T) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const uint16_t* wrow = W + (size_t)(n0 + nl) * K + (lane >> 4) * 8;
+  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
+  const bool xv = nl < T;
+  const int ksteps = K >> 5;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < ksteps; s0 += 64) {
+    u32x4 w[8], xa[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + 8 * j;
+      w[j] = s < ksteps ? ld16(wrow + s * 32) : u32x4{0, 0, 0, 0};
+      xa[j] = (xv && s < ksteps) ? ld16(xrow + s * 32) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + 8 * j < ksteps) acc = mfma_bf16(xa[j], w[j], acc);
+  }
+  return acc;
+}
+
+// wave partial -> LDS red[wave][row][col] (row stride 17)
 __device__ __forceinline__ void red_store(float* red, f32x4 acc) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -144,7 +300,6 @@ __device__ __forceinline__ void red_store(float* red, f32x4 acc) {
 #pragma unroll
   for (int r = 0; r < 4; ++r) p[(4 * g + r) * 17 + nl] = acc[r];
 }
-// Sum over the 8 waves, fixed order.
 __device__ __forceinline__ float red_sum(const float* red, int row, int col) {
   float v = 0.f;
 #pragma unroll
@@ -152,31 +307,43 @@ __device__ __forceinline__ float red_sum(const float* red, int row, int col) {
   return v;
 }
 
-// out_bf16[t][n0..n0+16) = bf16(residual + x W^T), written with coherent stores (4 columns
-// per thread, 8-byte stores).
-__device__ void dense_tile_bf16(const uint16_t* x, int T, int K, const uint16_t* W, int N, int n0,
-                                const uint16_t* residual, uint16_t* out, bool coherent, float* red) {
-  f32x4 acc = dense_partial(x, T, K, W, n0);
-  red_store(red, acc);
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 4;
-    if (row < T) {
-      float v[4];
+// Control wave: the 4 outputs (row, c0..c0+3) of a tile, summed over the 8 waves.
+__device__ __forceinline__ void ctl_tile_vals(const float* red, int row, int c0, float v[4]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] = red_sum(red, row, c0 + j);
-      if (residual) {
-        u32x2 r = *(const u32x2*)(residual + (size_t)row * N + n0 + c0);
-        v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16);
-        v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
-      }
-      uint64_t packed = (uint64_t)pack_bf2(v[0], v[1]) | ((uint64_t)pack_bf2(v[2], v[3]) << 32);
-      uint16_t* dst = out + (size_t)row * N + n0 + c0;
-      if (coherent) st_coh_u64(dst, packed);
-      else *(uint64_t*)dst = packed;
+  for (int j = 0; j < 4; ++j) v[j] = red_sum(red, row, c0 + j);
+}
+
+__device__ __forceinline__ uint64_t pack4_bf16(const float v[4]) {
+  return (uint64_t)pack_bf2(v[0], v[1]) | ((uint64_t)pack_bf2(v[2], v[3]) << 32);
+}
+
+// tile index of this workgroup in a phase whose tile t runs on workgroup (t + off) % n_wg
+__device__ __forceinline__ int first_tile(int off) {
+  const int n = gridDim.x;
+  return ((int)blockIdx.x - off % n + n) % n;
+}
+
+// Copy n 16-byte pieces to LDS with every load of a batch issued before any store (one
+// memory round trip per batch of up to 16 pieces per thread instead of one per piece).
+// piece(i) returns the global address of piece i, dst(i) its LDS address.  Compute
+// threads only; the caller synchronises afterwards.
+template <class SrcF, class DstF>
+__device__ __forceinline__ void stage_pieces(int n, SrcF piece, DstF dst) {
+  const int tid = threadIdx.x;
+  if (tid >= kCompute) return;
+  for (int base = 0; base < n; base += 8 * kCompute) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * kCompute + tid;
+      if (i < n) v[j] = ld16(piece(i));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = base + j * kCompute + tid;
+      if (i < n) *(u32x4*)dst(i) = v[j];
     }
   }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------------ attention
@@ -185,8 +352,9 @@ __device__ void dense_tile_bf16(const uint16_t* x, int T, int K, const uint16_t*
 // Rows are (token, q head of this kv head) pairs, row = t * G + (h - g*G), R = T*G <= 128;
 // wave w owns rows [16w, 16w + 16).  S^T = K Q^T puts keys on the MFMA M axis so that the
 // probabilities land in exactly the B-operand layout the P.V product needs.
-__device__ void attention_item(const KArgs& a, const Tree& tr, int item, char* smem) {
-  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
+// Called by all threads (the staging barrier counts every wave).
+__device__ __forceinline__ void attention_stage(const KArgs& a, int item, char* smem) {
+  const int d = a.d;
   const int g_kv = item / a.attn_chunks_per_head;
   const int chunk = item % a.attn_chunks_per_head;
   const bool tree_chunk = chunk == a.attn_chunks_per_head - 1;
@@ -197,139 +365,187 @@ __device__ void attention_item(const KArgs& a, const Tree& tr, int item, char* s
   const int vt_stride = CK + 8;                 // bf16 elements per V^T row in LDS
   uint16_t* Ks = (uint16_t*)smem;               // [CK][ks_stride]
   uint16_t* VT = Ks + CK * ks_stride;           // [d][vt_stride]
+  const int tid = threadIdx.x;
 
-  // stage K (row-major) and V (transposed) for keys kb..kb+nk, zero beyond nk
+  // stage K (row-major) and V (transposed) for keys kb..kb+nk, zero beyond nk; all loads
+  // of a thread are issued before its LDS stores
   const int per_row = d / 8;                    // 16-byte pieces per key row
-  for (int i = threadIdx.x; i < CK * per_row; i += blockDim.x) {
-    const int key = i / per_row, c = (i % per_row) * 8;
-    u32x4 kv = {0, 0, 0, 0}, vv = {0, 0, 0, 0};
-    if (key < nk) {
-      const size_t off = ((size_t)(kb + key) * a.Hkv + g_kv) * d + c;
-      kv = ld16(a.kc + off);
-      vv = ld16(a.vc + off);
-    }
-    *(u32x4*)(Ks + key * ks_stride + c) = kv;
+  if (tid < kCompute) {
+    constexpr int kMaxPer = (128 * 16) / kCompute;   // pieces per thread at d = 128
+    u32x4 kv[kMaxPer], vv[kMaxPer];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      VT[(c + 2 * j) * vt_stride + key] = (uint16_t)(vv[j] & 0xFFFF);
-      VT[(c + 2 * j + 1) * vt_stride + key] = (uint16_t)(vv[j] >> 16);
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = tid + j * kCompute;
+      const int key = i / per_row, c = (i % per_row) * 8;
+      kv[j] = u32x4{0, 0, 0, 0};
+      vv[j] = u32x4{0, 0, 0, 0};
+      if (i < CK * per_row && key < nk) {
+        const size_t off = ((size_t)(kb + key) * a.Hkv + g_kv) * d + c;
+        kv[j] = ld16(a.kc + off);
+        vv[j] = ld16(a.vc + off);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxPer; ++j) {
+      const int i = tid + j * kCompute;
+      if (i < CK * per_row) {
+        const int key = i / per_row, c = (i % per_row) * 8;
+        *(u32x4*)(Ks + key * ks_stride + c) = kv[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          VT[(c + 2 * q) * vt_stride + key] = (uint16_t)(vv[j][q] & 0xFFFF);
+          VT[(c + 2 * q + 1) * vt_stride + key] = (uint16_t)(vv[j][q] >> 16);
+        }
+      }
     }
   }
-  __syncthreads();
+  wg_sync();
+}
+
+// the compute half of an attention item (after the staging barrier); no barriers inside,
+// threads of the control wave return at once
+template <bool TS>
+__device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, int item, char* smem) {
+  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
+  const int g_kv = item / a.attn_chunks_per_head;
+  const int chunk = item % a.attn_chunks_per_head;
+  const bool tree_chunk = chunk == a.attn_chunks_per_head - 1;
+  const int kb = tree_chunk ? a.ctx : a.attn_lo + chunk * a.ck;
+  const int nk = tree_chunk ? a.T : min(a.ck, a.ctx - kb);
+  const int CK = 128;
+  const int ks_stride = d + 8;
+  const int vt_stride = CK + 8;
+  const uint16_t* Ks = (const uint16_t*)smem;
+  const uint16_t* VT = Ks + CK * ks_stride;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, grp = lane >> 4;
   const int row = wave * 16 + nl;               // this lane's query row (MFMA column)
-  if (wave * 16 < R) {
-    const bool rv = row < R;
-    const int tok = rv ? row / G : 0;
-    const int head = g_kv * G + (rv ? row % G : 0);
-    const int dsteps = d / 32;
-    u32x4 qf[4];
+  if (threadIdx.x >= kCompute || wave * 16 >= R) return;
+  const bool rv = row < R;
+  const int tok = rv ? row / G : 0;
+  const int head = g_kv * G + (rv ? row % G : 0);
+  const int dsteps = d / 32;
+  u32x4 qf[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      qf[s] = (s < dsteps && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
-                                 : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < 4; ++s) {
+    qf[s] = (s < dsteps && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
+                               : u32x4{0, 0, 0, 0};
+  }
+  if constexpr (TS) {   // q fragments arrived
+    if (threadIdx.x == 0 && item == (int)blockIdx.x) {
+      uint32_t x = qf[0][0] | qf[1][1];
+      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 39] = wall_clock64() + (x == 0x12345u ? 1 : 0);
     }
-    const float scale = 1.0f / sqrtf((float)d);
-    const int ktiles = (nk + 15) / 16;
-    f32x4 sc[8];
-    float mrow = -INFINITY;
+  }
+  const float scale = 1.0f / sqrtf((float)d);
+  const int ktiles = (nk + 15) / 16;
+  // visibility of chunk key kl for this lane's row: kl in [vis_lo, vis_hi) for context
+  // chunks (sliding-window lower bound), the ancestor mask for the tree chunk
+  const int vis_hi = rv ? nk : 0;
+  const int vis_lo = rv ? max(0, tr.lo[tok] - kb) : 0;
+  const uint32_t anc_m = rv ? tr.anc[tok] : 0u;
+  f32x4 sc[8];
+  float mrow = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (kt < ktiles) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kt = 0; kt < 8; ++kt) {
+    sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (kt < ktiles) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s < dsteps) {
-            u32x4 kf = *(const u32x4*)(Ks + (kt * 16 + nl) * ks_stride + s * 32 + grp * 8);
-            acc = mfma_bf16(kf, qf[s], acc);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kl = kt * 16 + 4 * grp + r;   // key index within the chunk
-          bool vis = rv && kl < nk;
-          if (vis) {
-            if (tree_chunk) vis = (tr.anc[tok] >> kl) & 1u;
-            else vis = kb + kl >= tr.lo[tok];
-          }
-          sc[kt][r] = vis ? acc[r] * scale : -INFINITY;
-          mrow = fmaxf(mrow, sc[kt][r]);
+      for (int s = 0; s < 4; ++s) {
+        if (s < dsteps) {
+          u32x4 kf = *(const u32x4*)(Ks + (kt * 16 + nl) * ks_stride + s * 32 + grp * 8);
+          acc = mfma_bf16(kf, qf[s], acc);
         }
       }
-    }
-    mrow = xgroup_max(mrow);
-    float lsum = 0.f;
-    uint32_t pb[8][2];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      float p[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = (mrow == -INFINITY || sc[kt][r] == -INFINITY) ? 0.f : __expf(sc[kt][r] - mrow);
-        lsum += p[r];
-      }
-      pb[kt][0] = pack_bf2(p[0], p[1]);
-      pb[kt][1] = pack_bf2(p[2], p[3]);
-    }
-    lsum = xgroup_sum(lsum);
-    // O^T[dd][row] = sum_keys V^T[dd][key] P^T[key][row]; a 32-key step pairs key tiles
-    // (2q, 2q+1): lane group grp supplies keys 4grp..4grp+3 of both tiles.
-    f32x4 o[8];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int dtiles = d / 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (2 * q < ktiles) {
-        u32x4 bfrag = {pb[2 * q][0], pb[2 * q][1], pb[2 * q + 1][0], pb[2 * q + 1][1]};
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          if (dt < dtiles) {
-            const uint16_t* vrow = VT + (dt * 16 + nl) * vt_stride;
-            u32x2 v0 = *(const u32x2*)(vrow + (2 * q) * 16 + 4 * grp);
-            u32x2 v1 = *(const u32x2*)(vrow + (2 * q + 1) * 16 + 4 * grp);
-            u32x4 afrag = {v0[0], v0[1], v1[0], v1[1]};
-            o[dt] = mfma_bf16(afrag, bfrag, o[dt]);
-          }
-        }
-      }
-    }
-    if (rv) {
-      float* po = a.part_o + ((size_t)item * 128 + row) * d;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        if (dt < dtiles) {
-          u32x4 v = {__float_as_uint(o[dt][0]), __float_as_uint(o[dt][1]), __float_as_uint(o[dt][2]),
-                     __float_as_uint(o[dt][3])};
-          st_coh_u128(po + dt * 16 + 4 * grp, v);
-        }
-      }
-      if (grp == 0) {
-        st_coh_u64(a.part_ml + ((size_t)item * 128 + row) * 2,
-                   (uint64_t)__float_as_uint(mrow) | ((uint64_t)__float_as_uint(lsum) << 32));
+        const int kl = kt * 16 + 4 * grp + r;   // key index within the chunk
+        const bool vis = kl < vis_hi && (tree_chunk ? ((anc_m >> kl) & 1u) != 0 : kl >= vis_lo);
+        sc[kt][r] = vis ? acc[r] * scale : -INFINITY;
+        mrow = fmaxf(mrow, sc[kt][r]);
       }
     }
   }
-  __syncthreads();
+  mrow = xgroup_max(mrow);
+  float lsum = 0.f;
+  uint32_t pb[8][2];
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      p[r] = (mrow == -INFINITY || sc[kt][r] == -INFINITY) ? 0.f : __expf(sc[kt][r] - mrow);
+      lsum += p[r];
+    }
+    pb[kt][0] = pack_bf2(p[0], p[1]);
+    pb[kt][1] = pack_bf2(p[2], p[3]);
+  }
+  lsum = xgroup_sum(lsum);
+  if constexpr (TS) {
+    if (threadIdx.x == 0 && item == (int)blockIdx.x)
+      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 40] = wall_clock64() + (lsum == -1.f ? 1 : 0);
+  }
+  // O^T[dd][row] = sum_keys V^T[dd][key] P^T[key][row]; a 32-key step pairs key tiles
+  // (2q, 2q+1): lane group grp supplies keys 4grp..4grp+3 of both tiles.
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int dtiles = d / 16;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (2 * q < ktiles) {
+      u32x4 bfrag = {pb[2 * q][0], pb[2 * q][1], pb[2 * q + 1][0], pb[2 * q + 1][1]};
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        if (dt < dtiles) {
+          const uint16_t* vrow = VT + (dt * 16 + nl) * vt_stride;
+          u32x2 v0 = *(const u32x2*)(vrow + (2 * q) * 16 + 4 * grp);
+          u32x2 v1 = *(const u32x2*)(vrow + (2 * q + 1) * 16 + 4 * grp);
+          u32x4 afrag = {v0[0], v0[1], v1[0], v1[1]};
+          o[dt] = mfma_bf16(afrag, bfrag, o[dt]);
+        }
+      }
+    }
+  }
+  if constexpr (TS) {
+    if (threadIdx.x == 0 && item == (int)blockIdx.x)
+      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 41] = wall_clock64() + (o[0][0] == -1.f ? 1 : 0);
+  }
+  if (rv) {
+    float* po = a.part_o + ((size_t)item * 128 + row) * d;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      if (dt < dtiles) {
+        u32x4 v = {__float_as_uint(o[dt][0]), __float_as_uint(o[dt][1]), __float_as_uint(o[dt][2]),
+                   __float_as_uint(o[dt][3])};
+        st_coh_u128(po + dt * 16 + 4 * grp, v);
+      }
+    }
+    if (grp == 0) {
+      st_coh_u64(a.part_ml + ((size_t)item * 128 + row) * 2,
+                 (uint64_t)__float_as_uint(mrow) | ((uint64_t)__float_as_uint(lsum) << 32));
+    }
+  }
 }
 
-// Merge of the per-chunk partials of one (kv head, row): flash-decoding style rescale.
-__device__ void merge_unit(const KArgs& a, int unit, float* scratch) {
-  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
+// Merge of the per-chunk partials of one (kv head, row), flash-decoding style rescale.
+// Compute waves: 16 chunk groups x 32 threads (4 d values each).  The merged row (bf16)
+// and its stats go to LDS `outrow` for the control wave to store.  Called by all threads.
+__device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scratch, uint32_t* outrow) {
+  const int d = a.d;
+  const int G = a.Hq / a.Hkv, R = a.T * G;
   const int g_kv = unit / R, row = unit % R;
-  const int tok = row / G, head = g_kv * G + row % G;
   const int nchunks = a.attn_chunks_per_head;
-  const int quads = d / 4;                      // threads per chunk-group
-  const int ngroups = blockDim.x / 32;          // 16 chunk groups of 32 threads
+  const int quads = d / 4;
+  const int ngroups = kCompute / 32;
   const int tq = threadIdx.x % 32, cg = threadIdx.x / 32;
   float M = -INFINITY, L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
-  if (tq < quads) {
+  if (tq < quads && threadIdx.x < kCompute) {
     for (int c = cg; c < nchunks; c += ngroups) {
       const int item = g_kv * nchunks + c;
-      const float* ml = a.part_ml + ((size_t)item * 128 + row) * 2;
+      const f32x2 ml = *(const f32x2*)(a.part_ml + ((size_t)item * 128 + row) * 2);
       const float m = ml[0], l = ml[1];
       if (l <= 0.f) continue;
       const f32x4 o = *(const f32x4*)(a.part_o + ((size_t)item * 128 + row) * d + tq * 4);
@@ -342,16 +558,17 @@ __device__ void merge_unit(const KArgs& a, int unit, float* scratch) {
       M = Mn;
     }
   }
-  float* sm = scratch;                          // [ngroups][32][6]
-  float* me = sm + (cg * 32 + tq) * 6;
-  me[0] = M; me[1] = L; me[2] = O[0]; me[3] = O[1]; me[4] = O[2]; me[5] = O[3];
-  __syncthreads();
+  if (threadIdx.x < kCompute) {
+    float* me = scratch + (cg * 32 + tq) * 6;
+    me[0] = M; me[1] = L; me[2] = O[0]; me[3] = O[1]; me[4] = O[2]; me[5] = O[3];
+  }
+  wg_sync();
   if (threadIdx.x < quads) {
     float Mt = -INFINITY;
-    for (int q = 0; q < ngroups; ++q) Mt = fmaxf(Mt, sm[(q * 32 + threadIdx.x) * 6]);
+    for (int q = 0; q < ngroups; ++q) Mt = fmaxf(Mt, scratch[(q * 32 + threadIdx.x) * 6]);
     float Lt = 0.f, Ot[4] = {0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < ngroups; ++q) {
-      const float* e = sm + (q * 32 + threadIdx.x) * 6;
+      const float* e = scratch + (q * 32 + threadIdx.x) * 6;
       if (e[0] == -INFINITY) continue;
       const float s = __expf(e[0] - Mt);
       Lt += e[1] * s;
@@ -359,297 +576,512 @@ __device__ void merge_unit(const KArgs& a, int unit, float* scratch) {
       for (int j = 0; j < 4; ++j) Ot[j] += e[2 + j] * s;
     }
     const float inv = 1.0f / Lt;
-    uint64_t packed = (uint64_t)pack_bf2(Ot[0] * inv, Ot[1] * inv) | ((uint64_t)pack_bf2(Ot[2] * inv, Ot[3] * inv) << 32);
-    st_coh_u64(a.attn + (size_t)tok * a.Hq * d + head * d + threadIdx.x * 4, packed);
-    if (threadIdx.x == 0 && a.attn_stats) {
-      a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 0] = Mt;
-      a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 1] = Lt;
+    outrow[2 * threadIdx.x] = pack_bf2(Ot[0] * inv, Ot[1] * inv);
+    outrow[2 * threadIdx.x + 1] = pack_bf2(Ot[2] * inv, Ot[3] * inv);
+    if (threadIdx.x == 0) {
+      outrow[64] = __float_as_uint(Mt);
+      outrow[65] = __float_as_uint(Lt);
     }
   }
-  __syncthreads();
 }
 
 // ------------------------------------------------------------------ routing
 
 // Top-k per token from the logits (value desc, index asc), softmax gates over the selected,
-// and the dispatch tables.  Every workgroup computes the same tables.
-__device__ void route_tables(const KArgs& a, Route& rt, float* lg) {
-  const int T = a.T, E = a.E, K = a.topk;
-  for (int i = threadIdx.x; i < T * E; i += blockDim.x) lg[i] = a.logits[i];
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int t = wave; t < T; t += 8) {
+// and the dispatch tables.  Every workgroup computes the same tables.  Called by all threads;
+// the work runs on the compute waves.
+__device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* lg) {
+  const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
+  const int npairs = T * K;
+  const bool cw = tid < kCompute;
+  stage_pieces(T * E / 4, [&](int i) { return (const void*)(a.logits + 4 * i); },
+               [&](int i) { return (void*)(lg + 4 * i); });
+  for (int i = tid; cw && i < E * 4; i += kCompute) rt.mask[i] = 0u;
+  wg_sync();
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int t = wave; cw && t < T; t += 8) {
+    // lane holds experts 4 lane .. 4 lane + 3, so a lower lane means a lower index
     float v[4];
-    int e_[4];
+    bool taken[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      e_[q] = lane + 64 * q;
-      v[q] = e_[q] < E ? lg[t * E + e_[q]] : -INFINITY;
+      const int e = 4 * lane + q;
+      taken[q] = e >= E;
+      v[q] = taken[q] ? -INFINITY : lg[t * E + e];
     }
-    bool taken[4] = {e_[0] >= E, e_[1] >= E, e_[2] >= E, e_[3] >= E};
-    float zsel[8];
+    float z0 = 0.f, s = 0.f, gsel = 0.f;
     for (int j = 0; j < K; ++j) {
-      // lane-local best
-      float bv = -INFINITY; int be = 0x7FFFFFFF;
+      float bv = -INFINITY;
+      int bq = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (!taken[q] && (v[q] > bv || (v[q] == bv && e_[q] < be))) { bv = v[q]; be = e_[q]; }
-      // wave argmax, ties to the lower index
+      for (int q = 3; q >= 0; --q)
+        if (!taken[q] && v[q] >= bv) { bv = v[q]; bq = q; }   // ties: the lower q wins
+      const float m = wave_max_f32(bv);
+      const uint64_t hit = __ballot(bv == m && !(taken[0] && taken[1] && taken[2] && taken[3]));
+      const int wl = __ffsll((unsigned long long)hit) - 1;      // lowest lane holding the max
+      const int be = 4 * wl + __builtin_amdgcn_readlane(bq, wl);
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        float ov = __shfl_xor(bv, off);
-        int oe = __shfl_xor(be, off);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) if (e_[q] == be) taken[q] = true;
-      zsel[j] = bv;
+      for (int q = 0; q < 4; ++q) if (lane == wl && q == (be & 3)) taken[q] = true;
+      if (j == 0) z0 = m;
+      const float ex = __expf(m - z0);
+      s += ex;
+      if (lane == j) gsel = ex;                 // lane j keeps slot j's weight
       if (lane == 0) rt.idx[t * K + j] = be;
     }
-    if (lane == 0) {
-      float s = 0.f, ex[8];
-      for (int j = 0; j < K; ++j) { ex[j] = __expf(zsel[j] - zsel[0]); s += ex[j]; }
-      for (int j = 0; j < K; ++j) rt.gate[t * K + j] = ex[j] / s;
+    if (lane < K) rt.gate[t * K + lane] = gsel / s;
+  }
+  wg_sync();
+  for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&rt.mask[rt.idx[p] * 4 + (p >> 5)], 1u << (p & 31));
+  wg_sync();
+  for (int e = tid; cw && e < E; e += kCompute)
+    rt.expert_cnt[e] = __popc(rt.mask[e * 4]) + __popc(rt.mask[e * 4 + 1]) + __popc(rt.mask[e * 4 + 2]) +
+                       __popc(rt.mask[e * 4 + 3]);
+  wg_sync();
+  if (tid < 64) {
+    // exclusive scans over experts: lane handles 4 consecutive experts
+    int cnt[4], act[4], sumc = 0, suma = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      cnt[q] = e < E ? rt.expert_cnt[e] : 0;
+      act[q] = cnt[q] > 0;
+      sumc += cnt[q];
+      suma += act[q];
     }
-  }
-  __syncthreads();
-  const int npairs = T * K;
-  // per-expert counts and first-pair ranks
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int c = 0;
-    for (int p = 0; p < npairs; ++p) c += rt.idx[p] == e;
-    rt.expert_cnt[e] = c;
-  }
-  __syncthreads();
-  if (threadIdx.x < 64) {
-    // serial-in-wave prefix over experts: lane handles 4 consecutive experts
-    int base = 0;
-    int n_act = 0;
-    for (int chunk = 0; chunk < E; chunk += 256) {
-      int cnt[4], act[4];
-      int sumc = 0, suma = 0;
+    int sc = sumc, sa = suma;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = chunk + threadIdx.x * 4 + q;
-        cnt[q] = e < E ? rt.expert_cnt[e] : 0;
-        act[q] = cnt[q] > 0;
-        sumc += cnt[q]; suma += act[q];
-      }
-      // exclusive scan across the wave
-      int sc = sumc, sa = suma;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        int oc = __shfl_up(sc, off), oa = __shfl_up(sa, off);
-        if ((int)threadIdx.x >= off) { sc += oc; sa += oa; }
-      }
-      int pc = base + sc - sumc, pa = n_act + sa - suma;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int e = chunk + threadIdx.x * 4 + q;
-        if (e < E) rt.expert_first[e] = pc;
-        if (act[q]) {
-          rt.act_expert[pa] = e;
-          rt.act_off[pa] = pc;
-          rt.act_cnt[pa] = cnt[q];
-          ++pa;
-        }
-        pc += cnt[q];
-      }
-      base += __shfl(sc, 63);
-      n_act += __shfl(sa, 63);
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oc = __shfl_up(sc, off), oa = __shfl_up(sa, off);
+      if (tid >= off) { sc += oc; sa += oa; }
     }
-    if (threadIdx.x == 0) rt.n_active = n_act;
+    int pc = sc - sumc, pa = sa - suma;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid * 4 + q;
+      if (e < E) rt.expert_first[e] = pc;
+      if (act[q]) {
+        rt.act_expert[pa] = e;
+        rt.act_off[pa] = pc;
+        rt.act_cnt[pa] = cnt[q];
+        ++pa;
+      }
+      pc += cnt[q];
+    }
+    if (tid == 63) rt.n_active = sa;
   }
-  __syncthreads();
-  for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
+  wg_sync();
+  for (int p = tid; cw && p < npairs; p += kCompute) {
     const int e = rt.idx[p];
-    int r = 0;
-    for (int q = 0; q < p; ++q) r += rt.idx[q] == e;
+    const uint32_t* m = rt.mask + e * 4;
+    const int w = p >> 5;
+    int r = __popc(m[w] & ((1u << (p & 31)) - 1u));
+    for (int q = 0; q < w; ++q) r += __popc(m[q]);
     rt.pair_list[rt.expert_first[e] + r] = p;
   }
-  __syncthreads();
+  wg_sync();
 }
 
 // ------------------------------------------------------------------ experts
 
-// GEMM1 task: expert act slot `ai`, intermediate columns [j0, j0+16).  Each wave covers a
-// share of K = P; the partial gate and up tiles are reduced across waves in LDS.
-__device__ void gemm1_task(const KArgs& a, const Route& rt, int ai, int j0, float* red, float* abuf) {
-  const int e = rt.act_expert[ai], cnt = rt.act_cnt[ai], off = rt.act_off[ai];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, grp = lane >> 4;
-  const int P = a.P, I = a.I, K = a.topk;
-  const int m = nl;                                   // A-operand row = token slot of this expert
-  const bool mv = m < cnt;
-  const int tok = mv ? rt.pair_list[off + m] / K : 0;
-  const uint16_t* xrow = a.xp + (size_t)tok * P;
-  f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-  if (a.fmt == 1) {
-    const size_t rows = 2 * (size_t)I;
-    const uint8_t* cg = a.w1_codes + ((size_t)e * rows + j0 + nl) * (P / 2);
-    const uint8_t* cu = a.w1_codes + ((size_t)e * rows + I + j0 + nl) * (P / 2);
-    const uint8_t* sg = a.w1_scales + ((size_t)e * rows + j0 + nl) * (P / 16);
-    const uint8_t* su = a.w1_scales + ((size_t)e * rows + I + j0 + nl) * (P / 16);
-    const int lsteps = P / 128;                       // 128 k per load step (16 B per lane)
-    for (int ls = wave; ls < lsteps; ls += 8) {
-      const u32x4 wg = ld16(cg + ls * 64 + grp * 16);
-      const u32x4 wu = ld16(cu + ls * 64 + grp * 16);
-      const uint32_t scg = *(const uint16_t*)(sg + ls * 8 + grp * 2);
-      const uint32_t scu = *(const uint16_t*)(su + ls * 8 + grp * 2);
-      const float sg0 = e4m3_to_f32(scg & 0xFF), sg1 = e4m3_to_f32(scg >> 8);
-      const float su0 = e4m3_to_f32(scu & 0xFF), su1 = e4m3_to_f32(scu >> 8);
+// GEMM1 for all of this workgroup's (expert, 16-column block) tasks: xp rows staged in LDS,
+// the weights of MAXT tasks loaded together (8 waves split K = P), per-task reduction over
+// the waves in LDS, SwiGLU, NVFP4 requantisation of the intermediate (tensor scale 1).
+// Called by all threads.
+template <bool TS>
+__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem) {
+  const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
+  const bool cw = tid < kCompute;
+  const int jblocks = I / 16;
+  const int ntasks = rt.n_active * jblocks;
+  const int nwg = gridDim.x;
+  if ((int)blockIdx.x >= ntasks) return;        // uniform over the workgroup
+  const int xstride = P + XS_STRIDE_PAD;
+  uint16_t* xs = (uint16_t*)smem;
+  float* red = (float*)(smem + G1_XS_BYTES);    // [MAXT][2][8 waves][16][17]
+  float* abuf = red + G1_RED_FLOATS;            // [MAXT][16][17]
+  stage_pieces(T * (P / 8), [&](int i) { return (const void*)(a.xp + (size_t)i * 8); },
+               [&](int i) { return (void*)(xs + (i / (P / 8)) * xstride + (i % (P / 8)) * 8); });
+  wg_sync();
+  stamp<TS>(a.timestamps, 44, 0);
+  const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
+  const int lsteps = P / 128;                   // NVFP4: 16 B of codes per lane = 128 k per step
+  for (int t0 = blockIdx.x; t0 < ntasks; t0 += MAXT * nwg) {
+    const int nb = min(MAXT, (ntasks - t0 + nwg - 1) / nwg);
+    if (cw) {
+      u32x4 cg[MAXT][2], cu[MAXT][2];
+      uint32_t sgv[MAXT][2], suv[MAXT][2];
+      if (a.fmt == 1) {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k = ls * 128 + grp * 32 + s * 8;
-        const u32x4 xa = mv ? ld16(xrow + k) : u32x4{0, 0, 0, 0};
-        accg = mfma_bf16(xa, fp4x8_to_bf16(wg[s], s < 2 ? sg0 : sg1), accg);
-        accu = mfma_bf16(xa, fp4x8_to_bf16(wu[s], s < 2 ? su0 : su1), accu);
-      }
-    }
-  } else {
-    const uint16_t* wgr = a.w1 + ((size_t)e * 2 * I + j0 + nl) * P;
-    const uint16_t* wur = a.w1 + ((size_t)e * 2 * I + I + j0 + nl) * P;
-    for (int s = wave; s < P / 32; s += 8) {
-      const int k = s * 32 + grp * 8;
-      const u32x4 xa = mv ? ld16(xrow + k) : u32x4{0, 0, 0, 0};
-      accg = mfma_bf16(xa, ld16(wgr + k), accg);
-      accu = mfma_bf16(xa, ld16(wur + k), accu);
-    }
-  }
-  float* pg = red + wave * (16 * 17);
-  float* pu = red + 8 * 16 * 17 + wave * (16 * 17);
+        for (int i = 0; i < MAXT; ++i) {
+          if (i < nb) {
+            const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
+            const size_t rows = 2 * (size_t)I, e = rt.act_expert[ai];
+            const uint8_t* cgp = a.w1_codes + (e * rows + j0 + nl) * (P / 2) + grp * 16;
+            const uint8_t* cup = a.w1_codes + (e * rows + I + j0 + nl) * (P / 2) + grp * 16;
+            const uint8_t* sgp = a.w1_scales + (e * rows + j0 + nl) * (P / 16) + grp * 2;
+            const uint8_t* sup = a.w1_scales + (e * rows + I + j0 + nl) * (P / 16) + grp * 2;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    pg[(4 * grp + r) * 17 + nl] = accg[r];
-    pu[(4 * grp + r) * 17 + nl] = accu[r];
-  }
-  __syncthreads();
-  if (threadIdx.x < 256) {
-    const int mm = threadIdx.x >> 4, j = threadIdx.x & 15;
-    float ug = red_sum(red, mm, j), uu = red_sum(red + 8 * 16 * 17, mm, j);
-    if (a.fmt == 1) { ug *= a.w1_ts[e]; uu *= a.w1_ts[e]; }
-    const float act = ug / (1.0f + __expf(-ug)) * uu;
-    abuf[mm * 17 + j] = act;
-  }
-  __syncthreads();
-  if (threadIdx.x < cnt) {
-    const int pair = rt.pair_list[off + threadIdx.x];
-    const float* v = abuf + threadIdx.x * 17;
-    if (a.fmt == 1) {
-      float amax = 0.f;
-      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      const uint32_t sc = e4m3_code_of_amax_over6(amax);
-      const float s = e4m3_to_f32(sc);
-      uint32_t w0 = 0, w1 = 0;
-      if (s > 0.f) {
-        for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], s) << (4 * j);
-        for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], s) << (4 * j);
+            for (int jj = 0; jj < 2; ++jj) {
+              const int ls = wave + 8 * jj;
+              if (ls < lsteps) {
+                cg[i][jj] = ld16(cgp + ls * 64);
+                cu[i][jj] = ld16(cup + ls * 64);
+                sgv[i][jj] = *(const uint16_t*)(sgp + ls * 8);
+                suv[i][jj] = *(const uint16_t*)(sup + ls * 8);
+              }
+            }
+          }
+        }
       }
-      st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
-    } else {
-      uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
-      for (int q = 0; q < 4; ++q) {
-        uint64_t packed = (uint64_t)pack_bf2(v[4 * q], v[4 * q + 1]) | ((uint64_t)pack_bf2(v[4 * q + 2], v[4 * q + 3]) << 32);
-        st_coh_u64(dst + 4 * q, packed);
+#pragma unroll
+      for (int i = 0; i < MAXT; ++i) {
+        if (i < nb) {
+          const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
+          const int e = rt.act_expert[ai], cnt = rt.act_cnt[ai], off = rt.act_off[ai];
+          const bool mv = nl < cnt;
+          const uint16_t* xrow = xs + (mv ? rt.pair_list[off + nl] / K : 0) * xstride;
+          f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
+          if (a.fmt == 1) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+              const int ls = wave + 8 * jj;
+              if (ls < lsteps) {
+                const float sg0 = e4m3_to_f32(sgv[i][jj] & 0xFF), sg1 = e4m3_to_f32(sgv[i][jj] >> 8);
+                const float su0 = e4m3_to_f32(suv[i][jj] & 0xFF), su1 = e4m3_to_f32(suv[i][jj] >> 8);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                  const int k = ls * 128 + grp * 32 + s * 8;
+                  const u32x4 xa = mv ? *(const u32x4*)(xrow + k) : u32x4{0, 0, 0, 0};
+                  accg = mfma_bf16(xa, fp4x8_to_bf16(cg[i][jj][s], s < 2 ? sg0 : sg1), accg);
+                  accu = mfma_bf16(xa, fp4x8_to_bf16(cu[i][jj][s], s < 2 ? su0 : su1), accu);
+                }
+              }
+            }
+          } else {
+            const uint16_t* wgr = a.w1 + ((size_t)e * 2 * I + j0 + nl) * P + grp * 8;
+            const uint16_t* wur = a.w1 + ((size_t)e * 2 * I + I + j0 + nl) * P + grp * 8;
+            for (int s = wave; s < P / 32; s += 8) {
+              const u32x4 xa = mv ? *(const u32x4*)(xrow + s * 32 + grp * 8) : u32x4{0, 0, 0, 0};
+              accg = mfma_bf16(xa, ld16(wgr + s * 32), accg);
+              accu = mfma_bf16(xa, ld16(wur + s * 32), accu);
+            }
+          }
+          float* pg = red + ((i * 2 + 0) * 8 + wave) * (16 * 17);
+          float* pu = red + ((i * 2 + 1) * 8 + wave) * (16 * 17);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pg[(4 * grp + r) * 17 + nl] = accg[r];
+            pu[(4 * grp + r) * 17 + nl] = accu[r];
+          }
+        }
       }
     }
+    wg_sync();
+    if (t0 == (int)blockIdx.x) stamp<TS>(a.timestamps, 45, 0);
+    for (int o = tid; cw && o < nb * 256; o += kCompute) {
+      const int i = o >> 8, m = (o >> 4) & 15, j = o & 15;
+      const int task = t0 + i * nwg, ai = task / jblocks;
+      const int e = rt.act_expert[ai];
+      if (m < rt.act_cnt[ai]) {
+        float ug = red_sum(red + (i * 2 + 0) * 8 * (16 * 17), m, j);
+        float uu = red_sum(red + (i * 2 + 1) * 8 * (16 * 17), m, j);
+        if (a.fmt == 1) { ug *= a.w1_ts[e]; uu *= a.w1_ts[e]; }
+        abuf[i * (16 * 17) + m * 17 + j] = ug / (1.0f + __expf(-ug)) * uu;
+      }
+    }
+    wg_sync();
+    for (int o = tid; cw && o < nb * 16; o += kCompute) {
+      const int i = o >> 4, m = o & 15;
+      const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
+      if (m < rt.act_cnt[ai]) {
+        const int pair = rt.pair_list[rt.act_off[ai] + m];
+        const float* v = abuf + i * (16 * 17) + m * 17;
+        if (a.fmt == 1) {
+          float amax = 0.f;
+          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+          const uint32_t sc = e4m3_code_of_amax_over6(amax);
+          const float s = e4m3_to_f32(sc);
+          uint32_t w0 = 0, w1 = 0;
+          if (s > 0.f) {
+            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], s) << (4 * j);
+            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], s) << (4 * j);
+          }
+          st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
+        } else {
+          uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
+          for (int q = 0; q < 4; ++q) st_coh_u64(dst + 4 * q, pack4_bf16(v + 4 * q));
+        }
+      }
+    }
+    wg_sync();
   }
-  __syncthreads();
 }
 
-// GEMM2 + combine for output columns [c0, c0+8) of P: every active expert's down projection
-// for those columns (waves take experts round-robin), then per token the gate-weighted sum
-// over its slots in slot order.
-__device__ void gemm2_slice(const KArgs& a, const Route& rt, int c0, float* outp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nl = lane & 15, grp = lane >> 4;
-  const int P = a.P, I = a.I, K = a.topk;
-  const bool nv = nl < 8;
-  for (int ai = wave; ai < rt.n_active; ai += 8) {
-    const int e = rt.act_expert[ai], cnt = rt.act_cnt[ai], off = rt.act_off[ai];
-    const int m = nl;
-    const bool mv = m < cnt;
-    const int pair = mv ? rt.pair_list[off + m] : 0;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (a.fmt == 1) {
-      const uint8_t* cw = a.w2_codes + ((size_t)e * P + c0 + (nv ? nl : 0)) * (I / 2);
-      const uint8_t* sw = a.w2_scales + ((size_t)e * P + c0 + (nv ? nl : 0)) * (I / 16);
-      const uint32_t* arec = a.act_q + (size_t)pair * (I / 16) * 4;
-      for (int s = 0; s < I / 32; ++s) {
-        // k = 32 s + 8 grp .. +8  -> block 2s + grp/2, half grp&1 of the block
-        const int blk = 2 * s + (grp >> 1);
-        uint32_t wc = nv ? *(const uint32_t*)(cw + 16 * s + 4 * grp) : 0u;
-        const float ws = nv ? e4m3_to_f32(sw[blk]) : 0.f;
-        uint32_t ac = 0u; float as = 0.f;
-        if (mv) {
-          ac = arec[blk * 4 + (grp & 1)];
-          as = e4m3_to_f32(arec[blk * 4 + 2]);
+// GEMM2 + combine for output columns [c0, c0+8) of P.
+//  * The fp4 intermediate of every (token, slot) pair is decoded once into LDS as bf16.
+//  * The 8 weight rows of one expert for these columns are contiguous (codes, then scales);
+//    the workgroup copies every active expert's rows into LDS with wide loads.
+//  * Two experts share one 16x16 MFMA tile: rows 0-7 / columns 0-7 carry expert A's tokens
+//    and columns, rows 8-15 / columns 8-15 expert B's, so every B-operand lane decodes real
+//    weights; the off-diagonal blocks are discarded.  An expert with more than 8 tokens runs
+//    alone (16 token rows, columns 0-7).
+//  * Per token, the gate-weighted sum over its slots in slot order goes to LDS `ytile`
+//    ([T][4] dwords of bf16 pairs) for the control wave to store.
+// Called by all threads.
+template <bool TS>
+__device__ __forceinline__ void gemm2_phase(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile) {
+  const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
+  const bool cw = tid < kCompute;
+  const int nwg = gridDim.x;
+  const int nslices = P / 8;
+  if ((int)blockIdx.x >= nslices) return;       // uniform over the workgroup
+  const int npairs = T * K;
+  const bool fp4 = a.fmt == 1;
+  const int astride = I + 8;                                        // bf16 per pair row in LDS
+  uint16_t* actbf = (uint16_t*)smem;                                // [pairs][I + 8]
+  float* outp = (float*)(smem + ((npairs * astride * 2 + 255) & ~255));   // [pairs][8]
+  char* wbuf = (char*)outp + 128 * 8 * 4;
+  const int code_bytes = fp4 ? 8 * (I / 2) : 8 * I * 2;             // per expert, per slice
+  const int chunk = code_bytes + (fp4 ? 8 * (I / 16) : 0);          // multiple of 16 (I % 32 == 0)
+  const int cap = (LDS_BYTES - (int)(wbuf - smem)) / chunk;         // experts per round
+  // decode the intermediate: one 16-element block (fp4) or 8 bf16 per piece
+  if (cw) {
+    const int nblk = fp4 ? npairs * (I / 16) : npairs * (I / 8);
+    for (int base = 0; base < nblk; base += 4 * kCompute) {
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * kCompute + tid;
+        if (i < nblk) v[j] = fp4 ? ld16(a.act_q + (size_t)i * 4) : ld16(a.act_bf + (size_t)i * 8);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = base + j * kCompute + tid;
+        if (i < nblk) {
+          if (fp4) {
+            const int pair = i / (I / 16), b = i % (I / 16);
+            const float sc = e4m3_to_f32(v[j][2]);
+            uint16_t* dst = actbf + pair * astride + b * 16;
+            *(u32x4*)dst = fp4x8_to_bf16(v[j][0], sc);
+            *(u32x4*)(dst + 8) = fp4x8_to_bf16(v[j][1], sc);
+          } else {
+            const int pair = i / (I / 8), b = i % (I / 8);
+            *(u32x4*)(actbf + pair * astride + b * 8) = v[j];
+          }
         }
-        acc = mfma_bf16(fp4x8_to_bf16(ac, as), fp4x8_to_bf16(wc, ws), acc);
-      }
-    } else {
-      const uint16_t* wr = a.w2 + ((size_t)e * P + c0 + (nv ? nl : 0)) * I;
-      const uint16_t* ar = a.act_bf + (size_t)pair * I;
-      for (int s = 0; s < I / 32; ++s) {
-        const int k = s * 32 + grp * 8;
-        u32x4 b = nv ? ld16(wr + k) : u32x4{0, 0, 0, 0};
-        u32x4 x = mv ? ld16(ar + k) : u32x4{0, 0, 0, 0};
-        acc = mfma_bf16(x, b, acc);
-      }
-    }
-    const float ts = a.fmt == 1 ? a.w2_ts[e] : 1.0f;
-    // C lane: col nl (output column), rows 4 grp + r (token slot of this expert)
-    if (nv) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int mm = 4 * grp + r;
-        if (mm < cnt) outp[rt.pair_list[off + mm] * 8 + nl] = acc[r] * ts;
       }
     }
   }
-  __syncthreads();
-  if (threadIdx.x < a.T) {
-    const int t = threadIdx.x;
-    float y[8];
+  const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
+  const int ksteps = I / 32;
+  const int pieces = chunk / 16, code_pieces = code_bytes / 16;
+  for (int sl = blockIdx.x; sl < nslices; sl += nwg) {
+    const int c0 = sl * 8;
+    for (int a0 = 0; a0 < rt.n_active; a0 += cap) {
+      const int na = min(cap, rt.n_active - a0);
+      stage_pieces(na * pieces, [&](int p) {
+        const int ai = a0 + p / pieces, q = p % pieces;
+        const size_t row0 = (size_t)rt.act_expert[ai] * P + c0;
+        if (!fp4) return (const void*)((const char*)a.w2 + row0 * I * 2 + q * 16);
+        if (q < code_pieces) return (const void*)(a.w2_codes + row0 * (I / 2) + q * 16);
+        return (const void*)(a.w2_scales + row0 * (I / 16) + (q - code_pieces) * 16);
+      }, [&](int p) { return (void*)(wbuf + (size_t)(p / pieces) * chunk + (p % pieces) * 16); });
+      wg_sync();
+      if (sl == (int)blockIdx.x && a0 == 0) stamp<TS>(a.timestamps, 42, 0);
+      // units: experts (2u, 2u+1) of this round together when both have <= 8 tokens
+      const int nunits = (na + 1) / 2;
+      for (int u = wave; cw && u < nunits; u += 8) {
+        const int iA = a0 + 2 * u, iB = iA + 1;
+        const bool hasB = iB < a0 + na;
+        const int cA = rt.act_cnt[iA], cB = hasB ? rt.act_cnt[iB] : 0;
+        const bool pairm = hasB && cA <= 8 && cB <= 8;
+        for (int pass = 0; pass < (pairm || !hasB ? 1 : 2); ++pass) {
+          // pass 0: expert A (with B when paired); pass 1: expert B alone
+          const int ia = pass == 0 ? iA : iB;
+          const int cnt_a = rt.act_cnt[ia], off_a = rt.act_off[ia];
+          const int cnt_b = pairm ? cB : 0, off_b = pairm ? rt.act_off[iB] : 0;
+          // B operand: column nl -> expert (nl < 8 ? ia : iB), weight row nl % 8
+          const bool bv = nl < 8 || pairm;
+          const int ib = nl < 8 ? ia : iB;
+          const char* wc = wbuf + (size_t)(ib - a0) * chunk;
+          // A operand: row m -> pair of expert ia (m < cnt_a, or m < 8 when paired) or iB
+          int pair_m = -1;
+          if (pairm) {
+            if (nl < 8) { if (nl < cnt_a) pair_m = rt.pair_list[off_a + nl]; }
+            else if (nl - 8 < cnt_b) pair_m = rt.pair_list[off_b + nl - 8];
+          } else if (nl < cnt_a) {
+            pair_m = rt.pair_list[off_a + nl];
+          }
+          const uint16_t* arow = actbf + (pair_m < 0 ? 0 : pair_m) * astride + grp * 8;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (fp4) {
+            const char* crow = wc + (nl & 7) * (I / 2) + 4 * grp;
+            const uint8_t* srow = (const uint8_t*)wc + code_bytes + (nl & 7) * (I / 16) + (grp >> 1);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) y[c] = 0.f;
-    for (int j = 0; j < K; ++j) {
-      const float gt = rt.gate[t * K + j];
-      const float* o = outp + (t * K + j) * 8;
+            for (int st = 0; st < 8; ++st) {
+              if (st < ksteps) {
+                const u32x4 x = pair_m >= 0 ? *(const u32x4*)(arow + st * 32) : u32x4{0, 0, 0, 0};
+                const uint32_t wcv = bv ? *(const uint32_t*)(crow + 16 * st) : 0u;
+                const float ws = bv ? e4m3_to_f32(srow[2 * st]) : 0.f;
+                acc = mfma_bf16(x, fp4x8_to_bf16(wcv, ws), acc);
+              }
+            }
+          } else {
+            const uint16_t* wr = (const uint16_t*)wc + (nl & 7) * I + grp * 8;
+            for (int st = 0; st < ksteps; ++st) {
+              const u32x4 b = bv ? *(const u32x4*)(wr + st * 32) : u32x4{0, 0, 0, 0};
+              const u32x4 x = pair_m >= 0 ? *(const u32x4*)(arow + st * 32) : u32x4{0, 0, 0, 0};
+              acc = mfma_bf16(x, b, acc);
+            }
+          }
+          // C lane: column nl, rows 4 grp + r; keep the diagonal block(s)
+          float ts = 1.0f;
+          if (fp4) ts = (nl < 8 || !pairm) ? a.w2_ts[rt.act_expert[ia]] : a.w2_ts[rt.act_expert[iB]];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) y[c] += gt * o[c];
+          for (int r = 0; r < 4; ++r) {
+            const int row = 4 * grp + r;
+            int pair = -1;
+            if (pairm) {
+              if (nl < 8 && row < 8 && row < cnt_a) pair = rt.pair_list[off_a + row];
+              else if (nl >= 8 && row >= 8 && row - 8 < cnt_b) pair = rt.pair_list[off_b + row - 8];
+            } else if (nl < 8 && row < cnt_a) {
+              pair = rt.pair_list[off_a + row];
+            }
+            if (pair >= 0) outp[pair * 8 + (nl & 7)] = acc[r] * ts;
+          }
+        }
+      }
+      wg_sync();
     }
-    uint16_t* dst = a.y + (size_t)t * P + c0;
-    st_coh_u64(dst, (uint64_t)pack_bf2(y[0], y[1]) | ((uint64_t)pack_bf2(y[2], y[3]) << 32));
-    st_coh_u64(dst + 4, (uint64_t)pack_bf2(y[4], y[5]) | ((uint64_t)pack_bf2(y[6], y[7]) << 32));
+    if (sl == (int)blockIdx.x) stamp<TS>(a.timestamps, 43, 0);
+    if (tid < T) {
+      float y[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = 0.f;
+      for (int j = 0; j < K; ++j) {
+        const float gt = rt.gate[tid * K + j];
+        const float* o = outp + (tid * K + j) * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] += gt * o[c];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ytile[tid * 4 + q] = pack_bf2(y[2 * q], y[2 * q + 1]);
+    }
+    wg_sync();
+    if (tid >= kCompute && (tid - kCompute) < T) {
+      const int t = tid - kCompute;
+      uint16_t* dst = a.y + (size_t)t * P + c0;
+      st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
+      st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
+    }
   }
-  __syncthreads();
+}
+
+// ------------------------------------------------------------------ dense phases
+
+// One dense phase: this workgroup's tiles t = first, first + n_wg, ...  Compute waves form
+// the wave partials (weights of the first tile already in `wf` when `have_pref`), the control
+// wave sums them and runs `epi(n0, red, it)`.  Two reduction buffers alternate so a tile needs
+// one workgroup barrier.  Called by all threads.
+template <int MAXS, class Epi>
+__device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
+                            const uint16_t* x, int K, int N, int off, float* red2, Epi epi) {
+  const int n = gridDim.x, ntiles = N / 16;
+  int it = 0;
+  for (int t = first_tile(off); t < ntiles; t += n, ++it) {
+    float* red = red2 + (it & 1) * (8 * 16 * 17);
+    if (threadIdx.x < kCompute) {
+      f32x4 acc;
+      if constexpr (MAXS == 0) {
+        acc = stream_mma(W, K, t * 16, x, a.T);
+      } else {
+        if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
+        acc = wfrag_mma(wf, x, a.T, K);
+      }
+      red_store(red, acc);
+    }
+    wg_sync();
+    if (threadIdx.x >= kCompute) epi(t * 16, red, it);
+  }
+}
+
+// End of a phase: compute waves run `pf` (loads for a later phase, left in flight) while the
+// control wave runs `ctlf`, signals and waits for the whole grid.  Returns true when the
+// launch is still alive.  Called by all threads; every compute-wave global store of the phase
+// must be complete before the call.
+template <bool TS, class PfF>
+__device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int phase, int32_t* dead_sh, PfF pf) {
+  wg_sync();
+  stamp<TS>(a.timestamps, 2 * phase);
+  if (threadIdx.x >= kCompute) {
+    const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0);
+    if (!ok && threadIdx.x == kCtl) *dead_sh = 1;
+    stamp<TS>(a.timestamps, 20 + phase);
+  } else {
+    pf();
+    stamp<TS>(a.timestamps, 28 + phase, 0);
+  }
+  wg_sync();
+  stamp<TS>(a.timestamps, 2 * phase + 1);
+  return *dead_sh == 0;
 }
 
 // ------------------------------------------------------------------ kernel
 
-template <bool TS>
-__global__ void __launch_bounds__(512) layer_kernel(KArgs a) {
+// SPEC 1: the shard shape of the pages' model on one GPU (hidden 4096, 8 q heads / 1 kv head
+// of 128, pooled 2048, 256 experts top-8, NVFP4 experts with local intermediate 192, a
+// 16-token tree) with every shape a compile-time constant; SPEC 0 takes shapes at run time.
+template <bool TS, int SPEC>
+__global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
+  KArgs a = a_in;
+  if constexpr (SPEC == 1) {
+    a.H = 4096; a.Hq = 8; a.Hkv = 1; a.d = 128; a.P = 2048; a.E = 256; a.topk = 8; a.I = 192;
+    a.fmt = 1; a.T = 16;
+  }
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ Route rt;
   __shared__ Tree tr;
-  uint64_t* ts = a.timestamps;
-  stamp<TS>(ts, 0);
-
-  Sync s;
-  s.flags = a.flags;
-  s.status = a.status;
-  s.spin_limit = a.spin_limit;
-  s.skip_wg = a.skip_wg;
-  s.dead = false;
+  __shared__ int32_t dead_sh;
   __shared__ uint32_t epoch_sh;
-  if (threadIdx.x == 0) epoch_sh = ld_coh_u32(a.epoch + blockIdx.x * 16);
-  // tree: ancestor masks, depths, first visible context row per token
-  if (threadIdx.x == 0) {
+  __shared__ int32_t par_sh[16];
+  __shared__ uint32_t outrow[68];
+  __shared__ uint32_t ytile[16 * 4];
+  const int tid = threadIdx.x;
+  const bool cw = tid < kCompute;
+  const int lane = tid & 63;
+  const int nwg = gridDim.x;
+  stamp<TS>(a.timestamps, 0);
+
+  // control lanes: row / columns of the 4 outputs they store in a dense tile epilogue
+  const int crow = lane >> 2, cc0 = (lane & 3) * 4;
+  const bool crv = crow < a.T;
+
+  // weights of the o-proj tile, and (control wave) its residual, fetched at launch
+  WFrag<MAXS_O> wo;
+  WFrag<0> wp;
+  WFrag<MAXS_R> wr;
+  WFrag<MAXS_U> wu;
+  WFrag<0> wq;
+  const int t_o = first_tile(0), t_p = first_tile(0), t_u = first_tile(0);
+  const int off_r = nwg - a.E / 16, off_q = a.P / 16 < nwg ? a.P / 16 : 0;
+  const int t_r = first_tile(off_r), t_q = first_tile(off_q);
+  const int qkv_n = (a.Hq + 2 * a.Hkv) * a.d;
+  const bool p_o = t_o < a.H / 16, p_p = t_p < a.P / 16, p_r = t_r < a.E / 16, p_u = t_u < a.H / 16,
+             p_q = t_q < qkv_n / 16;
+  u32x2 res = {0, 0};
+  if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
+
+  if (tid < a.T) par_sh[tid] = a.parent[tid];
+  if (tid == kCtl) {
+    epoch_sh = ld_coh_u32(a.epoch + blockIdx.x * 16);
+    dead_sh = 0;
+  }
+  wg_sync();
+  if (tid == 0) {
     int bad = 0;
     int depth[16];
     for (int i = 0; i < a.T; ++i) {
-      const int p = a.parent[i];
+      const int p = par_sh[i];
       if (i == 0) {
         bad |= p != -1;
         tr.anc[0] = 1u;
@@ -669,137 +1101,182 @@ __global__ void __launch_bounds__(512) layer_kernel(KArgs a) {
     if (bad && blockIdx.x == 0)
       __hip_atomic_store(a.status, (int32_t)MK_EBADTREE_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();
+  wg_sync();
+  stamp<TS>(a.timestamps, 1);
   const uint32_t epoch = epoch_sh;
+  Sync s;
+  s.flags = a.flags;
+  s.status = a.status;
   s.base = epoch * 64u;
-  const int nwg = gridDim.x;
+  s.spin_limit = a.spin_limit;
+  s.skip_wg = a.skip_wg;
+  float* red2 = (float*)smem;
+  auto nop = [] {};
+
   if (!tr.bad) {
-    float* red = (float*)smem;                       // dense reductions
-    // ---- ATTN
-    for (int it = blockIdx.x; it < a.attn_items; it += nwg) attention_item(a, tr, it, smem);
-    stamp<TS>(ts, 1);
-    grid_sync(s, 1);
-    // ---- MERGE
-    if (!s.dead) {
-      const int units = a.Hkv * a.T * (a.Hq / a.Hkv);
-      for (int u = blockIdx.x; u < units; u += nwg) merge_unit(a, u, (float*)smem);
+    bool alive = true;
+    uint32_t touched = 0;     // folded values of the cache-touch prefetches
+    // ---- 1 ATTN
+    for (int it = blockIdx.x; it < a.attn_items; it += nwg) {
+      attention_stage(a, it, smem);
+      if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 37, 0);
+      attention_compute<TS>(a, tr, it, smem);
+      if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 38, 0);
+      wg_sync();
     }
-    stamp<TS>(ts, 2);
-    grid_sync(s, 2);
-    // ---- OPROJ
-    if (!s.dead)
-      for (int t = blockIdx.x; t < a.H / 16; t += nwg)
-        dense_tile_bf16(a.attn, a.T, a.Hq * a.d, a.w_o, a.H, t * 16, a.h_in, a.h1, true, red);
-    stamp<TS>(ts, 3);
-    grid_sync(s, 3);
-    // ---- POOL
-    if (!s.dead)
-      for (int t = blockIdx.x; t < a.P / 16; t += nwg)
-        dense_tile_bf16(a.h1, a.T, a.H, a.w_pool, a.P, t * 16, nullptr, a.xp, true, red);
-    stamp<TS>(ts, 4);
-    grid_sync(s, 4);
-    // ---- ROUTER
-    if (!s.dead) {
-      for (int t = blockIdx.x; t < a.E / 16; t += nwg) {
-        f32x4 acc = dense_partial(a.xp, a.T, a.P, a.w_router, t * 16);
-        red_store(red, acc);
-        __syncthreads();
-        if (threadIdx.x < 64) {
-          const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 4;
-          if (row < a.T) {
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              v[j] = red_sum(red, row, c0 + j);
-              if (a.bias) v[j] += a.bias[(size_t)row * a.E + t * 16 + c0 + j];
-            }
-            float* dst = a.logits + (size_t)row * a.E + t * 16 + c0;
-            st_coh_u128(dst, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
-            if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)row * a.E + t * 16 + c0) = f32x4{v[0], v[1], v[2], v[3]};
+    if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
+    alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
+      if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
+      if (p_p) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
+    });
+    // ---- 2 MERGE
+    if (alive) {
+      const int units = a.Hkv * a.T * (a.Hq / a.Hkv);
+      const int G = a.Hq / a.Hkv, R = a.T * G;
+      for (int u = blockIdx.x; u < units; u += nwg) {
+        merge_unit(a, u, (float*)smem, outrow);
+        wg_sync();
+        if (!cw) {
+          const int g_kv = u / R, row = u % R, tok = row / G, head = g_kv * G + row % G;
+          if (lane < a.d / 4)
+            st_coh_u64(a.attn + (size_t)tok * a.Hq * a.d + head * a.d + lane * 4,
+                       (uint64_t)outrow[2 * lane] | ((uint64_t)outrow[2 * lane + 1] << 32));
+          if (lane == 0 && a.attn_stats) {
+            a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 0] = __uint_as_float(outrow[64]);
+            a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 1] = __uint_as_float(outrow[65]);
           }
         }
-        __syncthreads();
       }
     }
-    stamp<TS>(ts, 5);
-    grid_sync(s, 5);
-    // ---- ROUTE + GEMM1
-    if (!s.dead) {
+    alive = phase_end<TS>(a, s, 2, &dead_sh, nop) && alive;
+    // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T)
+    if (alive) {
+      dense_phase(a, wo, p_o, a.w_o, a.attn, a.Hq * a.d, a.H, 0, red2, [&](int n0, const float* red, int it) {
+        if (!crv) return;
+        float v[4];
+        ctl_tile_vals(red, crow, cc0, v);
+        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h_in + (size_t)crow * a.H + n0 + cc0);
+        v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
+        st_coh_u64(a.h1 + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
+      });
+    }
+    alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive;
+    // ---- 4 POOL: xp = bf16(h1 Wp^T)
+    if (alive) {
+      // control wave: the unpooler's residual (h1) for its first tile, needed in phase 8
+      if (!cw && p_u && crv) res = *(const u32x2*)(a.h1 + (size_t)crow * a.H + t_u * 16 + cc0);
+      dense_phase(a, wp, false, a.w_pool, a.h1, a.H, a.P, 0, red2, [&](int n0, const float* red, int) {
+        if (!crv) return;
+        float v[4];
+        ctl_tile_vals(red, crow, cc0, v);
+        st_coh_u64(a.xp + (size_t)crow * a.P + n0 + cc0, pack4_bf16(v));
+      });
+    }
+    alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
+    // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
+    if (alive) {
+      dense_phase(a, wr, p_r, a.w_router, a.xp, a.P, a.E, off_r, red2, [&](int n0, const float* red, int) {
+        if (!crv) return;
+        float v[4];
+        ctl_tile_vals(red, crow, cc0, v);
+        if (a.bias) {
+          const f32x4 b = *(const f32x4*)(a.bias + (size_t)crow * a.E + n0 + cc0);
+          v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
+        }
+        st_coh_u128(a.logits + (size_t)crow * a.E + n0 + cc0,
+                    u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+        if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)crow * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
+      });
+    }
+    alive = phase_end<TS>(a, s, 5, &dead_sh, nop) && alive;
+    // ---- 6 ROUTE + GEMM1
+    if (alive) {
       route_tables(a, rt, (float*)smem);
+      stamp<TS>(a.timestamps, 18);
+      gemm1_phase<TS>(a, rt, smem);
+      if (cw) __builtin_amdgcn_s_waitcnt(0);   // intermediate stores complete
+    }
+    alive = phase_end<TS>(a, s, 6, &dead_sh, [&] { if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
+    // ---- 7 GEMM2 + combine
+    if (alive) gemm2_phase<TS>(a, rt, smem, ytile);
+    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16); }) && alive;
+    // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
+    if (alive) {
+      dense_phase(a, wu, p_u, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
+        if (!crv) return;
+        float v[4];
+        ctl_tile_vals(red, crow, cc0, v);
+        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + (size_t)crow * a.H + n0 + cc0);
+        v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
+        st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
+      });
+    }
+    alive = phase_end<TS>(a, s, 8, &dead_sh, nop) && alive;
+    // ---- QKV + KV write
+    if (alive) {
+      const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
+      dense_phase(a, wq, false, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+        if (!crv) return;
+        float v[4];
+        ctl_tile_vals(red, crow, cc0, v);
+        const int n = n0 + cc0;
+        uint16_t* dst;
+        if (n < qd) dst = a.q_next + (size_t)crow * qd + n;
+        else if (n < qd + kd) dst = a.kn + (size_t)(a.ctx + crow) * kd + (n - qd);
+        else dst = a.vn + (size_t)(a.ctx + crow) * kd + (n - qd - kd);
+        *(uint64_t*)dst = pack4_bf16(v);
+      });
       if (blockIdx.x == 0) {
-        for (int p = threadIdx.x; p < a.T * a.topk; p += blockDim.x) {
+        for (int p = tid; p < a.T * a.topk; p += kThreads) {
           if (a.topk_idx) a.topk_idx[p] = rt.idx[p];
           if (a.topk_gate) a.topk_gate[p] = rt.gate[p];
         }
         if (a.hist)
-          for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.hist[e] += rt.expert_cnt[e];
-      }
-      stamp<TS>(ts, 6);
-      const int jblocks = a.I / 16;
-      const int ntasks = rt.n_active * jblocks;
-      float* abuf = red + 2 * 8 * 16 * 17;
-      for (int t = blockIdx.x; t < ntasks; t += nwg) gemm1_task(a, rt, t / jblocks, (t % jblocks) * 16, red, abuf);
-    }
-    stamp<TS>(ts, 7);
-    grid_sync(s, 6);
-    // ---- GEMM2 + combine
-    if (!s.dead)
-      for (int c = blockIdx.x; c < a.P / 8; c += nwg) gemm2_slice(a, rt, c * 8, (float*)smem);
-    stamp<TS>(ts, 8);
-    grid_sync(s, 7);
-    // ---- UNPOOL
-    if (!s.dead)
-      for (int t = blockIdx.x; t < a.H / 16; t += nwg)
-        dense_tile_bf16(a.y, a.T, a.P, a.w_unpool, a.H, t * 16, a.h1, a.h_out, true, red);
-    stamp<TS>(ts, 9);
-    grid_sync(s, 8);
-    // ---- QKV + KV write
-    if (!s.dead) {
-      const int qd = a.Hq * a.d, kd = a.Hkv * a.d, N = qd + 2 * kd;
-      for (int t = blockIdx.x; t < N / 16; t += nwg) {
-        const int n0 = t * 16;
-        f32x4 acc = dense_partial(a.h_out, a.T, a.H, a.w_qkv, n0);
-        red_store(red, acc);
-        __syncthreads();
-        if (threadIdx.x < 64) {
-          const int row = threadIdx.x >> 2, c0 = (threadIdx.x & 3) * 4;
-          if (row < a.T) {
-            float v[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = red_sum(red, row, c0 + j);
-            const uint64_t packed = (uint64_t)pack_bf2(v[0], v[1]) | ((uint64_t)pack_bf2(v[2], v[3]) << 32);
-            const int n = n0 + c0;
-            uint16_t* dst;
-            if (n < qd) dst = a.q_next + (size_t)row * qd + n;
-            else if (n < qd + kd) dst = a.kn + (size_t)(a.ctx + row) * kd + (n - qd);
-            else dst = a.vn + (size_t)(a.ctx + row) * kd + (n - qd - kd);
-            *(uint64_t*)dst = packed;
-          }
-        }
-        __syncthreads();
+          for (int e = tid; e < a.E; e += kThreads) a.hist[e] += rt.expert_cnt[e];
       }
     }
-    stamp<TS>(ts, 10);
+    stamp<TS>(a.timestamps, 19);
+    if (touched == 0x9E3779B9u) ytile[0] = touched;   // keeps the touch loads alive
   }
-  // next launch on this workspace uses the next epoch
-  if (threadIdx.x == 0) st_coh_u32(a.epoch + blockIdx.x * 16, epoch + 1);
+  // a launch that skipped its phases still advances its counter by the 8 hand-offs, so the
+  // next launch's targets line up
+  if constexpr (SYNC_MODE == 1) {
+    if (tid == kCtl && tr.bad)
+      __hip_atomic_fetch_add(a.flags + (blockIdx.x & 7) * 64, 8u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // the next launch on this workspace uses the next epoch
+  if (tid == kCtl) st_coh_u32(a.epoch + blockIdx.x * 16, epoch + 1);
 }
 
-template __global__ void layer_kernel<false>(KArgs);
-template __global__ void layer_kernel<true>(KArgs);
+template __global__ void layer_kernel<false, 0>(KArgs);
+template __global__ void layer_kernel<true, 0>(KArgs);
+template __global__ void layer_kernel<false, 1>(KArgs);
+template __global__ void layer_kernel<true, 1>(KArgs);
+
+int layer_lds_bytes() { return LDS_BYTES; }
+
+static bool is_spec1(const KArgs& a) {
+  return a.H == 4096 && a.Hq == 8 && a.Hkv == 1 && a.d == 128 && a.P == 2048 && a.E == 256 && a.topk == 8 &&
+         a.I == 192 && a.fmt == 1 && a.T == 16;
+}
 
 int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream) {
-  if (a.timestamps) {
-    hipLaunchKernelGGL(layer_kernel<true>, dim3(a.n_wg), dim3(512), lds_bytes, stream, a);
+  const dim3 g(a.n_wg), b(kThreads);
+  if (is_spec1(a)) {
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 1>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 1>), g, b, lds_bytes, stream, a);
   } else {
-    hipLaunchKernelGGL(layer_kernel<false>, dim3(a.n_wg), dim3(512), lds_bytes, stream, a);
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 0>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 0>), g, b, lds_bytes, stream, a);
   }
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 int set_layer_kernel_attrs(int lds_bytes) {
-  if (hipFuncSetAttribute((const void*)layer_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess) return -5;
-  if (hipFuncSetAttribute((const void*)layer_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess) return -5;
+  const void* fns[] = {(const void*)layer_kernel<false, 0>, (const void*)layer_kernel<true, 0>,
+                       (const void*)layer_kernel<false, 1>, (const void*)layer_kernel<true, 1>};
+  for (const void* f : fns)
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess) return -5;
   return 0;
 }
 
