@@ -11,7 +11,6 @@
 namespace {
 
 constexpr int kMaxDevices = 64;
-constexpr int kChunkKeys = 128;            // KV rows per attention work item
 constexpr int kDefaultSpin = 1 << 20;      // polls per wait before MK_ETIMEOUT
 
 std::mutex g_mu;
@@ -59,23 +58,32 @@ int check_cfg(const mk_layer_cfg* c, int T) {
 
 struct Layout {
   size_t status, epoch, flags, part_o, part_ml, attn, h1, xp, logits, act, y, total;
-  int n_wg, items, chunks_per_head, attn_lo;
+  int n_wg, items, chunks_per_head, attn_lo, ck;
 };
 
-// attention work split: context rows [attn_lo, ctx) in chunks of kChunkKeys, plus one chunk
+// attention work split: context rows [attn_lo, ctx) in chunks of ck keys (64 up to 8192
+// visible rows, so that more workgroups share a short context; 128 beyond), plus one chunk
 // holding the tree's own slots, for each kv head
-void attn_split(const mk_layer_cfg* c, int ctx, int* lo, int* chunks) {
+void attn_split(const mk_layer_cfg* c, int ctx, int* lo, int* chunks, int* ck) {
   const int l = c->window > 0 ? (ctx - c->window + 1 > 0 ? ctx - c->window + 1 : 0) : 0;
+  const int keys = ctx - l;
   *lo = l;
-  *chunks = (ctx - l + kChunkKeys - 1) / kChunkKeys + 1;
+  *ck = keys <= 8192 ? 64 : 128;
+  *chunks = (keys + *ck - 1) / *ck + 1;
 }
 
 Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   Layout L;
   memset(&L, 0, sizeof(L));
   L.n_wg = n_wg;
-  attn_split(c, ctx, &L.attn_lo, &L.chunks_per_head);
+  attn_split(c, ctx, &L.attn_lo, &L.chunks_per_head, &L.ck);
   L.items = c->n_kv_heads * L.chunks_per_head;
+  // the partial buffers must hold the largest split of any context up to `ctx`
+  if (ctx > 8192) {
+    int lo2, ch2, ck2;
+    attn_split(c, 8192, &lo2, &ch2, &ck2);
+    if (c->n_kv_heads * ch2 > L.items) L.items = c->n_kv_heads * ch2;
+  }
   const int H = c->hidden, Hq = c->n_q_heads, d = c->head_dim, P = c->pooled, E = c->n_experts,
             k = c->top_k, I = c->expert_inter;
   size_t o = 0;
@@ -188,7 +196,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
   a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
   a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
-  a.attn_lo = Lc.attn_lo; a.ck = kChunkKeys;
+  a.attn_lo = Lc.attn_lo; a.ck = Lc.ck;
   a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
   a.skip_wg = io->debug_skip_signal_wg;
   a.parent = io->tree_parent;

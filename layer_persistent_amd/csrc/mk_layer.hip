@@ -52,7 +52,6 @@ constexpr int MAXS_P = 16;         // pooler   K = H    <= 4096
 constexpr int MAXS_R = 8;          // router   K = P    <= 2048
 constexpr int MAXS_U = 8;          // unpooler K = P    <= 2048
 constexpr int MAXS_Q = 16;         // qkv      K = H    <= 4096
-constexpr int MAXT = 4;            // GEMM1 tasks per batch
 #ifndef MK_SYNC_MODE
 #define MK_SYNC_MODE 0
 #endif
@@ -61,9 +60,8 @@ constexpr int SYNC_MODE = MK_SYNC_MODE;   // grid hand-off: 1 sharded counters, 
 // dynamic LDS layout (byte offsets; phases reuse the same space)
 constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
 constexpr int G1_XS_BYTES = 16 * (2048 + 8) * 2;       // xp rows for GEMM1
-constexpr int G1_RED_FLOATS = MAXT * 2 * 8 * 16 * 17;  // per-task partial gate/up tiles
 constexpr int LDS_BYTES = 144 * 1024;                  // >= every phase's use (GEMM1: 136.5 KB)
-static_assert(G1_XS_BYTES + G1_RED_FLOATS * 4 + MAXT * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
+static_assert(G1_XS_BYTES + 16 * 16 * 128 + 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
 
 __device__ __forceinline__ void wg_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -352,7 +350,27 @@ __device__ __forceinline__ void stage_pieces(int n, SrcF piece, DstF dst) {
 // Rows are (token, q head of this kv head) pairs, row = t * G + (h - g*G), R = T*G <= 128;
 // wave w owns rows [16w, 16w + 16).  S^T = K Q^T puts keys on the MFMA M axis so that the
 // probabilities land in exactly the B-operand layout the P.V product needs.
-// Called by all threads (the staging barrier counts every wave).
+
+// This lane's query fragments (B operand of S^T): row = 16 wave + l%16, d = 32 s + 8 (l/16).
+__device__ __forceinline__ void attention_q(const KArgs& a, int item, u32x4 qf[4]) {
+  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
+  const int g_kv = item / a.attn_chunks_per_head;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = wave * 16 + (lane & 15), grp = lane >> 4;
+  const bool rv = threadIdx.x < kCompute && row < R;
+  const int tok = rv ? row / G : 0, head = g_kv * G + (rv ? row % G : 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    qf[s] = (s < d / 32 && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
+                               : u32x4{0, 0, 0, 0};
+}
+
+// LDS of an item: K row-major [128][d + 8] bf16, then V transposed as key pairs:
+// VT32[dd][kp] = V[2kp][dd] | V[2kp+1][dd] << 16, row stride 66 dwords (conflict-free reads).
+constexpr int kVtStride32 = 66;
+
+// Stage the item's K and V into LDS (keys beyond nk zeroed).  Every load of a thread is
+// issued before its LDS stores.  Called by all threads (ends in a workgroup barrier).
 __device__ __forceinline__ void attention_stage(const KArgs& a, int item, char* smem) {
   const int d = a.d;
   const int g_kv = item / a.attn_chunks_per_head;
@@ -361,40 +379,43 @@ __device__ __forceinline__ void attention_stage(const KArgs& a, int item, char* 
   const int kb = tree_chunk ? a.ctx : a.attn_lo + chunk * a.ck;
   const int nk = tree_chunk ? a.T : min(a.ck, a.ctx - kb);
   const int CK = 128;                           // LDS chunk capacity
-  const int ks_stride = d + 8;                  // bf16 elements per K row in LDS
-  const int vt_stride = CK + 8;                 // bf16 elements per V^T row in LDS
-  uint16_t* Ks = (uint16_t*)smem;               // [CK][ks_stride]
-  uint16_t* VT = Ks + CK * ks_stride;           // [d][vt_stride]
+  const int ks_stride = d + 8;
+  uint16_t* Ks = (uint16_t*)smem;
+  uint32_t* VT = (uint32_t*)(Ks + CK * ks_stride);
   const int tid = threadIdx.x;
-
-  // stage K (row-major) and V (transposed) for keys kb..kb+nk, zero beyond nk; all loads
-  // of a thread are issued before its LDS stores
   const int per_row = d / 8;                    // 16-byte pieces per key row
   if (tid < kCompute) {
-    constexpr int kMaxPer = (128 * 16) / kCompute;   // pieces per thread at d = 128
-    u32x4 kv[kMaxPer], vv[kMaxPer];
+    constexpr int kKPer = (128 * 16) / kCompute;     // K pieces per thread at d = 128
+    constexpr int kVPer = (64 * 16) / kCompute;      // V pair-pieces per thread at d = 128
+    u32x4 kv[kKPer], v0[kVPer], v1[kVPer];
+    const size_t rstride = (size_t)a.Hkv * d;
+    const uint16_t* kbase = a.kc + ((size_t)kb * a.Hkv + g_kv) * d;
+    const uint16_t* vbase = a.vc + ((size_t)kb * a.Hkv + g_kv) * d;
 #pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int i = tid + j * kCompute;
-      const int key = i / per_row, c = (i % per_row) * 8;
-      kv[j] = u32x4{0, 0, 0, 0};
-      vv[j] = u32x4{0, 0, 0, 0};
-      if (i < CK * per_row && key < nk) {
-        const size_t off = ((size_t)(kb + key) * a.Hkv + g_kv) * d + c;
-        kv[j] = ld16(a.kc + off);
-        vv[j] = ld16(a.vc + off);
-      }
+    for (int j = 0; j < kKPer; ++j) {
+      const int i = tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
+      kv[j] = (i < CK * per_row && key < nk) ? ld16(kbase + key * rstride + c) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < kMaxPer; ++j) {
-      const int i = tid + j * kCompute;
-      if (i < CK * per_row) {
-        const int key = i / per_row, c = (i % per_row) * 8;
-        *(u32x4*)(Ks + key * ks_stride + c) = kv[j];
+    for (int j = 0; j < kVPer; ++j) {
+      const int i = tid + j * kCompute, kp = i & 63, c = (i >> 6) * 8;
+      const bool ok = i < 8 * d;
+      v0[j] = (ok && 2 * kp < nk) ? ld16(vbase + (2 * kp) * rstride + c) : u32x4{0, 0, 0, 0};
+      v1[j] = (ok && 2 * kp + 1 < nk) ? ld16(vbase + (2 * kp + 1) * rstride + c) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < kKPer; ++j) {
+      const int i = tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
+      if (i < CK * per_row) *(u32x4*)(Ks + key * ks_stride + c) = kv[j];
+    }
+#pragma unroll
+    for (int j = 0; j < kVPer; ++j) {
+      const int i = tid + j * kCompute, kp = i & 63, c = (i >> 6) * 8;
+      if (i < 8 * d) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          VT[(c + 2 * q) * vt_stride + key] = (uint16_t)(vv[j][q] & 0xFFFF);
-          VT[(c + 2 * q + 1) * vt_stride + key] = (uint16_t)(vv[j][q] >> 16);
+          VT[(c + 2 * q) * kVtStride32 + kp] = (v0[j][q] & 0xFFFFu) | (v1[j][q] << 16);
+          VT[(c + 2 * q + 1) * kVtStride32 + kp] = (v0[j][q] >> 16) | (v1[j][q] & 0xFFFF0000u);
         }
       }
     }
@@ -405,7 +426,8 @@ __device__ __forceinline__ void attention_stage(const KArgs& a, int item, char* 
 // the compute half of an attention item (after the staging barrier); no barriers inside,
 // threads of the control wave return at once
 template <bool TS>
-__device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, int item, char* smem) {
+__device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, int item, char* smem,
+                                                  const u32x4 qf[4]) {
   const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
   const int g_kv = item / a.attn_chunks_per_head;
   const int chunk = item % a.attn_chunks_per_head;
@@ -414,9 +436,8 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
   const int nk = tree_chunk ? a.T : min(a.ck, a.ctx - kb);
   const int CK = 128;
   const int ks_stride = d + 8;
-  const int vt_stride = CK + 8;
   const uint16_t* Ks = (const uint16_t*)smem;
-  const uint16_t* VT = Ks + CK * ks_stride;
+  const uint32_t* VT = (const uint32_t*)(Ks + CK * ks_stride);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, grp = lane >> 4;
@@ -424,14 +445,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
   if (threadIdx.x >= kCompute || wave * 16 >= R) return;
   const bool rv = row < R;
   const int tok = rv ? row / G : 0;
-  const int head = g_kv * G + (rv ? row % G : 0);
   const int dsteps = d / 32;
-  u32x4 qf[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = (s < dsteps && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
-                               : u32x4{0, 0, 0, 0};
-  }
   if constexpr (TS) {   // q fragments arrived
     if (threadIdx.x == 0 && item == (int)blockIdx.x) {
       uint32_t x = qf[0][0] | qf[1][1];
@@ -469,6 +483,8 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
     }
   }
   mrow = xgroup_max(mrow);
+  // exp(-inf - m) = 0 for masked keys; a row with no visible key here uses m = 0 (all p = 0)
+  const float msafe = mrow == -INFINITY ? 0.f : mrow;
   float lsum = 0.f;
   uint32_t pb[8][2];
 #pragma unroll
@@ -476,7 +492,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      p[r] = (mrow == -INFINITY || sc[kt][r] == -INFINITY) ? 0.f : __expf(sc[kt][r] - mrow);
+      p[r] = __expf(sc[kt][r] - msafe);
       lsum += p[r];
     }
     pb[kt][0] = pack_bf2(p[0], p[1]);
@@ -500,9 +516,9 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         if (dt < dtiles) {
-          const uint16_t* vrow = VT + (dt * 16 + nl) * vt_stride;
-          u32x2 v0 = *(const u32x2*)(vrow + (2 * q) * 16 + 4 * grp);
-          u32x2 v1 = *(const u32x2*)(vrow + (2 * q + 1) * 16 + 4 * grp);
+          const uint32_t* vrow = VT + (dt * 16 + nl) * kVtStride32;
+          const u32x2 v0 = *(const u32x2*)(vrow + ((2 * q) * 16 + 4 * grp) / 2);
+          const u32x2 v1 = *(const u32x2*)(vrow + ((2 * q + 1) * 16 + 4 * grp) / 2);
           u32x4 afrag = {v0[0], v0[1], v1[0], v1[1]};
           o[dt] = mfma_bf16(afrag, bfrag, o[dt]);
         }
@@ -543,19 +559,29 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
   const int tq = threadIdx.x % 32, cg = threadIdx.x / 32;
   float M = -INFINITY, L = 0.f, O[4] = {0.f, 0.f, 0.f, 0.f};
   if (tq < quads && threadIdx.x < kCompute) {
-    for (int c = cg; c < nchunks; c += ngroups) {
-      const int item = g_kv * nchunks + c;
-      const f32x2 ml = *(const f32x2*)(a.part_ml + ((size_t)item * 128 + row) * 2);
-      const float m = ml[0], l = ml[1];
-      if (l <= 0.f) continue;
-      const f32x4 o = *(const f32x4*)(a.part_o + ((size_t)item * 128 + row) * d + tq * 4);
-      const float Mn = fmaxf(M, m);
-      const float s_old = (M == -INFINITY) ? 0.f : __expf(M - Mn);
-      const float s_new = __expf(m - Mn);
-      L = L * s_old + l * s_new;
+    // four chunks' partials loaded together per round trip
+    for (int c0 = cg; c0 < nchunks; c0 += 4 * ngroups) {
+      f32x2 ml[4];
+      f32x4 o[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) O[j] = O[j] * s_old + o[j] * s_new;
-      M = Mn;
+      for (int j = 0; j < 4; ++j) {
+        const int c = c0 + j * ngroups;
+        const size_t r = (size_t)(g_kv * nchunks + c) * 128 + row;
+        ml[j] = c < nchunks ? *(const f32x2*)(a.part_ml + r * 2) : f32x2{-INFINITY, 0.f};
+        o[j] = c < nchunks ? *(const f32x4*)(a.part_o + r * d + tq * 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float m = ml[j][0], l = ml[j][1];
+        if (l <= 0.f) continue;
+        const float Mn = fmaxf(M, m);
+        const float s_old = (M == -INFINITY) ? 0.f : __expf(M - Mn);
+        const float s_new = __expf(m - Mn);
+        L = L * s_old + l * s_new;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) O[q] = O[q] * s_old + o[j][q] * s_new;
+        M = Mn;
+      }
     }
   }
   if (threadIdx.x < kCompute) {
@@ -683,10 +709,18 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
 
 // ------------------------------------------------------------------ experts
 
-// GEMM1 for all of this workgroup's (expert, 16-column block) tasks: xp rows staged in LDS,
-// the weights of MAXT tasks loaded together (8 waves split K = P), per-task reduction over
-// the waves in LDS, SwiGLU, NVFP4 requantisation of the intermediate (tensor scale 1).
+// GEMM1 for this workgroup's tasks.  A task is (active expert, block of 16 intermediate
+// columns j0..j0+15); tasks are ordered by expert and each workgroup takes a contiguous
+// range, so its tasks mostly share one expert.  A task has two units: the 16 gate rows
+// (j0 + i) and the 16 up rows (I + j0 + i) of W1.  Each wave owns whole units over the full
+// K = P, so no reduction across waves is needed: it loads all its codes at once (16 bytes
+// per lane per 128 k), stages the unit's scales through LDS, reads the tokens' xp rows from
+// LDS, and leaves the 16x16 tile u = xp W1^T ts1 in LDS.  The workgroup then forms
+// a = silu(u_gate) * u_up and requantises it to NVFP4 (tensor scale 1) per 16-element block.
 // Called by all threads.
+constexpr int G1_UNITS = 16;                   // units per round (2 per compute wave)
+constexpr int G1_MAXLS = 16;                   // NVFP4 load steps (128 k each): P <= 2048
+
 template <bool TS>
 __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
@@ -694,121 +728,146 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   const int jblocks = I / 16;
   const int ntasks = rt.n_active * jblocks;
   const int nwg = gridDim.x;
-  if ((int)blockIdx.x >= ntasks) return;        // uniform over the workgroup
+  const int t_begin = (int)((long)blockIdx.x * ntasks / nwg), t_end = (int)((long)(blockIdx.x + 1) * ntasks / nwg);
+  if (t_begin >= t_end) return;                 // uniform over the workgroup
   const int xstride = P + XS_STRIDE_PAD;
-  uint16_t* xs = (uint16_t*)smem;
-  float* red = (float*)(smem + G1_XS_BYTES);    // [MAXT][2][8 waves][16][17]
-  float* abuf = red + G1_RED_FLOATS;            // [MAXT][16][17]
+  uint16_t* xs = (uint16_t*)smem;                                  // [T][P + 8] bf16
+  uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // [16 units][16 rows][P/16]
+  float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][16][17]
   stage_pieces(T * (P / 8), [&](int i) { return (const void*)(a.xp + (size_t)i * 8); },
                [&](int i) { return (void*)(xs + (i / (P / 8)) * xstride + (i % (P / 8)) * 8); });
   wg_sync();
   stamp<TS>(a.timestamps, 44, 0);
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
-  const int lsteps = P / 128;                   // NVFP4: 16 B of codes per lane = 128 k per step
-  for (int t0 = blockIdx.x; t0 < ntasks; t0 += MAXT * nwg) {
-    const int nb = min(MAXT, (ntasks - t0 + nwg - 1) / nwg);
-    if (cw) {
-      u32x4 cg[MAXT][2], cu[MAXT][2];
-      uint32_t sgv[MAXT][2], suv[MAXT][2];
-      if (a.fmt == 1) {
+  const int lsteps = P / 128;
+  const int nunits = 2 * (t_end - t_begin);
+  for (int u0 = 0; u0 < nunits; u0 += G1_UNITS) {
+    const int nu = min(G1_UNITS, nunits - u0);
+    if (cw && a.fmt == 1) {
+      // This wave's units u0 + wave and u0 + wave + 8, streamed as half-units (8 load steps
+      // of 128 k): the codes of the next half-unit (and, at a unit's start, its scales) are
+      // in flight while the current one is multiplied.
+      const int nh = lsteps > 8 ? 2 : 1;                         // halves per unit
+      const int my_units = (wave < nu) + (wave + 8 < nu);
+      const int nhu = my_units * nh;
+      auto unit_of = [&](int hu) { return wave + 8 * (hu / nh); };
+      auto load_half = [&](int hu, u32x4 (&cd)[8], u32x4 (&sv)[2]) {
+        const int u = unit_of(hu), hf = hu % nh;
+        const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
+        const int ai = task / jblocks, j0 = (task % jblocks) * 16;
+        const size_t wrow = (size_t)rt.act_expert[ai] * 2 * I + half * I + j0;
+        const uint8_t* cp = a.w1_codes + (wrow + nl) * (P / 2) + grp * 16 + hf * 8 * 64;
 #pragma unroll
-        for (int i = 0; i < MAXT; ++i) {
-          if (i < nb) {
-            const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
-            const size_t rows = 2 * (size_t)I, e = rt.act_expert[ai];
-            const uint8_t* cgp = a.w1_codes + (e * rows + j0 + nl) * (P / 2) + grp * 16;
-            const uint8_t* cup = a.w1_codes + (e * rows + I + j0 + nl) * (P / 2) + grp * 16;
-            const uint8_t* sgp = a.w1_scales + (e * rows + j0 + nl) * (P / 16) + grp * 2;
-            const uint8_t* sup = a.w1_scales + (e * rows + I + j0 + nl) * (P / 16) + grp * 2;
+        for (int j = 0; j < 8; ++j) if (hf * 8 + j < lsteps) cd[j] = ld16(cp + j * 64);
+        if (hf == 0) {
+          // the unit's 16 rows of scales (16 * P/16 bytes): 16 bytes per lane per 1 KB
+          const uint8_t* sp = a.w1_scales + wrow * (P / 16);
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int ls = wave + 8 * jj;
-              if (ls < lsteps) {
-                cg[i][jj] = ld16(cgp + ls * 64);
-                cu[i][jj] = ld16(cup + ls * 64);
-                sgv[i][jj] = *(const uint16_t*)(sgp + ls * 8);
-                suv[i][jj] = *(const uint16_t*)(sup + ls * 8);
-              }
-            }
-          }
+          for (int j = 0; j < 2; ++j) if ((lane + 64 * j) * 16 < 16 * (P / 16)) sv[j] = ld16(sp + (lane + 64 * j) * 16);
         }
-      }
-#pragma unroll
-      for (int i = 0; i < MAXT; ++i) {
-        if (i < nb) {
-          const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
+      };
+      u32x4 cA[8], cB[8], sA[2], sB[2];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (nhu > 0) load_half(0, cA, sA);
+#pragma unroll 1
+      for (int hu = 0; hu < nhu; hu += 2) {
+        // ---- half-unit hu in cA / sA; prefetch hu + 1 into cB / sB
+        for (int x = 0; x < 2; ++x) {
+          const int h = hu + x;
+          if (h >= nhu) break;
+          if (h + 1 < nhu) {
+            if (x == 0) load_half(h + 1, cB, sB); else load_half(h + 1, cA, sA);
+          }
+          const int u = unit_of(h), hf = h % nh;
+          const int task = t_begin + (u0 + u) / 2;
+          const int ai = task / jblocks;
           const int e = rt.act_expert[ai], cnt = rt.act_cnt[ai], off = rt.act_off[ai];
+          uint8_t* sd = sbuf + u * 16 * (P / 16);
+          if (hf == 0) {
+            const u32x4* sv = x == 0 ? sA : sB;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) if ((lane + 64 * j) * 16 < 16 * (P / 16)) *(u32x4*)(sd + (lane + 64 * j) * 16) = sv[j];
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
           const bool mv = nl < cnt;
-          const uint16_t* xrow = xs + (mv ? rt.pair_list[off + nl] / K : 0) * xstride;
-          f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-          if (a.fmt == 1) {
+          const uint16_t* xrow = xs + (mv ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
+          const uint8_t* srow = sd + nl * (P / 16) + grp * 2;
+          const u32x4* cd = x == 0 ? cA : cB;
 #pragma unroll
-            for (int jj = 0; jj < 2; ++jj) {
-              const int ls = wave + 8 * jj;
-              if (ls < lsteps) {
-                const float sg0 = e4m3_to_f32(sgv[i][jj] & 0xFF), sg1 = e4m3_to_f32(sgv[i][jj] >> 8);
-                const float su0 = e4m3_to_f32(suv[i][jj] & 0xFF), su1 = e4m3_to_f32(suv[i][jj] >> 8);
+          for (int j = 0; j < 8; ++j) {
+            const int ls = hf * 8 + j;
+            if (ls < lsteps) {
+              const uint32_t sc = *(const uint16_t*)(srow + ls * 8);
+              const float s0 = e4m3_to_f32(sc & 0xFF), s1 = e4m3_to_f32(sc >> 8);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                  const int k = ls * 128 + grp * 32 + s * 8;
-                  const u32x4 xa = mv ? *(const u32x4*)(xrow + k) : u32x4{0, 0, 0, 0};
-                  accg = mfma_bf16(xa, fp4x8_to_bf16(cg[i][jj][s], s < 2 ? sg0 : sg1), accg);
-                  accu = mfma_bf16(xa, fp4x8_to_bf16(cu[i][jj][s], s < 2 ? su0 : su1), accu);
-                }
+              for (int q = 0; q < 4; ++q) {
+                const u32x4 xa = mv ? *(const u32x4*)(xrow + ls * 128 + q * 8) : u32x4{0, 0, 0, 0};
+                acc = mfma_bf16(xa, fp4x8_to_bf16(cd[j][q], q < 2 ? s0 : s1), acc);
               }
             }
-          } else {
-            const uint16_t* wgr = a.w1 + ((size_t)e * 2 * I + j0 + nl) * P + grp * 8;
-            const uint16_t* wur = a.w1 + ((size_t)e * 2 * I + I + j0 + nl) * P + grp * 8;
-            for (int s = wave; s < P / 32; s += 8) {
-              const u32x4 xa = mv ? *(const u32x4*)(xrow + s * 32 + grp * 8) : u32x4{0, 0, 0, 0};
-              accg = mfma_bf16(xa, ld16(wgr + s * 32), accg);
-              accu = mfma_bf16(xa, ld16(wur + s * 32), accu);
-            }
           }
-          float* pg = red + ((i * 2 + 0) * 8 + wave) * (16 * 17);
-          float* pu = red + ((i * 2 + 1) * 8 + wave) * (16 * 17);
+          if (hf == nh - 1) {
+            const float ts = a.w1_ts[e];
+            float* ub = ubuf + u * (16 * 17);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            pg[(4 * grp + r) * 17 + nl] = accg[r];
-            pu[(4 * grp + r) * 17 + nl] = accu[r];
+            for (int r = 0; r < 4; ++r) ub[(4 * grp + r) * 17 + nl] = acc[r] * ts;
           }
+        }
+      }
+    } else if (cw) {
+      // bf16 experts: rows loaded as they are used
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int u = wave + 8 * h;
+        if (u < nu) {
+          const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
+          const int ai = task / jblocks, j0 = (task % jblocks) * 16;
+          const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
+          const bool mv = nl < cnt;
+          const uint16_t* xrow = xs + (mv ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 8;
+          const uint16_t* wr = a.w1 + ((size_t)rt.act_expert[ai] * 2 * I + half * I + j0 + nl) * P + grp * 8;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int st = 0; st < P / 32; ++st) {
+            const u32x4 xa = mv ? *(const u32x4*)(xrow + st * 32) : u32x4{0, 0, 0, 0};
+            acc = mfma_bf16(xa, ld16(wr + st * 32), acc);
+          }
+          float* ub = ubuf + u * (16 * 17);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ub[(4 * grp + r) * 17 + nl] = acc[r];
         }
       }
     }
     wg_sync();
-    if (t0 == (int)blockIdx.x) stamp<TS>(a.timestamps, 45, 0);
-    for (int o = tid; cw && o < nb * 256; o += kCompute) {
-      const int i = o >> 8, m = (o >> 4) & 15, j = o & 15;
-      const int task = t0 + i * nwg, ai = task / jblocks;
-      const int e = rt.act_expert[ai];
-      if (m < rt.act_cnt[ai]) {
-        float ug = red_sum(red + (i * 2 + 0) * 8 * (16 * 17), m, j);
-        float uu = red_sum(red + (i * 2 + 1) * 8 * (16 * 17), m, j);
-        if (a.fmt == 1) { ug *= a.w1_ts[e]; uu *= a.w1_ts[e]; }
-        abuf[i * (16 * 17) + m * 17 + j] = ug / (1.0f + __expf(-ug)) * uu;
-      }
-    }
-    wg_sync();
-    for (int o = tid; cw && o < nb * 16; o += kCompute) {
-      const int i = o >> 4, m = o & 15;
-      const int task = t0 + i * nwg, ai = task / jblocks, j0 = (task % jblocks) * 16;
+    if (u0 == 0) stamp<TS>(a.timestamps, 45, 0);
+    // SwiGLU + requantisation: thread (task of the round, token row m)
+    for (int o = tid; cw && o < (nu / 2) * 16; o += kCompute) {
+      const int tl = o >> 4, m = o & 15;
+      const int task = t_begin + u0 / 2 + tl;
+      const int ai = task / jblocks, j0 = (task % jblocks) * 16;
       if (m < rt.act_cnt[ai]) {
         const int pair = rt.pair_list[rt.act_off[ai] + m];
-        const float* v = abuf + i * (16 * 17) + m * 17;
+        const float* ug = ubuf + (2 * tl) * (16 * 17) + m * 17;
+        const float* uu = ubuf + (2 * tl + 1) * (16 * 17) + m * 17;
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = ug[j] / (1.0f + __expf(-ug[j])) * uu[j];
         if (a.fmt == 1) {
           float amax = 0.f;
+#pragma unroll
           for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
           const uint32_t sc = e4m3_code_of_amax_over6(amax);
-          const float s = e4m3_to_f32(sc);
+          const float sv = e4m3_to_f32(sc);
           uint32_t w0 = 0, w1 = 0;
-          if (s > 0.f) {
-            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], s) << (4 * j);
-            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], s) << (4 * j);
+          if (sv > 0.f) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], sv) << (4 * j);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], sv) << (4 * j);
           }
           st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
         } else {
           uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
+#pragma unroll
           for (int q = 0; q < 4; ++q) st_coh_u64(dst + 4 * q, pack4_bf16(v + 4 * q));
         }
       }
@@ -1118,9 +1177,11 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     uint32_t touched = 0;     // folded values of the cache-touch prefetches
     // ---- 1 ATTN
     for (int it = blockIdx.x; it < a.attn_items; it += nwg) {
+      u32x4 qf[4];
+      attention_q(a, it, qf);
       attention_stage(a, it, smem);
       if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 37, 0);
-      attention_compute<TS>(a, tr, it, smem);
+      attention_compute<TS>(a, tr, it, smem, qf);
       if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 38, 0);
       wg_sync();
     }
