@@ -13,14 +13,44 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+HERE = os.path.dirname(os.path.abspath(__file__))
+# sources that decide what the layer kernel reads and writes
+KERNEL_SOURCES = ["layer_persistent_amd/csrc/mk_layer.hip", "layer_persistent_amd/csrc/mk_device.h",
+                  "layer_persistent_amd/csrc/mk_internal.h", "layer_persistent_amd/csrc/mk_api.hip"]
+COPY_CALIB_ELEMS = 1 << 26          # fp32 elements of the copy-calibration kernel (256 MiB each way)
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counted_traffic(workload: str):
+    """HBM bytes per launch measured by the FETCH_SIZE / WRITE_SIZE counters (copy-kernel
+    calibrated), read from the committed counter summary -- but only if that summary was taken
+    on the current kernel sources; otherwise None."""
+    path = os.path.join(HERE, "profiles", f"layer_kernel_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    tb = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not sha or not tb or sha.group(1) != kernel_source_sha():
+        return None
+    return int(tb.group(1))
 
 
 def log(*a):
@@ -79,6 +109,9 @@ def main():
     ap.add_argument("--config", type=int, default=2, help="workload id (2: SWA ctx 8192, 3: global ctx 32768)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain elementwise copy of 256 MiB three times "
+                         "(the known-size kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (the layer kernel needs no collectives); "
@@ -167,6 +200,16 @@ def main():
     del big
     log(f"achievable streaming read (torch sum over 1 GiB): {read_gbs:.0f} GB/s")
 
+    if args.copy_calibration:
+        src = torch.ones(COPY_CALIB_ELEMS, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 x torch.neg over {COPY_CALIB_ELEMS * 4} B read + {COPY_CALIB_ELEMS * 4} B written")
+        del src, dst
+
     phases = None
     if not args.no_phases:
         dw0 = reps[0][0]
@@ -236,7 +279,7 @@ def main():
                    "top_k": shape.top_k, "expert_inter": shape.expert_inter, "expert_format": "nvfp4",
                    "active_experts": n_active, "replicas": args.replicas, "launches_per_layer": 1},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(shape.name),
                      "bytes_per_launch": ab["total"], "achievable_read_gbs": round(read_gbs, 1)},
         "median_us": round(med_us, 2),
         "p10_us": round(float(np.percentile(per, 10)), 2),
