@@ -232,6 +232,11 @@ def main():
         for p, n in enumerate(names, start=1):
             phases[n + "_poll_done"] = round(rel(20 + p), 2)
             phases[n + "_loads_issued"] = round(rel(28 + p), 2)
+        # per-workgroup work time of each phase (its work end minus its previous hand-off end):
+        # median and max over the workgroups
+        for p, n in enumerate(names, start=1):
+            dur = (tsv[:, 2 * p] - tsv[:, 2 * p - 1 if p > 1 else 1]) / 100.0
+            phases[n + "_wg_p50_max"] = [round(float(np.median(dur)), 2), round(float(dur.max()), 2)]
         starts = (tsv[:, 0] - t0) / 100.0
         phases["wg_start_spread"] = round(float(starts.max()), 2)
         items = tsv[:, 37] > 0
@@ -249,6 +254,16 @@ def main():
             d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
             phases["gemm2_staged_after_sync"] = d(42, 13, g2)
             phases["gemm2_experts_after_staged"] = d(43, 42, g2)
+        d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
+        rtm = tsv[:, 46] > 0
+        if rtm.any():
+            phases["route_staged_after_sync"] = d(46, 11, rtm)
+            phases["route_topk"] = d(47, 46, rtm)
+            phases["route_rest"] = d(18, 47, rtm)
+        g2b = tsv[:, 48] > 0
+        if g2b.any():
+            phases["gemm2_batch0"] = d(48, 42, g2b)
+            phases["gemm2_batch1"] = d(43, 48, g2b)
         g1 = tsv[:, 45] > 0
         if g1.any():
             d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)

@@ -53,7 +53,8 @@ typedef enum { MK_W_BF16 = 0, MK_W_NVFP4 = 1 } mk_wfmt;
  * <= 4096; pooled a multiple of 128 and <= 2048; head_dim 64 or 128; n_q_heads a multiple
  * of n_kv_heads with n_q_heads*head_dim <= 1024 and T*(n_q_heads/n_kv_heads) <= 128;
  * n_experts <= 256 (multiple of 16); 1 <= top_k <= 8; expert_inter a multiple of 32 and
- * <= 256; window 0 (global attention) or >= 1; T <= 16. */
+ * <= 256; window 0 (global attention) or >= 1; T <= 16; MK_W_NVFP4 experts also need
+ * pooled a multiple of 128. */
 typedef struct {
   int hidden, n_q_heads, n_kv_heads, head_dim;   /* H, Hq, Hkv, d                          */
   int pooled, n_experts, top_k, expert_inter;    /* P, E, k, I (this GPU's share of I)     */
@@ -110,7 +111,7 @@ typedef struct {
                                   so the others' bounded waits must end in MK_ETIMEOUT        */
 } mk_step_io;
 
-#define MK_TS_EVENTS 48
+#define MK_TS_EVENTS 64
 
 /* Stage hand-off buffers inside the workspace (byte offsets), for stage-local checks. */
 typedef struct {

@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK, MK_EINVAL, MK_ESHAPE, MK_EALIGN, MK_ECAPACITY, MK_EHIP, MK_ETIMEOUT, MK_EBADTREE = 0, -1, -2, -3, -4, -5, -6, -7
 MK_W_BF16, MK_W_NVFP4 = 0, 1
-MK_TS_EVENTS = 48
+MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step",
             "mk_kv_append", "mk_route_topk", "mk_nvfp4_pack", "mk_read_status", "mk_strerror"]

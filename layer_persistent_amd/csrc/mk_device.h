@@ -29,6 +29,32 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_f16: the same lane layout as the bf16 form, fp16 operands.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+}
+
+// Eight E2M1 codes times an E4M3 block scale -> eight fp16 in MFMA operand order, exactly:
+// the codes are decoded at scale 1.0 (exact), then one packed fp16 multiply per pair applies
+// the scale.  e2m1 x e4m3 products have <= 6 significant bits and lie in [2^-10, 2688], inside
+// fp16's normal range, so the product is the exact value.  `s` holds the scale in both halves.
+__device__ __forceinline__ u32x4 fp4x8_to_f16(uint32_t codes, f16x2_t s) {
+  const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+  const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+  const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+  const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+  return u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+               __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+}
+// an E4M3 byte as an fp16 pair (every E4M3 value is exact in fp16)
+__device__ __forceinline__ f16x2_t e4m3_to_f16x2(uint32_t byte) {
+  const _Float16 h = (_Float16)__builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+  return f16x2_t{h, h};
+}
+
 // Eight E2M1 codes (one dword, element 2q in the low nibble of byte q) times an fp32 block
 // scale -> eight bf16 in MFMA operand order.  The hardware converter applies only the
 // exponent of its scale operand, so it decodes the bare codes (scale 1.0, exact) and the

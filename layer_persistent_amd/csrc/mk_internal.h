@@ -4,7 +4,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define MK_TS_EVENTS_DEV 48
+#define MK_TS_EVENTS_DEV 64
 #define MK_ETIMEOUT_DEV (-6)
 #define MK_EBADTREE_DEV (-7)
 

@@ -60,7 +60,11 @@ constexpr int SYNC_MODE = MK_SYNC_MODE;   // grid hand-off: 1 sharded counters, 
 // dynamic LDS layout (byte offsets; phases reuse the same space)
 constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
 constexpr int G1_XS_BYTES = 16 * (2048 + 8) * 2;       // xp rows for GEMM1
-constexpr int LDS_BYTES = 144 * 1024;                  // >= every phase's use (GEMM1: 136.5 KB)
+constexpr int LDS_BYTES = 148 * 1024;                  // >= every phase's use (GEMM1: 136.5 KB)
+// A pooler tile (16 x K <= 4096 bf16 = 128 KB) held in LDS from launch start, above the 17 KB of
+// dense-phase reduction buffers and the merge scratch
+constexpr int POOL_LDS_OFF = 20 * 1024;
+static_assert(POOL_LDS_OFF + 16 * 4096 * 2 <= LDS_BYTES, "pooler tile in LDS");
 static_assert(G1_XS_BYTES + 16 * 16 * 128 + 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
 
 __device__ __forceinline__ void wg_sync() {
@@ -93,6 +97,7 @@ struct Route {            // routing tables, identical in every workgroup
   int32_t expert_cnt[256];
   int32_t expert_first[256];
   uint32_t mask[256 * 4]; // per expert: bit p set when pair p routes there
+  float ts1[256], ts2[256];  // NVFP4 tensor scales of every expert (W1, W2)
 };
 
 struct Tree {
@@ -286,6 +291,53 @@ __device__ __forceinline__ f32x4 stream_mma(const uint16_t* __restrict__ W, int 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (s0 + 8 * j < ksteps) acc = mfma_bf16(xa[j], w[j], acc);
+  }
+  return acc;
+}
+
+// A 16 x K weight tile copied into LDS: chunk (s, l) -- row n0 + l % 16, k = 32 s + 8 (l / 16)
+// .. + 8 -- at byte (64 s + l) * 16, so a wave reads 1 KB contiguous per k-step.  Compute
+// threads; the caller synchronises before the tile is read.
+__device__ __forceinline__ void lds_tile_fill(const uint16_t* __restrict__ W, int K, int n0, char* dst) {
+  const int tid = threadIdx.x;
+  if (tid >= kCompute) return;
+  const int nch = (K / 32) * 64;
+  for (int base = 0; base < nch; base += 8 * kCompute) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = base + j * kCompute + tid, sk = c >> 6, l = c & 63;
+      if (c < nch) v[j] = ld16(W + (size_t)(n0 + (l & 15)) * K + 32 * sk + 8 * (l >> 4));
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = base + j * kCompute + tid;
+      if (c < nch) *(u32x4*)(dst + (size_t)c * 16) = v[j];
+    }
+  }
+}
+
+// This wave's partial of a tile whose weights sit in LDS (lds_tile_fill layout); x rows are
+// loaded 16 k-steps at a time.
+__device__ __forceinline__ f32x4 lds_mma(const char* wl, const uint16_t* __restrict__ x, int T, int K) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15;
+  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
+  const bool xv = nl < T;
+  const int ksteps = K >> 5;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = wave; s0 < ksteps; s0 += 128) {
+    u32x4 xa[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int sk = s0 + 8 * j;
+      xa[j] = (xv && sk < ksteps) ? ld16(xrow + sk * 32) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int sk = s0 + 8 * j;
+      if (sk < ksteps) acc = mfma_bf16(xa[j], *(const u32x4*)(wl + (size_t)(sk * 64 + lane) * 16), acc);
+    }
   }
   return acc;
 }
@@ -616,47 +668,88 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
 // Top-k per token from the logits (value desc, index asc), softmax gates over the selected,
 // and the dispatch tables.  Every workgroup computes the same tables.  Called by all threads;
 // the work runs on the compute waves.
+template <bool TS>
 __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* lg) {
   const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
   const int npairs = T * K;
   const bool cw = tid < kCompute;
-  stage_pieces(T * E / 4, [&](int i) { return (const void*)(a.logits + 4 * i); },
-               [&](int i) { return (void*)(lg + 4 * i); });
+  // the logits, and (NVFP4) every expert's two tensor scales, in one batch of loads
+  const int nlg = T * E / 4, nts = a.fmt == 1 ? E / 4 : 0;
+  stage_pieces(nlg + 2 * nts, [&](int i) {
+    if (i < nlg) return (const void*)(a.logits + 4 * i);
+    i -= nlg;
+    return i < nts ? (const void*)(a.w1_ts + 4 * i) : (const void*)(a.w2_ts + 4 * (i - nts));
+  }, [&](int i) {
+    if (i < nlg) return (void*)(lg + 4 * i);
+    i -= nlg;
+    return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
+  });
   for (int i = tid; cw && i < E * 4; i += kCompute) rt.mask[i] = 0u;
   wg_sync();
+  stamp<TS>(a.timestamps, 46, 0);
   const int lane = tid & 63, wave = tid >> 6;
-  for (int t = wave; cw && t < T; t += 8) {
-    // lane holds experts 4 lane .. 4 lane + 3, so a lower lane means a lower index
-    float v[4];
-    bool taken[4];
+  // Top-k per token.  Wave w takes tokens w and w + 8 together (two independent chains).  A
+  // lane holds experts 4 lane .. 4 lane + 3 sorted by (logit desc, index asc); each round the
+  // wave's largest head wins (the lowest lane on ties, which holds the lowest index) and its
+  // lane pops it.  Lane j keeps round j's logit and expert.
+  for (int tA = wave; cw && tA < T; tA += 16) {
+    const int tB = tA + 8;
+    const bool hasB = tB < T;                                    // uniform over the wave
+    float va[4], vb[4];
+    int ia[4], ib[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
-      taken[q] = e >= E;
-      v[q] = taken[q] ? -INFINITY : lg[t * E + e];
+      ia[q] = ib[q] = e;
+      va[q] = e < E ? lg[tA * E + e] : -INFINITY;
+      vb[q] = (hasB && e < E) ? lg[tB * E + e] : -INFINITY;
     }
-    float z0 = 0.f, s = 0.f, gsel = 0.f;
+    auto cswap = [](float (&v)[4], int (&ix)[4], int i, int j) {
+      const bool sw = v[j] > v[i] || (v[j] == v[i] && ix[j] < ix[i]);
+      const float tv = v[i];
+      const int ti = ix[i];
+      v[i] = sw ? v[j] : v[i];
+      ix[i] = sw ? ix[j] : ix[i];
+      v[j] = sw ? tv : v[j];
+      ix[j] = sw ? ti : ix[j];
+    };
+    auto sort4 = [&](float (&v)[4], int (&ix)[4]) {
+      cswap(v, ix, 0, 1); cswap(v, ix, 2, 3); cswap(v, ix, 0, 2); cswap(v, ix, 1, 3); cswap(v, ix, 1, 2);
+    };
+    auto pop = [](float (&v)[4], int (&ix)[4], bool take) {
+      v[0] = take ? v[1] : v[0]; ix[0] = take ? ix[1] : ix[0];
+      v[1] = take ? v[2] : v[1]; ix[1] = take ? ix[2] : ix[1];
+      v[2] = take ? v[3] : v[2]; ix[2] = take ? ix[3] : ix[2];
+      v[3] = take ? -INFINITY : v[3];
+    };
+    sort4(va, ia);
+    sort4(vb, ib);
+    float mA = 0.f, mB = 0.f;
+    int eA = 0, eB = 0;
     for (int j = 0; j < K; ++j) {
-      float bv = -INFINITY;
-      int bq = 0;
-#pragma unroll
-      for (int q = 3; q >= 0; --q)
-        if (!taken[q] && v[q] >= bv) { bv = v[q]; bq = q; }   // ties: the lower q wins
-      const float m = wave_max_f32(bv);
-      const uint64_t hit = __ballot(bv == m && !(taken[0] && taken[1] && taken[2] && taken[3]));
-      const int wl = __ffsll((unsigned long long)hit) - 1;      // lowest lane holding the max
-      const int be = 4 * wl + __builtin_amdgcn_readlane(bq, wl);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) if (lane == wl && q == (be & 3)) taken[q] = true;
-      if (j == 0) z0 = m;
-      const float ex = __expf(m - z0);
-      s += ex;
-      if (lane == j) gsel = ex;                 // lane j keeps slot j's weight
-      if (lane == 0) rt.idx[t * K + j] = be;
+      const float xA = wave_max_f32(va[0]), xB = wave_max_f32(vb[0]);
+      const int lA = __ffsll((unsigned long long)__ballot(va[0] == xA)) - 1;
+      const int lB = __ffsll((unsigned long long)__ballot(vb[0] == xB)) - 1;
+      const int beA = __builtin_amdgcn_readlane(ia[0], lA), beB = __builtin_amdgcn_readlane(ib[0], lB);
+      pop(va, ia, lane == lA);
+      pop(vb, ib, lane == lB);
+      if (lane == j) { mA = xA; eA = beA; mB = xB; eB = beB; }
     }
-    if (lane < K) rt.gate[t * K + lane] = gsel / s;
+    // gates: softmax over the k selected logits, summed in slot order
+    const float zA = __expf(mA - __shfl(mA, 0)), zB = __expf(mB - __shfl(mB, 0));
+    float sA = 0.f, sB = 0.f;
+    for (int j = 0; j < K; ++j) { sA += __shfl(zA, j); sB += __shfl(zB, j); }
+    if (lane < K) {
+      rt.idx[tA * K + lane] = eA;
+      rt.gate[tA * K + lane] = zA / sA;
+      if (hasB) {
+        rt.idx[tB * K + lane] = eB;
+        rt.gate[tB * K + lane] = zB / sB;
+      }
+    }
   }
   wg_sync();
+  stamp<TS>(a.timestamps, 47, 0);
   for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&rt.mask[rt.idx[p] * 4 + (p >> 5)], 1u << (p & 31));
   wg_sync();
   for (int e = tid; cw && e < E; e += kCompute)
@@ -719,10 +812,84 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
 // a = silu(u_gate) * u_up and requantises it to NVFP4 (tensor scale 1) per 16-element block.
 // Called by all threads.
 constexpr int G1_UNITS = 16;                   // units per round (2 per compute wave)
-constexpr int G1_MAXLS = 16;                   // NVFP4 load steps (128 k each): P <= 2048
+
+// GEMM1 input rows.  NVFP4 experts multiply in fp16: xs[t][k] = fp16(xp[t][k] * 2^xk[t]),
+// where 2^xk[t] puts the row's largest magnitude in [2^14, 2^15).  Every element whose
+// magnitude is at least 2^-28 of the row maximum then converts exactly (a bf16 value has 8
+// significant bits) and lies in fp16's normal range, and its product with an exactly decoded
+// fp16 weight is exact in the fp32 accumulator; smaller elements may be rounded or flushed
+// (relative effect below 2^-28).  The GEMM1 result is scaled back by 2^-xk[t].  bf16 experts
+// take xs = xp unchanged.
+//
+// Part 1 (compute threads, no barrier; runs while the grid waits for the router): this
+// thread's pieces of xp (8 bf16 each, T * P / 8 <= 4096 pieces) into registers and, for NVFP4,
+// each piece's largest magnitude into pmax (LDS).
+__device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t* pmax) {
+  const int tid = threadIdx.x, n = a.T * (a.P / 8);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = j * kCompute + tid;
+    if (i < n) v[j] = ld16(a.xp + (size_t)i * 8);
+  }
+  if (a.fmt != 1) return;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int i = j * kCompute + tid;
+    if (i < n) {
+      // |x| of a bf16 orders like its bit pattern without the sign
+      uint32_t m = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = v[j][q] & 0x7FFF7FFFu;
+        m = max(m, max(w & 0xFFFFu, w >> 16));
+      }
+      pmax[i] = m;
+    }
+  }
+}
+
+// Part 2 (all threads; returns with the workgroup synchronised): the row scales and xs.
+__device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], uint16_t* xs, int xstride,
+                                         const uint32_t* pmax, int32_t* xk) {
+  const int T = a.T, tid = threadIdx.x, per_row = a.P / 8, n = T * per_row;
+  const bool cw = tid < kCompute, fp4 = a.fmt == 1;
+  const int lane = tid & 63, wave = tid >> 6;
+  if (fp4) {
+    for (int t = wave; cw && t < T; t += 8) {
+      uint32_t m = 0;
+      for (int i = lane; i < per_row; i += 64) m = max(m, pmax[t * per_row + i]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+      // bf16 exponent field E: the row maximum lies in [2^(E-127), 2^(E-126))
+      if (lane == 0) xk[t] = m == 0 ? 0 : min(126, max(-126, 141 - (int)(m >> 7)));
+    }
+    wg_sync();
+  }
+  if (cw) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = j * kCompute + tid;
+      if (i < n) {
+        const int t = i / per_row, c = i % per_row;
+        u32x4 o = v[j];
+        if (fp4) {
+          const float f = __uint_as_float((uint32_t)(127 + xk[t]) << 23);   // 2^xk[t], exact
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float lo = __uint_as_float(v[j][q] << 16) * f, hi = __uint_as_float(v[j][q] & 0xFFFF0000u) * f;
+            o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+          }
+        }
+        *(u32x4*)(xs + t * xstride + c * 8) = o;
+      }
+    }
+  }
+  wg_sync();
+}
 
 template <bool TS>
-__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem) {
+__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem, int32_t* xk,
+                                            const u32x4 (&xpv)[8]) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int jblocks = I / 16;
@@ -734,9 +901,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   uint16_t* xs = (uint16_t*)smem;                                  // [T][P + 8] bf16
   uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // [16 units][16 rows][P/16]
   float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][16][17]
-  stage_pieces(T * (P / 8), [&](int i) { return (const void*)(a.xp + (size_t)i * 8); },
-               [&](int i) { return (void*)(xs + (i / (P / 8)) * xstride + (i % (P / 8)) * 8); });
-  wg_sync();
+  xs_build(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
   stamp<TS>(a.timestamps, 44, 0);
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
   const int lsteps = P / 128;
@@ -789,8 +954,8 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
             for (int j = 0; j < 2; ++j) if ((lane + 64 * j) * 16 < 16 * (P / 16)) *(u32x4*)(sd + (lane + 64 * j) * 16) = sv[j];
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-          const bool mv = nl < cnt;
-          const uint16_t* xrow = xs + (mv ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
+          // rows past the expert's tokens read token 0 and are discarded after the product
+          const uint16_t* xrow = xs + (nl < cnt ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
           const uint8_t* srow = sd + nl * (P / 16) + grp * 2;
           const u32x4* cd = x == 0 ? cA : cB;
 #pragma unroll
@@ -798,16 +963,16 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
             const int ls = hf * 8 + j;
             if (ls < lsteps) {
               const uint32_t sc = *(const uint16_t*)(srow + ls * 8);
-              const float s0 = e4m3_to_f32(sc & 0xFF), s1 = e4m3_to_f32(sc >> 8);
+              const f16x2_t s0 = e4m3_to_f16x2(sc & 0xFF), s1 = e4m3_to_f16x2(sc >> 8);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
-                const u32x4 xa = mv ? *(const u32x4*)(xrow + ls * 128 + q * 8) : u32x4{0, 0, 0, 0};
-                acc = mfma_bf16(xa, fp4x8_to_bf16(cd[j][q], q < 2 ? s0 : s1), acc);
+                const u32x4 xa = *(const u32x4*)(xrow + ls * 128 + q * 8);
+                acc = mfma_f16(xa, fp4x8_to_f16(cd[j][q], q < 2 ? s0 : s1), acc);
               }
             }
           }
           if (hf == nh - 1) {
-            const float ts = a.w1_ts[e];
+            const float ts = rt.ts1[e];
             float* ub = ubuf + u * (16 * 17);
 #pragma unroll
             for (int r = 0; r < 4; ++r) ub[(4 * grp + r) * 17 + nl] = acc[r] * ts;
@@ -848,9 +1013,14 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
         const int pair = rt.pair_list[rt.act_off[ai] + m];
         const float* ug = ubuf + (2 * tl) * (16 * 17) + m * 17;
         const float* uu = ubuf + (2 * tl + 1) * (16 * 17) + m * 17;
+        // NVFP4: undo the token row's power-of-two input scale (exact)
+        const float f = a.fmt == 1 ? __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23) : 1.0f;
         float v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = ug[j] / (1.0f + __expf(-ug[j])) * uu[j];
+        for (int j = 0; j < 16; ++j) {
+          const float g = ug[j] * f;
+          v[j] = g / (1.0f + __expf(-g)) * (uu[j] * f);
+        }
         if (a.fmt == 1) {
           float amax = 0.f;
 #pragma unroll
@@ -876,7 +1046,181 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   }
 }
 
-// GEMM2 + combine for output columns [c0, c0+8) of P.
+// ---- GEMM2 for NVFP4 experts: output columns [c0, c0+8) of P per workgroup
+//
+// Unit U of the grid's expert list is the pair of active experts (2U, 2U+1); wave w takes
+// units w, w+8, ...  Two experts share one 16x16 MFMA tile: token rows 0-7 and weight
+// columns 0-7 belong to expert 2U, rows 8-15 and columns 8-15 to 2U+1, and the off-diagonal
+// blocks are discarded.  An expert with more than 8 tokens runs alone with all 16 token rows
+// (two passes over the same weights).  Lane (nl, grp) holds weight row c0 + nl % 8 of its
+// column's expert for the quarter k in [grp I/4, (grp+1) I/4) of the reduction: I/8 bytes of
+// codes and I/64 E4M3 block scales, loaded straight into registers (the first G2_UNITS units
+// while the grid waits for GEMM1).  The intermediate is read in the same permuted k order,
+// which MFMA allows.  Requires I % 64 == 0.
+constexpr int G2_UNITS = 4;   // units per register batch; two batches cover 64 units
+constexpr int G2_MAXB = 4;    // I/64 <= 4
+struct G2W {
+  u32x2 c[G2_UNITS][G2_MAXB];
+  uint32_t s[G2_UNITS][G2_MAXB];
+};
+
+// Loads unit U (the expert pair 2U, 2U+1 of the active list) into register slot `i` of `w`
+// for columns [c0, c0+8).  Compute waves only; `rt` must hold this launch's routing.
+__device__ __forceinline__ void g2_load_unit(const KArgs& a, const Route& rt, int c0, int U, G2W& w, int i) {
+  const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
+  const int I = a.I, nb = I / 64, na = rt.n_active;
+  if (2 * U < na) {                                              // uniform over the wave
+    const int ie = (nl >= 8 && 2 * U + 1 < na) ? 2 * U + 1 : 2 * U;
+    const size_t row = (size_t)rt.act_expert[ie] * a.P + c0 + (nl & 7);
+    const uint8_t* cp = a.w2_codes + row * (I / 2) + grp * (I / 8);   // 8-byte aligned
+    const uint8_t* sp = a.w2_scales + row * (I / 16) + grp * nb;
+#pragma unroll
+    for (int b = 0; b < G2_MAXB; ++b)
+      if (b < nb) {
+        w.c[i][b] = *(const u32x2*)(cp + 8 * b);
+        w.s[i][b] = sp[b];
+      }
+  }
+}
+
+// Batch `batch` of this wave: units wave + 8 (G2_UNITS batch + i), i < G2_UNITS.
+__device__ __forceinline__ void g2_load(const KArgs& a, const Route& rt, int c0, int batch, G2W& w) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < G2_UNITS; ++i) g2_load_unit(a, rt, c0, wave + 8 * (G2_UNITS * batch + i), w, i);
+}
+
+// One unit from registers slot `i` of `w`; writes gate-free expert outputs to outp[pair][8].
+__device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G2W& w, int i, int U,
+                                        const uint16_t* actf, int astride, float* outp) {
+  const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
+  const int I = a.I, na = rt.n_active;
+  const int iA = 2 * U, iB = 2 * U + 1;
+  const bool hasB = iB < na;
+  const int cA = rt.act_cnt[iA], cB = hasB ? rt.act_cnt[iB] : 0;
+  const bool pairm = hasB && cA <= 8 && cB <= 8;
+  const float ts = rt.ts2[rt.act_expert[(nl >= 8 && hasB) ? iB : iA]];
+  for (int pass = 0; pass < (pairm || !hasB ? 1 : 2); ++pass) {
+    // pass 0: expert 2U (with 2U+1 when paired); pass 1: expert 2U+1 alone, columns 8-15
+    const int ia = pass == 0 ? iA : iB;
+    const int cnt_a = rt.act_cnt[ia], off_a = rt.act_off[ia];
+    const int cnt_b = pairm ? cB : 0, off_b = pairm ? rt.act_off[iB] : 0;
+    int pair_m = -1;
+    if (pairm) {
+      if (nl < 8) { if (nl < cnt_a) pair_m = rt.pair_list[off_a + nl]; }
+      else if (nl - 8 < cnt_b) pair_m = rt.pair_list[off_b + nl - 8];
+    } else if (nl < cnt_a) {
+      pair_m = rt.pair_list[off_a + nl];
+    }
+    // rows without a pair read pair 0; their outputs are discarded
+    const uint16_t* arow = actf + (pair_m < 0 ? 0 : pair_m) * astride + grp * (I / 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2 * G2_MAXB; ++st) {
+      if (st < I / 32) {
+        const u32x4 x = *(const u32x4*)(arow + 8 * st);
+        acc = mfma_f16(x, fp4x8_to_f16(w.c[i][st / 2][st & 1], e4m3_to_f16x2(w.s[i][st / 2])), acc);
+      }
+    }
+    // C lane: weight column nl, token rows 4 grp + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * grp + r;
+      int pair = -1;
+      if (pairm) {
+        if (nl < 8 && row < 8 && row < cnt_a) pair = rt.pair_list[off_a + row];
+        else if (nl >= 8 && row >= 8 && row - 8 < cnt_b) pair = rt.pair_list[off_b + row - 8];
+      } else if ((pass == 0) == (nl < 8) && row < cnt_a) {
+        pair = rt.pair_list[off_a + row];
+      }
+      if (pair >= 0) outp[pair * 8 + (nl & 7)] = acc[r] * ts;
+    }
+  }
+}
+
+// Called by all threads.  `w0` holds batch 0 of this workgroup's first slice, loaded during
+// the hand-off after GEMM1.
+template <bool TS>
+__device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, G2W& w0) {
+  const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
+  const bool cw = tid < kCompute;
+  const int nwg = gridDim.x, nslices = P / 8;
+  if ((int)blockIdx.x >= nslices) return;       // uniform over the workgroup
+  const int npairs = T * K, na = rt.n_active;
+  const int astride = I + 8;                                        // fp16 per pair row in LDS
+  uint16_t* actf = (uint16_t*)smem;                                 // [pairs][I + 8]
+  float* outp = (float*)(smem + ((npairs * astride * 2 + 255) & ~255));   // [pairs][8]
+  const int wave = tid >> 6;
+  for (int sl = blockIdx.x; sl < nslices; sl += nwg) {
+    const int c0 = sl * 8;
+    const bool first = sl == (int)blockIdx.x;
+    if (first) {
+      // the intermediate: one 16-element block (codes, scale byte) per record, decoded once
+      const int nblk = npairs * (I / 16);                           // <= 2048
+      u32x4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = j * kCompute + tid;
+        if (cw && i < nblk) v[j] = ld16(a.act_q + (size_t)i * 4);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = j * kCompute + tid;
+        if (cw && i < nblk) {
+          const int pair = i / (I / 16), b = i % (I / 16);
+          const f16x2_t sc = e4m3_to_f16x2(v[j][2]);
+          uint16_t* dst = actf + pair * astride + b * 16;
+          *(u32x4*)dst = fp4x8_to_f16(v[j][0], sc);
+          *(u32x4*)(dst + 8) = fp4x8_to_f16(v[j][1], sc);
+        }
+      }
+    } else if (cw) {
+      g2_load(a, rt, c0, 0, w0);
+    }
+    wg_sync();
+    if (first) stamp<TS>(a.timestamps, 42, 0);
+    if (cw) {
+      // batch 0 from the registers; each slot is refilled with batch 1's unit once used
+#pragma unroll
+      for (int i = 0; i < G2_UNITS; ++i) {
+        const int U = wave + 8 * i;
+        if (2 * U < na) g2_unit(a, rt, w0, i, U, actf, astride, outp);
+        g2_load_unit(a, rt, c0, wave + 8 * (G2_UNITS + i), w0, i);
+      }
+      if (first) stamp<TS>(a.timestamps, 48, 0);
+#pragma unroll
+      for (int i = 0; i < G2_UNITS; ++i) {
+        const int U = wave + 8 * (G2_UNITS + i);
+        if (2 * U < na) g2_unit(a, rt, w0, i, U, actf, astride, outp);
+      }
+    }
+    wg_sync();
+    if (first) stamp<TS>(a.timestamps, 43, 0);
+    if (tid < T) {
+      float y[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = 0.f;
+      for (int j = 0; j < K; ++j) {
+        const float gt = rt.gate[tid * K + j];
+        const float* o = outp + (tid * K + j) * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] += gt * o[c];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ytile[tid * 4 + q] = pack_bf2(y[2 * q], y[2 * q + 1]);
+    }
+    wg_sync();
+    if (tid >= kCompute && (tid - kCompute) < T) {
+      const int t = tid - kCompute;
+      uint16_t* dst = a.y + (size_t)t * P + c0;
+      st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
+      st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
+    }
+  }
+}
+
+// ---- GEMM2 + combine, general form (bf16 experts, or NVFP4 with I % 64 != 0): output
+// columns [c0, c0+8) of P.
 //  * The fp4 intermediate of every (token, slot) pair is decoded once into LDS as bf16.
 //  * The 8 weight rows of one expert for these columns are contiguous (codes, then scales);
 //    the workgroup copies every active expert's rows into LDS with wide loads.
@@ -888,7 +1232,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
 //    ([T][4] dwords of bf16 pairs) for the control wave to store.
 // Called by all threads.
 template <bool TS>
-__device__ __forceinline__ void gemm2_phase(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile) {
+__device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int nwg = gridDim.x;
@@ -959,9 +1303,9 @@ __device__ __forceinline__ void gemm2_phase(const KArgs& a, const Route& rt, cha
           const int ia = pass == 0 ? iA : iB;
           const int cnt_a = rt.act_cnt[ia], off_a = rt.act_off[ia];
           const int cnt_b = pairm ? cB : 0, off_b = pairm ? rt.act_off[iB] : 0;
-          // B operand: column nl -> expert (nl < 8 ? ia : iB), weight row nl % 8
-          const bool bv = nl < 8 || pairm;
-          const int ib = nl < 8 ? ia : iB;
+          // B operand: column nl -> expert (nl < 8 ? ia : iB), weight row nl % 8; unpaired, the
+          // columns 8..15 repeat expert ia's rows and their outputs are discarded
+          const int ib = nl < 8 || !pairm ? ia : iB;
           const char* wc = wbuf + (size_t)(ib - a0) * chunk;
           // A operand: row m -> pair of expert ia (m < cnt_a, or m < 8 when paired) or iB
           int pair_m = -1;
@@ -979,23 +1323,24 @@ __device__ __forceinline__ void gemm2_phase(const KArgs& a, const Route& rt, cha
 #pragma unroll
             for (int st = 0; st < 8; ++st) {
               if (st < ksteps) {
-                const u32x4 x = pair_m >= 0 ? *(const u32x4*)(arow + st * 32) : u32x4{0, 0, 0, 0};
-                const uint32_t wcv = bv ? *(const uint32_t*)(crow + 16 * st) : 0u;
-                const float ws = bv ? e4m3_to_f32(srow[2 * st]) : 0.f;
+                // rows without a pair read pair 0; their outputs are discarded
+                const u32x4 x = *(const u32x4*)(arow + st * 32);
+                const uint32_t wcv = *(const uint32_t*)(crow + 16 * st);
+                const float ws = e4m3_to_f32(srow[2 * st]);
                 acc = mfma_bf16(x, fp4x8_to_bf16(wcv, ws), acc);
               }
             }
           } else {
             const uint16_t* wr = (const uint16_t*)wc + (nl & 7) * I + grp * 8;
             for (int st = 0; st < ksteps; ++st) {
-              const u32x4 b = bv ? *(const u32x4*)(wr + st * 32) : u32x4{0, 0, 0, 0};
-              const u32x4 x = pair_m >= 0 ? *(const u32x4*)(arow + st * 32) : u32x4{0, 0, 0, 0};
+              const u32x4 b = *(const u32x4*)(wr + st * 32);
+              const u32x4 x = *(const u32x4*)(arow + st * 32);
               acc = mfma_bf16(x, b, acc);
             }
           }
           // C lane: column nl, rows 4 grp + r; keep the diagonal block(s)
           float ts = 1.0f;
-          if (fp4) ts = (nl < 8 || !pairm) ? a.w2_ts[rt.act_expert[ia]] : a.w2_ts[rt.act_expert[iB]];
+          if (fp4) ts = rt.ts2[rt.act_expert[ib]];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int row = 4 * grp + r;
@@ -1044,14 +1389,17 @@ __device__ __forceinline__ void gemm2_phase(const KArgs& a, const Route& rt, cha
 // one workgroup barrier.  Called by all threads.
 template <int MAXS, class Epi>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
-                            const uint16_t* x, int K, int N, int off, float* red2, Epi epi) {
+                            const uint16_t* x, int K, int N, int off, float* red2, Epi epi,
+                            const char* wlds = nullptr) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
     float* red = red2 + (it & 1) * (8 * 16 * 17);
     if (threadIdx.x < kCompute) {
       f32x4 acc;
-      if constexpr (MAXS == 0) {
+      if (wlds && it == 0) {
+        acc = lds_mma(wlds, x, a.T, K);                // the first tile's weights are in LDS
+      } else if constexpr (MAXS == 0) {
         acc = stream_mma(W, K, t * 16, x, a.T);
       } else {
         if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
@@ -1103,6 +1451,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   __shared__ int32_t dead_sh;
   __shared__ uint32_t epoch_sh;
   __shared__ int32_t par_sh[16];
+  __shared__ int32_t xk_sh[16];     // GEMM1 input row scales (NVFP4 experts)
   __shared__ uint32_t outrow[68];
   __shared__ uint32_t ytile[16 * 4];
   const int tid = threadIdx.x;
@@ -1121,12 +1470,17 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   WFrag<MAXS_R> wr;
   WFrag<MAXS_U> wu;
   WFrag<0> wq;
-  const int t_o = first_tile(0), t_p = first_tile(0), t_u = first_tile(0);
+  // pooler tiles run on the last P/16 workgroups, away from the attention items, so that
+  // those workgroups can hold their tile in LDS from launch start
+  const int off_p = nwg > a.P / 16 ? nwg - a.P / 16 : 0;
+  const int t_o = first_tile(0), t_p = first_tile(off_p), t_u = first_tile(0);
   const int off_r = nwg - a.E / 16, off_q = a.P / 16 < nwg ? a.P / 16 : 0;
   const int t_r = first_tile(off_r), t_q = first_tile(off_q);
   const int qkv_n = (a.Hq + 2 * a.Hkv) * a.d;
   const bool p_o = t_o < a.H / 16, p_p = t_p < a.P / 16, p_r = t_r < a.E / 16, p_u = t_u < a.H / 16,
              p_q = t_q < qkv_n / 16;
+  // this workgroup's pooler tile lives in LDS: one tile, no attention item here, and it fits
+  const bool pool_lds = p_p && (int)blockIdx.x >= a.attn_items && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
   u32x2 res = {0, 0};
   if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
 
@@ -1185,10 +1539,11 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 38, 0);
       wg_sync();
     }
+    if (pool_lds) lds_tile_fill(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF);
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
       if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
-      if (p_p) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
+      if (p_p && !pool_lds) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
     });
     // ---- 2 MERGE
     if (alive) {
@@ -1226,12 +1581,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (alive) {
       // control wave: the unpooler's residual (h1) for its first tile, needed in phase 8
       if (!cw && p_u && crv) res = *(const u32x2*)(a.h1 + (size_t)crow * a.H + t_u * 16 + cc0);
-      dense_phase(a, wp, false, a.w_pool, a.h1, a.H, a.P, 0, red2, [&](int n0, const float* red, int) {
+      dense_phase(a, wp, false, a.w_pool, a.h1, a.H, a.P, off_p, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         st_coh_u64(a.xp + (size_t)crow * a.P + n0 + cc0, pack4_bf16(v));
-      });
+      }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
@@ -1249,18 +1604,33 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)crow * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
       });
     }
-    alive = phase_end<TS>(a, s, 5, &dead_sh, nop) && alive;
+    // GEMM1's input rows are fetched while the grid waits for the router (piece maxima go to
+    // the LDS area GEMM1 later uses for scales, which the routing tables leave alone)
+    u32x4 xpv[8];
+    alive = phase_end<TS>(a, s, 5, &dead_sh, [&] {
+      if (alive) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
+    }) && alive;
     // ---- 6 ROUTE + GEMM1
     if (alive) {
-      route_tables(a, rt, (float*)smem);
+      route_tables<TS>(a, rt, (float*)smem);
       stamp<TS>(a.timestamps, 18);
-      gemm1_phase<TS>(a, rt, smem);
+      gemm1_phase<TS>(a, rt, smem, xk_sh, xpv);
       if (cw) __builtin_amdgcn_s_waitcnt(0);   // intermediate stores complete
     }
-    alive = phase_end<TS>(a, s, 6, &dead_sh, [&] { if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
+    G2W g2w;
+    alive = phase_end<TS>(a, s, 6, &dead_sh, [&] {
+      // this workgroup's first W2 registers (routing is known once phase 6 ran)
+      if (alive && a.fmt == 1 && a.I % 64 == 0 && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
+    }) && alive;
     // ---- 7 GEMM2 + combine
-    if (alive) gemm2_phase<TS>(a, rt, smem, ytile);
-    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16); }) && alive;
+    if (alive) {
+      if (a.fmt == 1 && a.I % 64 == 0) gemm2_fp4<TS>(a, rt, smem, ytile, g2w);
+      else gemm2_staged<TS>(a, rt, smem, ytile);
+    }
+    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] {
+      if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16);
+      if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16);
+    }) && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
       dense_phase(a, wu, p_u, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
