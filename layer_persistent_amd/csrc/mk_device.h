@@ -122,6 +122,32 @@ __device__ __forceinline__ float wave_max_f32(float v) {
                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48))));
 }
 
+// Maximum of a signed 32-bit value over the 64 lanes of a wave (all lanes active), returned
+// uniform: DPP exchanges inside each row of 16, then row broadcasts 15 and 31 carry the row
+// maxima up to lane 63.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
+}
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
+  v = max(v, dpp_i32<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
+  v = max(v, dpp_i32<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]
+  v = max(v, dpp_i32<0x141, 0xF>(v));   // row_half_mirror
+  v = max(v, dpp_i32<0x140, 0xF>(v));   // row_mirror
+  v = max(v, dpp_i32<0x142, 0xA>(v));   // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_i32<0x143, 0xC>(v));   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// fp32 -> signed integer with the same order (-0 counts as +0); finite or infinite inputs
+__device__ __forceinline__ int32_t f32_order_key(float v) {
+  const int32_t b = __float_as_int(v + 0.0f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float f32_from_order_key(int32_t k) {
+  return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF);
+}
+
 // E4M3 code of RNE(v / 6) for v >= 0 (fp32), saturating at 448, by binary search over the
 // exact thresholds 6*mid (a midpoint of two neighbouring E4M3 values has <= 5 significant
 // bits, so 6*mid is exact in fp32).  A tie goes to the even code.

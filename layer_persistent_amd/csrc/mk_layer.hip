@@ -695,46 +695,49 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
   for (int tA = wave; cw && tA < T; tA += 16) {
     const int tB = tA + 8;
     const bool hasB = tB < T;                                    // uniform over the wave
-    float va[4], vb[4];
-    int ia[4], ib[4];
+    // logits as order-preserving integers (exact, so ties stay ties)
+    int32_t va[4], vb[4], ia[4], ib[4];
+    constexpr int32_t kNone = (int32_t)0x80000000;               // below every logit
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = 4 * lane + q;
       ia[q] = ib[q] = e;
-      va[q] = e < E ? lg[tA * E + e] : -INFINITY;
-      vb[q] = (hasB && e < E) ? lg[tB * E + e] : -INFINITY;
+      va[q] = e < E ? f32_order_key(lg[tA * E + e]) : kNone;
+      vb[q] = (hasB && e < E) ? f32_order_key(lg[tB * E + e]) : kNone;
     }
-    auto cswap = [](float (&v)[4], int (&ix)[4], int i, int j) {
+    auto cswap = [](int32_t (&v)[4], int32_t (&ix)[4], int i, int j) {
       const bool sw = v[j] > v[i] || (v[j] == v[i] && ix[j] < ix[i]);
-      const float tv = v[i];
-      const int ti = ix[i];
+      const int32_t tv = v[i], ti = ix[i];
       v[i] = sw ? v[j] : v[i];
       ix[i] = sw ? ix[j] : ix[i];
       v[j] = sw ? tv : v[j];
       ix[j] = sw ? ti : ix[j];
     };
-    auto sort4 = [&](float (&v)[4], int (&ix)[4]) {
+    auto sort4 = [&](int32_t (&v)[4], int32_t (&ix)[4]) {
       cswap(v, ix, 0, 1); cswap(v, ix, 2, 3); cswap(v, ix, 0, 2); cswap(v, ix, 1, 3); cswap(v, ix, 1, 2);
     };
-    auto pop = [](float (&v)[4], int (&ix)[4], bool take) {
+    auto pop = [](int32_t (&v)[4], int32_t (&ix)[4], bool take) {
       v[0] = take ? v[1] : v[0]; ix[0] = take ? ix[1] : ix[0];
       v[1] = take ? v[2] : v[1]; ix[1] = take ? ix[2] : ix[1];
       v[2] = take ? v[3] : v[2]; ix[2] = take ? ix[3] : ix[2];
-      v[3] = take ? -INFINITY : v[3];
+      v[3] = take ? kNone : v[3];
     };
     sort4(va, ia);
     sort4(vb, ib);
-    float mA = 0.f, mB = 0.f;
-    int eA = 0, eB = 0;
+    int32_t kA = 0, kB = 0, eA = 0, eB = 0;
     for (int j = 0; j < K; ++j) {
-      const float xA = wave_max_f32(va[0]), xB = wave_max_f32(vb[0]);
+      const int32_t xA = wave_max_i32(va[0]), xB = wave_max_i32(vb[0]);
       const int lA = __ffsll((unsigned long long)__ballot(va[0] == xA)) - 1;
       const int lB = __ffsll((unsigned long long)__ballot(vb[0] == xB)) - 1;
       const int beA = __builtin_amdgcn_readlane(ia[0], lA), beB = __builtin_amdgcn_readlane(ib[0], lB);
       pop(va, ia, lane == lA);
       pop(vb, ib, lane == lB);
-      if (lane == j) { mA = xA; eA = beA; mB = xB; eB = beB; }
+      kA = lane == j ? xA : kA;
+      eA = lane == j ? beA : eA;
+      kB = lane == j ? xB : kB;
+      eB = lane == j ? beB : eB;
     }
+    const float mA = f32_from_order_key(kA), mB = f32_from_order_key(kB);
     // gates: softmax over the k selected logits, summed in slot order
     const float zA = __expf(mA - __shfl(mA, 0)), zB = __expf(mB - __shfl(mB, 0));
     float sA = 0.f, sB = 0.f;
@@ -1387,12 +1390,20 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
 // the wave partials (weights of the first tile already in `wf` when `have_pref`), the control
 // wave sums them and runs `epi(n0, red, it)`.  Two reduction buffers alternate so a tile needs
 // one workgroup barrier.  Called by all threads.
-template <int MAXS, class Epi>
+struct NoHook {
+  __device__ void operator()() const {}
+};
+
+// `after` runs on the compute threads once their last tile's products are formed (registers of
+// this phase's weights are free then): loads for the next phase can start there.
+template <int MAXS, class Epi, class After = NoHook>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
                             const uint16_t* x, int K, int N, int off, float* red2, Epi epi,
-                            const char* wlds = nullptr) {
+                            const char* wlds = nullptr, After after = After()) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
+  // a workgroup without a tile in this phase runs `after` at once
+  if (threadIdx.x < kCompute && first_tile(off) >= ntiles) after();
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
     float* red = red2 + (it & 1) * (8 * 16 * 17);
     if (threadIdx.x < kCompute) {
@@ -1405,6 +1416,7 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
         if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
         acc = wfrag_mma(wf, x, a.T, K);
       }
+      if (t + n >= ntiles) after();
       red_store(red, acc);
     }
     wg_sync();
@@ -1469,7 +1481,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   WFrag<0> wp;
   WFrag<MAXS_R> wr;
   WFrag<MAXS_U> wu;
-  WFrag<0> wq;
+  WFrag<MAXS_Q> wq;
   // pooler tiles run on the last P/16 workgroups, away from the attention items, so that
   // those workgroups can hold their tile in LDS from launch start
   const int off_p = nwg > a.P / 16 ? nwg - a.P / 16 : 0;
@@ -1490,29 +1502,34 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     dead_sh = 0;
   }
   wg_sync();
-  if (tid == 0) {
-    int bad = 0;
-    int depth[16];
-    for (int i = 0; i < a.T; ++i) {
-      const int p = par_sh[i];
-      if (i == 0) {
-        bad |= p != -1;
-        tr.anc[0] = 1u;
-        depth[0] = 0;
-      } else if (p < 0 || p >= i) {
-        bad = 1;
-        tr.anc[i] = 1u << i;
-        depth[i] = 0;
-      } else {
-        tr.anc[i] = tr.anc[p] | (1u << i);
-        depth[i] = depth[p] + 1;
+  if (tid < 64) {
+    // lanes i < T: ancestor-or-self set by pointer jumping (4 rounds cover depth <= 15);
+    // depth = |ancestors| - 1
+    const int lane = tid;
+    const int p = lane < a.T ? par_sh[lane] : -1;
+    const bool ok = lane >= a.T || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+    const bool bad = __ballot(!ok) != 0;
+    uint32_t anc = lane < a.T ? 1u << lane : 0u;
+    int jump = (lane < a.T && lane > 0 && ok) ? p : -1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t aj = __shfl(anc, jump < 0 ? lane : jump);
+      const int jj = __shfl(jump, jump < 0 ? lane : jump);
+      if (jump >= 0) {
+        anc |= aj;
+        jump = jj;
       }
-      const int pos = a.ctx + depth[i];
-      tr.lo[i] = a.window > 0 ? max(0, pos - a.window + 1) : 0;
     }
-    tr.bad = bad;
-    if (bad && blockIdx.x == 0)
-      __hip_atomic_store(a.status, (int32_t)MK_EBADTREE_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane < a.T) {
+      const int pos = a.ctx + __popc(anc) - 1;
+      tr.anc[lane] = bad ? 1u << lane : anc;
+      tr.lo[lane] = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+    }
+    if (lane == 0) {
+      tr.bad = bad;
+      if (bad && blockIdx.x == 0)
+        __hip_atomic_store(a.status, (int32_t)MK_EBADTREE_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   wg_sync();
   stamp<TS>(a.timestamps, 1);
@@ -1540,6 +1557,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       wg_sync();
     }
     if (pool_lds) lds_tile_fill(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF);
+    // workgroups without an attention item pull their unpooler and qkv tiles into the
+    // device-side caches while memory is otherwise idle; they are read at the end of the layer
+    if (cw && (int)blockIdx.x >= a.attn_items) {
+      if (p_u) touched ^= touch_tile<1>(a.w_unpool, a.P, t_u * 16);
+      if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16);
+    }
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
       if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
@@ -1627,10 +1650,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       if (a.fmt == 1 && a.I % 64 == 0) gemm2_fp4<TS>(a, rt, smem, ytile, g2w);
       else gemm2_staged<TS>(a, rt, smem, ytile);
     }
-    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] {
-      if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16);
-      if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16);
-    }) && alive;
+    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
       dense_phase(a, wu, p_u, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
@@ -1640,13 +1660,16 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + (size_t)crow * a.H + n0 + cc0);
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
         st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
+      }, nullptr, [&] {
+        // the qkv tile's weights load while the unpooler finishes and the grid hands off
+        if (p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
       });
     }
     alive = phase_end<TS>(a, s, 8, &dead_sh, nop) && alive;
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
-      dense_phase(a, wq, false, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+      dense_phase(a, wq, p_q, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
