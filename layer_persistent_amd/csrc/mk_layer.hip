@@ -94,10 +94,13 @@ struct Route {            // routing tables, identical in every workgroup
   int32_t act_off[128];
   int32_t act_cnt[128];
   int32_t pair_list[128]; // pair id t*k + slot, grouped by expert (ascending), then by pair id
-  int32_t expert_cnt[256];
-  int32_t expert_first[256];
-  uint32_t mask[256 * 4]; // per expert: bit p set when pair p routes there
   float ts1[256], ts2[256];  // NVFP4 tensor scales of every expert (W1, W2)
+  // GEMM2 slots: each active expert's first (up to) 8 pairs, then the rest of every expert
+  // with more than 8 pairs; a slot holds at most 8 pairs
+  int32_t n_slots;
+  int32_t slot_expert[144];
+  int32_t slot_off[144];  // into pair_list
+  int32_t slot_cnt[144];
 };
 
 struct Tree {
@@ -684,7 +687,11 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     i -= nlg;
     return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
   });
-  for (int i = tid; cw && i < E * 4; i += kCompute) rt.mask[i] = 0u;
+  // scratch after the logits: per expert, a bitmask of the pairs routed there, counts, offsets
+  uint32_t* mask = (uint32_t*)(lg + T * E);
+  int32_t* ecnt = (int32_t*)(mask + E * 4);
+  int32_t* efirst = ecnt + E;
+  for (int i = tid; cw && i < E * 4; i += kCompute) mask[i] = 0u;
   wg_sync();
   stamp<TS>(a.timestamps, 46, 0);
   const int lane = tid & 63, wave = tid >> 6;
@@ -753,11 +760,10 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
   }
   wg_sync();
   stamp<TS>(a.timestamps, 47, 0);
-  for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&rt.mask[rt.idx[p] * 4 + (p >> 5)], 1u << (p & 31));
+  for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&mask[rt.idx[p] * 4 + (p >> 5)], 1u << (p & 31));
   wg_sync();
   for (int e = tid; cw && e < E; e += kCompute)
-    rt.expert_cnt[e] = __popc(rt.mask[e * 4]) + __popc(rt.mask[e * 4 + 1]) + __popc(rt.mask[e * 4 + 2]) +
-                       __popc(rt.mask[e * 4 + 3]);
+    ecnt[e] = __popc(mask[e * 4]) + __popc(mask[e * 4 + 1]) + __popc(mask[e * 4 + 2]) + __popc(mask[e * 4 + 3]);
   wg_sync();
   if (tid < 64) {
     // exclusive scans over experts: lane handles 4 consecutive experts
@@ -765,7 +771,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
-      cnt[q] = e < E ? rt.expert_cnt[e] : 0;
+      cnt[q] = e < E ? ecnt[e] : 0;
       act[q] = cnt[q] > 0;
       sumc += cnt[q];
       suma += act[q];
@@ -780,7 +786,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
-      if (e < E) rt.expert_first[e] = pc;
+      if (e < E) efirst[e] = pc;
       if (act[q]) {
         rt.act_expert[pa] = e;
         rt.act_off[pa] = pc;
@@ -792,13 +798,39 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     if (tid == 63) rt.n_active = sa;
   }
   wg_sync();
+  if (blockIdx.x == 0 && a.hist)
+    for (int e = tid; e < E; e += kThreads) a.hist[e] += ecnt[e];
+  if (!cw) {
+    // GEMM2 slots (control wave): slot i is active expert i's first min(cnt, 8) pairs; the
+    // experts with more than 8 pairs get a second slot each, after all the first slots
+    const int lane = tid & 63, na = rt.n_active;
+    int nsplit = 0;
+    for (int base = 0; base < na; base += 64) {
+      const int i = base + lane;
+      const int c = i < na ? rt.act_cnt[i] : 0;
+      const uint64_t split = __ballot(c > 8);
+      if (i < na) {
+        rt.slot_expert[i] = rt.act_expert[i];
+        rt.slot_off[i] = rt.act_off[i];
+        rt.slot_cnt[i] = min(c, 8);
+        if (c > 8) {
+          const int j = na + nsplit + __popcll(split & ((1ull << lane) - 1ull));
+          rt.slot_expert[j] = rt.act_expert[i];
+          rt.slot_off[j] = rt.act_off[i] + 8;
+          rt.slot_cnt[j] = c - 8;
+        }
+      }
+      nsplit += __popcll(split);
+    }
+    if (lane == 0) rt.n_slots = na + nsplit;
+  }
   for (int p = tid; cw && p < npairs; p += kCompute) {
     const int e = rt.idx[p];
-    const uint32_t* m = rt.mask + e * 4;
+    const uint32_t* m = mask + e * 4;
     const int w = p >> 5;
     int r = __popc(m[w] & ((1u << (p & 31)) - 1u));
     for (int q = 0; q < w; ++q) r += __popc(m[q]);
-    rt.pair_list[rt.expert_first[e] + r] = p;
+    rt.pair_list[efirst[e] + r] = p;
   }
   wg_sync();
 }
@@ -1051,30 +1083,30 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
 
 // ---- GEMM2 for NVFP4 experts: output columns [c0, c0+8) of P per workgroup
 //
-// Unit U of the grid's expert list is the pair of active experts (2U, 2U+1); wave w takes
-// units w, w+8, ...  Two experts share one 16x16 MFMA tile: token rows 0-7 and weight
-// columns 0-7 belong to expert 2U, rows 8-15 and columns 8-15 to 2U+1, and the off-diagonal
-// blocks are discarded.  An expert with more than 8 tokens runs alone with all 16 token rows
-// (two passes over the same weights).  Lane (nl, grp) holds weight row c0 + nl % 8 of its
-// column's expert for the quarter k in [grp I/4, (grp+1) I/4) of the reduction: I/8 bytes of
-// codes and I/64 E4M3 block scales, loaded straight into registers (the first G2_UNITS units
-// while the grid waits for GEMM1).  The intermediate is read in the same permuted k order,
-// which MFMA allows.  Requires I % 64 == 0.
-constexpr int G2_UNITS = 4;   // units per register batch; two batches cover 64 units
+// Work comes in slots of at most 8 (token, slot) pairs of one expert (an expert with more
+// than 8 pairs has two slots).  Unit U is the slot pair (2U, 2U+1), one 16x16 MFMA tile:
+// token rows 0-7 and weight columns 0-7 belong to slot 2U, rows 8-15 and columns 8-15 to slot
+// 2U+1, and the off-diagonal blocks are discarded.  Wave w takes units w, w+8, ...  Lane
+// (nl, grp) holds weight row c0 + nl % 8 of its column's expert for the quarter k in
+// [grp I/4, (grp+1) I/4) of the reduction: I/8 bytes of codes and I/64 E4M3 block scales,
+// loaded straight into registers (a wave's first G2_UNITS units while the grid waits for
+// GEMM1).  The intermediate is read in the same permuted k order, which MFMA allows.
+// Requires I % 64 == 0.
+constexpr int G2_UNITS = 4;   // units per register batch
 constexpr int G2_MAXB = 4;    // I/64 <= 4
 struct G2W {
   u32x2 c[G2_UNITS][G2_MAXB];
   uint32_t s[G2_UNITS][G2_MAXB];
 };
 
-// Loads unit U (the expert pair 2U, 2U+1 of the active list) into register slot `i` of `w`
-// for columns [c0, c0+8).  Compute waves only; `rt` must hold this launch's routing.
+// Loads unit U into register slot `i` of `w` for columns [c0, c0+8).  Compute waves only;
+// `rt` must hold this launch's routing.
 __device__ __forceinline__ void g2_load_unit(const KArgs& a, const Route& rt, int c0, int U, G2W& w, int i) {
   const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
-  const int I = a.I, nb = I / 64, na = rt.n_active;
-  if (2 * U < na) {                                              // uniform over the wave
-    const int ie = (nl >= 8 && 2 * U + 1 < na) ? 2 * U + 1 : 2 * U;
-    const size_t row = (size_t)rt.act_expert[ie] * a.P + c0 + (nl & 7);
+  const int I = a.I, nb = I / 64, ns = rt.n_slots;
+  if (2 * U < ns) {                                              // uniform over the wave
+    const int sl = (nl >= 8 && 2 * U + 1 < ns) ? 2 * U + 1 : 2 * U;
+    const size_t row = (size_t)rt.slot_expert[sl] * a.P + c0 + (nl & 7);
     const uint8_t* cp = a.w2_codes + row * (I / 2) + grp * (I / 8);   // 8-byte aligned
     const uint8_t* sp = a.w2_scales + row * (I / 16) + grp * nb;
 #pragma unroll
@@ -1093,51 +1125,32 @@ __device__ __forceinline__ void g2_load(const KArgs& a, const Route& rt, int c0,
   for (int i = 0; i < G2_UNITS; ++i) g2_load_unit(a, rt, c0, wave + 8 * (G2_UNITS * batch + i), w, i);
 }
 
-// One unit from registers slot `i` of `w`; writes gate-free expert outputs to outp[pair][8].
+// One unit from register slot `i` of `w`.  urow[U][m] is the pair on token row m (-1: none).
+// Writes the expert outputs (before gates) to outp[pair][8].
 __device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G2W& w, int i, int U,
-                                        const uint16_t* actf, int astride, float* outp) {
+                                        const int32_t* urow, const uint16_t* actf, int astride, float* outp) {
   const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
-  const int I = a.I, na = rt.n_active;
-  const int iA = 2 * U, iB = 2 * U + 1;
-  const bool hasB = iB < na;
-  const int cA = rt.act_cnt[iA], cB = hasB ? rt.act_cnt[iB] : 0;
-  const bool pairm = hasB && cA <= 8 && cB <= 8;
-  const float ts = rt.ts2[rt.act_expert[(nl >= 8 && hasB) ? iB : iA]];
-  for (int pass = 0; pass < (pairm || !hasB ? 1 : 2); ++pass) {
-    // pass 0: expert 2U (with 2U+1 when paired); pass 1: expert 2U+1 alone, columns 8-15
-    const int ia = pass == 0 ? iA : iB;
-    const int cnt_a = rt.act_cnt[ia], off_a = rt.act_off[ia];
-    const int cnt_b = pairm ? cB : 0, off_b = pairm ? rt.act_off[iB] : 0;
-    int pair_m = -1;
-    if (pairm) {
-      if (nl < 8) { if (nl < cnt_a) pair_m = rt.pair_list[off_a + nl]; }
-      else if (nl - 8 < cnt_b) pair_m = rt.pair_list[off_b + nl - 8];
-    } else if (nl < cnt_a) {
-      pair_m = rt.pair_list[off_a + nl];
-    }
-    // rows without a pair read pair 0; their outputs are discarded
-    const uint16_t* arow = actf + (pair_m < 0 ? 0 : pair_m) * astride + grp * (I / 4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int I = a.I;
+  const int32_t* ur = urow + U * 16;
+  const int pair_m = ur[nl];
+  // rows without a pair read pair 0; their outputs are discarded
+  const uint16_t* arow = actf + (pair_m < 0 ? 0 : pair_m) * astride + grp * (I / 4);
+  const int sl = (nl >= 8 && 2 * U + 1 < rt.n_slots) ? 2 * U + 1 : 2 * U;
+  const float ts = rt.ts2[rt.slot_expert[sl]];
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int st = 0; st < 2 * G2_MAXB; ++st) {
-      if (st < I / 32) {
-        const u32x4 x = *(const u32x4*)(arow + 8 * st);
-        acc = mfma_f16(x, fp4x8_to_f16(w.c[i][st / 2][st & 1], e4m3_to_f16x2(w.s[i][st / 2])), acc);
-      }
+  for (int st = 0; st < 2 * G2_MAXB; ++st) {
+    if (st < I / 32) {
+      const u32x4 x = *(const u32x4*)(arow + 8 * st);
+      acc = mfma_f16(x, fp4x8_to_f16(w.c[i][st / 2][st & 1], e4m3_to_f16x2(w.s[i][st / 2])), acc);
     }
-    // C lane: weight column nl, token rows 4 grp + r
+  }
+  // C lane: weight column nl, token rows 4 grp + r; keep the diagonal blocks
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 4 * grp + r;
-      int pair = -1;
-      if (pairm) {
-        if (nl < 8 && row < 8 && row < cnt_a) pair = rt.pair_list[off_a + row];
-        else if (nl >= 8 && row >= 8 && row - 8 < cnt_b) pair = rt.pair_list[off_b + row - 8];
-      } else if ((pass == 0) == (nl < 8) && row < cnt_a) {
-        pair = rt.pair_list[off_a + row];
-      }
-      if (pair >= 0) outp[pair * 8 + (nl & 7)] = acc[r] * ts;
-    }
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * grp + r;
+    const int pair = ur[row];
+    if (pair >= 0 && (row >> 3) == (nl >> 3)) outp[pair * 8 + (nl & 7)] = acc[r] * ts;
   }
 }
 
@@ -1149,10 +1162,12 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
   const bool cw = tid < kCompute;
   const int nwg = gridDim.x, nslices = P / 8;
   if ((int)blockIdx.x >= nslices) return;       // uniform over the workgroup
-  const int npairs = T * K, na = rt.n_active;
+  const int npairs = T * K, ns = rt.n_slots, nu = (ns + 1) / 2;
   const int astride = I + 8;                                        // fp16 per pair row in LDS
   uint16_t* actf = (uint16_t*)smem;                                 // [pairs][I + 8]
-  float* outp = (float*)(smem + ((npairs * astride * 2 + 255) & ~255));   // [pairs][8]
+  const int actb = (npairs * astride * 2 + 255) & ~255;
+  float* outp = (float*)(smem + actb);                              // [pairs][8]
+  int32_t* urow = (int32_t*)(smem + actb + 128 * 8 * 4);            // [units][16]
   const int wave = tid >> 6;
   for (int sl = blockIdx.x; sl < nslices; sl += nwg) {
     const int c0 = sl * 8;
@@ -1165,6 +1180,11 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
       for (int j = 0; j < 4; ++j) {
         const int i = j * kCompute + tid;
         if (cw && i < nblk) v[j] = ld16(a.act_q + (size_t)i * 4);
+      }
+      // token-row tables of the units
+      for (int e = tid; cw && e < nu * 16; e += kCompute) {
+        const int s2 = 2 * (e >> 4) + ((e >> 3) & 1), j = e & 7;
+        urow[e] = (s2 < ns && j < rt.slot_cnt[s2]) ? rt.pair_list[rt.slot_off[s2] + j] : -1;
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -1183,18 +1203,16 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
     wg_sync();
     if (first) stamp<TS>(a.timestamps, 42, 0);
     if (cw) {
-      // batch 0 from the registers; each slot is refilled with batch 1's unit once used
+      // batches of G2_UNITS units from the registers; each slot is refilled with the next
+      // batch's unit as soon as it is used
+      for (int b = 0; wave + 8 * G2_UNITS * b < nu; ++b) {
 #pragma unroll
-      for (int i = 0; i < G2_UNITS; ++i) {
-        const int U = wave + 8 * i;
-        if (2 * U < na) g2_unit(a, rt, w0, i, U, actf, astride, outp);
-        g2_load_unit(a, rt, c0, wave + 8 * (G2_UNITS + i), w0, i);
-      }
-      if (first) stamp<TS>(a.timestamps, 48, 0);
-#pragma unroll
-      for (int i = 0; i < G2_UNITS; ++i) {
-        const int U = wave + 8 * (G2_UNITS + i);
-        if (2 * U < na) g2_unit(a, rt, w0, i, U, actf, astride, outp);
+        for (int i = 0; i < G2_UNITS; ++i) {
+          const int U = wave + 8 * (G2_UNITS * b + i);
+          if (U < nu) g2_unit(a, rt, w0, i, U, urow, actf, astride, outp);
+          g2_load_unit(a, rt, c0, U + 8 * G2_UNITS, w0, i);
+        }
+        if (first && b == 0) stamp<TS>(a.timestamps, 48, 0);
       }
     }
     wg_sync();
@@ -1685,8 +1703,6 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
           if (a.topk_idx) a.topk_idx[p] = rt.idx[p];
           if (a.topk_gate) a.topk_gate[p] = rt.gate[p];
         }
-        if (a.hist)
-          for (int e = tid; e < a.E; e += kThreads) a.hist[e] += rt.expert_cnt[e];
       }
     }
     stamp<TS>(a.timestamps, 19);
