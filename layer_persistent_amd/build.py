@@ -14,7 +14,7 @@ ARCH = "gfx950"
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-    # keep the compiler from emitting packed fp32 VALU ops (see DESIGN notes)
+    # no packed fp32 VALU forms (v_pk_fma/mul/add_f32) in the generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]

@@ -65,7 +65,7 @@ constexpr int LDS_BYTES = 148 * 1024;                  // >= every phase's use (
 // dense-phase reduction buffers and the merge scratch
 constexpr int POOL_LDS_OFF = 20 * 1024;
 static_assert(POOL_LDS_OFF + 16 * 4096 * 2 <= LDS_BYTES, "pooler tile in LDS");
-static_assert(G1_XS_BYTES + 16 * 16 * 128 + 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
+static_assert(G1_XS_BYTES + 16 * 16 * 128 + 2 * 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
 
 __device__ __forceinline__ void wg_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -935,82 +935,78 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   const int xstride = P + XS_STRIDE_PAD;
   uint16_t* xs = (uint16_t*)smem;                                  // [T][P + 8] bf16
   uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // [16 units][16 rows][P/16]
-  float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][16][17]
-  xs_build(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
-  stamp<TS>(a.timestamps, 44, 0);
+  float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][2 K halves][16][17]
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
   const int lsteps = P / 128;
   const int nunits = 2 * (t_end - t_begin);
+  // NVFP4: a round's units are split into pieces (unit, K half) dealt to the compute waves
+  // round-robin (piece pc: unit pc / nh, half pc % nh), so the waves carry equal work.  A wave
+  // streams its pieces with the next piece's codes and block scales in flight while the
+  // current one is multiplied; each piece leaves its partial tile in ubuf[unit][half].
+  const int nh = lsteps > 8 ? 2 : 1;                             // pieces per unit
+  const int hsteps = (lsteps + nh - 1) / nh;                     // load steps per piece (<= 8)
+  const int srow_b = (P / 16) / nh;                              // scale bytes per row and piece
+  u32x4 cA[8], cB[8], sA, sB;
+  auto load_piece = [&](int u0, int pc, u32x4 (&cd)[8], u32x4& sv) {
+    const int u = pc / nh, hf = pc % nh;
+    const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
+    const int ai = task / jblocks, j0 = (task % jblocks) * 16;
+    const size_t wrow = (size_t)rt.act_expert[ai] * 2 * I + half * I + j0;
+    const uint8_t* cp = a.w1_codes + (wrow + nl) * (P / 2) + grp * 16 + hf * hsteps * 64;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) if (j < hsteps && hf * hsteps + j < lsteps) cd[j] = ld16(cp + j * 64);
+    // this piece's scales: 16 rows x srow_b bytes, 16 bytes per lane
+    const int sb = lane * 16;
+    if (sb < 16 * srow_b) sv = ld16(a.w1_scales + (wrow + sb / srow_b) * (P / 16) + hf * srow_b + sb % srow_b);
+  };
+  // the first round's first piece is requested before the input rows are built
+  if (cw && a.fmt == 1 && wave < nh * min(G1_UNITS, nunits)) load_piece(0, wave, cA, sA);
+  xs_build(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
+  stamp<TS>(a.timestamps, 44, 0);
   for (int u0 = 0; u0 < nunits; u0 += G1_UNITS) {
     const int nu = min(G1_UNITS, nunits - u0);
     if (cw && a.fmt == 1) {
-      // This wave's units u0 + wave and u0 + wave + 8, streamed as half-units (8 load steps
-      // of 128 k): the codes of the next half-unit (and, at a unit's start, its scales) are
-      // in flight while the current one is multiplied.
-      const int nh = lsteps > 8 ? 2 : 1;                         // halves per unit
-      const int my_units = (wave < nu) + (wave + 8 < nu);
-      const int nhu = my_units * nh;
-      auto unit_of = [&](int hu) { return wave + 8 * (hu / nh); };
-      auto load_half = [&](int hu, u32x4 (&cd)[8], u32x4 (&sv)[2]) {
-        const int u = unit_of(hu), hf = hu % nh;
-        const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
-        const int ai = task / jblocks, j0 = (task % jblocks) * 16;
-        const size_t wrow = (size_t)rt.act_expert[ai] * 2 * I + half * I + j0;
-        const uint8_t* cp = a.w1_codes + (wrow + nl) * (P / 2) + grp * 16 + hf * 8 * 64;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) if (hf * 8 + j < lsteps) cd[j] = ld16(cp + j * 64);
-        if (hf == 0) {
-          // the unit's 16 rows of scales (16 * P/16 bytes): 16 bytes per lane per 1 KB
-          const uint8_t* sp = a.w1_scales + wrow * (P / 16);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) if ((lane + 64 * j) * 16 < 16 * (P / 16)) sv[j] = ld16(sp + (lane + 64 * j) * 16);
-        }
-      };
-      u32x4 cA[8], cB[8], sA[2], sB[2];
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (nhu > 0) load_half(0, cA, sA);
+      const int npc = nh * nu;
+      const int my = wave < npc ? (npc - 1 - wave) / 8 + 1 : 0;
+      if (my > 0 && u0 > 0) load_piece(u0, wave, cA, sA);
 #pragma unroll 1
-      for (int hu = 0; hu < nhu; hu += 2) {
-        // ---- half-unit hu in cA / sA; prefetch hu + 1 into cB / sB
+      for (int j = 0; j < my; j += 2) {
         for (int x = 0; x < 2; ++x) {
-          const int h = hu + x;
-          if (h >= nhu) break;
-          if (h + 1 < nhu) {
-            if (x == 0) load_half(h + 1, cB, sB); else load_half(h + 1, cA, sA);
+          const int jj = j + x;
+          if (jj >= my) break;
+          if (jj + 1 < my) {
+            if (x == 0) load_piece(u0, wave + 8 * (jj + 1), cB, sB); else load_piece(u0, wave + 8 * (jj + 1), cA, sA);
           }
-          const int u = unit_of(h), hf = h % nh;
+          const int pc = wave + 8 * jj, u = pc / nh, hf = pc % nh;
           const int task = t_begin + (u0 + u) / 2;
           const int ai = task / jblocks;
-          const int e = rt.act_expert[ai], cnt = rt.act_cnt[ai], off = rt.act_off[ai];
-          uint8_t* sd = sbuf + u * 16 * (P / 16);
-          if (hf == 0) {
-            const u32x4* sv = x == 0 ? sA : sB;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) if ((lane + 64 * j) * 16 < 16 * (P / 16)) *(u32x4*)(sd + (lane + 64 * j) * 16) = sv[j];
-            acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          }
+          const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
+          // the piece's scales into this wave's LDS buffer (wave-private: no barrier)
+          uint8_t* sd = sbuf + (wave * 2 + x) * 1024;
+          if (lane * 16 < 16 * srow_b) *(u32x4*)(sd + lane * 16) = x == 0 ? sA : sB;
           // rows past the expert's tokens read token 0 and are discarded after the product
           const uint16_t* xrow = xs + (nl < cnt ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
-          const uint8_t* srow = sd + nl * (P / 16) + grp * 2;
+          const uint8_t* srow = sd + nl * srow_b + grp * 2;
           const u32x4* cd = x == 0 ? cA : cB;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int ls = hf * 8 + j;
-            if (ls < lsteps) {
-              const uint32_t sc = *(const uint16_t*)(srow + ls * 8);
+          for (int k = 0; k < 8; ++k) {
+            const int ls = hf * hsteps + k;
+            if (k < hsteps && ls < lsteps) {
+              const uint32_t sc = *(const uint16_t*)(srow + k * 8);
               const f16x2_t s0 = e4m3_to_f16x2(sc & 0xFF), s1 = e4m3_to_f16x2(sc >> 8);
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const u32x4 xa = *(const u32x4*)(xrow + ls * 128 + q * 8);
-                acc = mfma_f16(xa, fp4x8_to_f16(cd[j][q], q < 2 ? s0 : s1), acc);
+                acc = mfma_f16(xa, fp4x8_to_f16(cd[k][q], q < 2 ? s0 : s1), acc);
               }
             }
           }
-          if (hf == nh - 1) {
-            const float ts = rt.ts1[e];
-            float* ub = ubuf + u * (16 * 17);
+          float* ub = ubuf + (2 * u + hf) * (16 * 17);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ub[(4 * grp + r) * 17 + nl] = acc[r] * ts;
+          for (int r = 0; r < 4; ++r) {
+            ub[(4 * grp + r) * 17 + nl] = acc[r];
+            if (nh == 1) ub[16 * 17 + (4 * grp + r) * 17 + nl] = 0.f;
           }
         }
       }
@@ -1031,9 +1027,12 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
             const u32x4 xa = mv ? *(const u32x4*)(xrow + st * 32) : u32x4{0, 0, 0, 0};
             acc = mfma_bf16(xa, ld16(wr + st * 32), acc);
           }
-          float* ub = ubuf + u * (16 * 17);
+          float* ub = ubuf + (2 * u) * (16 * 17);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ub[(4 * grp + r) * 17 + nl] = acc[r];
+          for (int r = 0; r < 4; ++r) {
+            ub[(4 * grp + r) * 17 + nl] = acc[r];
+            ub[16 * 17 + (4 * grp + r) * 17 + nl] = 0.f;
+          }
         }
       }
     }
@@ -1046,15 +1045,17 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
       const int ai = task / jblocks, j0 = (task % jblocks) * 16;
       if (m < rt.act_cnt[ai]) {
         const int pair = rt.pair_list[rt.act_off[ai] + m];
-        const float* ug = ubuf + (2 * tl) * (16 * 17) + m * 17;
-        const float* uu = ubuf + (2 * tl + 1) * (16 * 17) + m * 17;
-        // NVFP4: undo the token row's power-of-two input scale (exact)
-        const float f = a.fmt == 1 ? __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23) : 1.0f;
+        // the two K halves of the gate unit (2 tl) and of the up unit (2 tl + 1)
+        const float* ug = ubuf + (4 * tl) * (16 * 17) + m * 17;
+        const float* uu = ubuf + (4 * tl + 2) * (16 * 17) + m * 17;
+        // NVFP4: the tensor scale, and undo the token row's power-of-two input scale (exact)
+        const float f = a.fmt == 1 ? rt.ts1[rt.act_expert[ai]] * __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23)
+                                   : 1.0f;
         float v[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
-          const float g = ug[j] * f;
-          v[j] = g / (1.0f + __expf(-g)) * (uu[j] * f);
+          const float g = (ug[j] + ug[16 * 17 + j]) * f;
+          v[j] = g / (1.0f + __expf(-g)) * ((uu[j] + uu[16 * 17 + j]) * f);
         }
         if (a.fmt == 1) {
           float amax = 0.f;
