@@ -264,6 +264,11 @@ def main():
         if g2b.any():
             phases["gemm2_batch0"] = d(48, 42, g2b)
             phases["gemm2_batch1"] = d(43, 48, g2b)
+        g1e = tsv[:, 49] > 0
+        if g1e.any():
+            phases["gemm1_first_loads_issued"] = d(49, 18, g1e)
+            phases["gemm1_xs_rowmax"] = d(50, 49, g1e)
+            phases["gemm1_xs_convert"] = d(44, 50, g1e)
         g1 = tsv[:, 45] > 0
         if g1.any():
             d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
