@@ -98,6 +98,12 @@ typedef struct {
   const int32_t *prefetch_experts; /* [n_prefetch] or NULL: expert ids to pull into the
                                   device-side cache at launch start (speculative prefetch)    */
   int n_prefetch;              /* [host] 0..16                                              */
+  int32_t *prefetch_next;      /* [n_prefetch_next] or NULL: receives this step's most-used
+                                  experts by (pair count desc, index asc), -1 after the last
+                                  used one -- the next step's prefetch_experts (the pages'
+                                  expert prefetch from the previous step's usage: alphasignal.ai
+                                  "Four mechanisms keep work moving")                         */
+  int n_prefetch_next;         /* [host] 0..16                                              */
   const float *router_bias;    /* [T][E] or NULL   added to the logits before top-k           */
   void *workspace;             /* >= mk_workspace_bytes(); initialised once by
                                   mk_workspace_init(); holds the status word, the

@@ -39,7 +39,8 @@ class mk_step_io(C.Structure):
                 ("k_cache_next", C.c_void_p), ("v_cache_next", C.c_void_p), ("h_out", C.c_void_p),
                 ("q_next", C.c_void_p), ("topk_idx", C.c_void_p), ("topk_gate", C.c_void_p),
                 ("router_logits", C.c_void_p), ("attn_stats", C.c_void_p), ("expert_hist", C.c_void_p),
-                ("prefetch_experts", C.c_void_p), ("n_prefetch", C.c_int), ("router_bias", C.c_void_p),
+                ("prefetch_experts", C.c_void_p), ("n_prefetch", C.c_int),
+                ("prefetch_next", C.c_void_p), ("n_prefetch_next", C.c_int), ("router_bias", C.c_void_p),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("timestamps", C.c_void_p),
                 ("spin_limit", C.c_int), ("debug_skip_signal_wg", C.c_int)]
 

@@ -174,6 +174,8 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   }
   if (io->n_prefetch < 0 || io->n_prefetch > 16) return MK_ESHAPE;
   if (io->n_prefetch > 0 && !io->prefetch_experts) return MK_EINVAL;
+  if (io->n_prefetch_next < 0 || io->n_prefetch_next > 16) return MK_ESHAPE;
+  if (io->n_prefetch_next > 0 && !io->prefetch_next) return MK_EINVAL;
   if (io->spin_limit < 0) return MK_EINVAL;
   const void* al[] = {io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next, io->v_cache_next,
                       io->h_out, io->q_next, io->workspace, io->topk_idx, io->topk_gate,
@@ -207,6 +209,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.topk_idx = io->topk_idx; a.topk_gate = io->topk_gate; a.router_logits = io->router_logits;
   a.attn_stats = io->attn_stats; a.hist = io->expert_hist;
   a.prefetch = io->prefetch_experts; a.n_prefetch = io->n_prefetch; a.bias = io->router_bias;
+  a.prefetch_next = io->prefetch_next; a.n_prefetch_next = io->n_prefetch_next;
   a.w_o = (const uint16_t*)w->w_o; a.w_pool = (const uint16_t*)w->w_pool;
   a.w_router = (const uint16_t*)w->w_router; a.w_unpool = (const uint16_t*)w->w_unpool;
   a.w_qkv = (const uint16_t*)w->w_qkv_next;

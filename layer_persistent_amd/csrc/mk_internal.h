@@ -26,6 +26,8 @@ struct KArgs {
   int32_t* hist;
   const int32_t* prefetch;
   int n_prefetch;
+  int32_t* prefetch_next;
+  int n_prefetch_next;
   const float* bias;
   // weights
   const uint16_t *w_o, *w_pool, *w_router, *w_unpool, *w_qkv, *w1, *w2;

@@ -247,6 +247,36 @@ __device__ __forceinline__ uint32_t touch_tile(const uint16_t* __restrict__ W, i
   return x;
 }
 
+// Speculative expert prefetch: pull the listed experts' W1 and W2 (codes and block scales for
+// NVFP4, the bf16 matrices otherwise) into the device-side caches, one dword per 128-byte line.
+// Worker w of nworkers takes every nworkers-th line of the concatenated slices; expert ids
+// outside [0, E) are skipped.  Compute threads; the folded value must be kept alive.
+__device__ __forceinline__ uint32_t expert_touch(const KArgs& a, int worker, int nworkers) {
+  const size_t P = a.P, I = a.I;
+  const bool fp4 = a.fmt == 1;
+  // per expert: up to four contiguous regions
+  const size_t r0 = fp4 ? 2 * I * P / 2 : 2 * I * P * 2;       // W1 codes | W1 bf16
+  const size_t r1 = fp4 ? 2 * I * P / 16 : 0;                  // W1 scales
+  const size_t r2 = fp4 ? P * I / 2 : P * I * 2;               // W2 codes | W2 bf16
+  const size_t r3 = fp4 ? P * I / 16 : 0;                      // W2 scales
+  const size_t per = (r0 + r1 + r2 + r3 + 127) / 128;          // lines per expert (regions rounded)
+  const size_t lines = per * (size_t)a.n_prefetch;
+  uint32_t v = 0;
+  for (size_t l = (size_t)worker * kCompute + threadIdx.x; l < lines; l += (size_t)nworkers * kCompute) {
+    const int e = a.prefetch[l / per];
+    if (e < 0 || e >= a.E) continue;
+    const size_t o = (l % per) * 128;
+    const uint8_t* p;
+    if (o < r0) p = (fp4 ? a.w1_codes : (const uint8_t*)a.w1) + (size_t)e * r0 + o;
+    else if (o < r0 + r1) p = a.w1_scales + (size_t)e * r1 + (o - r0);
+    else if (o < r0 + r1 + r2) p = (fp4 ? a.w2_codes : (const uint8_t*)a.w2) + (size_t)e * r2 + (o - r0 - r1);
+    else if (o < r0 + r1 + r2 + r3) p = a.w2_scales + (size_t)e * r3 + (o - r0 - r1 - r2);
+    else continue;
+    v ^= *(const uint32_t*)p;
+  }
+  return v;
+}
+
 // This wave's partial of the tile: x [rows][K] (rows >= T are zero) times the fragments.
 template <int MAXS>
 __device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t* __restrict__ x, int T, int K) {
@@ -823,6 +853,23 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
       nsplit += __popcll(split);
     }
     if (lane == 0) rt.n_slots = na + nsplit;
+    // workgroup 0: this step's most-used experts, the next step's prefetch list, by a
+    // tournament over keys (count, then lower index) that are unique per expert
+    if (blockIdx.x == 0 && a.prefetch_next && a.n_prefetch_next > 0) {
+      int32_t key[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * lane + q;
+        key[q] = (e < E && ecnt[e] > 0) ? (ecnt[e] << 16) | (0xFFFF - e) : -1;
+      }
+      for (int j = 0; j < a.n_prefetch_next; ++j) {
+        const int32_t best = max(max(key[0], key[1]), max(key[2], key[3]));
+        const int32_t m = wave_max_i32(best);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) key[q] = key[q] == m ? -1 : key[q];
+        if (lane == 0) a.prefetch_next[j] = m < 0 ? -1 : 0xFFFF - (m & 0xFFFF);
+      }
+    }
   }
   for (int p = tid; cw && p < npairs; p += kCompute) {
     const int e = rt.idx[p];
@@ -1579,6 +1626,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // workgroups without an attention item pull their unpooler and qkv tiles into the
     // device-side caches while memory is otherwise idle; they are read at the end of the layer
     if (cw && (int)blockIdx.x >= a.attn_items) {
+      // the previous step's most-used experts, before the routing of this step is known
+      if (a.n_prefetch > 0 && nwg > a.attn_items)
+        touched ^= expert_touch(a, blockIdx.x - a.attn_items, nwg - a.attn_items);
       if (p_u) touched ^= touch_tile<1>(a.w_unpool, a.P, t_u * 16);
       if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16);
     }

@@ -102,13 +102,16 @@ class DeviceStep:
     timestamps: torch.Tensor | None = None
     prefetch: torch.Tensor | None = None
     n_prefetch: int = 0
+    prefetch_next: torch.Tensor | None = None
+    n_prefetch_next: int = 0
 
     def struct(self, spin_limit: int = 0, skip_wg: int = -1) -> abi.mk_step_io:
         p = lambda t: None if t is None else t.data_ptr()
         return abi.mk_step_io(self.T, self.ctx, p(self.parent), p(self.q_in), p(self.h_in), p(self.k_cache),
                               p(self.v_cache), p(self.k_next), p(self.v_next), p(self.h_out), p(self.q_next),
                               p(self.topk_idx), p(self.topk_gate), p(self.logits), p(self.stats), p(self.hist),
-                              p(self.prefetch), self.n_prefetch, p(self.bias), p(self.workspace),
+                              p(self.prefetch), self.n_prefetch, p(self.prefetch_next), self.n_prefetch_next,
+                              p(self.bias), p(self.workspace),
                               self.workspace.numel(), p(self.timestamps), spin_limit, skip_wg)
 
     def ws_u16(self, off: int, n: int) -> np.ndarray:

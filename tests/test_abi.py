@@ -48,10 +48,12 @@ def _weights(ptr=GOOD):
 def _io(T=16, ctx=8192, ptr=GOOD, **kw):
     io = mk.mk_step_io()
     for f, _ in mk.mk_step_io._fields_:
-        if f not in ("T", "ctx_len", "n_prefetch", "workspace_bytes", "spin_limit", "debug_skip_signal_wg"):
+        if f not in ("T", "ctx_len", "n_prefetch", "n_prefetch_next", "workspace_bytes", "spin_limit",
+                     "debug_skip_signal_wg"):
             setattr(io, f, ptr)
     io.T, io.ctx_len, io.workspace_bytes, io.debug_skip_signal_wg = T, ctx, 1 << 30, -1
     io.prefetch_experts = None
+    io.prefetch_next = None
     for k, v in kw.items():
         setattr(io, k, v)
     return io
@@ -80,6 +82,8 @@ def test_layer_step_rejects_bad_T_capacity_alignment_and_enum():
     assert mk.mk_layer_step(_cfg(expert_fmt=7), _weights(), _io(), check=False) == mk.MK_EINVAL
     assert mk.mk_layer_step(_cfg(), _weights(), _io(n_prefetch=17), check=False) == mk.MK_ESHAPE
     assert mk.mk_layer_step(_cfg(), _weights(), _io(n_prefetch=3), check=False) == mk.MK_EINVAL
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(n_prefetch_next=17), check=False) == mk.MK_ESHAPE
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(n_prefetch_next=14), check=False) == mk.MK_EINVAL
     w = _weights()
     w.w1_codes = None
     assert mk.mk_layer_step(_cfg(), w, _io(), check=False) == mk.MK_EINVAL

@@ -186,6 +186,37 @@ def test_deterministic_and_timing_build_identical():
         assert np.array_equal(outs[0][key], outs[2][key]), key
 
 
+@pytest.mark.parametrize("shape,cfg_id,n", [(SMALL_NVFP4, 86, 16), (synth.CFG2, 2, 14)])
+def test_expert_prefetch_lists_and_changes_no_output(shape, cfg_id, n):
+    """The kernel's next-step prefetch list equals the most-used experts of its own routing
+    (count desc, index asc, -1 past the used ones), and a launch that prefetches -- a real
+    list, or one with ids outside [0, E) -- returns bit-identical outputs."""
+    log(f"[prefetch] {shape.name}")
+    inp = synth.make_layer_inputs(shape, cfg_id)
+    dw = dt.upload_weights(inp)
+    st = dt.make_step(inp)
+    st.prefetch_next = torch.full((16,), -7, dtype=torch.int32, device="cuda")
+    st.n_prefetch_next = n
+    dt.run_step(dw, st)
+    base = dt.outputs(st)
+    _, top = oracle.usage_top(base["idx"], shape.n_experts, n)
+    want = np.full(n, -1, dtype=np.int32)
+    want[:len(top)] = top
+    got = st.prefetch_next.cpu().numpy()
+    assert np.array_equal(got[:n], want), (got[:n], want)
+    assert np.all(got[n:] == -7)
+    lists = [st.prefetch_next[:n].clone(),
+             torch.tensor([-1, shape.n_experts, 1 << 20, 0, shape.n_experts - 1], dtype=torch.int32, device="cuda")]
+    for lst in lists:
+        st2 = dt.make_step(inp)
+        st2.prefetch, st2.n_prefetch = lst, lst.numel()
+        dt.run_step(dw, st2)
+        out = dt.outputs(st2)
+        for key in ("h_out", "q_next", "k_cache_next", "v_cache_next", "idx", "gate", "logits", "stats", "y", "xp"):
+            assert np.array_equal(base[key], out[key]), key
+    log(f"  prefetch list {got[:n].tolist()}")
+
+
 def test_repeated_steps_on_one_workspace():
     """Successive launches on one workspace (as layer after layer / step after step)."""
     dw = None
