@@ -13,6 +13,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import os
@@ -100,13 +101,103 @@ def cpu_baseline(inp) -> dict:
                       f"{cores} host cores visible, {blas_threads} BLAS threads"}
 
 
+def stack_bytes(shape, n_active_per_layer) -> int:
+    """Algorithmic bytes of one verify step of the stack: every layer's dense weights, its
+    active experts, the KV rows it can see (global every fourth layer), activations."""
+    import dataclasses
+    from layer_persistent_amd.stack import is_global
+    tot = 0
+    for L, na in enumerate(n_active_per_layer):
+        lsh = dataclasses.replace(shape, window=0 if is_global(L) else shape.window)
+        ab = algorithmic_bytes(lsh, na)
+        if L + 1 == len(n_active_per_layer):        # the last layer has no next-layer projection
+            ab["total"] -= 2 * shape.qkv_out * shape.hidden + ab["kv_write"]
+        tot += ab["total"]
+    return tot
+
+
+def bench_stack(args) -> dict:
+    """Configs 4 and 5: a stack of fused layers (62 by default), one launch per layer per
+    verify step; per-step time is the median over the timed steps (each step is a new tree,
+    residual and layer-0 queries); config 5 adds Markov routing (expert reuse between steps)
+    and the speculative expert prefetch."""
+    import torch
+    import synth
+    from layer_persistent_amd.stack import Stack, is_global
+    shape = synth.CONFIGS[args.config]
+    n_layers = args.layers
+    t0 = time.time()
+    stk = Stack(shape, args.config, n_layers)
+    log(f"stack of {n_layers} layers built in {time.time() - t0:.1f} s "
+        f"({sum(l.w.nbytes() for l in stk.layers) / 1e9:.2f} GB of weights)")
+    n_steps = args.warmup + args.steps
+    ins = [synth.stack_step_inputs(shape, args.config, s) for s in range(n_steps)]
+    if args.config == 5:
+        variants = []
+        for reuse in (0.8, 0.0):
+            b = synth.stack_router_biases(shape, args.config, n_layers, n_steps, reuse)
+            variants += [(f"reuse{int(reuse * 100)}_noprefetch", b, False), (f"reuse{int(reuse * 100)}_prefetch", b, True)]
+    else:
+        variants = [("stack", None, False)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    res = {}
+    n_active = None
+    for name, biases, pf in variants:
+        structs = [stk.structs(pf, biases is not None, parity) for parity in (0, 1)]
+        step_us, layer_us = [], []
+        for s in range(n_steps):
+            stk.set_step_inputs(ins[s], None if biases is None else biases[s])
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
+            st = structs[s % 2]
+            ev[0].record(stream)
+            for L in range(n_layers):
+                c, w, io = st[L]
+                rc = stk.lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), sp)
+                if rc != 0:
+                    raise RuntimeError(f"mk_layer_step: {rc}")
+                ev[L + 1].record(stream)
+            torch.cuda.synchronize()
+            if s >= args.warmup:
+                lt = [ev[L].elapsed_time(ev[L + 1]) * 1000.0 for L in range(n_layers)]
+                layer_us.append(lt)
+                step_us.append(ev[0].elapsed_time(ev[n_layers]) * 1000.0)
+        st0 = mk_read_status_ok(stk)
+        lu = np.array(layer_us)
+        glob = [L for L in range(n_layers) if is_global(L)]
+        swa = [L for L in range(n_layers) if not is_global(L)]
+        if n_active is None:
+            n_active = [int(len(torch.unique(l.topk_idx))) for l in stk.layers]
+        res[name] = dict(step_us_median=round(float(np.median(step_us)), 1),
+                         step_us_p10=round(float(np.percentile(step_us, 10)), 1),
+                         step_us_p90=round(float(np.percentile(step_us, 90)), 1),
+                         layer_us_mean=round(float(lu.mean()), 2),
+                         swa_layer_us_mean=round(float(lu[:, swa].mean()), 2),
+                         global_layer_us_mean=round(float(lu[:, glob].mean()), 2) if glob else None,
+                         last_layer_us_mean=round(float(lu[:, -1].mean()), 2), status=st0)
+        log(f"{name}: step median {res[name]['step_us_median']} us, layer mean {res[name]['layer_us_mean']} us "
+            f"(SWA {res[name]['swa_layer_us_mean']}, global {res[name]['global_layer_us_mean']})")
+    return dict(results=res, n_active_last_step=n_active, n_layers=n_layers)
+
+
+def mk_read_status_ok(stk) -> int:
+    import layer_persistent_amd as mk
+    s = mk.mk_read_status(stk.ws)
+    if s != 0:
+        raise RuntimeError(f"in-kernel status {mk.mk_strerror(s)}")
+    return s
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=4)
-    ap.add_argument("--config", type=int, default=2, help="workload id (2: SWA ctx 8192, 3: global ctx 32768)")
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id (2: SWA layer ctx 8192, 3: global layer ctx 32768, "
+                         "4: 62-layer stack ctx 4096, 5: stack with expert reuse and prefetch)")
+    ap.add_argument("--layers", type=int, default=62, help="stack depth for configs 4 and 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -126,6 +217,25 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.config in (4, 5):
+        out = bench_stack(args)
+        main_name = "stack" if args.config == 4 else "reuse80_prefetch"
+        r = out["results"][main_name]
+        shape = synth.CONFIGS[args.config]
+        nbytes = stack_bytes(shape, out["n_active_last_step"])
+        achieved = nbytes / (r["step_us_median"] * 1e-6) / 1e9
+        print(json.dumps({
+            "metric": "us per verify step (stack of fused decoder layers, 16-token tree, 1 GPU)",
+            "value": r["step_us_median"], "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(r["step_us_median"] / 1000.0, 4), "higher_is_better": False, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": shape.name, "layers": out["n_layers"], "global_every": 4, "T": shape.T,
+                       "ctx": shape.ctx, "window": shape.window, "launches_per_step": out["n_layers"]},
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "bytes_per_step": nbytes},
+            "results": out["results"], "n_active_per_layer": out["n_active_last_step"],
+            "cpu_baseline": None}), flush=True)
+        return
     shape = synth.CONFIGS[args.config]
     log(f"workload {shape.name}: generating inputs")
     t0 = time.time()

@@ -69,7 +69,11 @@ typedef struct {
   const void *w_pool;      /* bf16 [P][H]             pooler                                */
   const void *w_router;    /* bf16 [E][P]             router                                */
   const void *w_unpool;    /* bf16 [H][P]             unpooler                              */
-  const void *w_qkv_next;  /* bf16 [(Hq+2Hkv)*d][H]   next layer's q, k, v rows, in that order */
+  const void *w_qkv_next;  /* bf16 [(Hq+2Hkv)*d][H]   next layer's q, k, v rows, in that order;
+                              NULL for the last layer of the stack: the launch then ends after
+                              the unpooler and q_next / k_cache_next / v_cache_next may be
+                              NULL (first and last layers differ: orcarouter.ai write-up,
+                              "where the kernel boundary sits")                              */
   const void *w1, *w2;     /* MK_W_BF16:  bf16 [E][2I][P] (rows [0,I) gate, [I,2I) up), [E][P][I] */
   const uint8_t *w1_codes, *w1_scales;  /* MK_W_NVFP4: [E][2I][P/2], [E][2I][P/16] (mk_nvfp4_pack) */
   const uint8_t *w2_codes, *w2_scales;  /*             [E][P][I/2],  [E][P][I/16]                  */
@@ -86,9 +90,9 @@ typedef struct {
   const void *h_in;            /* bf16 [T][H]      residual stream entering the layer         */
   const void *k_cache, *v_cache;      /* bf16 [cap][Hkv][d]; rows [0, ctx_len+T) valid        */
   void *k_cache_next, *v_cache_next;  /* bf16 [cap][Hkv][d]; rows ctx_len..ctx_len+T-1 written,
-                                         every other row left untouched                       */
+                                         every other row left untouched (NULL: last layer)    */
   void *h_out;                 /* bf16 [T][H]      residual stream leaving the layer          */
-  void *q_next;                /* bf16 [T][Hq*d]   next layer's queries                       */
+  void *q_next;                /* bf16 [T][Hq*d]   next layer's queries (NULL: last layer)    */
   int32_t *topk_idx;           /* [T][k] or NULL   experts per token, best first              */
   float *topk_gate;            /* [T][k] or NULL   softmax over the k selected logits         */
   float *router_logits;        /* [T][E] or NULL   fp32 logits (bias included)                */

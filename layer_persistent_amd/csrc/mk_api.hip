@@ -161,10 +161,11 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   if (rc) return rc;
   const int T = io->T, ctx = io->ctx_len;
   if (ctx < 0 || ctx + T > c->kv_capacity) return MK_ECAPACITY;
-  const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next,
-                       io->v_cache_next, io->h_out, io->q_next, io->workspace, w->w_o, w->w_pool,
-                       w->w_router, w->w_unpool, w->w_qkv_next};
+  const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->h_out, io->workspace,
+                       w->w_o, w->w_pool, w->w_router, w->w_unpool};
   for (const void* p : req) if (!p) return MK_EINVAL;
+  // the next layer's q/k/v are produced unless this is the stack's last layer (w_qkv_next NULL)
+  if (w->w_qkv_next && (!io->q_next || !io->k_cache_next || !io->v_cache_next)) return MK_EINVAL;
   if (c->expert_fmt == MK_W_BF16) {
     if (!w->w1 || !w->w2) return MK_EINVAL;
   } else {

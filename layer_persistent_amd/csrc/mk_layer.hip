@@ -1555,8 +1555,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   const int off_r = nwg - a.E / 16, off_q = a.P / 16 < nwg ? a.P / 16 : 0;
   const int t_r = first_tile(off_r), t_q = first_tile(off_q);
   const int qkv_n = (a.Hq + 2 * a.Hkv) * a.d;
+  // the stack's last layer (no next-layer weights) ends after the unpooler
+  const bool has_qkv = a.w_qkv != nullptr;
   const bool p_o = t_o < a.H / 16, p_p = t_p < a.P / 16, p_r = t_r < a.E / 16, p_u = t_u < a.H / 16,
-             p_q = t_q < qkv_n / 16;
+             p_q = has_qkv && t_q < qkv_n / 16;
   // this workgroup's pooler tile lives in LDS: one tile, no attention item here, and it fits
   const bool pool_lds = p_p && (int)blockIdx.x >= a.attn_items && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
   u32x2 res = {0, 0};
@@ -1738,7 +1740,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
-      dense_phase(a, wq, p_q, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+      if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);

@@ -1,0 +1,128 @@
+"""A decoder stack of fused layer launches: one mk_layer_step launch per layer, all on one
+stream, as the verify step of the pages' system runs its layers (one kernel per decoder
+layer: orcarouter.ai write-up, "where the kernel boundary sits").
+
+Layer L's launch reads its own KV cache and writes the tree rows of layer L+1's cache, so the
+next launch finds them in place; h_out / q_next of layer L are h_in / q_in of layer L+1.
+Every fourth layer (0, 4, ..., 60) attends globally and the rest over a 2048-token window
+(46 + 16 of 62).  The last layer has no next-layer projection.  The caller supplies layer 0's
+inputs (queries, residual and its tree K/V rows), standing in for the embedding prologue.
+
+This module only places tensors in HBM and fills the C-ABI structs; all arithmetic runs in
+libmk.so.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+
+import numpy as np
+import torch
+
+import synth
+from . import _abi as abi
+from .tensors import DeviceWeights, layer_cfg
+
+
+@dataclasses.dataclass
+class StackLayer:
+    cfg: abi.mk_layer_cfg
+    w: DeviceWeights
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    prefetch: list                  # two lists: a step reads one and writes the other
+    topk_idx: torch.Tensor
+
+
+def is_global(layer: int) -> bool:
+    return layer % 4 == 0
+
+
+class Stack:
+    def __init__(self, shape: synth.LayerShape, cfg_id: int, n_layers: int = 62, device: str = "cuda",
+                 n_prefetch: int = 14):
+        self.shape, self.cfg_id, self.n_layers, self.device = shape, cfg_id, n_layers, device
+        self.n_prefetch = n_prefetch
+        sh = shape
+        E, I, P, T, k = sh.n_experts, sh.expert_inter, sh.pooled, sh.T, sh.top_k
+        u8 = dict(dtype=torch.uint8, device=device)
+        self.layers: list[StackLayer] = []
+        for L in range(n_layers):
+            lsh = dataclasses.replace(sh, window=0 if is_global(L) else sh.window)
+            wd = synth.device_layer_weights(lsh, cfg_id, L, device)
+            asi16 = lambda t: t.view(torch.int16)
+            dw = DeviceWeights(asi16(wd["w_o"]), asi16(wd["w_pool"]), asi16(wd["w_router"]),
+                               asi16(wd["w_unpool"]), asi16(wd["w_qkv_next"]) if L + 1 < n_layers else None)
+            dw.w1_codes = torch.empty((E, 2 * I, P // 2), **u8)
+            dw.w1_scales = torch.empty((E, 2 * I, P // 16), **u8)
+            dw.w2_codes = torch.empty((E, P, I // 2), **u8)
+            dw.w2_scales = torch.empty((E, P, I // 16), **u8)
+            dw.w1_ts = torch.empty(E, dtype=torch.float32, device=device)
+            dw.w2_ts = torch.empty(E, dtype=torch.float32, device=device)
+            abi.mk_nvfp4_pack(wd["w1"], 0, E, 2 * I, P, dw.w1_codes, dw.w1_scales, dw.w1_ts)
+            abi.mk_nvfp4_pack(wd["w2"], 0, E, P, I, dw.w2_codes, dw.w2_scales, dw.w2_ts)
+            torch.cuda.synchronize()
+            del wd
+            kc, vc = synth.device_kv_context(lsh, cfg_id, L, device)
+            self.layers.append(StackLayer(layer_cfg(lsh), dw, kc.view(torch.int16), vc.view(torch.int16),
+                                          [torch.full((16,), -1, dtype=torch.int32, device=device) for _ in range(2)],
+                                          torch.zeros((T, k), dtype=torch.int32, device=device)))
+        # one workspace serves every launch (launches on one stream run one after another)
+        self.ws_bytes = max(abi.mk_workspace_bytes(l.cfg, T) for l in self.layers[:2])
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        abi.mk_workspace_init(self.ws, self.ws_bytes)
+        i16 = dict(dtype=torch.int16, device=device)
+        self.h = [torch.zeros((T, sh.hidden), **i16) for _ in range(2)]
+        self.q = [torch.zeros((T, sh.n_q_heads * sh.head_dim), **i16) for _ in range(2)]
+        self.parent = torch.zeros(T, dtype=torch.int32, device=device)
+        self.bias = None
+        self.lib = abi.lib()
+        self._structs = None
+
+    def set_step_inputs(self, step_in: dict, bias: np.ndarray | None = None) -> None:
+        """Layer 0's inputs for a step (host arrays from synth.stack_step_inputs), written into
+        place: the tree, h_in, q_in, and layer 0's tree K/V rows; router biases [L][T][E]."""
+        sh = self.shape
+        self.parent.copy_(torch.from_numpy(step_in["parent"].astype(np.int32)))
+        self.h[0].copy_(torch.from_numpy(step_in["h_in"].view(np.int16)))
+        self.q[0].copy_(torch.from_numpy(step_in["q_in"].view(np.int16)))
+        k0 = torch.from_numpy(step_in["k_tree"].view(np.int16)).to(self.device)
+        v0 = torch.from_numpy(step_in["v_tree"].view(np.int16)).to(self.device)
+        l0 = self.layers[0]
+        abi.mk_kv_append(l0.k_cache, l0.v_cache, sh.kv_capacity, sh.n_kv_heads, sh.head_dim, sh.ctx, k0, v0, sh.T)
+        if bias is not None:
+            if self.bias is None:
+                self.bias = torch.empty(bias.shape, dtype=torch.float32, device=self.device)
+            self.bias.copy_(torch.from_numpy(bias))
+        torch.cuda.synchronize()
+
+    def structs(self, prefetch: bool, use_bias: bool, parity: int = 0):
+        """The argument structs of one step's launches (kept alive by the caller).  Every
+        launch writes its layer's most-used experts into list 1 - parity; with `prefetch` it
+        prefetches the experts of list `parity` (the previous step's), so steps alternate."""
+        sh = self.shape
+        out = []
+        for L, lay in enumerate(self.layers):
+            nxt = self.layers[L + 1] if L + 1 < self.n_layers else None
+            hi, ho = self.h[L % 2], self.h[(L + 1) % 2]
+            qi, qo = self.q[L % 2], self.q[(L + 1) % 2]
+            p = lambda t: None if t is None else t.data_ptr()
+            io = abi.mk_step_io(
+                sh.T, sh.ctx, p(self.parent), p(qi), p(hi), p(lay.k_cache), p(lay.v_cache),
+                p(nxt.k_cache) if nxt else None, p(nxt.v_cache) if nxt else None, p(ho), p(qo) if nxt else None,
+                p(lay.topk_idx), None, None, None, None,
+                p(lay.prefetch[parity]) if prefetch else None, self.n_prefetch if prefetch else 0,
+                p(lay.prefetch[1 - parity]), self.n_prefetch,
+                p(self.bias[L]) if (use_bias and self.bias is not None) else None,
+                p(self.ws), self.ws_bytes, None, 0, -1)
+            out.append((lay.cfg, lay.w.struct(), io))
+        return out
+
+    def launch_step(self, structs, stream_ptr) -> None:
+        for c, w, io in structs:
+            rc = self.lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), stream_ptr)
+            if rc != 0:
+                raise abi.MKError(rc, "mk_layer_step")
+
+    def h_out(self) -> torch.Tensor:
+        return self.h[self.n_layers % 2]

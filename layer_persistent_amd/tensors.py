@@ -32,7 +32,7 @@ class DeviceWeights:
     w_pool: torch.Tensor
     w_router: torch.Tensor
     w_unpool: torch.Tensor
-    w_qkv: torch.Tensor
+    w_qkv: torch.Tensor | None              # None: the stack's last layer (no next-layer q/k/v)
     w1: torch.Tensor | None = None          # bf16 experts
     w2: torch.Tensor | None = None
     w1_codes: torch.Tensor | None = None    # NVFP4 experts

@@ -60,7 +60,8 @@ CFG1 = LayerShape("tiny-global-bf16", 256, 4, 1, 64, 128, 16, 2, 128, 0, 128, 1,
 CFG2 = LayerShape("swa2048-ctx8192-nvfp4", 4096, 8, 1, 128, 2048, 256, 8, 192, 2048, 8192, 16, True)
 CFG3 = LayerShape("global-ctx32768-zipf49", 4096, 8, 1, 128, 2048, 256, 8, 192, 0, 32768, 16, True, "zipf")
 CFG4 = LayerShape("stack62-ctx4096", 4096, 8, 1, 128, 2048, 256, 8, 192, 2048, 4096, 16, True)
-CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4}
+CFG5 = LayerShape("stack62-ctx4096-markov80", 4096, 8, 1, 128, 2048, 256, 8, 192, 2048, 4096, 16, True, "markov")
+CONFIGS = {1: CFG1, 2: CFG2, 3: CFG3, 4: CFG4, 5: CFG5}
 
 
 def base_seed(cfg_id: int) -> int:
@@ -194,3 +195,76 @@ def make_layer_inputs(shape: LayerShape, cfg_id: int, layer: int = 0, step: int 
     return LayerInputs(shape, parent, h_in, q_in, k_cache, v_cache, kn[0].copy(), kn[1].copy(),
                        w(T_WO, (H, Hq * d)), w(T_WP, (P, H)), w(T_WR, (E, P)), w(T_WU, (H, P)),
                        w(T_WQKV, (shape.qkv_out, H)), w1, w2, bias)
+
+
+# ---------------------------------------------------------------- device-side draws (stacks)
+#
+# A 62-layer stack holds ~14 GB of weights; drawing them with NumPy would take minutes, so
+# the stack workloads draw on the device with torch's counter-based CUDA generator, seeded per
+# (workload, layer, tensor).  The same bits are then copied to the host wherever the oracle
+# needs them, so both sides still consume identical inputs.
+
+def _torch_gen(device, base: int, layer: int, tensor_id: int, step: int = 0):
+    import torch
+    g = torch.Generator(device=device)
+    seed = int(np.random.SeedSequence([base, layer, tensor_id, step]).generate_state(1, np.uint64)[0])
+    g.manual_seed(seed & 0x7FFFFFFFFFFFFFFF)
+    return g
+
+
+def device_normal_bf16(shape, std: float, device, base: int, layer: int, tensor_id: int, step: int = 0):
+    """N(0, std) draw stored as bf16 (torch tensor, bfloat16, round to nearest even)."""
+    import torch
+    g = _torch_gen(device, base, layer, tensor_id, step)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32) * std
+    return x.to(torch.bfloat16)
+
+
+def device_layer_weights(shape: LayerShape, cfg_id: int, layer: int, device) -> dict:
+    """One layer's weights drawn on the device (bf16 torch tensors): the dense matrices and
+    the expert masters w1 [E][2I][P], w2 [E][P][I] (NVFP4 layers pack these)."""
+    b = base_seed(cfg_id)
+    H, Hq, d, P, E, I = shape.hidden, shape.n_q_heads, shape.head_dim, shape.pooled, shape.n_experts, shape.expert_inter
+    w = lambda tid, shp: device_normal_bf16(shp, 0.02, device, b, layer, tid)
+    return dict(w_o=w(T_WO, (H, Hq * d)), w_pool=w(T_WP, (P, H)), w_router=w(T_WR, (E, P)),
+                w_unpool=w(T_WU, (H, P)), w_qkv_next=w(T_WQKV, (shape.qkv_out, H)),
+                w1=w(T_W1, (E, 2 * I, P)), w2=w(T_W2, (E, P, I)))
+
+
+def device_kv_context(shape: LayerShape, cfg_id: int, layer: int, device):
+    """A layer's KV cache [cap][Hkv][d] bf16 with rows [0, ctx) drawn N(0, 1), the rest zero."""
+    import torch
+    b = base_seed(cfg_id)
+    cap, ctx, Hkv, d = shape.kv_capacity, shape.ctx, shape.n_kv_heads, shape.head_dim
+    k = torch.zeros((cap, Hkv, d), dtype=torch.bfloat16, device=device)
+    v = torch.zeros((cap, Hkv, d), dtype=torch.bfloat16, device=device)
+    k[:ctx] = device_normal_bf16((ctx, Hkv, d), 1.0, device, b, layer, T_KCTX)
+    v[:ctx] = device_normal_bf16((ctx, Hkv, d), 1.0, device, b, layer, T_VCTX)
+    return k, v
+
+
+def stack_step_inputs(shape: LayerShape, cfg_id: int, step: int) -> dict:
+    """Per-step host inputs of a stack: the tree, layer 0's residual and queries, and layer
+    0's own tree K/V rows (what the step's first launch consumes)."""
+    b = base_seed(cfg_id)
+    H, Hq, Hkv, d, T = shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim, shape.T
+    return dict(parent=tree_parents(T, rng(b, 0, T_TREE, 0, step)),
+                h_in=normal_bf16(rng(b, 0, T_HIN, 0, step), (T, H), 1.0),
+                q_in=normal_bf16(rng(b, 0, T_QIN, 0, step), (T, Hq * d), 1.0),
+                k_tree=normal_bf16(rng(b, 0, T_KTREE, 0, step), (T, Hkv, d), 1.0),
+                v_tree=normal_bf16(rng(b, 0, T_VTREE, 0, step), (T, Hkv, d), 1.0))
+
+
+def stack_router_biases(shape: LayerShape, cfg_id: int, n_layers: int, n_steps: int, reuse: float) -> np.ndarray:
+    """Router biases [steps][layers][T][E] of the routing-locality workload: per layer a
+    Markov chain over steps where each (token, slot) reuses the previous step's experts with
+    probability `reuse` (the bias margin fixes the routing, so the chain is known in advance)."""
+    b = base_seed(cfg_id)
+    out = np.zeros((n_steps, n_layers, shape.T, shape.n_experts), np.float32)
+    for L in range(n_layers):
+        prev = None
+        for s in range(n_steps):
+            bias = markov_router_bias(shape, rng(b, L, T_MARKOV, 0, s), prev, reuse, shape.zipf_s)
+            out[s, L] = bias
+            prev = np.stack([np.flatnonzero(bias[t]) for t in range(shape.T)])
+    return out

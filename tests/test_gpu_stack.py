@@ -1,0 +1,120 @@
+"""GPU tests of the stack mechanics: the last-layer launch mode, and a stack of fused layers
+(global every fourth layer, the last one without a next-layer projection) checked layer by
+layer against the oracle and, run in one go by the stack runner, bit for bit against the
+layer-by-layer chain."""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import layer_persistent_amd as mk
+from layer_persistent_amd import tensors as dt
+from layer_persistent_amd.stack import Stack, is_global
+
+from gpu_util import assert_close_bf16, log
+from test_gpu_parity import SMALL_NVFP4, _check_layer
+
+pytestmark = pytest.mark.gpu
+
+SMALL_STACK = synth.LayerShape("small-stack-nvfp4", 256, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
+N_LAYERS = 6
+CFG_ID = 90
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def test_last_layer_mode_ends_after_the_unpooler():
+    inp = synth.make_layer_inputs(SMALL_NVFP4, 87)
+    dw = dt.upload_weights(inp)
+    st = dt.make_step(inp)
+    dt.run_step(dw, st)
+    full = dt.outputs(st)
+    dw_last = dataclasses.replace(dw, w_qkv=None)
+    st2 = dt.make_step(inp)
+    dt.run_step(dw_last, st2)
+    last = dt.outputs(st2)
+    assert last["status"] == 0
+    for key in ("h_out", "idx", "gate", "logits", "stats", "y", "xp", "h1", "attn"):
+        assert np.array_equal(full[key], last[key]), key
+    assert np.all(last["q_next"] == 0)                       # never written
+    assert np.array_equal(last["k_cache_next"], inp.k_cache_next)
+    assert np.array_equal(last["v_cache_next"], inp.v_cache_next)
+
+
+def _host(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _layer_inputs(L, step_in, prev) -> synth.LayerInputs:
+    """Host inputs of stack layer L, drawn by the same device generators the stack uses; the
+    tree rows, residual and queries come from the step inputs (L = 0) or from layer L-1."""
+    sh = dataclasses.replace(SMALL_STACK, window=0 if is_global(L) else SMALL_STACK.window)
+    w = synth.device_layer_weights(sh, CFG_ID, L, "cuda")
+    kc, vc = synth.device_kv_context(sh, CFG_ID, L, "cuda")
+    k_cache, v_cache = _host(kc), _host(vc)
+    T, ctx = sh.T, sh.ctx
+    if prev is None:
+        h_in, q_in = step_in["h_in"], step_in["q_in"]
+        k_cache[ctx:ctx + T], v_cache[ctx:ctx + T] = step_in["k_tree"], step_in["v_tree"]
+    else:
+        h_in, q_in = prev["h_out"], prev["q_next"]
+        k_cache[ctx:ctx + T] = prev["k_cache_next"].reshape(k_cache.shape)[ctx:ctx + T]
+        v_cache[ctx:ctx + T] = prev["v_cache_next"].reshape(v_cache.shape)[ctx:ctx + T]
+    if L + 1 < N_LAYERS:
+        shn = dataclasses.replace(SMALL_STACK, window=0 if is_global(L + 1) else SMALL_STACK.window)
+        kn, vn = synth.device_kv_context(shn, CFG_ID, L + 1, "cuda")
+        kn, vn = _host(kn), _host(vn)
+    else:
+        kn, vn = np.zeros_like(k_cache), np.zeros_like(v_cache)
+    return synth.LayerInputs(sh, step_in["parent"].astype(np.int32), h_in, q_in, k_cache, v_cache, kn, vn,
+                             _host(w["w_o"]), _host(w["w_pool"]), _host(w["w_router"]), _host(w["w_unpool"]),
+                             _host(w["w_qkv_next"]), _host(w["w1"]), _host(w["w2"]), None)
+
+
+def test_small_stack_layer_by_layer_and_in_one_go():
+    step_in = synth.stack_step_inputs(SMALL_STACK, CFG_ID, 0)
+    chain = []
+    prev = None
+    for L in range(N_LAYERS):
+        log(f"[stack layer {L}] {'global' if is_global(L) else 'swa'}{' (last)' if L + 1 == N_LAYERS else ''}")
+        inp = _layer_inputs(L, step_in, prev)
+        dw = dt.upload_weights(inp)
+        if L + 1 == N_LAYERS:
+            dw = dataclasses.replace(dw, w_qkv=None)
+        st = dt.make_step(inp)
+        dt.run_step(dw, st)
+        out = dt.outputs(st)
+        if L + 1 < N_LAYERS:
+            _check_layer(inp, out)
+        else:
+            assert out["status"] == 0
+            ref = oracle.layer_step_auto(inp)
+            assert_close_bf16("last layer h_out end-to-end", out["h_out"], ref["h_out"])
+        chain.append(out)
+        prev = out
+    # the stack runner, all launches back to back on one stream
+    stk = Stack(SMALL_STACK, CFG_ID, N_LAYERS)
+    stk.set_step_inputs(step_in)
+    stk.launch_step(stk.structs(False, False), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk.ws) == 0
+    assert np.array_equal(_host(stk.h_out()), chain[-1]["h_out"])
+    for L in range(N_LAYERS):
+        assert np.array_equal(stk.layers[L].topk_idx.cpu().numpy(), chain[L]["idx"]), L
+        if L + 1 < N_LAYERS:
+            T, ctx = SMALL_STACK.T, SMALL_STACK.ctx
+            kn = _host(stk.layers[L + 1].k_cache).reshape(SMALL_STACK.kv_capacity, -1)[ctx:ctx + T]
+            vn = _host(stk.layers[L + 1].v_cache).reshape(SMALL_STACK.kv_capacity, -1)[ctx:ctx + T]
+            cap = SMALL_STACK.kv_capacity
+            assert np.array_equal(kn, chain[L]["k_cache_next"].reshape(cap, -1)[ctx:ctx + T]), L
+            assert np.array_equal(vn, chain[L]["v_cache_next"].reshape(cap, -1)[ctx:ctx + T]), L
+    log("  stack in one go: bit-identical to the layer-by-layer chain")
