@@ -148,6 +148,17 @@ def bench_stack(args) -> dict:
         step_us, layer_us = [], []
         for s in range(n_steps):
             stk.set_step_inputs(ins[s], None if biases is None else biases[s])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            stk.launch_step(structs[s % 2], sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if s >= args.warmup:
+                step_us.append(e0.elapsed_time(e1) * 1000.0)
+        # per-layer split: the same steps again with an event after every launch (the records
+        # add ~3 us per launch of their own)
+        for s in range(args.warmup, n_steps):
+            stk.set_step_inputs(ins[s], None if biases is None else biases[s])
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
             st = structs[s % 2]
             ev[0].record(stream)
@@ -158,10 +169,7 @@ def bench_stack(args) -> dict:
                     raise RuntimeError(f"mk_layer_step: {rc}")
                 ev[L + 1].record(stream)
             torch.cuda.synchronize()
-            if s >= args.warmup:
-                lt = [ev[L].elapsed_time(ev[L + 1]) * 1000.0 for L in range(n_layers)]
-                layer_us.append(lt)
-                step_us.append(ev[0].elapsed_time(ev[n_layers]) * 1000.0)
+            layer_us.append([ev[L].elapsed_time(ev[L + 1]) * 1000.0 for L in range(n_layers)])
         st0 = mk_read_status_ok(stk)
         lu = np.array(layer_us)
         glob = [L for L in range(n_layers) if is_global(L)]
@@ -171,7 +179,8 @@ def bench_stack(args) -> dict:
         res[name] = dict(step_us_median=round(float(np.median(step_us)), 1),
                          step_us_p10=round(float(np.percentile(step_us, 10)), 1),
                          step_us_p90=round(float(np.percentile(step_us, 90)), 1),
-                         layer_us_mean=round(float(lu.mean()), 2),
+                         layer_us_mean=round(float(np.median(step_us)) / n_layers, 2),
+                         layer_us_evented_mean=round(float(lu.mean()), 2),
                          swa_layer_us_mean=round(float(lu[:, swa].mean()), 2),
                          global_layer_us_mean=round(float(lu[:, glob].mean()), 2) if glob else None,
                          last_layer_us_mean=round(float(lu[:, -1].mean()), 2), status=st0)
@@ -271,26 +280,32 @@ def main():
     n_active = int(len(np.unique(out["idx"])))
     ab = algorithmic_bytes(shape, n_active)
 
-    # timed region: K launches, an event pair around each on the launch stream
+    # timed region: K launches back to back on the launch stream, one event pair around all
+    # of them; value = elapsed / K (the inter-launch gap counts, per-launch event records do not)
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     wall0 = torch.cuda.Event(enable_timing=True)
     wall1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0.record(stream)
     for i in range(K):
-        ev[i][0].record(stream)
         launch(args.warmup + i)
-        ev[i][1].record(stream)
     wall1.record(stream)
     torch.cuda.synchronize()
-    per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])     # us per launch
     wall_us = wall0.elapsed_time(wall1) * 1000.0
     ms_per_step = wall_us / K / 1000.0
-    kern_us = float(np.mean(per))
+    kern_us = wall_us / K
+    # spread: a second, untimed pass with an event pair around every launch (those records
+    # add ~3 us per launch of their own)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for i in range(K):
+        ev[i][0].record(stream)
+        launch(args.warmup + K + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) * 1000.0 for a, b in ev])     # us per launch
     med_us = float(np.median(per))
-    log(f"per-launch us: mean {kern_us:.2f} median {med_us:.2f} p10 {np.percentile(per, 10):.2f} "
-        f"p90 {np.percentile(per, 90):.2f}; wall per step {ms_per_step * 1000:.2f} us")
+    log(f"per launch: {kern_us:.2f} us over {K} back-to-back launches; with an event pair around each launch: "
+        f"median {med_us:.2f} p10 {np.percentile(per, 10):.2f} p90 {np.percentile(per, 90):.2f}")
     achieved = ab["total"] / (kern_us * 1e-6) / 1e9
     log(f"algorithmic bytes {ab['total'] / 1e6:.2f} MB ({n_active} active experts) -> {achieved:.0f} GB/s "
         f"= {achieved / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f} GB/s")
@@ -347,6 +362,9 @@ def main():
         for p, n in enumerate(names, start=1):
             dur = (tsv[:, 2 * p] - tsv[:, 2 * p - 1 if p > 1 else 1]) / 100.0
             phases[n + "_wg_p50_max"] = [round(float(np.median(dur)), 2), round(float(dur.max()), 2)]
+        for p, n in enumerate(names, start=1):
+            if (tsv[:, 53 + p] > 0).any():
+                phases[n + "_stores_done"] = round(rel(53 + p), 2)
         starts = (tsv[:, 0] - t0) / 100.0
         phases["wg_start_spread"] = round(float(starts.max()), 2)
         items = tsv[:, 37] > 0
@@ -411,9 +429,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(shape.name),
                      "bytes_per_launch": ab["total"], "achievable_read_gbs": round(read_gbs, 1)},
-        "median_us": round(med_us, 2),
-        "p10_us": round(float(np.percentile(per, 10)), 2),
-        "p90_us": round(float(np.percentile(per, 90)), 2),
+        "evented_launch_us": {"median": round(med_us, 2), "p10": round(float(np.percentile(per, 10)), 2),
+                              "p90": round(float(np.percentile(per, 90)), 2),
+                              "note": "an event pair around every launch adds ~3 us per launch"},
         "phases_end_us": phases,
         "cpu_baseline": cpu,
     }

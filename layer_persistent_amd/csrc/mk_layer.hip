@@ -65,6 +65,9 @@ constexpr int LDS_BYTES = 148 * 1024;                  // >= every phase's use (
 // dense-phase reduction buffers and the merge scratch
 constexpr int POOL_LDS_OFF = 20 * 1024;
 static_assert(POOL_LDS_OFF + 16 * 4096 * 2 <= LDS_BYTES, "pooler tile in LDS");
+// An unpooler tile (16 x P <= 2048 bf16 = 64 KB), filled during GEMM2 above GEMM2's own LDS use
+constexpr int WU_LDS_OFF = 64 * 1024;
+static_assert(WU_LDS_OFF + 16 * 2048 * 2 <= LDS_BYTES, "unpooler tile in LDS");
 static_assert(G1_XS_BYTES + 16 * 16 * 128 + 2 * 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
 
 __device__ __forceinline__ void wg_sync() {
@@ -348,6 +351,18 @@ __device__ __forceinline__ void lds_tile_fill(const uint16_t* __restrict__ W, in
       if (c < nch) *(u32x4*)(dst + (size_t)c * 16) = v[j];
     }
   }
+}
+
+// The same tile layout filled by one wave through the LDS-DMA path (global_load_lds, 16 bytes
+// per lane, lane l landing at base + 16 l): instruction s moves the 1 KB of k-step s.  No
+// registers hold the data.  The LDS is written asynchronously: the wave must wait for its loads
+// (s_waitcnt) before a workgroup barrier that precedes any read of the tile.
+__device__ __forceinline__ void lds_tile_dma(const uint16_t* __restrict__ W, int K, int n0, char* dst) {
+  const int lane = threadIdx.x & 63;
+  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + 8 * (lane >> 4);
+  for (int sk = 0; sk < K / 32; ++sk)
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(row + 32 * sk),
+                                     (__attribute__((address_space(3))) void*)(dst + sk * 1024), 16, 0, 0);
 }
 
 // This wave's partial of a tile whose weights sit in LDS (lds_tile_fill layout); x rows are
@@ -1499,6 +1514,11 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
   wg_sync();
   stamp<TS>(a.timestamps, 2 * phase);
   if (threadIdx.x >= kCompute) {
+    if constexpr (TS) {
+      // the control wave's hand-off stores complete (just before the flag is raised)
+      __builtin_amdgcn_s_waitcnt(0);
+      stamp<TS>(a.timestamps, 53 + phase);
+    }
     const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0);
     if (!ok && threadIdx.x == kCtl) *dead_sh = 1;
     stamp<TS>(a.timestamps, 20 + phase);
@@ -1717,21 +1737,27 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       if (alive && a.fmt == 1 && a.I % 64 == 0 && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
     }) && alive;
     // ---- 7 GEMM2 + combine
+    // NVFP4 experts: GEMM2 leaves LDS above 64 KB free, so the control wave streams the
+    // unpooler tile there while the experts run (waited for at this phase's hand-off)
+    const int g2_lds_end = ((a.T * a.topk * (a.I + 8) * 2 + 255) & ~255) + 128 * 8 * 4 + 72 * 16 * 4;
+    const bool wu_lds = a.fmt == 1 && a.I % 64 == 0 && p_u && g2_lds_end <= WU_LDS_OFF &&
+                        WU_LDS_OFF + 32 * a.P <= LDS_BYTES;
     if (alive) {
+      if (!cw && wu_lds) lds_tile_dma(a.w_unpool, a.P, t_u * 16, smem + WU_LDS_OFF);
       if (a.fmt == 1 && a.I % 64 == 0) gemm2_fp4<TS>(a, rt, smem, ytile, g2w);
       else gemm2_staged<TS>(a, rt, smem, ytile);
     }
-    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
+    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u && !wu_lds) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
-      dense_phase(a, wu, p_u, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
+      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + (size_t)crow * a.H + n0 + cc0);
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
         st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
-      }, nullptr, [&] {
+      }, wu_lds ? smem + WU_LDS_OFF : nullptr, [&] {
         // the qkv tile's weights load while the unpooler finishes and the grid hands off
         if (p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
       });
