@@ -58,31 +58,53 @@ int check_cfg(const mk_layer_cfg* c, int T) {
 
 struct Layout {
   size_t status, epoch, flags, part_o, part_ml, attn, h1, xp, logits, act, y, total;
-  int n_wg, items, chunks_per_head, attn_lo, ck;
+  int n_wg, items, chunks_per_head, attn_lo, ck, rw, nrb, part_slots;
 };
 
-// attention work split: context rows [attn_lo, ctx) in chunks of ck keys (64 up to 8192
-// visible rows, so that more workgroups share a short context; 128 beyond), plus one chunk
-// holding the tree's own slots, for each kv head
-void attn_split(const mk_layer_cfg* c, int ctx, int* lo, int* chunks, int* ck) {
+constexpr int kChunkMax = 256;     // keys per attention chunk held in LDS
+
+// Attention work split.  The visible context rows [attn_lo, ctx) of each kv head are cut into
+// chunks of ck keys, plus one chunk holding the tree's own slots; each chunk's (token, q head)
+// rows are cut into row blocks of rw tiles of 16 rows.  An item is one (kv head, chunk, row
+// block); its 8 waves split it as rw row tiles x 8/rw key groups.  Among rw = 1, 2, 4, 8 the
+// split taken is the one that moves the fewest bytes through one workgroup: the K/V it stages
+// and the partials it stores per round of items, plus what one merge unit reads back.
+void attn_split(const mk_layer_cfg* c, int T, int ctx, int n_wg, Layout* L) {
   const int l = c->window > 0 ? (ctx - c->window + 1 > 0 ? ctx - c->window + 1 : 0) : 0;
-  const int keys = ctx - l;
-  *lo = l;
-  *ck = keys <= 8192 ? 64 : 128;
-  *chunks = (keys + *ck - 1) / *ck + 1;
+  const int keys = ctx - l, d = c->head_dim, Hkv = c->n_kv_heads;
+  const int RT = (T * (c->n_q_heads / Hkv) + 15) / 16;    // row tiles, <= 8
+  double best = -1.0;
+  for (int rw = 1; rw <= 8; rw *= 2) {
+    if (rw > 1 && rw / 2 >= RT) break;                     // whole row tiles of nothing
+    const int nrb = (RT + rw - 1) / rw, nkw = 8 / rw, gran = 16 * nkw;
+    const int slots = n_wg / (Hkv * nrb) - 1;              // context chunks per round
+    int ck = slots > 0 ? (keys + slots - 1) / slots : kChunkMax;
+    ck = (ck + gran - 1) / gran * gran;
+    if (ck < gran) ck = gran;
+    if (ck > kChunkMax) ck = kChunkMax;                    // gran divides kChunkMax
+    const int chunks = (keys + ck - 1) / ck + 1;
+    const long items = (long)Hkv * nrb * chunks;
+    const long rounds = (items + n_wg - 1) / n_wg;
+    const double cost = (double)rounds * ((double)ck * 4 * d + (double)rw * 16 * d * 4) + (double)chunks * (d * 4 + 8);
+    if (best < 0 || cost < best) {
+      best = cost;
+      L->attn_lo = l; L->chunks_per_head = chunks; L->ck = ck; L->rw = rw; L->nrb = nrb;
+      L->items = (int)items;
+    }
+  }
 }
 
 Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   Layout L;
   memset(&L, 0, sizeof(L));
   L.n_wg = n_wg;
-  attn_split(c, ctx, &L.attn_lo, &L.chunks_per_head, &L.ck);
-  L.items = c->n_kv_heads * L.chunks_per_head;
-  // the partial buffers must hold the largest split of any context up to `ctx`
-  if (ctx > 8192) {
-    int lo2, ch2, ck2;
-    attn_split(c, 8192, &lo2, &ch2, &ck2);
-    if (c->n_kv_heads * ch2 > L.items) L.items = c->n_kv_heads * ch2;
+  attn_split(c, T, ctx, n_wg, &L);
+  // partial slots [kv head][chunk]: a split within one round has at most n_wg of them;
+  // beyond, chunks are kChunkMax keys and their count grows with the context
+  {
+    const int keys_max = ctx - (c->window > 0 && ctx - c->window + 1 > 0 ? ctx - c->window + 1 : 0);
+    const int big = c->n_kv_heads * ((keys_max + kChunkMax - 1) / kChunkMax + 1);
+    L.part_slots = big > n_wg ? big : n_wg;
   }
   const int H = c->hidden, Hq = c->n_q_heads, d = c->head_dim, P = c->pooled, E = c->n_experts,
             k = c->top_k, I = c->expert_inter;
@@ -90,8 +112,8 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   L.status = o; o = up256(o + 4);
   L.epoch = o; o = up256(o + (size_t)n_wg * 64);
   L.flags = o; o = up256(o + (size_t)n_wg * 64);
-  L.part_o = o; o = up256(o + (size_t)L.items * 128 * d * 4);
-  L.part_ml = o; o = up256(o + (size_t)L.items * 128 * 2 * 4);
+  L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
+  L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
   L.attn = o; o = up256(o + (size_t)T * Hq * d * 2);
   L.h1 = o; o = up256(o + (size_t)T * H * 2);
   L.xp = o; o = up256(o + (size_t)T * P * 2);
@@ -192,6 +214,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   Layout L = layout(c, T, c->kv_capacity - T, n_wg);
   Layout Lc = layout(c, T, ctx, n_wg);
   if (io->workspace_bytes < L.total) return MK_ECAPACITY;
+  if (c->n_kv_heads * Lc.chunks_per_head > L.part_slots) return MK_ECAPACITY;
 
   mk::KArgs a;
   memset(&a, 0, sizeof(a));
@@ -199,7 +222,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
   a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
   a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
-  a.attn_lo = Lc.attn_lo; a.ck = Lc.ck;
+  a.attn_lo = Lc.attn_lo; a.ck = Lc.ck; a.attn_rw = Lc.rw; a.attn_nrb = Lc.nrb;
   a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
   a.skip_wg = io->debug_skip_signal_wg;
   a.parent = io->tree_parent;

@@ -29,6 +29,14 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x16_bf16: lane l supplies A[l%16][4*(l/16) + j] and B[4*(l/16) + j][l%16]
+// (j = 0..3); C as in the 32-deep form.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_bf16_k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a), __builtin_bit_cast(s16x4_t, b),
+                                                   c, 0, 0, 0);
+}
+
 // v_mfma_f32_16x16x32_f16: the same lane layout as the bf16 form, fp16 operands.
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));

@@ -16,6 +16,7 @@ struct KArgs {
   int H, Hq, Hkv, d, P, E, topk, I, window, fmt, cap, T, ctx;
   // launch geometry
   int n_wg, attn_items, attn_chunks_per_head, attn_lo, ck;
+  int attn_rw, attn_nrb;     // row tiles per attention item, row blocks per chunk
   int spin_limit, skip_wg;
   // step inputs / outputs
   const int32_t* parent;

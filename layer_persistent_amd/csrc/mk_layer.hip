@@ -80,10 +80,13 @@ __device__ __forceinline__ void wg_sync() {
 // Events: 0 start, 1 setup done, 2p work of phase p done, 2p+1 its hand-off done (p = 1..8),
 // 18 routing tables built, 19 end, 20+p control wave's wait for phase p done, 28+p compute
 // waves' loads for a later phase issued, 37 / 38 first attention item staged / computed.
+// Events are recorded in LDS and written out once at the end of the launch, so that the
+// timing build issues no global stores (and waits for none) while the phases run.
+__shared__ uint64_t ts_lds[MK_TS_EVENTS_DEV];
 template <bool TS>
 __device__ __forceinline__ void stamp(uint64_t* ts, int ev, int who = kCtl) {
   if constexpr (TS) {
-    if ((int)threadIdx.x == who) ts[blockIdx.x * MK_TS_EVENTS_DEV + ev] = wall_clock64();
+    if ((int)threadIdx.x == who) ts_lds[ev] = wall_clock64();
   }
 }
 
@@ -357,10 +360,12 @@ __device__ __forceinline__ void lds_tile_fill(const uint16_t* __restrict__ W, in
 // per lane, lane l landing at base + 16 l): instruction s moves the 1 KB of k-step s.  No
 // registers hold the data.  The LDS is written asynchronously: the wave must wait for its loads
 // (s_waitcnt) before a workgroup barrier that precedes any read of the tile.
-__device__ __forceinline__ void lds_tile_dma(const uint16_t* __restrict__ W, int K, int n0, char* dst) {
+// Waves may share a tile: this wave moves k-steps first, first + stride, ...
+__device__ __forceinline__ void lds_tile_dma(const uint16_t* __restrict__ W, int K, int n0, char* dst,
+                                             int first = 0, int stride = 1) {
   const int lane = threadIdx.x & 63;
   const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + 8 * (lane >> 4);
-  for (int sk = 0; sk < K / 32; ++sk)
+  for (int sk = first; sk < K / 32; sk += stride)
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(row + 32 * sk),
                                      (__attribute__((address_space(3))) void*)(dst + sk * 1024), 16, 0, 0);
 }
@@ -446,202 +451,283 @@ __device__ __forceinline__ void stage_pieces(int n, SrcF piece, DstF dst) {
 
 // ------------------------------------------------------------------ attention
 
-// One work item: kv head `g`, keys [kb, kb + nk) (context rows) or the tree slots.
-// Rows are (token, q head of this kv head) pairs, row = t * G + (h - g*G), R = T*G <= 128;
-// wave w owns rows [16w, 16w + 16).  S^T = K Q^T puts keys on the MFMA M axis so that the
-// probabilities land in exactly the B-operand layout the P.V product needs.
+// A work item is one (kv head g, key chunk, row block).  Chunk keys are context rows
+// [kb, kb + nk) or, for the last chunk of a head, the tree's own slots.  Rows are the
+// (token, q head of g) pairs, row = t * G + (h - g*G), R = T*G <= 128, in tiles of 16; a row
+// block holds rw tiles.  The 8 compute waves split an item as rw row tiles x 8/rw key groups:
+// wave w takes row tile rb*rw + w % rw and the w / rw-th of the chunk's keys.  S^T = K Q^T
+// puts keys on the MFMA M axis so that the probabilities land in exactly the B-operand layout
+// the P.V product needs.
+struct AttnItem {
+  int g, chunk, rb, kb, nk;
+  bool tree;
+};
+__device__ __forceinline__ AttnItem attn_item(const KArgs& a, int item) {
+  AttnItem t;
+  const int per_g = a.attn_chunks_per_head * a.attn_nrb;
+  t.g = item / per_g;
+  const int r = item % per_g;
+  t.chunk = r / a.attn_nrb;
+  t.rb = r % a.attn_nrb;
+  t.tree = t.chunk == a.attn_chunks_per_head - 1;
+  t.kb = t.tree ? a.ctx : a.attn_lo + t.chunk * a.ck;
+  t.nk = t.tree ? a.T : min(a.ck, a.ctx - t.kb);
+  return t;
+}
 
-// This lane's query fragments (B operand of S^T): row = 16 wave + l%16, d = 32 s + 8 (l/16).
-__device__ __forceinline__ void attention_q(const KArgs& a, int item, u32x4 qf[4]) {
+// This lane's query fragments (B operand of S^T): row = 16 tile + l%16, d = 32 s + 8 (l/16).
+__device__ __forceinline__ void attention_q(const KArgs& a, const AttnItem& it, u32x4 qf[4]) {
   const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
-  const int g_kv = item / a.attn_chunks_per_head;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = wave * 16 + (lane & 15), grp = lane >> 4;
+  const int row = (it.rb * a.attn_rw + wave % a.attn_rw) * 16 + (lane & 15), grp = lane >> 4;
   const bool rv = threadIdx.x < kCompute && row < R;
-  const int tok = rv ? row / G : 0, head = g_kv * G + (rv ? row % G : 0);
+  const int tok = rv ? row / G : 0, head = it.g * G + (rv ? row % G : 0);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     qf[s] = (s < d / 32 && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
                                : u32x4{0, 0, 0, 0};
 }
 
-// LDS of an item: K row-major [128][d + 8] bf16, then V transposed as key pairs:
-// VT32[dd][kp] = V[2kp][dd] | V[2kp+1][dd] << 16, row stride 66 dwords (conflict-free reads).
-constexpr int kVtStride32 = 66;
+__device__ __forceinline__ int vt_stride(int ck) { return ck / 2 + 2; }
 
-// Stage the item's K and V into LDS (keys beyond nk zeroed).  Every load of a thread is
-// issued before its LDS stores.  Called by all threads (ends in a workgroup barrier).
-__device__ __forceinline__ void attention_stage(const KArgs& a, int item, char* smem) {
-  const int d = a.d;
-  const int g_kv = item / a.attn_chunks_per_head;
-  const int chunk = item % a.attn_chunks_per_head;
-  const bool tree_chunk = chunk == a.attn_chunks_per_head - 1;
-  const int kb = tree_chunk ? a.ctx : a.attn_lo + chunk * a.ck;
-  const int nk = tree_chunk ? a.T : min(a.ck, a.ctx - kb);
-  const int CK = 128;                           // LDS chunk capacity
-  const int ks_stride = d + 8;
-  uint16_t* Ks = (uint16_t*)smem;
-  uint32_t* VT = (uint32_t*)(Ks + CK * ks_stride);
-  const int tid = threadIdx.x;
-  const int per_row = d / 8;                    // 16-byte pieces per key row
-  if (tid < kCompute) {
-    constexpr int kKPer = (128 * 16) / kCompute;     // K pieces per thread at d = 128
-    constexpr int kVPer = (64 * 16) / kCompute;      // V pair-pieces per thread at d = 128
-    u32x4 kv[kKPer], v0[kVPer], v1[kVPer];
-    const size_t rstride = (size_t)a.Hkv * d;
-    const uint16_t* kbase = a.kc + ((size_t)kb * a.Hkv + g_kv) * d;
-    const uint16_t* vbase = a.vc + ((size_t)kb * a.Hkv + g_kv) * d;
+// Staging of an item's K and V into LDS (keys nk..ck-1 zeroed), in batches of 4 K pieces and
+// 2 V key-pair pieces per compute thread (at d = 128 a batch covers 128 keys): a batch's loads
+// are all issued (stage_load) before its LDS stores (stage_store), so the first batch of a
+// workgroup's first item can be in flight during the launch's setup.
+struct StageRegs {
+  u32x4 kv[4], v0[2], v1[2];
+};
+__device__ __forceinline__ int stage_batches(const KArgs& a) { return (a.ck * (a.d / 8) + 4 * kCompute - 1) / (4 * kCompute); }
+
+__device__ __forceinline__ void stage_load(const KArgs& a, const AttnItem& it, int b, StageRegs& r) {
+  // recomputed per item: indexing hoisted out of the item loop would hold registers
+  // through the whole phase
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  if (tid >= kCompute) return;
+  const int d = a.d, per_row = d / 8, nkp = a.ck / 2;
+  const int kpieces = a.ck * per_row, vpieces = nkp * per_row;
+  const size_t rstride = (size_t)a.Hkv * d;
+  const uint16_t* kbase = a.kc + ((size_t)it.kb * a.Hkv + it.g) * d;
+  const uint16_t* vbase = a.vc + ((size_t)it.kb * a.Hkv + it.g) * d;
 #pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int i = tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
-      kv[j] = (i < CK * per_row && key < nk) ? ld16(kbase + key * rstride + c) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = tid + j * kCompute, kp = i & 63, c = (i >> 6) * 8;
-      const bool ok = i < 8 * d;
-      v0[j] = (ok && 2 * kp < nk) ? ld16(vbase + (2 * kp) * rstride + c) : u32x4{0, 0, 0, 0};
-      v1[j] = (ok && 2 * kp + 1 < nk) ? ld16(vbase + (2 * kp + 1) * rstride + c) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < kKPer; ++j) {
-      const int i = tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
-      if (i < CK * per_row) *(u32x4*)(Ks + key * ks_stride + c) = kv[j];
-    }
-#pragma unroll
-    for (int j = 0; j < kVPer; ++j) {
-      const int i = tid + j * kCompute, kp = i & 63, c = (i >> 6) * 8;
-      if (i < 8 * d) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          VT[(c + 2 * q) * kVtStride32 + kp] = (v0[j][q] & 0xFFFFu) | (v1[j][q] << 16);
-          VT[(c + 2 * q + 1) * kVtStride32 + kp] = (v0[j][q] >> 16) | (v1[j][q] & 0xFFFF0000u);
-        }
-      }
-    }
+  for (int j = 0; j < 4; ++j) {
+    const int i = b * 4 * kCompute + tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
+    r.kv[j] = (i < kpieces && key < it.nk) ? ld16(kbase + key * rstride + c) : u32x4{0, 0, 0, 0};
   }
-  wg_sync();
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = b * 2 * kCompute + tid + j * kCompute, kp = i % nkp, c = (i / nkp) * 8;
+    const bool ok = i < vpieces;
+    r.v0[j] = (ok && 2 * kp < it.nk) ? ld16(vbase + (2 * kp) * rstride + c) : u32x4{0, 0, 0, 0};
+    r.v1[j] = (ok && 2 * kp + 1 < it.nk) ? ld16(vbase + (2 * kp + 1) * rstride + c) : u32x4{0, 0, 0, 0};
+  }
 }
 
-// the compute half of an attention item (after the staging barrier); no barriers inside,
-// threads of the control wave return at once
-template <bool TS>
-__device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, int item, char* smem,
-                                                  const u32x4 qf[4]) {
-  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
-  const int g_kv = item / a.attn_chunks_per_head;
-  const int chunk = item % a.attn_chunks_per_head;
-  const bool tree_chunk = chunk == a.attn_chunks_per_head - 1;
-  const int kb = tree_chunk ? a.ctx : a.attn_lo + chunk * a.ck;
-  const int nk = tree_chunk ? a.T : min(a.ck, a.ctx - kb);
-  const int CK = 128;
-  const int ks_stride = d + 8;
-  const uint16_t* Ks = (const uint16_t*)smem;
-  const uint32_t* VT = (const uint32_t*)(Ks + CK * ks_stride);
+// LDS of an item (ck <= 256 keys): K row-major [ck][d + 8] bf16, then V transposed as key
+// pairs: VT32[dd][kp] = V[2kp][dd] | V[2kp+1][dd] << 16, row stride ck/2 + 2 dwords.
+__device__ __forceinline__ void stage_store(const KArgs& a, int b, const StageRegs& r, char* smem) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  if (tid >= kCompute) return;
+  const int d = a.d, ck = a.ck, per_row = d / 8, nkp = ck / 2;
+  const int ks_stride = d + 8, vs = vt_stride(ck);
+  const int kpieces = ck * per_row, vpieces = nkp * per_row;
+  uint16_t* Ks = (uint16_t*)smem;
+  uint32_t* VT = (uint32_t*)(Ks + ck * ks_stride);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = b * 4 * kCompute + tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
+    if (i < kpieces) *(u32x4*)(Ks + key * ks_stride + c) = r.kv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = b * 2 * kCompute + tid + j * kCompute, kp = i % nkp, c = (i / nkp) * 8;
+    if (i < vpieces) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        VT[(c + 2 * q) * vs + kp] = (r.v0[j][q] & 0xFFFFu) | (r.v1[j][q] << 16);
+        VT[(c + 2 * q + 1) * vs + kp] = (r.v0[j][q] >> 16) | (r.v1[j][q] & 0xFFFF0000u);
+      }
+    }
+  }
+}
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// The compute half of an attention item, after the staging barrier.  Each wave runs an online
+// softmax over its key group, 32 keys (two key tiles) a step: scores, a new running row max m,
+// the running sum l and O^T rescaled by exp(m_old - m_new), then O^T += V^T P^T.  With one key
+// group per row tile the wave stores its partial (O unnormalised, m, l); otherwise the key
+// groups' partials of a row are combined in LDS, flash-decoding style, and stored once.
+// Called by all threads (contains workgroup barriers when the item is split over keys).
+__device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, const AttnItem& it, char* smem,
+                                                  const u32x4 qf[4]) {
+  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G, ck = a.ck;
+  const int rw = a.attn_rw, nkw = 8 / rw;
+  const int ks_stride = d + 8, vs = vt_stride(ck);
+  const uint16_t* Ks = (const uint16_t*)smem;
+  const uint32_t* VT = (const uint32_t*)(Ks + ck * ks_stride);
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));                 // (no per-thread indexing hoisted out of the item loop)
+  const int lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, grp = lane >> 4;
-  const int row = wave * 16 + nl;               // this lane's query row (MFMA column)
-  if (threadIdx.x >= kCompute || wave * 16 >= R) return;
-  const bool rv = row < R;
+  const int rt = it.rb * rw + wave % rw, kg = wave / rw;
+  const int row = rt * 16 + nl;                 // this lane's query row (MFMA column)
+  const bool active = threadIdx.x < kCompute && rt * 16 < R;
+  const bool rv = active && row < R;
   const int tok = rv ? row / G : 0;
-  const int dsteps = d / 32;
-  if constexpr (TS) {   // q fragments arrived
-    if (threadIdx.x == 0 && item == (int)blockIdx.x) {
-      uint32_t x = qf[0][0] | qf[1][1];
-      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 39] = wall_clock64() + (x == 0x12345u ? 1 : 0);
-    }
-  }
+  const int dsteps = d / 32, dtiles = d / 16;
   const float scale = 1.0f / sqrtf((float)d);
-  const int ktiles = (nk + 15) / 16;
-  // visibility of chunk key kl for this lane's row: kl in [vis_lo, vis_hi) for context
-  // chunks (sliding-window lower bound), the ancestor mask for the tree chunk
-  const int vis_hi = rv ? nk : 0;
-  const int vis_lo = rv ? max(0, tr.lo[tok] - kb) : 0;
+  // this wave's keys within the chunk: [k0, k1)
+  const int kpg = ck / nkw;
+  const int k0 = kg * kpg, k1 = min(k0 + kpg, it.nk);
+  // visibility of chunk key kl for this lane's row: kl in [vis_lo, nk) for context chunks
+  // (sliding-window lower bound), the ancestor mask for the tree chunk
+  const int vis_lo = rv ? max(0, tr.lo[tok] - it.kb) : 0;
+  const int vis_hi = rv ? it.nk : 0;
   const uint32_t anc_m = rv ? tr.anc[tok] : 0u;
-  f32x4 sc[8];
-  float mrow = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    sc[kt] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (kt < ktiles) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        if (s < dsteps) {
-          u32x4 kf = *(const u32x4*)(Ks + (kt * 16 + nl) * ks_stride + s * 32 + grp * 8);
-          acc = mfma_bf16(kf, qf[s], acc);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kl = kt * 16 + 4 * grp + r;   // key index within the chunk
-        const bool vis = kl < vis_hi && (tree_chunk ? ((anc_m >> kl) & 1u) != 0 : kl >= vis_lo);
-        sc[kt][r] = vis ? acc[r] * scale : -INFINITY;
-        mrow = fmaxf(mrow, sc[kt][r]);
-      }
-    }
-  }
-  mrow = xgroup_max(mrow);
-  // exp(-inf - m) = 0 for masked keys; a row with no visible key here uses m = 0 (all p = 0)
-  const float msafe = mrow == -INFINITY ? 0.f : mrow;
-  float lsum = 0.f;
-  uint32_t pb[8][2];
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      p[r] = __expf(sc[kt][r] - msafe);
-      lsum += p[r];
-    }
-    pb[kt][0] = pack_bf2(p[0], p[1]);
-    pb[kt][1] = pack_bf2(p[2], p[3]);
-  }
-  lsum = xgroup_sum(lsum);
-  if constexpr (TS) {
-    if (threadIdx.x == 0 && item == (int)blockIdx.x)
-      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 40] = wall_clock64() + (lsum == -1.f ? 1 : 0);
-  }
-  // O^T[dd][row] = sum_keys V^T[dd][key] P^T[key][row]; a 32-key step pairs key tiles
-  // (2q, 2q+1): lane group grp supplies keys 4grp..4grp+3 of both tiles.
+  float m = -INFINITY, lpart = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int dtiles = d / 16;
+  if (active) {
+    for (int kt = k0 / 16; kt * 16 < k1; kt += 2) {
+      const bool two = kt * 16 + 16 < k1;
+      u32x4 kf[2][4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (2 * q < ktiles) {
-      u32x4 bfrag = {pb[2 * q][0], pb[2 * q][1], pb[2 * q + 1][0], pb[2 * q + 1][1]};
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          if (s < dsteps && (h == 0 || two))
+            kf[h][s] = *(const u32x4*)(Ks + ((kt + h) * 16 + nl) * ks_stride + s * 32 + grp * 8);
+      f32x4 sc[2];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (h == 0 || two) {
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            if (s < dsteps) acc = mfma_bf16(kf[h][s], qf[s], acc);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kl = (kt + h) * 16 + 4 * grp + r;   // key index within the chunk
+          const bool vis = (h == 0 || two) && kl < vis_hi &&
+                           (it.tree ? ((anc_m >> kl) & 1u) != 0 : kl >= vis_lo);
+          sc[h][r] = vis ? acc[r] * scale : -INFINITY;
+          mx = fmaxf(mx, sc[h][r]);
+        }
+      }
+      const float mnew = fmaxf(m, xgroup_max(mx));
+      // exp(-inf - x) = 0 for masked keys; with nothing visible yet the row uses 0 as its max
+      const float msafe = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = __expf(m - msafe);
+      uint32_t pb[2][2];
+      float ps = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          p[r] = __expf(sc[h][r] - msafe);
+          ps += p[r];
+        }
+        pb[h][0] = pack_bf2(p[0], p[1]);
+        pb[h][1] = pack_bf2(p[2], p[3]);
+      }
+      lpart = lpart * alpha + ps;
+      m = mnew;
+      // O^T[dd][row] += sum_keys V^T[dd][key] P^T[key][row]; a 32-key step pairs the two key
+      // tiles (lane group grp supplies keys 4grp..4grp+3 of both), a lone tile takes the
+      // 16-key form
+      const uint32_t* vt0 = VT + nl * vs + kt * 8 + 2 * grp;
+      if (two) {
+        const u32x4 pf = {pb[0][0], pb[0][1], pb[1][0], pb[1][1]};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {                 // d tiles in two groups of 4
+          u32x4 vf[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * h + j < dtiles) {
+              const uint32_t* v = vt0 + (4 * h + j) * 16 * vs;
+              const u32x2 v0 = *(const u32x2*)v, v1 = *(const u32x2*)(v + 8);
+              vf[j] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+            }
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (4 * h + j < dtiles) o[4 * h + j] = mfma_bf16(vf[j], pf, o[4 * h + j] * alpha);
+        }
+      } else {
+        u32x2 vf[8];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          if (dt < dtiles) vf[dt] = *(const u32x2*)(vt0 + dt * 16 * vs);
+        const u32x2 pf = {pb[0][0], pb[0][1]};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+          if (dt < dtiles) o[dt] = mfma_bf16_k16(vf[dt], pf, o[dt] * alpha);
+      }
+    }
+  }
+  const float lsum = xgroup_sum(lpart);
+  const int slot = it.g * a.attn_chunks_per_head + it.chunk;
+  if (nkw == 1) {
+    if (rv) {
+      float* po = a.part_o + ((size_t)slot * 128 + row) * d;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         if (dt < dtiles) {
-          const uint32_t* vrow = VT + (dt * 16 + nl) * kVtStride32;
-          const u32x2 v0 = *(const u32x2*)(vrow + ((2 * q) * 16 + 4 * grp) / 2);
-          const u32x2 v1 = *(const u32x2*)(vrow + ((2 * q + 1) * 16 + 4 * grp) / 2);
-          u32x4 afrag = {v0[0], v0[1], v1[0], v1[1]};
-          o[dt] = mfma_bf16(afrag, bfrag, o[dt]);
+          u32x4 v = {__float_as_uint(o[dt][0]), __float_as_uint(o[dt][1]), __float_as_uint(o[dt][2]),
+                     __float_as_uint(o[dt][3])};
+          st_coh_u128(po + dt * 16 + 4 * grp, v);
         }
       }
+      if (grp == 0)
+        st_coh_u64(a.part_ml + ((size_t)slot * 128 + row) * 2,
+                   (uint64_t)__float_as_uint(m) | ((uint64_t)__float_as_uint(lsum) << 32));
     }
+    return;
   }
-  if constexpr (TS) {
-    if (threadIdx.x == 0 && item == (int)blockIdx.x)
-      a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + 41] = wall_clock64() + (o[0][0] == -1.f ? 1 : 0);
-  }
-  if (rv) {
-    float* po = a.part_o + ((size_t)item * 128 + row) * d;
+  // key groups combined in LDS over the staged chunk: [wave][16 rows][d + 4] fp32, then
+  // [wave][16 rows] (m, l)
+  const int cs = d + 4;
+  float* cb = (float*)smem;
+  float* cml = cb + 8 * 16 * cs;
+  wg_sync();                                    // every wave is done with K and V
+  if (active) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      if (dt < dtiles) {
-        u32x4 v = {__float_as_uint(o[dt][0]), __float_as_uint(o[dt][1]), __float_as_uint(o[dt][2]),
-                   __float_as_uint(o[dt][3])};
-        st_coh_u128(po + dt * 16 + 4 * grp, v);
-      }
-    }
+    for (int dt = 0; dt < 8; ++dt)
+      if (dt < dtiles) *(f32x4*)(cb + (wave * 16 + nl) * cs + dt * 16 + 4 * grp) = o[dt];
     if (grp == 0) {
-      st_coh_u64(a.part_ml + ((size_t)item * 128 + row) * 2,
-                 (uint64_t)__float_as_uint(mrow) | ((uint64_t)__float_as_uint(lsum) << 32));
+      cml[(wave * 16 + nl) * 2 + 0] = m;
+      cml[(wave * 16 + nl) * 2 + 1] = lsum;
+    }
+  }
+  wg_sync();
+  if (threadIdx.x < kCompute) {
+    const int quads = d / 4;
+    for (int e = threadIdx.x; e < rw * 16 * quads; e += kCompute) {
+      const int lr = e / quads, dq = e % quads;
+      const int j = lr / 16, r16 = lr % 16;
+      const int grow = (it.rb * rw + j) * 16 + r16;
+      if (grow >= R) continue;
+      float M = -INFINITY;
+      for (int q = 0; q < nkw; ++q) M = fmaxf(M, cml[((j + rw * q) * 16 + r16) * 2]);
+      const float Ms = M == -INFINITY ? 0.f : M;
+      float L = 0.f;
+      f32x4 O = {0.f, 0.f, 0.f, 0.f};
+      for (int q = 0; q < nkw; ++q) {
+        const int w = j + rw * q;
+        const float sw = __expf(cml[(w * 16 + r16) * 2] - Ms);
+        L += cml[(w * 16 + r16) * 2 + 1] * sw;
+        O += *(const f32x4*)(cb + (w * 16 + r16) * cs + 4 * dq) * sw;
+      }
+      float* po = a.part_o + ((size_t)slot * 128 + grow) * d;
+      st_coh_u128(po + 4 * dq, u32x4{__float_as_uint(O[0]), __float_as_uint(O[1]), __float_as_uint(O[2]),
+                                     __float_as_uint(O[3])});
+      if (dq == 0)
+        st_coh_u64(a.part_ml + ((size_t)slot * 128 + grow) * 2,
+                   (uint64_t)__float_as_uint(M) | ((uint64_t)__float_as_uint(L) << 32));
     }
   }
 }
@@ -1556,6 +1642,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   const bool cw = tid < kCompute;
   const int lane = tid & 63;
   const int nwg = gridDim.x;
+  if constexpr (TS) {
+    if (tid >= kCtl && tid - kCtl < MK_TS_EVENTS_DEV) ts_lds[tid - kCtl] = 0;   // same wave as event 0
+  }
   stamp<TS>(a.timestamps, 0);
 
   // control lanes: row / columns of the 4 outputs they store in a dense tile epilogue
@@ -1579,8 +1668,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   const bool has_qkv = a.w_qkv != nullptr;
   const bool p_o = t_o < a.H / 16, p_p = t_p < a.P / 16, p_r = t_r < a.E / 16, p_u = t_u < a.H / 16,
              p_q = has_qkv && t_q < qkv_n / 16;
-  // this workgroup's pooler tile lives in LDS: one tile, no attention item here, and it fits
-  const bool pool_lds = p_p && (int)blockIdx.x >= a.attn_items && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
+  // the pooler tile sits in LDS; a workgroup with an attention item fills it afterwards
+  const bool pool_lds = p_p && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
+  const bool pool_dma = pool_lds && (int)blockIdx.x < a.attn_items;
   u32x2 res = {0, 0};
   if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
 
@@ -1588,6 +1678,14 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   if (tid == kCtl) {
     epoch_sh = ld_coh_u32(a.epoch + blockIdx.x * 16);
     dead_sh = 0;
+  }
+  // the first attention item's queries and first K/V batch load during the setup
+  u32x4 qf0[4];
+  StageRegs sreg0;
+  if ((int)blockIdx.x < a.attn_items) {
+    const AttnItem it0 = attn_item(a, blockIdx.x);
+    attention_q(a, it0, qf0);
+    stage_load(a, it0, 0, sreg0);
   }
   wg_sync();
   if (tid < 64) {
@@ -1635,29 +1733,43 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     bool alive = true;
     uint32_t touched = 0;     // folded values of the cache-touch prefetches
     // ---- 1 ATTN
-    for (int it = blockIdx.x; it < a.attn_items; it += nwg) {
-      u32x4 qf[4];
-      attention_q(a, it, qf);
-      attention_stage(a, it, smem);
-      if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 37, 0);
-      attention_compute<TS>(a, tr, it, smem, qf);
-      if (it == (int)blockIdx.x) stamp<TS>(a.timestamps, 38, 0);
+    // one item: stage (its first batch already loaded), compute, store the partials
+    auto attn_item_run = [&](const AttnItem& it, const StageRegs& r0, const u32x4 qf[4], bool first) {
+      stage_store(a, 0, r0, smem);
+      for (int b = 1; b < stage_batches(a); ++b) {
+        StageRegs r;
+        stage_load(a, it, b, r);
+        stage_store(a, b, r, smem);
+      }
       wg_sync();
+      if (first) stamp<TS>(a.timestamps, 37, 0);
+      attention_compute(a, tr, it, smem, qf);
+      if (first) stamp<TS>(a.timestamps, 38, 0);
+      wg_sync();
+    };
+    if ((int)blockIdx.x < a.attn_items) attn_item_run(attn_item(a, blockIdx.x), sreg0, qf0, true);
+    for (int i = blockIdx.x + nwg; i < a.attn_items; i += nwg) {
+      const AttnItem it = attn_item(a, i);
+      u32x4 qf[4];
+      StageRegs r;
+      attention_q(a, it, qf);
+      stage_load(a, it, 0, r);
+      attn_item_run(it, r, qf, false);
     }
-    if (pool_lds) lds_tile_fill(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF);
-    // workgroups without an attention item pull their unpooler and qkv tiles into the
-    // device-side caches while memory is otherwise idle; they are read at the end of the layer
-    if (cw && (int)blockIdx.x >= a.attn_items) {
-      // the previous step's most-used experts, before the routing of this step is known
-      if (a.n_prefetch > 0 && nwg > a.attn_items)
-        touched ^= expert_touch(a, blockIdx.x - a.attn_items, nwg - a.attn_items);
-      if (p_u) touched ^= touch_tile<1>(a.w_unpool, a.P, t_u * 16);
-      if (p_q) touched ^= touch_tile<2>(a.w_qkv, a.H, t_q * 16);
-    }
+    if (pool_lds && !pool_dma) lds_tile_fill(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF);
+    // workgroups without an attention item pull the previous step's most-used experts into
+    // the device-side caches before the routing of this step is known.  (The unpooler and
+    // qkv tiles are not touched here: that traffic slows the attention phase more than it
+    // speeds up the end of the layer; the unpooler tile streams into LDS during GEMM2.)
+    if (cw && (int)blockIdx.x >= a.attn_items && a.n_prefetch > 0 && nwg > a.attn_items)
+      touched ^= expert_touch(a, blockIdx.x - a.attn_items, nwg - a.attn_items);
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
       if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
       if (p_p && !pool_lds) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
+      // the attention item's LDS is free now; the merge and output-projection phases use
+      // LDS below POOL_LDS_OFF only (loads are waited for before the oproj hand-off)
+      if (pool_dma) lds_tile_dma(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF, tid >> 6, kCompute / 64);
     });
     // ---- 2 MERGE
     if (alive) {
@@ -1690,6 +1802,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         st_coh_u64(a.h1 + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
       });
     }
+    if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
     alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive;
     // ---- 4 POOL: xp = bf16(h1 Wp^T)
     if (alive) {
@@ -1795,6 +1908,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
   // the next launch on this workspace uses the next epoch
   if (tid == kCtl) st_coh_u32(a.epoch + blockIdx.x * 16, epoch + 1);
+  if constexpr (TS) {
+    wg_sync();
+    if (tid < MK_TS_EVENTS_DEV) a.timestamps[blockIdx.x * MK_TS_EVENTS_DEV + tid] = ts_lds[tid];
+  }
 }
 
 template __global__ void layer_kernel<false, 0>(KArgs);

@@ -19,6 +19,9 @@ from gpu_util import (assert_close_bf16, assert_stats, check_routing, fp32_dot_b
 SMALL_NVFP4 = synth.LayerShape("small-tree-swa-nvfp4", 256, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
 SMALL_GQA = synth.LayerShape("small-tree-gqa2-global-bf16", 256, 8, 2, 64, 128, 32, 3, 64, 0, 200, 16, False)
 SMALL_T5 = synth.LayerShape("small-t5-window-nvfp4", 256, 4, 1, 128, 256, 16, 2, 96, 40, 60, 5, True)
+# a long global context with 8 q heads of 64: on a 256-CU device its attention items hold
+# four row tiles each, with two key groups per tile
+SMALL_RW4 = synth.LayerShape("small-global-ctx8100-nvfp4", 256, 8, 1, 64, 256, 16, 4, 64, 0, 8100, 16, True)
 
 
 @pytest.fixture(autouse=True)
@@ -145,7 +148,8 @@ def _check_layer(inp, out, n_sample_pairs=None):
     assert_close_bf16("v_new end-to-end", vn[ctx:ctx + T], ref["v_new"].reshape(T, -1))
 
 
-@pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83)])
+@pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83),
+                                           (SMALL_RW4, 84)])
 def test_layer_small_shapes(shape, cfg_id):
     log(f"[layer parity] {shape.name}")
     inp = synth.make_layer_inputs(shape, cfg_id)
