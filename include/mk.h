@@ -123,14 +123,18 @@ typedef struct {
 
 #define MK_TS_EVENTS 64
 
-/* Stage hand-off buffers inside the workspace (byte offsets), for stage-local checks. */
+/* Stage hand-off buffers inside the workspace (byte offsets), for stage-local checks.
+ * The bf16 activations (attn, h1, xp, y) hold 16 rows (T padded; rows >= T undefined) of K
+ * columns in MFMA fragment order: element (t, c) is at index
+ *     ((c / 32) * 64 + ((c / 8) % 4) * 16 + t) * 8 + c % 8,
+ * so that one 64-lane operand fetch of 32 columns reads 1 KB contiguously. */
 typedef struct {
   size_t status;       /* int32 status word                                      */
-  size_t attn;         /* bf16 [T][Hq*d]   attention output                      */
-  size_t h1;           /* bf16 [T][H]      residual after the output projection  */
-  size_t xp;           /* bf16 [T][P]      pooler output                         */
+  size_t attn;         /* bf16 [16][Hq*d]  attention output (fragment order)     */
+  size_t h1;           /* bf16 [16][H]     residual after the output projection  */
+  size_t xp;           /* bf16 [16][P]     pooler output (fragment order)        */
   size_t logits;       /* fp32 [T][E]      router logits (bias included)         */
-  size_t y;            /* bf16 [T][P]      combined expert output                */
+  size_t y;            /* bf16 [16][P]     combined expert output (fragment order) */
   size_t total;        /* bytes needed                                           */
   int n_wg;            /* workgroups per launch (= CUs of the current device)    */
   int attn_items;      /* attention work items (KV chunks)                       */

@@ -57,7 +57,7 @@ int check_cfg(const mk_layer_cfg* c, int T) {
 }
 
 struct Layout {
-  size_t status, epoch, flags, part_o, part_ml, attn, h1, xp, logits, act, y, total;
+  size_t status, epoch, flags, part_o, part_ml, attn, h1, h_frag, xp, logits, act, y, total;
   int n_wg, items, chunks_per_head, attn_lo, ck, rw, nrb, part_slots;
 };
 
@@ -114,13 +114,15 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   L.flags = o; o = up256(o + (size_t)n_wg * 64);
   L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
   L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
-  L.attn = o; o = up256(o + (size_t)T * Hq * d * 2);
-  L.h1 = o; o = up256(o + (size_t)T * H * 2);
-  L.xp = o; o = up256(o + (size_t)T * P * 2);
+  // hand-off activations: 16 rows (T padded) in MFMA fragment order
+  L.attn = o; o = up256(o + (size_t)16 * Hq * d * 2);
+  L.h1 = o; o = up256(o + (size_t)16 * H * 2);
+  L.h_frag = o; o = up256(o + (size_t)16 * H * 2);
+  L.xp = o; o = up256(o + (size_t)16 * P * 2);
   L.logits = o; o = up256(o + (size_t)T * E * 4);
   const size_t act_q = (size_t)T * k * (I / 16) * 16, act_b = (size_t)T * k * I * 2;
   L.act = o; o = up256(o + (act_q > act_b ? act_q : act_b));
-  L.y = o; o = up256(o + (size_t)T * P * 2);
+  L.y = o; o = up256(o + (size_t)16 * P * 2);
   L.total = o;
   return L;
 }
@@ -248,6 +250,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.part_ml = (float*)(ws + L.part_ml);
   a.attn = (uint16_t*)(ws + L.attn);
   a.h1 = (uint16_t*)(ws + L.h1);
+  a.h_frag = (uint16_t*)(ws + L.h_frag);
   a.xp = (uint16_t*)(ws + L.xp);
   a.logits = (float*)(ws + L.logits);
   a.act_q = (uint32_t*)(ws + L.act);

@@ -38,11 +38,12 @@ struct KArgs {
   int32_t* status;
   uint32_t *epoch, *flags;
   float *part_o, *part_ml;
-  uint16_t *attn, *h1, *xp;
+  uint16_t *attn, *h1, *xp;   // hand-off activations, [16][K] bf16 in MFMA fragment order
+  uint16_t* h_frag;           // h_out in fragment order (the qkv phase's x)
   float* logits;
   uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes lo, codes hi, scale byte, 0
   uint16_t* act_bf;     // bf16 intermediate [T*k][I]
-  uint16_t* y;
+  uint16_t* y;                // fragment order
   uint64_t* timestamps;
 };
 

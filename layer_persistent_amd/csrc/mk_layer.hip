@@ -220,15 +220,20 @@ struct WFrag {
   u32x4 v[MAXS > 0 ? MAXS : 1];
 };
 
+// Dense tiles split K over the 8 compute waves in contiguous blocks: wave w takes k-steps
+// w * J .. w * J + J - 1, J = ceil(K / 256), so a wave's consecutive operand fetches are 64 B
+// (weights) and 1 KB (fragment-order x) apart and fit the load instructions' immediate offsets.
+__device__ __forceinline__ int kblock(int ksteps) { return (ksteps + 7) >> 3; }
+
 template <int MAXS>
 __device__ __forceinline__ void wfrag_load(WFrag<MAXS>& f, const uint16_t* __restrict__ W, int K, int n0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + (lane >> 4) * 8;
-  const int ksteps = K >> 5;
+  const int ksteps = K >> 5, J = kblock(ksteps);
+  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + (lane >> 4) * 8 + wave * J * 32;
 #pragma unroll
   for (int j = 0; j < MAXS; ++j) {
-    const int s = wave + 8 * j;
-    f.v[j] = s < ksteps ? ld16(row + s * 32) : u32x4{0, 0, 0, 0};
+    const int s = wave * J + j;
+    f.v[j] = (j < J && s < ksteps) ? ld16(row + j * 32) : u32x4{0, 0, 0, 0};
   }
 }
 
@@ -283,14 +288,24 @@ __device__ __forceinline__ uint32_t expert_touch(const KArgs& a, int worker, int
   return v;
 }
 
-// This wave's partial of the tile: x [rows][K] (rows >= T are zero) times the fragments.
+// Activations handed between phases ([16 rows][K] bf16, rows >= T unused) are kept in MFMA
+// fragment order: element (t, c) at frag_off(t, c), so the B operand of k-step s -- lane
+// (l % 16, l / 16) holding row l % 16, columns 32 s + 8 (l / 16) .. + 8 -- is the 1 KB at
+// x + 512 s, 16 bytes per lane in lane order.  Row-major [16][K] would put the 64 lanes on 16
+// rows 2K bytes apart; measured on gfx950, a workgroup then reads 128 KB in ~2.9 us against
+// ~0.9 us for contiguous 1 KB per instruction.
+__host__ __device__ __forceinline__ int frag_off(int t, int c) {
+  return (((c >> 5) * 64 + ((c >> 3) & 3) * 16 + t) << 3) + (c & 7);
+}
+
+// This wave's partial of the tile: x (fragment order; rows >= T are zero) times the fragments.
 template <int MAXS>
 __device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t* __restrict__ x, int T, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
-  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
   const bool xv = nl < T;
-  const int ksteps = K >> 5;
+  const int ksteps = K >> 5, J = kblock(ksteps);
+  const uint16_t* xrow = x + lane * 8 + wave * J * 512;
   constexpr int XB = MAXS < 8 ? MAXS : 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -298,12 +313,14 @@ __device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t*
     u32x4 xa[XB];
 #pragma unroll
     for (int j = 0; j < XB; ++j) {
-      const int s = wave + 8 * (j0 + j);
-      xa[j] = (xv && s < ksteps) ? ld16(xrow + s * 32) : u32x4{0, 0, 0, 0};
+      const int jj = j0 + j, s = wave * J + jj;
+      xa[j] = (xv && jj < J && s < ksteps) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < XB; ++j)
-      if (wave + 8 * (j0 + j) < ksteps) acc = mfma_bf16(xa[j], f.v[j0 + j], acc);
+    for (int j = 0; j < XB; ++j) {
+      const int jj = j0 + j, s = wave * J + jj;
+      if (jj < J && s < ksteps) acc = mfma_bf16(xa[j], f.v[jj], acc);
+    }
   }
   return acc;
 }
@@ -314,22 +331,25 @@ __device__ __forceinline__ f32x4 stream_mma(const uint16_t* __restrict__ W, int 
                                            const uint16_t* __restrict__ x, int T) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
-  const uint16_t* wrow = W + (size_t)(n0 + nl) * K + (lane >> 4) * 8;
-  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
   const bool xv = nl < T;
-  const int ksteps = K >> 5;
+  const int ksteps = K >> 5, J = kblock(ksteps);
+  const uint16_t* wrow = W + (size_t)(n0 + nl) * K + (lane >> 4) * 8 + wave * J * 32;
+  const uint16_t* xrow = x + lane * 8 + wave * J * 512;   // fragment order
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < ksteps; s0 += 64) {
+  for (int b = 0; b < J; b += 8) {
     u32x4 w[8], xa[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int s = s0 + 8 * j;
-      w[j] = s < ksteps ? ld16(wrow + s * 32) : u32x4{0, 0, 0, 0};
-      xa[j] = (xv && s < ksteps) ? ld16(xrow + s * 32) : u32x4{0, 0, 0, 0};
+      const int jj = b + j, s = wave * J + jj;
+      const bool ok = jj < J && s < ksteps;
+      w[j] = ok ? ld16(wrow + jj * 32) : u32x4{0, 0, 0, 0};
+      xa[j] = (xv && ok) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (s0 + 8 * j < ksteps) acc = mfma_bf16(xa[j], w[j], acc);
+    for (int j = 0; j < 8; ++j) {
+      const int jj = b + j, s = wave * J + jj;
+      if (jj < J && s < ksteps) acc = mfma_bf16(xa[j], w[j], acc);
+    }
   }
   return acc;
 }
@@ -375,21 +395,21 @@ __device__ __forceinline__ void lds_tile_dma(const uint16_t* __restrict__ W, int
 __device__ __forceinline__ f32x4 lds_mma(const char* wl, const uint16_t* __restrict__ x, int T, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
-  const uint16_t* xrow = x + (size_t)nl * K + (lane >> 4) * 8;
   const bool xv = nl < T;
-  const int ksteps = K >> 5;
+  const int ksteps = K >> 5, J = kblock(ksteps);
+  const uint16_t* xrow = x + lane * 8 + wave * J * 512;   // fragment order
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = wave; s0 < ksteps; s0 += 128) {
+  for (int b = 0; b < J; b += 16) {
     u32x4 xa[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int sk = s0 + 8 * j;
-      xa[j] = (xv && sk < ksteps) ? ld16(xrow + sk * 32) : u32x4{0, 0, 0, 0};
+      const int jj = b + j, sk = wave * J + jj;
+      xa[j] = (xv && jj < J && sk < ksteps) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-      const int sk = s0 + 8 * j;
-      if (sk < ksteps) acc = mfma_bf16(xa[j], *(const u32x4*)(wl + (size_t)(sk * 64 + lane) * 16), acc);
+      const int jj = b + j, sk = wave * J + jj;
+      if (jj < J && sk < ksteps) acc = mfma_bf16(xa[j], *(const u32x4*)(wl + (size_t)(sk * 64 + lane) * 16), acc);
     }
   }
   return acc;
@@ -1005,20 +1025,23 @@ constexpr int G1_UNITS = 16;                   // units per round (2 per compute
 // take xs = xp unchanged.
 //
 // Part 1 (compute threads, no barrier; runs while the grid waits for the router): this
-// thread's pieces of xp (8 bf16 each, T * P / 8 <= 4096 pieces) into registers and, for NVFP4,
-// each piece's largest magnitude into pmax (LDS).
+// thread's pieces of xp into registers and, for NVFP4, each piece's largest magnitude into
+// pmax[t][c / 8] (LDS).  xp is in fragment order: piece i (8 bf16, 16 * P / 8 <= 4096 pieces)
+// is row i % 16, columns 8 ((i / 64) * 4 + (i / 16) % 4) .. + 8; pieces of rows >= T are skipped.
+__device__ __forceinline__ int piece_row(int i) { return i & 15; }
+__device__ __forceinline__ int piece_col8(int i) { return ((i >> 6) << 2) + ((i >> 4) & 3); }
 __device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t* pmax) {
-  const int tid = threadIdx.x, n = a.T * (a.P / 8);
+  const int tid = threadIdx.x, n = 16 * (a.P / 8);
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = j * kCompute + tid;
-    if (i < n) v[j] = ld16(a.xp + (size_t)i * 8);
+    if (i < n && piece_row(i) < a.T) v[j] = ld16(a.xp + (size_t)i * 8);
   }
   if (a.fmt != 1) return;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = j * kCompute + tid;
-    if (i < n) {
+    if (i < n && piece_row(i) < a.T) {
       // |x| of a bf16 orders like its bit pattern without the sign
       uint32_t m = 0;
 #pragma unroll
@@ -1026,7 +1049,7 @@ __device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t
         const uint32_t w = v[j][q] & 0x7FFF7FFFu;
         m = max(m, max(w & 0xFFFFu, w >> 16));
       }
-      pmax[i] = m;
+      pmax[piece_row(i) * (a.P / 8) + piece_col8(i)] = m;
     }
   }
 }
@@ -1052,8 +1075,8 @@ __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], ui
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int i = j * kCompute + tid;
-      if (i < n) {
-        const int t = i / per_row, c = i % per_row;
+      if (i < 16 * per_row && piece_row(i) < T) {
+        const int t = piece_row(i), c = piece_col8(i);
         u32x4 o = v[j];
         if (fp4) {
           const float f = __uint_as_float((uint32_t)(127 + xk[t]) << 23);   // 2^xk[t], exact
@@ -1382,7 +1405,7 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
     wg_sync();
     if (tid >= kCompute && (tid - kCompute) < T) {
       const int t = tid - kCompute;
-      uint16_t* dst = a.y + (size_t)t * P + c0;
+      uint16_t* dst = a.y + frag_off(t, c0);            // 8 columns: 16 contiguous bytes
       st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
       st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
     }
@@ -1544,7 +1567,7 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
     wg_sync();
     if (tid >= kCompute && (tid - kCompute) < T) {
       const int t = tid - kCompute;
-      uint16_t* dst = a.y + (size_t)t * P + c0;
+      uint16_t* dst = a.y + frag_off(t, c0);            // 8 columns: 16 contiguous bytes
       st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
       st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
     }
@@ -1781,7 +1804,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         if (!cw) {
           const int g_kv = u / R, row = u % R, tok = row / G, head = g_kv * G + row % G;
           if (lane < a.d / 4)
-            st_coh_u64(a.attn + (size_t)tok * a.Hq * a.d + head * a.d + lane * 4,
+            st_coh_u64(a.attn + frag_off(tok, head * a.d + lane * 4),
                        (uint64_t)outrow[2 * lane] | ((uint64_t)outrow[2 * lane + 1] << 32));
           if (lane == 0 && a.attn_stats) {
             a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 0] = __uint_as_float(outrow[64]);
@@ -1799,7 +1822,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         ctl_tile_vals(red, crow, cc0, v);
         const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h_in + (size_t)crow * a.H + n0 + cc0);
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
-        st_coh_u64(a.h1 + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
+        st_coh_u64(a.h1 + frag_off(crow, n0 + cc0), pack4_bf16(v));
       });
     }
     if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
@@ -1807,12 +1830,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- 4 POOL: xp = bf16(h1 Wp^T)
     if (alive) {
       // control wave: the unpooler's residual (h1) for its first tile, needed in phase 8
-      if (!cw && p_u && crv) res = *(const u32x2*)(a.h1 + (size_t)crow * a.H + t_u * 16 + cc0);
+      if (!cw && p_u && crv) res = *(const u32x2*)(a.h1 + frag_off(crow, t_u * 16 + cc0));
       dense_phase(a, wp, false, a.w_pool, a.h1, a.H, a.P, off_p, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        st_coh_u64(a.xp + (size_t)crow * a.P + n0 + cc0, pack4_bf16(v));
+        st_coh_u64(a.xp + frag_off(crow, n0 + cc0), pack4_bf16(v));
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
@@ -1867,9 +1890,11 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + (size_t)crow * a.H + n0 + cc0);
+        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + frag_off(crow, n0 + cc0));
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
-        st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, pack4_bf16(v));
+        const uint64_t hv = pack4_bf16(v);
+        st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, hv);     // the step's output, row-major
+        st_coh_u64(a.h_frag + frag_off(crow, n0 + cc0), hv);          // the qkv phase's x
       }, wu_lds ? smem + WU_LDS_OFF : nullptr, [&] {
         // the qkv tile's weights load while the unpooler finishes and the grid hands off
         if (p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
@@ -1879,7 +1904,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
-      if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_out, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+      if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_frag, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);

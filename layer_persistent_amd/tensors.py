@@ -149,6 +149,12 @@ def run_step(dw: DeviceWeights, st: DeviceStep, stream=None, spin_limit: int = 0
     return abi.mk_layer_step(st.cfg, dw.struct(), io, stream)
 
 
+def untile_frag(buf: np.ndarray, T: int, K: int) -> np.ndarray:
+    """[16][K] bf16 held in MFMA fragment order (element (t, c) at ((c//32)*64 + (c//8)%4*16 + t)*8
+    + c%8) back to row-major [T][K]."""
+    return buf.reshape(K // 32, 4, 16, 8).transpose(2, 0, 1, 3).reshape(16, K)[:T].copy()
+
+
 def outputs(st: DeviceStep) -> dict:
     """Copy a step's outputs and stage hand-off buffers to the host."""
     torch.cuda.synchronize()
@@ -160,9 +166,9 @@ def outputs(st: DeviceStep) -> dict:
         k_cache_next=host_u16(st.k_next), v_cache_next=host_u16(st.v_next),
         idx=st.topk_idx.cpu().numpy(), gate=st.topk_gate.cpu().numpy(), logits=st.logits.cpu().numpy(),
         stats=st.stats.cpu().numpy(), hist=st.hist.cpu().numpy(),
-        attn=st.ws_u16(L.attn, sh_T * c.n_q_heads * c.head_dim).reshape(sh_T, -1),
-        h1=st.ws_u16(L.h1, sh_T * c.hidden).reshape(sh_T, -1),
-        xp=st.ws_u16(L.xp, sh_T * c.pooled).reshape(sh_T, -1),
-        y=st.ws_u16(L.y, sh_T * c.pooled).reshape(sh_T, -1),
+        attn=untile_frag(st.ws_u16(L.attn, 16 * c.n_q_heads * c.head_dim), sh_T, c.n_q_heads * c.head_dim),
+        h1=untile_frag(st.ws_u16(L.h1, 16 * c.hidden), sh_T, c.hidden),
+        xp=untile_frag(st.ws_u16(L.xp, 16 * c.pooled), sh_T, c.pooled),
+        y=untile_frag(st.ws_u16(L.y, 16 * c.pooled), sh_T, c.pooled),
         status=int(st.ws_f32(L.status, 1).view(np.int32)[0]),
     )

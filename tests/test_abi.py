@@ -130,3 +130,20 @@ int main(void) {
     assert r.returncode == 0, r.stderr
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     assert out.returncode == 0, out.stdout + out.stderr
+
+
+def test_fragment_order_untile_matches_the_documented_index():
+    """The hand-off activations' layout as include/mk.h states it, element by element, against
+    the reshape that tensors.untile_frag uses to read them back."""
+    import numpy as np
+    from layer_persistent_amd.tensors import untile_frag
+    with open(os.path.join(ROOT, "include", "mk.h")) as f:
+        assert "((c / 32) * 64 + ((c / 8) % 4) * 16 + t) * 8 + c % 8" in f.read()
+    rng = np.random.default_rng(5)
+    for T, K in ((16, 256), (5, 64), (1, 4096)):
+        x = rng.integers(0, 1 << 16, size=(T, K), dtype=np.uint16)
+        buf = np.zeros(16 * K, dtype=np.uint16)
+        for t in range(T):
+            for c in range(K):
+                buf[((c // 32) * 64 + ((c // 8) % 4) * 16 + t) * 8 + c % 8] = x[t, c]
+        assert np.array_equal(untile_frag(buf, T, K), x)
