@@ -75,7 +75,8 @@ typedef struct {
                               NULL (first and last layers differ: orcarouter.ai write-up,
                               "where the kernel boundary sits")                              */
   const void *w1, *w2;     /* MK_W_BF16:  bf16 [E][2I][P] (rows [0,I) gate, [I,2I) up), [E][P][I] */
-  const uint8_t *w1_codes, *w1_scales;  /* MK_W_NVFP4: [E][2I][P/2], [E][2I][P/16] (mk_nvfp4_pack) */
+  const uint8_t *w1_codes, *w1_scales;  /* MK_W_NVFP4: W1 in GEMM1's operand order, from
+                                           mk_nvfp4_pack then mk_nvfp4_tile_w1 */
   const uint8_t *w2_codes, *w2_scales;  /*             [E][P][I/2],  [E][P][I/16]                  */
   const float *w1_tscale, *w2_tscale;   /*             fp32 [E] tensor scales                      */
 } mk_layer_weights;
@@ -173,6 +174,19 @@ int mk_route_topk(const void *x, const void *w_router, const float *bias, int T,
  * scales uint8 [batch][N][K/16], tensor_scale fp32 [batch]. */
 int mk_nvfp4_pack(const void *w, int w_is_fp32, int batch, int N, int K, uint8_t *codes,
                   uint8_t *scales, float *tensor_scale, void *stream);
+
+/* Rearranges W1's NVFP4 codes and scales (as mk_nvfp4_pack writes them: codes [batch][N][K/2],
+ * scales [batch][N][K/16]) into the order GEMM1 reads them, so that every 64-lane weight fetch
+ * is 1 KB contiguous.  N % 16 == 0, K % 128 == 0.  With L = K/128 k-steps per row,
+ * p = (L > 8 ? 2 : 1) pieces per row and S = 8 * ceil(L / p) scale bytes per piece and row:
+ *   codes_t  [batch][N/16][L][64][16]: codes_t[b][t][s][l][i] = codes[b][16t + l%16][64s + 16(l/16) + i]
+ *   scales_t [batch][N/16][p][16][S]:  scales_t[b][t][q][r][i] = scales[b][16t + r][qS + i], 0 past K/16
+ * scales_t takes mk_nvfp4_w1_scales_bytes(batch, N, K) bytes (batch * N * K/16 when L is even or
+ * at most 8).  Pure byte permutation; codes, codes_t and scales_t 16-byte aligned. */
+int mk_nvfp4_tile_w1(const uint8_t *codes, const uint8_t *scales, int batch, int N, int K,
+                     uint8_t *codes_t, uint8_t *scales_t, void *stream);
+/* Bytes of mk_nvfp4_tile_w1's scales_t, or 0 for an unsupported shape. */
+size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K);
 
 /* Synchronise `stream` and return the status word of the last mk_layer_step on this
  * workspace (MK_OK, MK_EBADTREE or MK_ETIMEOUT), or MK_EHIP if the copy failed. */

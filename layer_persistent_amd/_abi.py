@@ -17,7 +17,8 @@ MK_W_BF16, MK_W_NVFP4 = 0, 1
 MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step",
-            "mk_kv_append", "mk_route_topk", "mk_nvfp4_pack", "mk_read_status", "mk_strerror"]
+            "mk_kv_append", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
+            "mk_read_status", "mk_strerror"]
 
 
 class mk_layer_cfg(C.Structure):
@@ -71,11 +72,14 @@ def lib() -> C.CDLL:
         L.mk_kv_append.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_route_topk.argtypes = [P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.mk_nvfp4_pack.argtypes = [P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
+        L.mk_nvfp4_tile_w1.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P, P]
+        L.mk_nvfp4_w1_scales_bytes.argtypes = [C.c_int, C.c_int, C.c_int]
+        L.mk_nvfp4_w1_scales_bytes.restype = C.c_size_t
         L.mk_read_status.argtypes = [P, P]
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_kv_append",
-                     "mk_route_topk", "mk_nvfp4_pack", "mk_read_status"):
+                     "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_read_status"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -149,6 +153,16 @@ def mk_nvfp4_pack(w, w_is_fp32, batch, N, K, codes, scales, tensor_scale, stream
     rc = lib().mk_nvfp4_pack(_ptr(w), int(w_is_fp32), batch, N, K, _ptr(codes), _ptr(scales),
                              _ptr(tensor_scale), _stream(stream))
     return _check(rc, "mk_nvfp4_pack") if check else rc
+
+
+def mk_nvfp4_tile_w1(codes, scales, batch, N, K, codes_t, scales_t, stream=None, check=True):
+    rc = lib().mk_nvfp4_tile_w1(_ptr(codes), _ptr(scales), batch, N, K, _ptr(codes_t), _ptr(scales_t),
+                                _stream(stream))
+    return _check(rc, "mk_nvfp4_tile_w1") if check else rc
+
+
+def mk_nvfp4_w1_scales_bytes(batch, N, K) -> int:
+    return int(lib().mk_nvfp4_w1_scales_bytes(batch, N, K))
 
 
 def mk_read_status(workspace, stream=None) -> int:

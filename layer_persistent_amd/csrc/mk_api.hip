@@ -291,6 +291,20 @@ int mk_nvfp4_pack(const void* w, int w_is_fp32, int batch, int N, int K, uint8_t
              ? MK_EHIP : MK_OK;
 }
 
+int mk_nvfp4_tile_w1(const uint8_t* codes, const uint8_t* scales, int batch, int N, int K, uint8_t* codes_t,
+                     uint8_t* scales_t, void* stream) {
+  if (!codes || !scales || !codes_t || !scales_t) return MK_EINVAL;
+  if (batch < 1 || batch > 65535 || N < 16 || N % 16 || K < 128 || K % 128) return MK_ESHAPE;
+  if (!aligned16(codes) || !aligned16(codes_t) || !aligned16(scales_t)) return MK_EALIGN;
+  return mk::launch_nvfp4_tile_w1(codes, scales, batch, N, K, codes_t, scales_t, (hipStream_t)stream) ? MK_EHIP
+                                                                                                     : MK_OK;
+}
+
+size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K) {
+  if (batch < 1 || N < 16 || N % 16 || K < 128 || K % 128) return 0;
+  return (size_t)batch * N * mk::g1_scale_row_bytes(K);
+}
+
 int mk_read_status(const void* workspace, void* stream) {
   if (!workspace) return MK_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_EHIP;

@@ -216,4 +216,46 @@ int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// W1 codes and scales from row-major into GEMM1's operand order (g1_* in mk_internal.h): one
+// thread per 16-byte chunk of tiled codes, then one per (tile, piece, row) of tiled scales.
+__global__ void tile_w1_codes_kernel(const uint8_t* codes, int N, int K, size_t nchunks, uint8_t* codes_t) {
+  const int ls_n = g1_lsteps(K);
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < nchunks; o += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(o % 64);
+    const size_t tl = o / 64;                   // (matrix, tile, k-step)
+    const int ls = (int)(tl % ls_n);
+    const size_t row = (tl / ls_n) * 16 + (l & 15);   // row over the whole batch (N % 16 == 0)
+    const u32x4 v = *(const u32x4*)(codes + row * (K / 2) + ls * 64 + (l >> 4) * 16);
+    *(u32x4*)(codes_t + o * 16) = v;
+  }
+}
+__global__ void tile_w1_scales_kernel(const uint8_t* scales, int N, int K, size_t nrows, uint8_t* scales_t) {
+  const int np = g1_pieces(K), sb = g1_sb(K), rb = K / 16;
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < nrows; o += (size_t)gridDim.x * blockDim.x) {
+    const int r = (int)(o % 16);
+    const size_t tp = o / 16;                   // (matrix, tile, piece)
+    const int p = (int)(tp % np);
+    const size_t row = (tp / np) * 16 + r;
+    uint8_t* dst = scales_t + o * sb;
+    for (int i = 0; i < sb; ++i) {
+      const int c = p * sb + i;
+      dst[i] = c < rb ? scales[row * rb + c] : (uint8_t)0;
+    }
+  }
+}
+
+int launch_nvfp4_tile_w1(const uint8_t* codes, const uint8_t* scales, int batch, int N, int K,
+                         uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream) {
+  const size_t nchunks = (size_t)batch * N * (K / 2) / 16;
+  size_t g = (nchunks + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(tile_w1_codes_kernel, dim3((unsigned)g), dim3(256), 0, stream, codes, N, K, nchunks, codes_t);
+  if (hipGetLastError() != hipSuccess) return -5;
+  const size_t nrows = (size_t)batch * N * g1_pieces(K);
+  g = (nrows + 255) / 256;
+  if (g > 65536) g = 65536;
+  hipLaunchKernelGGL(tile_w1_scales_kernel, dim3((unsigned)g), dim3(256), 0, stream, scales, N, K, nrows, scales_t);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 }  // namespace mk

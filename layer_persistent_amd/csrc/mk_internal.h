@@ -47,6 +47,18 @@ struct KArgs {
   uint64_t* timestamps;
 };
 
+// GEMM1's W1 operand order (NVFP4).  A row of K codes is cut into k-steps of 128 elements
+// (64 code bytes, 8 scale bytes); a piece is half of a 16-row tile's k-steps when there are
+// more than 8, else all of them.  Codes: [N/16][K/128][64 lanes][16 B], lane l holding row
+// 16t + l % 16, code bytes 64 ls + 16 (l / 16) .. + 16.  Scales: [N/16][pieces][16 rows]
+// [g1_sb(K) B], the piece's scale bytes of each row, zero past the row's end.
+__host__ __device__ inline int g1_lsteps(int K) { return K / 128; }
+__host__ __device__ inline int g1_pieces(int K) { return g1_lsteps(K) > 8 ? 2 : 1; }
+__host__ __device__ inline int g1_hsteps(int K) { return (g1_lsteps(K) + g1_pieces(K) - 1) / g1_pieces(K); }
+__host__ __device__ inline int g1_sb(int K) { return g1_hsteps(K) * 8; }
+// scale bytes per W1 row in that order (>= K / 16)
+__host__ __device__ inline size_t g1_scale_row_bytes(int K) { return (size_t)g1_pieces(K) * g1_sb(K); }
+
 int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream);
 int layer_lds_bytes();
 int set_layer_kernel_attrs(int lds_bytes);
@@ -58,5 +70,7 @@ int launch_route_topk(const uint16_t* x, const uint16_t* w, const float* bias, i
                       int k, int32_t* idx, float* gate, float* logits, hipStream_t stream);
 int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8_t* codes,
                       uint8_t* scales, float* ts, hipStream_t stream);
+int launch_nvfp4_tile_w1(const uint8_t* codes, const uint8_t* scales, int batch, int N, int K,
+                         uint8_t* codes_t, uint8_t* scales_t, hipStream_t stream);
 
 }  // namespace mk

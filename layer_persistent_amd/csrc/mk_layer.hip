@@ -267,7 +267,7 @@ __device__ __forceinline__ uint32_t expert_touch(const KArgs& a, int worker, int
   const bool fp4 = a.fmt == 1;
   // per expert: up to four contiguous regions
   const size_t r0 = fp4 ? 2 * I * P / 2 : 2 * I * P * 2;       // W1 codes | W1 bf16
-  const size_t r1 = fp4 ? 2 * I * P / 16 : 0;                  // W1 scales
+  const size_t r1 = fp4 ? 2 * I * g1_scale_row_bytes(a.P) : 0; // W1 scales (GEMM1 operand order)
   const size_t r2 = fp4 ? P * I / 2 : P * I * 2;               // W2 codes | W2 bf16
   const size_t r3 = fp4 ? P * I / 16 : 0;                      // W2 scales
   const size_t per = (r0 + r1 + r2 + r3 + 127) / 128;          // lines per expert (regions rounded)
@@ -1105,30 +1105,74 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   if (t_begin >= t_end) return;                 // uniform over the workgroup
   const int xstride = P + XS_STRIDE_PAD;
   uint16_t* xs = (uint16_t*)smem;                                  // [T][P + 8] bf16
-  uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // [16 units][16 rows][P/16]
+  // sbuf: the piece maxima while xs is built, then the wave-private piece-scale buffers (16 rows
+  // x srow_b bytes each, 2 per wave: within 16 P bytes for every P % 128 == 0 up to 2048)
+  uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // 16 P bytes
   float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][2 K halves][16][17]
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
-  const int lsteps = P / 128;
+  const int lsteps = g1_lsteps(P);
   const int nunits = 2 * (t_end - t_begin);
   // NVFP4: a round's units are split into pieces (unit, K half) dealt to the compute waves
   // round-robin (piece pc: unit pc / nh, half pc % nh), so the waves carry equal work.  A wave
   // streams its pieces with the next piece's codes and block scales in flight while the
   // current one is multiplied; each piece leaves its partial tile in ubuf[unit][half].
-  const int nh = lsteps > 8 ? 2 : 1;                             // pieces per unit
-  const int hsteps = (lsteps + nh - 1) / nh;                     // load steps per piece (<= 8)
-  const int srow_b = (P / 16) / nh;                              // scale bytes per row and piece
+  const int nh = g1_pieces(P);                                   // pieces per unit
+  const int hsteps = g1_hsteps(P);                               // load steps per piece (<= 8)
+  const int srow_b = g1_sb(P);                                   // scale bytes per row and piece
   u32x4 cA[8], cB[8], sA, sB;
   auto load_piece = [&](int u0, int pc, u32x4 (&cd)[8], u32x4& sv) {
     const int u = pc / nh, hf = pc % nh;
     const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
     const int ai = task / jblocks, j0 = (task % jblocks) * 16;
-    const size_t wrow = (size_t)rt.act_expert[ai] * 2 * I + half * I + j0;
-    const uint8_t* cp = a.w1_codes + (wrow + nl) * (P / 2) + grp * 16 + hf * hsteps * 64;
+    // W1 is in GEMM1's operand order: k-step ls of the 16-row tile is 1 KB, lane l's 16 B at
+    // 16 l; the piece's scales are 16 rows x srow_b bytes, one contiguous block
+    const size_t tile = ((size_t)rt.act_expert[ai] * 2 * I + half * I + j0) / 16;
+    const uint8_t* cp = a.w1_codes + (tile * lsteps + hf * hsteps) * 1024 + lane * 16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) if (j < hsteps && hf * hsteps + j < lsteps) cd[j] = ld16(cp + j * 64);
-    // this piece's scales: 16 rows x srow_b bytes, 16 bytes per lane
-    const int sb = lane * 16;
-    if (sb < 16 * srow_b) sv = ld16(a.w1_scales + (wrow + sb / srow_b) * (P / 16) + hf * srow_b + sb % srow_b);
+    for (int j = 0; j < 8; ++j) if (j < hsteps && hf * hsteps + j < lsteps) cd[j] = ld16(cp + j * 1024);
+    if (lane * 16 < 16 * srow_b) sv = ld16(a.w1_scales + (tile * nh + hf) * 16 * srow_b + lane * 16);
+  };
+  // SwiGLU + requantisation of the round at unit u0 (nu units): thread (task, token row m)
+  auto swiglu_round = [&](int u0, int nu) {
+    for (int o = tid; cw && o < (nu / 2) * 16; o += kCompute) {
+      const int tl = o >> 4, m = o & 15;
+      const int task = t_begin + u0 / 2 + tl;
+      const int ai = task / jblocks, j0 = (task % jblocks) * 16;
+      if (m < rt.act_cnt[ai]) {
+        const int pair = rt.pair_list[rt.act_off[ai] + m];
+        // the two K halves of the gate unit (2 tl) and of the up unit (2 tl + 1)
+        const float* ug = ubuf + (4 * tl) * (16 * 17) + m * 17;
+        const float* uu = ubuf + (4 * tl + 2) * (16 * 17) + m * 17;
+        // NVFP4: the tensor scale, and undo the token row's power-of-two input scale (exact)
+        const float f = a.fmt == 1 ? rt.ts1[rt.act_expert[ai]] * __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23)
+                                   : 1.0f;
+        float v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const float g = (ug[j] + ug[16 * 17 + j]) * f;
+          v[j] = g / (1.0f + __expf(-g)) * ((uu[j] + uu[16 * 17 + j]) * f);
+        }
+        if (a.fmt == 1) {
+          float amax = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+          const uint32_t sc = e4m3_code_of_amax_over6(amax);
+          const float sv = e4m3_to_f32(sc);
+          uint32_t w0 = 0, w1 = 0;
+          if (sv > 0.f) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], sv) << (4 * j);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], sv) << (4 * j);
+          }
+          st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
+        } else {
+          uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) st_coh_u64(dst + 4 * q, pack4_bf16(v + 4 * q));
+        }
+      }
+    }
   };
   // the first round's first piece is requested before the input rows are built
   if (cw && a.fmt == 1 && wave < nh * min(G1_UNITS, nunits)) load_piece(0, wave, cA, sA);
@@ -1153,7 +1197,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
           const int ai = task / jblocks;
           const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
           // the piece's scales into this wave's LDS buffer (wave-private: no barrier)
-          uint8_t* sd = sbuf + (wave * 2 + x) * 1024;
+          uint8_t* sd = sbuf + (wave * 2 + x) * 16 * srow_b;
           if (lane * 16 < 16 * srow_b) *(u32x4*)(sd + lane * 16) = x == 0 ? sA : sB;
           // rows past the expert's tokens read token 0 and are discarded after the product
           const uint16_t* xrow = xs + (nl < cnt ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
@@ -1209,46 +1253,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
     }
     wg_sync();
     if (u0 == 0) stamp<TS>(a.timestamps, 45, 0);
-    // SwiGLU + requantisation: thread (task of the round, token row m)
-    for (int o = tid; cw && o < (nu / 2) * 16; o += kCompute) {
-      const int tl = o >> 4, m = o & 15;
-      const int task = t_begin + u0 / 2 + tl;
-      const int ai = task / jblocks, j0 = (task % jblocks) * 16;
-      if (m < rt.act_cnt[ai]) {
-        const int pair = rt.pair_list[rt.act_off[ai] + m];
-        // the two K halves of the gate unit (2 tl) and of the up unit (2 tl + 1)
-        const float* ug = ubuf + (4 * tl) * (16 * 17) + m * 17;
-        const float* uu = ubuf + (4 * tl + 2) * (16 * 17) + m * 17;
-        // NVFP4: the tensor scale, and undo the token row's power-of-two input scale (exact)
-        const float f = a.fmt == 1 ? rt.ts1[rt.act_expert[ai]] * __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23)
-                                   : 1.0f;
-        float v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float g = (ug[j] + ug[16 * 17 + j]) * f;
-          v[j] = g / (1.0f + __expf(-g)) * ((uu[j] + uu[16 * 17 + j]) * f);
-        }
-        if (a.fmt == 1) {
-          float amax = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-          const uint32_t sc = e4m3_code_of_amax_over6(amax);
-          const float sv = e4m3_to_f32(sc);
-          uint32_t w0 = 0, w1 = 0;
-          if (sv > 0.f) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], sv) << (4 * j);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], sv) << (4 * j);
-          }
-          st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
-        } else {
-          uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st_coh_u64(dst + 4 * q, pack4_bf16(v + 4 * q));
-        }
-      }
-    }
+    swiglu_round(u0, nu);
     wg_sync();
   }
 }
@@ -1584,16 +1589,16 @@ struct NoHook {
   __device__ void operator()() const {}
 };
 
-// `after` runs on the compute threads once their last tile's products are formed (registers of
-// this phase's weights are free then): loads for the next phase can start there.
+// `after` runs on the compute threads once their last tile's partials are in LDS (registers of
+// this phase's weights are free then), while the control wave stores the last tile: loads for
+// the next phase can start there.  (Issued before the tile's barrier instead, they made the
+// compiler wait for them at that barrier.)
 template <int MAXS, class Epi, class After = NoHook>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
                             const uint16_t* x, int K, int N, int off, float* red2, Epi epi,
                             const char* wlds = nullptr, After after = After()) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
-  // a workgroup without a tile in this phase runs `after` at once
-  if (threadIdx.x < kCompute && first_tile(off) >= ntiles) after();
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
     float* red = red2 + (it & 1) * (8 * 16 * 17);
     if (threadIdx.x < kCompute) {
@@ -1606,12 +1611,12 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
         if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
         acc = wfrag_mma(wf, x, a.T, K);
       }
-      if (t + n >= ntiles) after();
       red_store(red, acc);
     }
     wg_sync();
     if (threadIdx.x >= kCompute) epi(t * 16, red, it);
   }
+  if (threadIdx.x < kCompute) after();
 }
 
 // End of a phase: compute waves run `pf` (loads for a later phase, left in flight) while the

@@ -21,7 +21,7 @@ import torch
 
 import synth
 from . import _abi as abi
-from .tensors import DeviceWeights, layer_cfg
+from .tensors import DeviceWeights, layer_cfg, tile_w1
 
 
 @dataclasses.dataclass
@@ -61,6 +61,7 @@ class Stack:
             dw.w2_ts = torch.empty(E, dtype=torch.float32, device=device)
             abi.mk_nvfp4_pack(wd["w1"], 0, E, 2 * I, P, dw.w1_codes, dw.w1_scales, dw.w1_ts)
             abi.mk_nvfp4_pack(wd["w2"], 0, E, P, I, dw.w2_codes, dw.w2_scales, dw.w2_ts)
+            tile_w1(dw, E, I, P)
             torch.cuda.synchronize()
             del wd
             kc, vc = synth.device_kv_context(lsh, cfg_id, L, device)

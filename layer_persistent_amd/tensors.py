@@ -71,9 +71,20 @@ def upload_weights(inp, device="cuda", stream=None) -> DeviceWeights:
     dw.w2_ts = torch.empty(E, dtype=torch.float32, device=device)
     abi.mk_nvfp4_pack(w1, 0, E, 2 * I, P, dw.w1_codes, dw.w1_scales, dw.w1_ts, stream)
     abi.mk_nvfp4_pack(w2, 0, E, P, I, dw.w2_codes, dw.w2_scales, dw.w2_ts, stream)
+    tile_w1(dw, E, I, P, stream)
     torch.cuda.synchronize()
     del w1, w2
     return dw
+
+
+def tile_w1(dw, E: int, I: int, P: int, stream=None) -> None:
+    """Replace dw.w1_codes / dw.w1_scales (row-major, as mk_nvfp4_pack writes them) by their
+    GEMM1 operand order (mk_nvfp4_tile_w1)."""
+    codes_t = torch.empty_like(dw.w1_codes)
+    scales_t = torch.empty(abi.mk_nvfp4_w1_scales_bytes(E, 2 * I, P), dtype=torch.uint8, device=dw.w1_codes.device)
+    abi.mk_nvfp4_tile_w1(dw.w1_codes, dw.w1_scales, E, 2 * I, P, codes_t, scales_t, stream)
+    torch.cuda.synchronize()
+    dw.w1_codes, dw.w1_scales = codes_t, scales_t
 
 
 @dataclasses.dataclass

@@ -102,6 +102,18 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_nvfp4_pack(GOOD, 2, 1, 16, 32, GOOD, GOOD, GOOD, check=False) == mk.MK_EINVAL
     assert mk.mk_nvfp4_pack(GOOD, 0, 1, 16, 32, BAD, GOOD, GOOD, check=False) == mk.MK_EALIGN
     assert mk.mk_nvfp4_pack(None, 0, 1, 16, 32, GOOD, GOOD, GOOD, check=False) == mk.MK_EINVAL
+    assert mk.mk_nvfp4_tile_w1(None, GOOD, 1, 16, 128, GOOD, GOOD, check=False) == mk.MK_EINVAL
+    assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 24, 128, GOOD, GOOD, check=False) == mk.MK_ESHAPE
+    assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 16, 192, GOOD, GOOD, check=False) == mk.MK_ESHAPE
+    assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 16, 128, BAD, GOOD, check=False) == mk.MK_EALIGN
+
+
+def test_w1_scale_bytes_follow_the_piece_rule():
+    # L = K/128 k-steps; 2 pieces when L > 8; 8 * ceil(L / pieces) bytes per piece and row
+    assert mk.mk_nvfp4_w1_scales_bytes(1, 16, 2048) == 16 * 128       # L = 16: 2 x 64 = K/16
+    assert mk.mk_nvfp4_w1_scales_bytes(3, 32, 256) == 3 * 32 * 16      # L = 2: one piece of 16
+    assert mk.mk_nvfp4_w1_scales_bytes(1, 16, 1152) == 16 * 80         # L = 9: 2 x 40 > K/16 = 72
+    assert mk.mk_nvfp4_w1_scales_bytes(1, 16, 1000) == 0
 
 
 def test_c_host_caller_compiles_against_header(tmp_path):

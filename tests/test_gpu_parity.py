@@ -22,6 +22,9 @@ SMALL_T5 = synth.LayerShape("small-t5-window-nvfp4", 256, 4, 1, 128, 256, 16, 2,
 # a long global context with 8 q heads of 64: on a 256-CU device its attention items hold
 # four row tiles each, with two key groups per tile
 SMALL_RW4 = synth.LayerShape("small-global-ctx8100-nvfp4", 256, 8, 1, 64, 256, 16, 4, 64, 0, 8100, 16, True)
+# pooled 1152: nine 128-wide k-steps per W1 row, split 5 + 4 over two pieces (the second
+# piece's scale bytes start at 40, not at half the row)
+SMALL_P1152 = synth.LayerShape("small-p1152-nvfp4", 256, 4, 1, 64, 1152, 16, 4, 64, 128, 300, 16, True)
 
 
 @pytest.fixture(autouse=True)
@@ -55,6 +58,44 @@ def test_nvfp4_pack_bit_exact():
             assert np.array_equal(scales[b].cpu().numpy(), rs)
             assert ts[b].item() == rt
     log("  nvfp4 pack: bit-exact (bf16 and fp32 inputs)")
+
+
+def _tile_w1_reference(codes, scales, K):
+    """GEMM1's W1 operand order as include/mk.h states it, element by element."""
+    B, N, _ = codes.shape
+    L = K // 128
+    p = 2 if L > 8 else 1
+    S = 8 * ((L + p - 1) // p)
+    ct = np.zeros((B, N // 16, L, 64, 16), dtype=np.uint8)
+    st = np.zeros((B, N // 16, p, 16, S), dtype=np.uint8)
+    for b in range(B):
+        for t in range(N // 16):
+            for s_ in range(L):
+                for l in range(64):
+                    ct[b, t, s_, l] = codes[b, 16 * t + l % 16, 64 * s_ + 16 * (l // 16):64 * s_ + 16 * (l // 16) + 16]
+            for q in range(p):
+                for r in range(16):
+                    for i in range(S):
+                        if q * S + i < K // 16:
+                            st[b, t, q, r, i] = scales[b, 16 * t + r, q * S + i]
+    return ct.reshape(-1), st.reshape(-1)
+
+
+@pytest.mark.parametrize("K", [256, 1152, 2048])
+def test_nvfp4_tile_w1_is_the_documented_permutation(K):
+    g = np.random.default_rng(K)
+    B, N = 2, 48
+    codes = g.integers(0, 256, size=(B, N, K // 2), dtype=np.uint8)
+    scales = g.integers(0, 256, size=(B, N, K // 16), dtype=np.uint8)
+    nbytes = mk.mk_nvfp4_w1_scales_bytes(B, N, K)
+    ct = torch.empty(B * N * K // 2, dtype=torch.uint8, device="cuda")
+    st = torch.full((nbytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    mk.mk_nvfp4_tile_w1(torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda(), B, N, K, ct, st)
+    torch.cuda.synchronize()
+    rc, rs = _tile_w1_reference(codes, scales, K)
+    assert np.array_equal(ct.cpu().numpy(), rc)
+    assert np.array_equal(st.cpu().numpy(), rs)
+    log(f"  W1 operand order, K = {K}: bit-exact permutation")
 
 
 def test_kv_append_bit_exact_and_untouched_rows():
@@ -149,7 +190,7 @@ def _check_layer(inp, out, n_sample_pairs=None):
 
 
 @pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83),
-                                           (SMALL_RW4, 84)])
+                                           (SMALL_RW4, 84), (SMALL_P1152, 85)])
 def test_layer_small_shapes(shape, cfg_id):
     log(f"[layer parity] {shape.name}")
     inp = synth.make_layer_inputs(shape, cfg_id)
