@@ -137,6 +137,23 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ int32_t dpp_i32(int32_t v) {
   return __builtin_amdgcn_update_dpp(v, v, CTRL, ROWS, 0xF, false);
 }
+// Maxima of a signed 32-bit value over each half (lanes 0-31, 32-63) of a wave (all lanes
+// active): lane 31 ends with the first half's, lane 63 with the second's.  Each step's DPP
+// move takes no old value (all rows written) or the max identity (row broadcast into rows 1
+// and 3 only), so the compiler folds it into the max as one DPP instruction.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_max_i32(int32_t v) {
+  const int32_t moved = ROWS == 0xF ? __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true)
+                                    : __builtin_amdgcn_update_dpp((int32_t)0x80000000, v, CTRL, ROWS, 0xF, false);
+  return max(v, moved);
+}
+__device__ __forceinline__ int32_t half_max_i32(int32_t v) {
+  v = dpp_max_i32<0xB1, 0xF>(v);        // quad_perm [1,0,3,2]
+  v = dpp_max_i32<0x4E, 0xF>(v);        // quad_perm [2,3,0,1]
+  v = dpp_max_i32<0x141, 0xF>(v);       // row_half_mirror
+  v = dpp_max_i32<0x140, 0xF>(v);       // row_mirror
+  return dpp_max_i32<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
+}
 __device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
   v = max(v, dpp_i32<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
   v = max(v, dpp_i32<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]

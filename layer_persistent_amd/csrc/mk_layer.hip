@@ -846,60 +846,66 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
   wg_sync();
   stamp<TS>(a.timestamps, 46, 0);
   const int lane = tid & 63, wave = tid >> 6;
-  // Top-k per token.  Wave w takes tokens w and w + 8 together (two independent chains).  A
-  // lane holds experts 4 lane .. 4 lane + 3 sorted by (logit desc, index asc); each round the
-  // wave's largest head wins (the lowest lane on ties, which holds the lowest index) and its
-  // lane pops it.  Lane j keeps round j's logit and expert.
+  // Top-k per token.  Wave w takes tokens w (lanes 0-31) and w + 8 (lanes 32-63), so one DPP
+  // reduction serves both.  Lane l of a half holds experts 8 (l % 32) .. + 7, sorted by (logit
+  // desc, index asc); each round a half's largest head wins (the lowest lane on ties, which
+  // holds the lowest index) and its lane pops it.  Lane j of the wave keeps round j's logits
+  // and experts of both tokens.
   for (int tA = wave; cw && tA < T; tA += 16) {
     const int tB = tA + 8;
-    const bool hasB = tB < T;                                    // uniform over the wave
+    const bool hi = lane >= 32;
+    const int t = hi ? tB : tA;
+    const bool tv = t < T;
     // logits as order-preserving integers (exact, so ties stay ties)
-    int32_t va[4], vb[4], ia[4], ib[4];
+    int32_t v[8], ix[8];
     constexpr int32_t kNone = (int32_t)0x80000000;               // below every logit
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = 4 * lane + q;
-      ia[q] = ib[q] = e;
-      va[q] = e < E ? f32_order_key(lg[tA * E + e]) : kNone;
-      vb[q] = (hasB && e < E) ? f32_order_key(lg[tB * E + e]) : kNone;
+    for (int q = 0; q < 8; ++q) {
+      const int e = 8 * (lane & 31) + q;
+      ix[q] = e;
+      v[q] = (tv && e < E) ? f32_order_key(lg[t * E + e]) : kNone;
     }
-    auto cswap = [](int32_t (&v)[4], int32_t (&ix)[4], int i, int j) {
+    auto cswap = [&](int i, int j) {
       const bool sw = v[j] > v[i] || (v[j] == v[i] && ix[j] < ix[i]);
-      const int32_t tv = v[i], ti = ix[i];
+      const int32_t tvv = v[i], ti = ix[i];
       v[i] = sw ? v[j] : v[i];
       ix[i] = sw ? ix[j] : ix[i];
-      v[j] = sw ? tv : v[j];
+      v[j] = sw ? tvv : v[j];
       ix[j] = sw ? ti : ix[j];
     };
-    auto sort4 = [&](int32_t (&v)[4], int32_t (&ix)[4]) {
-      cswap(v, ix, 0, 1); cswap(v, ix, 2, 3); cswap(v, ix, 0, 2); cswap(v, ix, 1, 3); cswap(v, ix, 1, 2);
-    };
-    auto pop = [](int32_t (&v)[4], int32_t (&ix)[4], bool take) {
-      v[0] = take ? v[1] : v[0]; ix[0] = take ? ix[1] : ix[0];
-      v[1] = take ? v[2] : v[1]; ix[1] = take ? ix[2] : ix[1];
-      v[2] = take ? v[3] : v[2]; ix[2] = take ? ix[3] : ix[2];
-      v[3] = take ? kNone : v[3];
-    };
-    sort4(va, ia);
-    sort4(vb, ib);
+    // Batcher's odd-even merge sort of 8 (19 comparators)
+    cswap(0, 1); cswap(2, 3); cswap(4, 5); cswap(6, 7);
+    cswap(0, 2); cswap(1, 3); cswap(4, 6); cswap(5, 7);
+    cswap(1, 2); cswap(5, 6);
+    cswap(0, 4); cswap(1, 5); cswap(2, 6); cswap(3, 7);
+    cswap(2, 4); cswap(3, 5);
+    cswap(1, 2); cswap(3, 4); cswap(5, 6);
     int32_t kA = 0, kB = 0, eA = 0, eB = 0;
     for (int j = 0; j < K; ++j) {
-      const int32_t xA = wave_max_i32(va[0]), xB = wave_max_i32(vb[0]);
-      const int lA = __ffsll((unsigned long long)__ballot(va[0] == xA)) - 1;
-      const int lB = __ffsll((unsigned long long)__ballot(vb[0] == xB)) - 1;
-      const int beA = __builtin_amdgcn_readlane(ia[0], lA), beB = __builtin_amdgcn_readlane(ib[0], lB);
-      pop(va, ia, lane == lA);
-      pop(vb, ib, lane == lB);
+      const int32_t m = half_max_i32(v[0]);
+      const int32_t xA = __builtin_amdgcn_readlane(m, 31), xB = __builtin_amdgcn_readlane(m, 63);
+      const uint64_t bal = __ballot(v[0] == (hi ? xB : xA));
+      const int lA = __ffs((unsigned)bal) - 1, lB = 32 + __ffs((unsigned)(bal >> 32)) - 1;
+      const int beA = __builtin_amdgcn_readlane(ix[0], lA), beB = __builtin_amdgcn_readlane(ix[0], lB);
+      const bool take = lane == lA || lane == lB;
+#pragma unroll
+      for (int q = 0; q < 7; ++q) {
+        v[q] = take ? v[q + 1] : v[q];
+        ix[q] = take ? ix[q + 1] : ix[q];
+      }
+      v[7] = take ? kNone : v[7];
       kA = lane == j ? xA : kA;
       eA = lane == j ? beA : eA;
       kB = lane == j ? xB : kB;
       eB = lane == j ? beB : eB;
     }
+    const bool hasB = tB < T;                                    // uniform over the wave
     const float mA = f32_from_order_key(kA), mB = f32_from_order_key(kB);
-    // gates: softmax over the k selected logits, summed in slot order
-    const float zA = __expf(mA - __shfl(mA, 0)), zB = __expf(mB - __shfl(mB, 0));
+    // gates: softmax over the k selected logits, summed in slot order (lane reads, no LDS)
+    auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+    const float zA = __expf(mA - rl(mA, 0)), zB = __expf(mB - rl(mB, 0));
     float sA = 0.f, sB = 0.f;
-    for (int j = 0; j < K; ++j) { sA += __shfl(zA, j); sB += __shfl(zB, j); }
+    for (int j = 0; j < K; ++j) { sA += rl(zA, j); sB += rl(zB, j); }
     if (lane < K) {
       rt.idx[tA * K + lane] = eA;
       rt.gate[tA * K + lane] = zA / sA;
@@ -1793,7 +1799,6 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       touched ^= expert_touch(a, blockIdx.x - a.attn_items, nwg - a.attn_items);
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
-      if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
       if (p_p && !pool_lds) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
       // the attention item's LDS is free now; the merge and output-projection phases use
       // LDS below POOL_LDS_OFF only (loads are waited for before the oproj hand-off)
@@ -1818,7 +1823,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         }
       }
     }
-    alive = phase_end<TS>(a, s, 2, &dead_sh, nop) && alive;
+    // the o-proj tile loads while the grid waits for the merge (issued during the attention
+    // hand-off instead, its 8 MB over the grid slowed that hand-off by ~2 us)
+    alive = phase_end<TS>(a, s, 2, &dead_sh, [&] { if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16); }) && alive;
     // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T)
     if (alive) {
       dense_phase(a, wo, p_o, a.w_o, a.attn, a.Hq * a.d, a.H, 0, red2, [&](int n0, const float* red, int it) {
