@@ -56,6 +56,10 @@ constexpr int MAXS_Q = 16;         // qkv      K = H    <= 4096
 #define MK_SYNC_MODE 0
 #endif
 constexpr int SYNC_MODE = MK_SYNC_MODE;   // grid hand-off: 1 sharded counters, 0 per-workgroup flags
+#ifndef MK_SYNC_COUNTERS
+#define MK_SYNC_COUNTERS 8
+#endif
+constexpr int kCounters = MK_SYNC_COUNTERS;   // sharded counters (mode 1), a power of two <= 64
 
 // dynamic LDS layout (byte offsets; phases reuse the same space)
 constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
@@ -138,17 +142,18 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
   const int n = gridDim.x;
   __builtin_amdgcn_s_waitcnt(0);           // this wave's hand-off stores are complete
   if constexpr (SYNC_MODE == 1) {
-    // Eight counters, one per XCD group (workgroup w adds to counter w % 8, 256 bytes
-    // apart); each add is fire-and-forget.  Counter j has grown by (epoch*8 + phase) * n_j
-    // once every member of group j has signalled `phase`, n_j = members of group j.
+    // kCounters counters (workgroup w adds to counter w % kCounters, 256 bytes apart); each
+    // add is fire-and-forget.  Counter j has grown by (epoch*8 + phase) * n_j once every
+    // member of group j has signalled `phase`, n_j = members of group j.
     if (lane == 0 && (int)blockIdx.x != s.skip_wg)
-      __hip_atomic_fetch_add(s.flags + (blockIdx.x & 7) * 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(s.flags + (blockIdx.x & (kCounters - 1)) * 64, 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     if (dead) return false;
-    const int j = lane & 7;
-    const uint32_t members = (uint32_t)((n - j + 7) / 8);
+    const int j = lane & (kCounters - 1);
+    const uint32_t members = (uint32_t)((n - j + kCounters - 1) / kCounters);
     const uint32_t target = (s.base / 64u * 8u + (uint32_t)phase) * members;
     const uint32_t* f = s.flags + j * 64;
-    auto poll = [&]() -> uint32_t { return lane < 8 ? ld_coh_u32(f) : target; };
+    auto poll = [&]() -> uint32_t { return lane < kCounters ? ld_coh_u32(f) : target; };
     auto done = [&](uint32_t x) { return __all((int32_t)(x - target) >= 0); };
     uint32_t a = poll(), b = poll();
     int polls = 0;
@@ -1800,9 +1805,6 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
       if (p_p && !pool_lds) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
-      // the attention item's LDS is free now; the merge and output-projection phases use
-      // LDS below POOL_LDS_OFF only (loads are waited for before the oproj hand-off)
-      if (pool_dma) lds_tile_dma(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF, tid >> 6, kCompute / 64);
     });
     // ---- 2 MERGE
     if (alive) {
@@ -1823,9 +1825,15 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         }
       }
     }
-    // the o-proj tile loads while the grid waits for the merge (issued during the attention
-    // hand-off instead, its 8 MB over the grid slowed that hand-off by ~2 us)
-    alive = phase_end<TS>(a, s, 2, &dead_sh, [&] { if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16); }) && alive;
+    // While the grid waits for the merge: the o-proj tile into registers, and the pooler tile of
+    // a workgroup that had an attention item into LDS (the merge and o-proj phases use LDS below
+    // POOL_LDS_OFF only; the loads are waited for before the o-proj hand-off).  Issued during
+    // the attention hand-off instead, each slowed that hand-off by ~2 us (the 8 MB o-proj
+    // prefetch over the grid, and even the 0.5 MB of pooler LDS-DMA on 4 workgroups).
+    alive = phase_end<TS>(a, s, 2, &dead_sh, [&] {
+      if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
+      if (pool_dma) lds_tile_dma(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF, tid >> 6, kCompute / 64);
+    }) && alive;
     // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T)
     if (alive) {
       dense_phase(a, wo, p_o, a.w_o, a.attn, a.Hq * a.d, a.H, 0, red2, [&](int n0, const float* red, int it) {
@@ -1941,7 +1949,8 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   // next launch's targets line up
   if constexpr (SYNC_MODE == 1) {
     if (tid == kCtl && tr.bad)
-      __hip_atomic_fetch_add(a.flags + (blockIdx.x & 7) * 64, 8u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(a.flags + (blockIdx.x & (kCounters - 1)) * 64, 8u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   // the next launch on this workspace uses the next epoch
   if (tid == kCtl) st_coh_u32(a.epoch + blockIdx.x * 16, epoch + 1);
