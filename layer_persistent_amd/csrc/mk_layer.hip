@@ -583,11 +583,14 @@ __device__ __forceinline__ void stage_store(const KArgs& a, int b, const StageRe
 // the running sum l and O^T rescaled by exp(m_old - m_new), then O^T += V^T P^T.  With one key
 // group per row tile the wave stores its partial (O unnormalised, m, l); otherwise the key
 // groups' partials of a row are combined in LDS, flash-decoding style, and stored once.
-// Called by all threads (contains workgroup barriers when the item is split over keys).
+// Called by all threads (contains workgroup barriers when the item is split over keys).  RW is
+// the item's row tiles (a.attn_rw), a template parameter so that the wave roles and the combine
+// compile to shifts and unrolled loops.
+template <int RW>
 __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, const AttnItem& it, char* smem,
                                                   const u32x4 qf[4]) {
   const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G, ck = a.ck;
-  const int rw = a.attn_rw, nkw = 8 / rw;
+  constexpr int rw = RW, nkw = 8 / RW;
   const int ks_stride = d + 8, vs = vt_stride(ck);
   const uint16_t* Ks = (const uint16_t*)smem;
   const uint32_t* VT = (const uint32_t*)(Ks + ck * ks_stride);
@@ -737,10 +740,12 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
       const int grow = (it.rb * rw + j) * 16 + r16;
       if (grow >= R) continue;
       float M = -INFINITY;
+#pragma unroll
       for (int q = 0; q < nkw; ++q) M = fmaxf(M, cml[((j + rw * q) * 16 + r16) * 2]);
       const float Ms = M == -INFINITY ? 0.f : M;
       float L = 0.f;
       f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int q = 0; q < nkw; ++q) {
         const int w = j + rw * q;
         const float sw = __expf(cml[(w * 16 + r16) * 2] - Ms);
@@ -1782,7 +1787,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       }
       wg_sync();
       if (first) stamp<TS>(a.timestamps, 37, 0);
-      attention_compute(a, tr, it, smem, qf);
+      switch (a.attn_rw) {                     // uniform over the grid
+        case 1: attention_compute<1>(a, tr, it, smem, qf); break;
+        case 2: attention_compute<2>(a, tr, it, smem, qf); break;
+        case 4: attention_compute<4>(a, tr, it, smem, qf); break;
+        default: attention_compute<8>(a, tr, it, smem, qf); break;
+      }
       if (first) stamp<TS>(a.timestamps, 38, 0);
       wg_sync();
     };
