@@ -507,10 +507,12 @@ __device__ __forceinline__ void attention_q(const KArgs& a, const AttnItem& it, 
   const int row = (it.rb * a.attn_rw + wave % a.attn_rw) * 16 + (lane & 15), grp = lane >> 4;
   const bool rv = threadIdx.x < kCompute && row < R;
   const int tok = rv ? row / G : 0, head = it.g * G + (rv ? row % G : 0);
+  // every lane loads, unconditionally (conditional loads would leave join copies that wait for
+  // every load in flight): a row outside the item reads row 0, whose finite values only reach
+  // scores that are masked for that row; k-steps past d/32 are never used
+  const uint16_t* q = a.q_in + (size_t)tok * a.Hq * d + head * d + grp * 8;
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    qf[s] = (s < d / 32 && rv) ? ld16(a.q_in + (size_t)tok * a.Hq * d + head * d + s * 32 + grp * 8)
-                               : u32x4{0, 0, 0, 0};
+  for (int s = 0; s < 4; ++s) qf[s] = ld16(q + (s < d / 32 ? s : 0) * 32);
 }
 
 __device__ __forceinline__ int vt_stride(int ck) { return ck / 2 + 2; }
@@ -535,23 +537,30 @@ __device__ __forceinline__ void stage_load(const KArgs& a, const AttnItem& it, i
   const size_t rstride = (size_t)a.Hkv * d;
   const uint16_t* kbase = a.kc + ((size_t)it.kb * a.Hkv + it.g) * d;
   const uint16_t* vbase = a.vc + ((size_t)it.kb * a.Hkv + it.g) * d;
+  // Every piece is loaded unconditionally from a valid address (a key past the chunk's rows
+  // reads its last row, a piece past the chunk reads piece 0); stage_store zeroes or skips
+  // those.  Conditional loads would leave join copies that wait for every load in flight.
+  const int klast = it.nk - 1;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int i = b * 4 * kCompute + tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
-    r.kv[j] = (i < kpieces && key < it.nk) ? ld16(kbase + key * rstride + c) : u32x4{0, 0, 0, 0};
+    int i = b * 4 * kCompute + tid + j * kCompute;
+    i = i < kpieces ? i : 0;
+    const int key = min(i / per_row, klast), c = (i % per_row) * 8;
+    r.kv[j] = ld16(kbase + key * rstride + c);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int i = b * 2 * kCompute + tid + j * kCompute, kp = i % nkp, c = (i / nkp) * 8;
-    const bool ok = i < vpieces;
-    r.v0[j] = (ok && 2 * kp < it.nk) ? ld16(vbase + (2 * kp) * rstride + c) : u32x4{0, 0, 0, 0};
-    r.v1[j] = (ok && 2 * kp + 1 < it.nk) ? ld16(vbase + (2 * kp + 1) * rstride + c) : u32x4{0, 0, 0, 0};
+    int i = b * 2 * kCompute + tid + j * kCompute;
+    i = i < vpieces ? i : 0;
+    const int kp = i % nkp, c = (i / nkp) * 8;
+    r.v0[j] = ld16(vbase + min(2 * kp, klast) * rstride + c);
+    r.v1[j] = ld16(vbase + min(2 * kp + 1, klast) * rstride + c);
   }
 }
 
 // LDS of an item (ck <= 256 keys): K row-major [ck][d + 8] bf16, then V transposed as key
 // pairs: VT32[dd][kp] = V[2kp][dd] | V[2kp+1][dd] << 16, row stride ck/2 + 2 dwords.
-__device__ __forceinline__ void stage_store(const KArgs& a, int b, const StageRegs& r, char* smem) {
+__device__ __forceinline__ void stage_store(const KArgs& a, const AttnItem& it, int b, const StageRegs& r, char* smem) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   if (tid >= kCompute) return;
@@ -563,16 +572,18 @@ __device__ __forceinline__ void stage_store(const KArgs& a, int b, const StageRe
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int i = b * 4 * kCompute + tid + j * kCompute, key = i / per_row, c = (i % per_row) * 8;
-    if (i < kpieces) *(u32x4*)(Ks + key * ks_stride + c) = r.kv[j];
+    if (i < kpieces) *(u32x4*)(Ks + key * ks_stride + c) = key < it.nk ? r.kv[j] : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = b * 2 * kCompute + tid + j * kCompute, kp = i % nkp, c = (i / nkp) * 8;
     if (i < vpieces) {
+      const u32x4 z = {0, 0, 0, 0};
+      const u32x4 a0 = 2 * kp < it.nk ? r.v0[j] : z, a1 = 2 * kp + 1 < it.nk ? r.v1[j] : z;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        VT[(c + 2 * q) * vs + kp] = (r.v0[j][q] & 0xFFFFu) | (r.v1[j][q] << 16);
-        VT[(c + 2 * q + 1) * vs + kp] = (r.v0[j][q] >> 16) | (r.v1[j][q] & 0xFFFF0000u);
+        VT[(c + 2 * q) * vs + kp] = (a0[q] & 0xFFFFu) | (a1[q] << 16);
+        VT[(c + 2 * q + 1) * vs + kp] = (a0[q] >> 16) | (a1[q] & 0xFFFF0000u);
       }
     }
   }
@@ -1718,10 +1729,17 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   u32x2 res = {0, 0};
   if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
 
-  if (tid < a.T) par_sh[tid] = a.parent[tid];
-  if (tid == kCtl) {
-    epoch_sh = ld_coh_u32(a.epoch + blockIdx.x * 16);
-    dead_sh = 0;
+  // the control wave reads the tree and this workgroup's epoch, both loads in flight together
+  // (wave 0 issues its attention loads meanwhile)
+  if (!cw) {
+    const int l = tid - kCtl;
+    const int32_t par = l < a.T ? a.parent[l] : 0;
+    const uint32_t ep = ld_coh_u32(a.epoch + blockIdx.x * 16);
+    if (l < a.T) par_sh[l] = par;
+    if (l == 0) {
+      epoch_sh = ep;
+      dead_sh = 0;
+    }
   }
   // the first attention item's queries and first K/V batch load during the setup
   u32x4 qf0[4];
@@ -1779,11 +1797,11 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- 1 ATTN
     // one item: stage (its first batch already loaded), compute, store the partials
     auto attn_item_run = [&](const AttnItem& it, const StageRegs& r0, const u32x4 qf[4], bool first) {
-      stage_store(a, 0, r0, smem);
+      stage_store(a, it, 0, r0, smem);
       for (int b = 1; b < stage_batches(a); ++b) {
         StageRegs r;
         stage_load(a, it, b, r);
-        stage_store(a, b, r, smem);
+        stage_store(a, it, b, r, smem);
       }
       wg_sync();
       if (first) stamp<TS>(a.timestamps, 37, 0);
