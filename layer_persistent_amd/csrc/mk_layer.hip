@@ -1159,45 +1159,46 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
     for (int j = 0; j < 8; ++j) if (j < hsteps && hf * hsteps + j < lsteps) cd[j] = ld16(cp + j * 1024);
     if (lane * 16 < 16 * srow_b) sv = ld16(a.w1_scales + (tile * nh + hf) * 16 * srow_b + lane * 16);
   };
-  // SwiGLU + requantisation of the round at unit u0 (nu units): thread (task, token row m)
+  // SwiGLU + requantisation of the round at unit u0 (nu units, nu even).  A wave takes one task
+  // (16 intermediate columns) at a time: lane = 4 m + q holds token row m, columns 4q..4q+3, so
+  // a 16-column block's E4M3 scale is a maximum over a lane quad (DPP) and its 64-bit code word
+  // is gathered into the quad's first lane.
   auto swiglu_round = [&](int u0, int nu) {
-    for (int o = tid; cw && o < (nu / 2) * 16; o += kCompute) {
-      const int tl = o >> 4, m = o & 15;
+    const int m = lane >> 2, q = lane & 3;
+    for (int tl = wave; cw && tl < nu / 2; tl += 8) {
       const int task = t_begin + u0 / 2 + tl;
       const int ai = task / jblocks, j0 = (task % jblocks) * 16;
-      if (m < rt.act_cnt[ai]) {
-        const int pair = rt.pair_list[rt.act_off[ai] + m];
-        // the two K halves of the gate unit (2 tl) and of the up unit (2 tl + 1)
-        const float* ug = ubuf + (4 * tl) * (16 * 17) + m * 17;
-        const float* uu = ubuf + (4 * tl + 2) * (16 * 17) + m * 17;
-        // NVFP4: the tensor scale, and undo the token row's power-of-two input scale (exact)
-        const float f = a.fmt == 1 ? rt.ts1[rt.act_expert[ai]] * __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23)
-                                   : 1.0f;
-        float v[16];
+      const bool valid = m < rt.act_cnt[ai];
+      const int pair = valid ? rt.pair_list[rt.act_off[ai] + m] : 0;
+      // the two K halves of the gate unit (2 tl) and of the up unit (2 tl + 1)
+      const float* ug = ubuf + (4 * tl) * (16 * 17) + m * 17 + 4 * q;
+      const float* uu = ubuf + (4 * tl + 2) * (16 * 17) + m * 17 + 4 * q;
+      // NVFP4: the tensor scale, and undo the token row's power-of-two input scale (exact)
+      const float f = a.fmt == 1 ? rt.ts1[rt.act_expert[ai]] * __uint_as_float((uint32_t)(127 - xk[pair / K]) << 23)
+                                 : 1.0f;
+      float v[4];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const float g = (ug[j] + ug[16 * 17 + j]) * f;
-          v[j] = g / (1.0f + __expf(-g)) * ((uu[j] + uu[16 * 17 + j]) * f);
+      for (int j = 0; j < 4; ++j) {
+        const float g = (ug[j] + ug[16 * 17 + j]) * f;
+        v[j] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * ((uu[j] + uu[16 * 17 + j]) * f);
+      }
+      if (a.fmt == 1) {
+        float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        amax = fmaxf(amax, dpp_f32<0xB1>(amax));   // quad_perm [1,0,3,2]
+        amax = fmaxf(amax, dpp_f32<0x4E>(amax));   // quad_perm [2,3,0,1]
+        const uint32_t sc = e4m3_code_of_amax_over6(amax);
+        const float sv = e4m3_to_f32(sc);
+        uint32_t c = 0;
+        if (sv > 0.f) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) c |= e2m1_code(v[j], sv) << (4 * j);
         }
-        if (a.fmt == 1) {
-          float amax = 0.f;
-#pragma unroll
-          for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
-          const uint32_t sc = e4m3_code_of_amax_over6(amax);
-          const float sv = e4m3_to_f32(sc);
-          uint32_t w0 = 0, w1 = 0;
-          if (sv > 0.f) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w0 |= e2m1_code(v[j], sv) << (4 * j);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) w1 |= e2m1_code(v[8 + j], sv) << (4 * j);
-          }
-          st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w0, w1, sc, 0u});
-        } else {
-          uint16_t* dst = a.act_bf + (size_t)pair * I + j0;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) st_coh_u64(dst + 4 * q, pack4_bf16(v + 4 * q));
-        }
+        // codes of columns 8h..8h+7 on lanes q = 2h; the odd lane's half shifted in
+        const uint32_t w = c | ((uint32_t)__builtin_amdgcn_update_dpp((int)c, (int)c, 0xB1, 0xF, 0xF, true) << 16);
+        const uint32_t w1 = (uint32_t)__builtin_amdgcn_update_dpp((int)w, (int)w, 0x4E, 0xF, 0xF, true);
+        if (valid && q == 0) st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w, w1, sc, 0u});
+      } else if (valid) {
+        st_coh_u64(a.act_bf + (size_t)pair * I + j0 + 4 * q, pack4_bf16(v));
       }
     }
   };
