@@ -211,6 +211,8 @@ def main():
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--dump-timestamps", default=None,
                     help="save the timing build's per-workgroup event ticks ([n_wg][64] int64, .npy)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-replay timing of the same K launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain elementwise copy of 256 MiB three times "
                          "(the known-size kernel that scales the HBM byte counters)")
@@ -308,6 +310,44 @@ def main():
     med_us = float(np.median(per))
     log(f"per launch: {kern_us:.2f} us over {K} back-to-back launches; with an event pair around each launch: "
         f"median {med_us:.2f} p10 {np.percentile(per, 10):.2f} p90 {np.percentile(per, 90):.2f}")
+    # the same K launches captured once in a HIP graph and replayed (the pages replay each
+    # verify step as one graph); outputs after the replays must equal the eager ones bit for bit
+    graph = None
+    if not args.no_graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            gsp = torch.cuda.current_stream().cuda_stream
+            for i in range(K):
+                c, w, io = structs[i % len(structs)]
+                rc = lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), gsp)
+                if rc != 0:
+                    raise RuntimeError(f"mk_layer_step (capture): {mk.mk_strerror(rc)}")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        reps_us = []
+        for _ in range(3):
+            g0.record(stream)
+            g.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            reps_us.append(g0.elapsed_time(g1) * 1000.0 / K)
+        for _, st in reps:
+            s = mk.mk_read_status(st.workspace)
+            if s != 0:
+                raise RuntimeError(f"in-kernel status after graph replay {mk.mk_strerror(s)}")
+        outg = dt.outputs(reps[0][1])
+        same = all(np.array_equal(outg[k], out[k]) for k in ("h_out", "q_next", "idx", "gate"))
+        if not same:
+            raise RuntimeError("graph replay outputs differ from the eager launch")
+        graph = {"us_per_launch_best": round(min(reps_us), 2), "us_per_launch_all": [round(x, 2) for x in reps_us],
+                 "launches_per_graph": K, "outputs_equal_eager": same}
+        log(f"graph replay of {K} launches: {min(reps_us):.2f} us per launch (best of 3)")
+        del g
     achieved = ab["total"] / (kern_us * 1e-6) / 1e9
     log(f"algorithmic bytes {ab['total'] / 1e6:.2f} MB ({n_active} active experts) -> {achieved:.0f} GB/s "
         f"= {achieved / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f} GB/s")
@@ -431,6 +471,7 @@ def main():
         "evented_launch_us": {"median": round(med_us, 2), "p10": round(float(np.percentile(per, 10)), 2),
                               "p90": round(float(np.percentile(per, 90)), 2),
                               "note": "an event pair around every launch adds ~3 us per launch"},
+        "graph_replay": graph,
         "phases_end_us": phases,
         "cpu_baseline": cpu,
     }
