@@ -416,6 +416,9 @@ def main():
             phases["attn_stage_us_max"] = round(float(((tsv[items, 37] - tsv[items, 1]) / 100.0).max()), 2)
             phases["attn_compute_us_max"] = round(float(((tsv[items, 38] - tsv[items, 37]) / 100.0).max()), 2)
             phases["attn_setup_end_max"] = round(float(((tsv[items, 1] - t0) / 100.0).max()), 2)
+            if (tsv[items, 39] > 0).all():
+                phases["attn_keyloop_us_max"] = round(float(((tsv[items, 39] - tsv[items, 37]) / 100.0).max()), 2)
+                phases["attn_combine_us_max"] = round(float(((tsv[items, 38] - tsv[items, 39]) / 100.0).max()), 2)
         g2 = tsv[:, 42] > 0
         if g2.any():
             d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)

@@ -83,7 +83,11 @@ __device__ __forceinline__ void wg_sync() {
 // Timestamp event `ev` of this workgroup, written by thread `who` (timing build only).
 // Events: 0 start, 1 setup done, 2p work of phase p done, 2p+1 its hand-off done (p = 1..8),
 // 18 routing tables built, 19 end, 20+p control wave's wait for phase p done, 28+p compute
-// waves' loads for a later phase issued, 37 / 38 first attention item staged / computed.
+// waves' loads for a later phase issued, 37 / 38 first attention item staged / computed,
+// 39 / 40 its key loop done / key groups' partials in LDS, 42 / 43 / 48 GEMM2 intermediate
+// staged / experts done / first register batch done, 44 / 45 GEMM1 input rows built / first
+// round multiplied, 46 / 47 routing logits staged / top-k done, 49 / 50 GEMM1 first pieces
+// requested / row scales known, 53+p control wave's hand-off stores of phase p complete.
 // Events are recorded in LDS and written out once at the end of the launch, so that the
 // timing build issues no global stores (and waits for none) while the phases run.
 __shared__ uint64_t ts_lds[MK_TS_EVENTS_DEV];
@@ -597,7 +601,7 @@ __device__ __forceinline__ void stage_store(const KArgs& a, const AttnItem& it, 
 // Called by all threads (contains workgroup barriers when the item is split over keys).  RW is
 // the item's row tiles (a.attn_rw), a template parameter so that the wave roles and the combine
 // compile to shifts and unrolled loops.
-template <int RW>
+template <int RW, bool TS>
 __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, const AttnItem& it, char* smem,
                                                   const u32x4 qf[4]) {
   const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G, ck = a.ck;
@@ -708,6 +712,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
       }
     }
   }
+  stamp<TS>(a.timestamps, 39, 0);
   const float lsum = xgroup_sum(lpart);
   const int slot = it.g * a.attn_chunks_per_head + it.chunk;
   if (nkw == 1) {
@@ -743,6 +748,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
     }
   }
   wg_sync();
+  stamp<TS>(a.timestamps, 40, 0);
   if (threadIdx.x < kCompute) {
     const int quads = d / 4;
     for (int e = threadIdx.x; e < rw * 16 * quads; e += kCompute) {
@@ -1082,6 +1088,7 @@ __device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t
 }
 
 // Part 2 (all threads; returns with the workgroup synchronised): the row scales and xs.
+template <bool TS>
 __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], uint16_t* xs, int xstride,
                                          const uint32_t* pmax, int32_t* xk) {
   const int T = a.T, tid = threadIdx.x, per_row = a.P / 8, n = T * per_row;
@@ -1097,6 +1104,7 @@ __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], ui
       if (lane == 0) xk[t] = m == 0 ? 0 : min(126, max(-126, 141 - (int)(m >> 7)));
     }
     wg_sync();
+    stamp<TS>(a.timestamps, 50, 0);
   }
   if (cw) {
 #pragma unroll
@@ -1147,20 +1155,30 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   const int hsteps = g1_hsteps(P);                               // load steps per piece (<= 8)
   const int srow_b = g1_sb(P);                                   // scale bytes per row and piece
   u32x4 cA[8], cB[8], sA, sB;
-  auto load_piece = [&](int u0, int pc, u32x4 (&cd)[8], u32x4& sv) {
-    const int u = pc / nh, hf = pc % nh;
+  // Piece pc of the round at unit u0 into cd / sv.  A piece that does not exist (`real` false)
+  // loads the first bytes of W1 at one address for all lanes instead: a few cache lines whose
+  // data is discarded.  Every lane of every wave thus issues the same loads in the same order
+  // whatever its pieces, which keeps the compiler's load counters exact: a piece is waited for
+  // while the next one stays in flight.  Past-the-end k-steps of a piece load its last k-step.
+  auto load_piece = [&](int u0, int pc, bool real, u32x4 (&cd)[8], u32x4& sv) {
+    const int pcr = real ? pc : 0;
+    const int u = pcr / nh, hf = pcr % nh;
     const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
     const int ai = task / jblocks, j0 = (task % jblocks) * 16;
     // W1 is in GEMM1's operand order: k-step ls of the 16-row tile is 1 KB, lane l's 16 B at
     // 16 l; the piece's scales are 16 rows x srow_b bytes, one contiguous block
     const size_t tile = ((size_t)rt.act_expert[ai] * 2 * I + half * I + j0) / 16;
-    const uint8_t* cp = a.w1_codes + (tile * lsteps + hf * hsteps) * 1024 + lane * 16;
+    const uint8_t* cp = real ? a.w1_codes + (tile * lsteps + hf * hsteps) * 1024 + lane * 16 : a.w1_codes;
+    const uint8_t* spp = real ? a.w1_scales + (tile * nh + hf) * 16 * srow_b + min(lane * 16, 16 * srow_b - 16)
+                              : a.w1_scales;
     // expert codes are read once per launch: non-temporal loads keep the stream from evicting
     // the hand-off activations every workgroup re-reads from L2 (about 1.5 us per layer)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < hsteps && hf * hsteps + j < lsteps) cd[j] = __builtin_nontemporal_load((const u32x4*)(cp + j * 1024));
-    if (lane * 16 < 16 * srow_b) sv = ld16(a.w1_scales + (tile * nh + hf) * 16 * srow_b + lane * 16);
+    for (int j = 0; j < 8; ++j) {
+      const int ls = min(hf * hsteps + min(j, hsteps - 1), lsteps - 1) - hf * hsteps;
+      cd[j] = __builtin_nontemporal_load((const u32x4*)(cp + (real ? ls : min(j, lsteps - 1)) * 1024));
+    }
+    sv = ld16(spp);
   };
   // SwiGLU + requantisation of the round at unit u0 (nu units, nu even).  A wave takes one task
   // (16 intermediate columns) at a time: lane = 4 m + q holds token row m, columns 4q..4q+3, so
@@ -1205,56 +1223,65 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
       }
     }
   };
-  // the first round's first piece is requested before the input rows are built
-  if (cw && a.fmt == 1 && wave < nh * min(G1_UNITS, nunits)) load_piece(0, wave, cA, sA);
-  xs_build(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
+  // The first round's first piece is requested before the input rows are built, by every wave
+  // (the control wave's is a dummy).  Nothing useful is in flight here: the explicit wait lets
+  // the compiler's load counters start from zero, so later waits count these loads exactly.
+  if (a.fmt == 1) {
+    __builtin_amdgcn_s_waitcnt(0);
+    load_piece(0, wave, cw && wave < nh * min(G1_UNITS, nunits), cA, sA);
+  }
+  stamp<TS>(a.timestamps, 49, 0);
+  xs_build<TS>(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
   stamp<TS>(a.timestamps, 44, 0);
   for (int u0 = 0; u0 < nunits; u0 += G1_UNITS) {
     const int nu = min(G1_UNITS, nunits - u0);
     if (cw && a.fmt == 1) {
       const int npc = nh * nu;
-      const int my = wave < npc ? (npc - 1 - wave) / 8 + 1 : 0;
-      if (my > 0 && u0 > 0) load_piece(u0, wave, cA, sA);
-#pragma unroll 1
-      for (int j = 0; j < my; j += 2) {
-        for (int x = 0; x < 2; ++x) {
-          const int jj = j + x;
-          if (jj >= my) break;
-          if (jj + 1 < my) {
-            if (x == 0) load_piece(u0, wave + 8 * (jj + 1), cB, sB); else load_piece(u0, wave + 8 * (jj + 1), cA, sA);
-          }
-          const int pc = wave + 8 * jj, u = pc / nh, hf = pc % nh;
-          const int task = t_begin + (u0 + u) / 2;
-          const int ai = task / jblocks;
-          const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
-          // the piece's scales into this wave's LDS buffer (wave-private: no barrier)
-          uint8_t* sd = sbuf + (wave * 2 + x) * 16 * srow_b;
-          if (lane * 16 < 16 * srow_b) *(u32x4*)(sd + lane * 16) = x == 0 ? sA : sB;
-          // rows past the expert's tokens read token 0 and are discarded after the product
-          const uint16_t* xrow = xs + (nl < cnt ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
-          const uint8_t* srow = sd + nl * srow_b + grp * 2;
-          const u32x4* cd = x == 0 ? cA : cB;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      const int my = wave < npc ? (npc - 1 - wave) / 8 + 1 : 0;     // this wave's pieces
+      const int mmax = (npc + 7) / 8;                                // wave 0's: uniform
+      if (u0 > 0) load_piece(u0, wave, wave < npc, cA, sA);
+      // piece jj of this wave (pc = wave + 8 jj) from cd / sv into ubuf[unit][half]; x picks
+      // the wave's scale buffer
+      auto piece_mma = [&](int jj, const u32x4 (&cd)[8], const u32x4& sv, int x) {
+        const int pc = wave + 8 * jj, u = pc / nh, hf = pc % nh;
+        const int task = t_begin + (u0 + u) / 2;
+        const int ai = task / jblocks;
+        const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
+        // the piece's scales into this wave's LDS buffer (wave-private: no barrier)
+        uint8_t* sd = sbuf + (wave * 2 + x) * 16 * srow_b;
+        if (lane * 16 < 16 * srow_b) *(u32x4*)(sd + lane * 16) = sv;
+        // rows past the expert's tokens read token 0 and are discarded after the product
+        const uint16_t* xrow = xs + (nl < cnt ? rt.pair_list[off + nl] / K : 0) * xstride + grp * 32;
+        const uint8_t* srow = sd + nl * srow_b + grp * 2;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const int ls = hf * hsteps + k;
-            if (k < hsteps && ls < lsteps) {
-              const uint32_t sc = *(const uint16_t*)(srow + k * 8);
-              const f16x2_t s0 = e4m3_to_f16x2(sc & 0xFF), s1 = e4m3_to_f16x2(sc >> 8);
+        for (int k = 0; k < 8; ++k) {
+          const int ls = hf * hsteps + k;
+          if (k < hsteps && ls < lsteps) {
+            const uint32_t sc = *(const uint16_t*)(srow + k * 8);
+            const f16x2_t s0 = e4m3_to_f16x2(sc & 0xFF), s1 = e4m3_to_f16x2(sc >> 8);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const u32x4 xa = *(const u32x4*)(xrow + ls * 128 + q * 8);
-                acc = mfma_f16(xa, fp4x8_to_f16(cd[k][q], q < 2 ? s0 : s1), acc);
-              }
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 xa = *(const u32x4*)(xrow + ls * 128 + q * 8);
+              acc = mfma_f16(xa, fp4x8_to_f16(cd[k][q], q < 2 ? s0 : s1), acc);
             }
           }
-          float* ub = ubuf + (2 * u + hf) * (16 * 17);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            ub[(4 * grp + r) * 17 + nl] = acc[r];
-            if (nh == 1) ub[16 * 17 + (4 * grp + r) * 17 + nl] = 0.f;
-          }
         }
+        float* ub = ubuf + (2 * u + hf) * (16 * 17);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          ub[(4 * grp + r) * 17 + nl] = acc[r];
+          if (nh == 1) ub[16 * 17 + (4 * grp + r) * 17 + nl] = 0.f;
+        }
+      };
+      // two pieces per trip, each loaded one piece ahead; the loads do not depend on which
+      // pieces exist, only the products do
+#pragma unroll 1
+      for (int j = 0; j < mmax; j += 2) {
+        load_piece(u0, wave + 8 * (j + 1), j + 1 < my, cB, sB);
+        if (j < my) piece_mma(j, cA, sA, 0);
+        load_piece(u0, wave + 8 * (j + 2), j + 2 < my, cA, sA);
+        if (j + 1 < my) piece_mma(j + 1, cB, sB, 1);
       }
     } else if (cw) {
       // bf16 experts: rows loaded as they are used
@@ -1811,10 +1838,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       wg_sync();
       if (first) stamp<TS>(a.timestamps, 37, 0);
       switch (a.attn_rw) {                     // uniform over the grid
-        case 1: attention_compute<1>(a, tr, it, smem, qf); break;
-        case 2: attention_compute<2>(a, tr, it, smem, qf); break;
-        case 4: attention_compute<4>(a, tr, it, smem, qf); break;
-        default: attention_compute<8>(a, tr, it, smem, qf); break;
+        case 1: attention_compute<1, TS>(a, tr, it, smem, qf); break;
+        case 2: attention_compute<2, TS>(a, tr, it, smem, qf); break;
+        case 4: attention_compute<4, TS>(a, tr, it, smem, qf); break;
+        default: attention_compute<8, TS>(a, tr, it, smem, qf); break;
       }
       if (first) stamp<TS>(a.timestamps, 38, 0);
       wg_sync();
