@@ -883,22 +883,23 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     const bool hi = lane >= 32;
     const int t = hi ? tB : tA;
     const bool tv = t < T;
-    // logits as order-preserving integers (exact, so ties stay ties)
-    int32_t v[8], ix[8];
-    constexpr int32_t kNone = (int32_t)0x80000000;               // below every logit
+    // Each candidate is one 64-bit word: the logit's order-preserving integer with its sign bit
+    // flipped (exact, so ties stay ties) above 0xFFFF - expert, so that a larger word comes
+    // first in (logit desc, index asc) order; 0 stands for no expert.  One unsigned compare
+    // then orders two candidates, with no branch on ties.
+    uint64_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int e = 8 * (lane & 31) + q;
-      ix[q] = e;
-      v[q] = (tv && e < E) ? f32_order_key(lg[t * E + e]) : kNone;
+      w[q] = (tv && e < E) ? ((uint64_t)((uint32_t)f32_order_key(lg[t * E + e]) ^ 0x80000000u) << 32) |
+                                 (uint32_t)(0xFFFF - e)
+                           : 0ull;
     }
     auto cswap = [&](int i, int j) {
-      const bool sw = v[j] > v[i] || (v[j] == v[i] && ix[j] < ix[i]);
-      const int32_t tvv = v[i], ti = ix[i];
-      v[i] = sw ? v[j] : v[i];
-      ix[i] = sw ? ix[j] : ix[i];
-      v[j] = sw ? tvv : v[j];
-      ix[j] = sw ? ti : ix[j];
+      const bool sw = w[j] > w[i];
+      const uint64_t x = w[i], y = w[j];
+      w[i] = sw ? y : x;
+      w[j] = sw ? x : y;
     };
     // Batcher's odd-even merge sort of 8 (19 comparators)
     cswap(0, 1); cswap(2, 3); cswap(4, 5); cswap(6, 7);
@@ -909,18 +910,17 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     cswap(1, 2); cswap(3, 4); cswap(5, 6);
     int32_t kA = 0, kB = 0, eA = 0, eB = 0;
     for (int j = 0; j < K; ++j) {
-      const int32_t m = half_max_i32(v[0]);
+      const int32_t head = (int32_t)((uint32_t)(w[0] >> 32) ^ 0x80000000u);   // the logit's key
+      const int32_t m = half_max_i32(head);
       const int32_t xA = __builtin_amdgcn_readlane(m, 31), xB = __builtin_amdgcn_readlane(m, 63);
-      const uint64_t bal = __ballot(v[0] == (hi ? xB : xA));
+      const uint64_t bal = __ballot(head == (hi ? xB : xA));
       const int lA = __ffs((unsigned)bal) - 1, lB = 32 + __ffs((unsigned)(bal >> 32)) - 1;
-      const int beA = __builtin_amdgcn_readlane(ix[0], lA), beB = __builtin_amdgcn_readlane(ix[0], lB);
+      const int lo = (int)(uint32_t)w[0];
+      const int beA = 0xFFFF - __builtin_amdgcn_readlane(lo, lA), beB = 0xFFFF - __builtin_amdgcn_readlane(lo, lB);
       const bool take = lane == lA || lane == lB;
 #pragma unroll
-      for (int q = 0; q < 7; ++q) {
-        v[q] = take ? v[q + 1] : v[q];
-        ix[q] = take ? ix[q + 1] : ix[q];
-      }
-      v[7] = take ? kNone : v[7];
+      for (int q = 0; q < 7; ++q) w[q] = take ? w[q + 1] : w[q];
+      w[7] = take ? 0ull : w[7];
       kA = lane == j ? xA : kA;
       eA = lane == j ? beA : eA;
       kB = lane == j ? xB : kB;
