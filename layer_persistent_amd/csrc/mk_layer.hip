@@ -1975,12 +1975,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         const uint64_t hv = pack4_bf16(v);
         st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, hv);     // the step's output, row-major
         st_coh_u64(a.h_frag + frag_off(crow, n0 + cc0), hv);          // the qkv phase's x
-      }, wu_lds ? smem + WU_LDS_OFF : nullptr, [&] {
-        // the qkv tile's weights load while the unpooler finishes and the grid hands off
-        if (p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
-      });
+      }, wu_lds ? smem + WU_LDS_OFF : nullptr);
     }
-    alive = phase_end<TS>(a, s, 8, &dead_sh, nop) && alive;
+    // the qkv tile's weights load while the grid hands off.  (Issued before the hand-off, the
+    // 128 KB per workgroup kept the issuing waves from the barrier until the CU's load queue
+    // drained, and the unpooler's hand-off ended about 2.5 us later on those workgroups.)
+    alive = phase_end<TS>(a, s, 8, &dead_sh, [&] { if (alive && p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16); }) && alive;
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
