@@ -170,6 +170,28 @@ def bench_stack(args) -> dict:
                 ev[L + 1].record(stream)
             torch.cuda.synchronize()
             layer_us.append([ev[L].elapsed_time(ev[L + 1]) * 1000.0 for L in range(n_layers)])
+        # the same steps with each step's launches replayed as one HIP graph (one graph per
+        # prefetch-list parity); the last step's output must equal its eager launches bit for bit
+        graph_us = []
+        if not args.no_graph:
+            graphs = [stk.capture_step(structs[parity]) for parity in (0, 1)]
+            for s in range(n_steps):
+                stk.set_step_inputs(ins[s], None if biases is None else biases[s])
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                graphs[s % 2].replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if s >= args.warmup:
+                    graph_us.append(e0.elapsed_time(e1) * 1000.0)
+            h_graph = stk.h_out().clone()
+            s = n_steps - 1
+            stk.set_step_inputs(ins[s], None if biases is None else biases[s])
+            stk.launch_step(structs[s % 2], sp)
+            torch.cuda.synchronize()
+            if not torch.equal(h_graph, stk.h_out()):
+                raise RuntimeError("stack graph replay differs from the eager launches")
+            del graphs
         st0 = mk_read_status_ok(stk)
         lu = np.array(layer_us)
         glob = [L for L in range(n_layers) if is_global(L)]
@@ -183,9 +205,11 @@ def bench_stack(args) -> dict:
                          layer_us_evented_mean=round(float(lu.mean()), 2),
                          swa_layer_us_mean=round(float(lu[:, swa].mean()), 2),
                          global_layer_us_mean=round(float(lu[:, glob].mean()), 2) if glob else None,
-                         last_layer_us_mean=round(float(lu[:, -1].mean()), 2), status=st0)
+                         last_layer_us_mean=round(float(lu[:, -1].mean()), 2), status=st0,
+                         graph_step_us_median=round(float(np.median(graph_us)), 1) if graph_us else None)
         log(f"{name}: step median {res[name]['step_us_median']} us, layer mean {res[name]['layer_us_mean']} us "
-            f"(SWA {res[name]['swa_layer_us_mean']}, global {res[name]['global_layer_us_mean']})")
+            f"(SWA {res[name]['swa_layer_us_mean']}, global {res[name]['global_layer_us_mean']}); "
+            f"replayed as one graph: step median {res[name]['graph_step_us_median']} us")
     return dict(results=res, n_active_last_step=n_active, n_layers=n_layers)
 
 

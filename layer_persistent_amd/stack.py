@@ -125,5 +125,19 @@ class Stack:
             if rc != 0:
                 raise abi.MKError(rc, "mk_layer_step")
 
+    def capture_step(self, structs) -> torch.cuda.CUDAGraph:
+        """One step's launches captured once as a HIP graph (the pages switch the stack on per
+        server flag and replay each verify step as one graph: orcarouter.ai write-up, "where the
+        5.9 ms still goes").  A replay runs the same launches on the stream it is replayed on;
+        the step's inputs are written into place (set_step_inputs) before each replay, and the
+        kernels keep their epoch in the workspace, so replays need no host-side state."""
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.graph(g, stream=side):
+            self.launch_step(structs, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.current_stream().wait_stream(side)
+        return g
+
     def h_out(self) -> torch.Tensor:
         return self.h[self.n_layers % 2]

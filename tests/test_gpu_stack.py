@@ -1,7 +1,7 @@
-"""GPU tests of the stack mechanics: the last-layer launch mode, and a stack of fused layers
+"""GPU tests of the stack mechanics: the last-layer launch mode, a stack of fused layers
 (global every fourth layer, the last one without a next-layer projection) checked layer by
 layer against the oracle and, run in one go by the stack runner, bit for bit against the
-layer-by-layer chain."""
+layer-by-layer chain, and the stack's verify step replayed as one HIP graph."""
 from __future__ import annotations
 
 import dataclasses
@@ -118,3 +118,52 @@ def test_small_stack_layer_by_layer_and_in_one_go():
             assert np.array_equal(kn, chain[L]["k_cache_next"].reshape(cap, -1)[ctx:ctx + T]), L
             assert np.array_equal(vn, chain[L]["v_cache_next"].reshape(cap, -1)[ctx:ctx + T]), L
     log("  stack in one go: bit-identical to the layer-by-layer chain")
+
+
+def _step_outputs(stk: Stack) -> dict:
+    T, ctx, cap = SMALL_STACK.T, SMALL_STACK.ctx, SMALL_STACK.kv_capacity
+    out = {"h_out": _host(stk.h_out())}
+    for L, lay in enumerate(stk.layers):
+        out[f"idx{L}"] = lay.topk_idx.cpu().numpy()
+        out[f"k{L}"] = _host(lay.k_cache).reshape(cap, -1)[ctx:ctx + T].copy()
+        out[f"v{L}"] = _host(lay.v_cache).reshape(cap, -1)[ctx:ctx + T].copy()
+    return out
+
+
+def test_stack_step_replayed_as_one_graph():
+    """The step's launches captured once; over three steps with different trees and inputs (the
+    inputs written eagerly, with a kernel launch, between replays) every replay equals the eager
+    launches of the same step bit for bit, and the graph is replayed again after eager work."""
+    stk = Stack(SMALL_STACK, CFG_ID, N_LAYERS)
+    stream = torch.cuda.current_stream()
+    structs = stk.structs(False, False)
+    # warm launch (kernel attributes set, code loaded) before capture
+    stk.set_step_inputs(synth.stack_step_inputs(SMALL_STACK, CFG_ID, 0))
+    stk.launch_step(structs, stream.cuda_stream)
+    torch.cuda.synchronize()
+    g = stk.capture_step(structs)
+    torch.cuda.synchronize()
+    for s in (1, 2, 3, 1):
+        step_in = synth.stack_step_inputs(SMALL_STACK, CFG_ID, s)
+        log(f"[graph step inputs {s}]")
+        stk.set_step_inputs(step_in)
+        stk.launch_step(structs, stream.cuda_stream)
+        torch.cuda.synchronize()
+        assert mk.mk_read_status(stk.ws) == 0
+        eager = _step_outputs(stk)
+        # wipe what the step writes, so that a replay that wrote nothing cannot pass
+        T, ctx, cap = SMALL_STACK.T, SMALL_STACK.ctx, SMALL_STACK.kv_capacity
+        for t in stk.h + stk.q:
+            t.zero_()
+        for lay in stk.layers:
+            lay.topk_idx.zero_()
+            lay.k_cache.view(cap, -1)[ctx:ctx + T].zero_()
+            lay.v_cache.view(cap, -1)[ctx:ctx + T].zero_()
+        stk.set_step_inputs(step_in)
+        g.replay()
+        torch.cuda.synchronize()
+        assert mk.mk_read_status(stk.ws) == 0
+        replay = _step_outputs(stk)
+        for key in eager:
+            assert np.array_equal(eager[key], replay[key]), (s, key)
+    log("  graph replays bit-identical to the eager launches")
