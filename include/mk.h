@@ -158,6 +158,21 @@ int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *
 int mk_kv_append(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int head_dim, int pos,
                  const void *k_new, const void *v_new, int n, void *stream);
 
+/* First-layer prologue.  The pages' first and last launches differ from the others
+ * (alphasignal.ai, "Draft and verify share one graph"; orcarouter.ai, "where the kernel
+ * boundary sits"): no launch before layer 0 produces its queries and tree K/V rows, so this
+ * call computes them from the tokens' embeddings.  [q; k; v] = h . w_qkv^T with one bf16
+ * rounding (fp32 accumulation): q -> q_out, k and v -> rows pos..pos+T-1 of layer 0's cache
+ * (every other row untouched).
+ * h bf16 [T][hidden]; w_qkv bf16 [(n_q_heads + 2 n_kv_heads) head_dim][hidden] (query rows,
+ * then key rows, then value rows); q_out bf16 [T][n_q_heads head_dim]; k_cache, v_cache bf16
+ * [capacity][n_kv_heads][head_dim].  1 <= T <= 16, hidden % 32 == 0, the output width a
+ * multiple of 16, n_kv_heads dividing n_q_heads; pos + T > capacity -> MK_ECAPACITY.
+ * Enqueues one kernel. */
+int mk_qkv_prologue(const void *h, const void *w_qkv, int T, int hidden, int n_q_heads, int n_kv_heads,
+                    int head_dim, void *q_out, void *k_cache, void *v_cache, int capacity, int pos,
+                    void *stream);
+
 /* Router on its own: logits = x . w_router^T (+ bias) in fp32, then the top-k experts per
  * token ordered by (logit desc, index asc) and softmax gates over the k selected logits.
  * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k];

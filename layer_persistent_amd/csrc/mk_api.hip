@@ -272,6 +272,21 @@ int mk_kv_append(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int
              ? MK_EHIP : MK_OK;
 }
 
+int mk_qkv_prologue(const void* h, const void* w_qkv, int T, int hidden, int n_q_heads, int n_kv_heads,
+                    int head_dim, void* q_out, void* k_cache, void* v_cache, int capacity, int pos, void* stream) {
+  if (!h || !w_qkv || !q_out || !k_cache || !v_cache) return MK_EINVAL;
+  if (T < 1 || T > 16 || hidden <= 0 || hidden % 32 || n_q_heads <= 0 || n_kv_heads <= 0 || head_dim <= 0 ||
+      n_q_heads % n_kv_heads || ((n_q_heads + 2 * n_kv_heads) * head_dim) % 16 || capacity <= 0)
+    return MK_ESHAPE;
+  if (pos < 0 || pos + T > capacity) return MK_ECAPACITY;
+  if (!aligned16(h) || !aligned16(w_qkv) || !aligned16(q_out) || !aligned16(k_cache) || !aligned16(v_cache))
+    return MK_EALIGN;
+  return mk::launch_qkv_prologue((const uint16_t*)h, (const uint16_t*)w_qkv, T, hidden, n_q_heads * head_dim,
+                                 n_kv_heads * head_dim, (uint16_t*)q_out, (uint16_t*)k_cache, (uint16_t*)v_cache,
+                                 pos, (hipStream_t)stream)
+             ? MK_EHIP : MK_OK;
+}
+
 int mk_route_topk(const void* x, const void* w_router, const float* bias, int T, int P, int E, int k,
                   int32_t* idx, float* gate, float* logits, void* stream) {
   if (!x || !w_router || !idx || !gate) return MK_EINVAL;

@@ -50,6 +50,52 @@ int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const u
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// ------------------------------------------------------------------ first-layer prologue
+
+// [q; k; v] = h W^T for the step's T <= 16 tokens: h bf16 [T][H] (the tokens' embeddings),
+// W bf16 [N][H] with N = qd + 2 kd (layer 0's query, key and value projections stacked); q
+// goes to q_out [T][qd], k and v to the cache rows pos..pos+T-1 ([capacity][kd]).  One
+// workgroup of 4 waves per 16 output columns: the 16 token rows are one MFMA tile, wave w takes
+// the 32-element k-steps w, w+4, ..., and the four partial tiles are summed in LDS in wave
+// order before the single bf16 rounding.  Rows past T are zero.
+__global__ void __launch_bounds__(256) qkv_prologue_kernel(const uint16_t* __restrict__ h,
+                                                           const uint16_t* __restrict__ w, int T, int H,
+                                                           int qd, int kd, uint16_t* __restrict__ q_out,
+                                                           uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                                           int pos) {
+  __shared__ float red[4][16][17];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 16, ksteps = H / 32;
+  const bool xv = nl < T;
+  const uint16_t* xrow = h + (size_t)(xv ? nl : 0) * H + 8 * g;
+  const uint16_t* wrow = w + (size_t)(n0 + nl) * H + 8 * g;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = wave; s < ksteps; s += 4) {
+    const u32x4 xa = xv ? *(const u32x4*)(xrow + 32 * s) : u32x4{0, 0, 0, 0};
+    acc = mfma_bf16(xa, *(const u32x4*)(wrow + 32 * s), acc);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][4 * g + r][nl] = acc[r];
+  __syncthreads();
+  const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
+  if (t < T) {
+    const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
+    const uint16_t b = (uint16_t)f2bf(v);
+    const int n = n0 + c;
+    if (n < qd) q_out[(size_t)t * qd + n] = b;
+    else if (n < qd + kd) kc[(size_t)(pos + t) * kd + (n - qd)] = b;
+    else vc[(size_t)(pos + t) * kd + (n - qd - kd)] = b;
+  }
+}
+
+int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int qd, int kd, uint16_t* q_out,
+                        uint16_t* kc, uint16_t* vc, int pos, hipStream_t stream) {
+  hipLaunchKernelGGL(qkv_prologue_kernel, dim3((qd + 2 * kd) / 16), dim3(256), 0, stream, h, w, T, H, qd, kd,
+                     q_out, kc, vc, pos);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 // ------------------------------------------------------------------ router top-k
 
 // One workgroup (256 threads) per token: fp32 logits by per-expert dot products, then the

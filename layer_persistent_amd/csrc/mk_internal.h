@@ -66,6 +66,8 @@ int set_layer_kernel_attrs(int lds_bytes);
 int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
 int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,
                      const uint16_t* vn, int n, hipStream_t stream);
+int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int qd, int kd, uint16_t* q_out,
+                        uint16_t* kc, uint16_t* vc, int pos, hipStream_t stream);
 int launch_route_topk(const uint16_t* x, const uint16_t* w, const float* bias, int T, int P, int E,
                       int k, int32_t* idx, float* gate, float* logits, hipStream_t stream);
 int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8_t* codes,

@@ -179,6 +179,21 @@ def usage_top(idx, n_experts: int, n: int = 14):
     return hist, np.array(top, dtype=np.int32)
 
 
+def qkv_project(h_bits, w_qkv_bits, n_q_heads: int, n_kv_heads: int, head_dim: int):
+    """The next layer's query / key / value projection (the launch's last step, and on its own
+    the first layer's prologue: the pages' first launch has no earlier launch to produce its
+    inputs): qkv = h . W^T in fp64, each part rounded once to bf16.  h bf16 [T][H]; W bf16
+    [(Hq + 2 Hkv) d][H], query rows, then key rows, then value rows.  Returns q [T][Hq d] and
+    k, v [T][Hkv][d] (bit patterns) and the fp64 products."""
+    qkv = bf16_to_f64(h_bits) @ bf16_to_f64(w_qkv_bits).T
+    T = qkv.shape[0]
+    qd, kd = n_q_heads * head_dim, n_kv_heads * head_dim
+    q = bf16_round(qkv[:, :qd])
+    k = bf16_round(qkv[:, qd:qd + kd]).reshape(T, n_kv_heads, head_dim)
+    v = bf16_round(qkv[:, qd + kd:]).reshape(T, n_kv_heads, head_dim)
+    return q, k, v, qkv
+
+
 def layer_step(inp, experts: dict, anchors: dict | None = None) -> dict:
     """The whole launch.  `inp` is a synth.LayerInputs.  `anchors` may replace a
     stage's input by another implementation's value (stage-local checks): keys
@@ -200,12 +215,7 @@ def layer_step(inp, experts: dict, anchors: dict | None = None) -> dict:
     y_in = a.get("y", y)
     h_out = dense(y_in, inp.w_unpool, h1_in)
     h_out_in = a.get("h_out", h_out)
-    qkv = bf16_to_f64(h_out_in) @ bf16_to_f64(inp.w_qkv_next).T
-    qd = sh.n_q_heads * sh.head_dim
-    kd = sh.n_kv_heads * sh.head_dim
-    q_next = bf16_round(qkv[:, :qd])
-    k_new = bf16_round(qkv[:, qd:qd + kd]).reshape(T, sh.n_kv_heads, sh.head_dim)
-    v_new = bf16_round(qkv[:, qd + kd:]).reshape(T, sh.n_kv_heads, sh.head_dim)
+    q_next, k_new, v_new, qkv = qkv_project(h_out_in, inp.w_qkv_next, sh.n_q_heads, sh.n_kv_heads, sh.head_dim)
     k_next = inp.k_cache_next.copy()
     v_next = inp.v_cache_next.copy()
     k_next[ctx:ctx + T] = k_new

@@ -94,6 +94,14 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_kv_append(GOOD, GOOD, 64, 1, 64, 62, GOOD, GOOD, 4, check=False) == mk.MK_ECAPACITY
     assert mk.mk_kv_append(GOOD, GOOD, 64, 1, 60, 0, GOOD, GOOD, 4, check=False) == mk.MK_ESHAPE
     assert mk.mk_kv_append(GOOD, BAD, 64, 1, 64, 0, GOOD, GOOD, 4, check=False) == mk.MK_EALIGN
+    # first-layer prologue: h, w_qkv, T, hidden, Hq, Hkv, d, q_out, k_cache, v_cache, capacity, pos
+    assert mk.mk_qkv_prologue(None, GOOD, 16, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_EINVAL
+    assert mk.mk_qkv_prologue(GOOD, GOOD, 17, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_ESHAPE
+    assert mk.mk_qkv_prologue(GOOD, GOOD, 0, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_ESHAPE
+    assert mk.mk_qkv_prologue(GOOD, GOOD, 16, 4080, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_ESHAPE
+    assert mk.mk_qkv_prologue(GOOD, GOOD, 16, 4096, 8, 3, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_ESHAPE
+    assert mk.mk_qkv_prologue(GOOD, GOOD, 16, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 49, check=False) == mk.MK_ECAPACITY
+    assert mk.mk_qkv_prologue(GOOD, BAD, 16, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_EALIGN
     assert mk.mk_route_topk(GOOD, GOOD, None, 16, 2048, 256, 9, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(GOOD, GOOD, None, 65, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(BAD, GOOD, None, 16, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_EALIGN

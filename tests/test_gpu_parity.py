@@ -115,6 +115,37 @@ def test_kv_append_bit_exact_and_untouched_rows():
     assert mk.mk_kv_append(K, V, cap, Hkv, d, cap - 2, KN, VN, n, check=False) == mk.MK_ECAPACITY
 
 
+@pytest.mark.parametrize("T,H,Hq,Hkv,d,cap,pos", [(16, 4096, 8, 1, 128, 8208, 8192),   # the shard shape
+                                                      (16, 256, 4, 1, 64, 320, 300),
+                                                      (5, 256, 8, 2, 64, 64, 59),        # ragged T, GQA
+                                                      (1, 128, 2, 1, 64, 8, 0)])
+def test_qkv_prologue_against_the_oracle(T, H, Hq, Hkv, d, cap, pos):
+    """First-layer prologue: q, and the k / v rows at pos..pos+T-1, against the oracle's qkv
+    projection (fp64, one rounding); every other cache row untouched."""
+    log(f"[qkv prologue T={T} H={H} Hq={Hq} Hkv={Hkv} d={d} pos={pos}]")
+    g = np.random.default_rng(24 + T)
+    h = synth.normal_bf16(g, (T, H), 1.0)
+    w = synth.normal_bf16(g, ((Hq + 2 * Hkv) * d, H), 0.02)
+    kc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+    vc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+    q_out = torch.zeros((T, Hq * d), dtype=torch.int16, device="cuda")
+    K, V = dt.dev_u16(kc), dt.dev_u16(vc)
+    mk.mk_qkv_prologue(dt.dev_u16(h), dt.dev_u16(w), T, H, Hq, Hkv, d, q_out, K, V, cap, pos)
+    torch.cuda.synchronize()
+    q_ref, k_ref, v_ref, _ = oracle.qkv_project(h, w, Hq, Hkv, d)
+    kg, vg = dt.host_u16(K), dt.host_u16(V)
+    assert_close_bf16("prologue q", dt.host_u16(q_out), q_ref)
+    assert_close_bf16("prologue k", kg[pos:pos + T], k_ref)
+    assert_close_bf16("prologue v", vg[pos:pos + T], v_ref)
+    rest = np.ones(cap, bool)
+    rest[pos:pos + T] = False
+    assert np.array_equal(kg[rest], kc[rest]) and np.array_equal(vg[rest], vc[rest])
+    # one rounding of an fp32 sum: nearly every element equals the fp64 oracle's rounding
+    exact = np.mean(dt.host_u16(q_out) == q_ref)
+    log(f"  q equal to the oracle's bf16 bit for bit: {exact:.4f} of elements")
+    assert exact > 0.95
+
+
 def test_route_topk_standalone():
     g = np.random.default_rng(23)
     T, P, E, k = 16, 2048, 256, 8
