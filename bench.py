@@ -136,14 +136,20 @@ def bench_stack(args) -> dict:
         variants = []
         for reuse in (0.8, 0.0):
             b = synth.stack_router_biases(shape, args.config, n_layers, n_steps, reuse)
-            variants += [(f"reuse{int(reuse * 100)}_noprefetch", b, False), (f"reuse{int(reuse * 100)}_prefetch", b, True)]
+            variants += [(f"reuse{int(reuse * 100)}_noprefetch", b, False, False),
+                         (f"reuse{int(reuse * 100)}_prefetch", b, True, False)]
     else:
-        variants = [("stack", None, False)]
+        # the step as given (layer 0's queries and tree K/V rows supplied), and the step from the
+        # tokens' embeddings with the first-layer prologue in front of layer 0
+        variants = [("stack", None, False, False), ("stack_from_embeddings", None, False, True)]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     res = {}
     n_active = None
-    for name, biases, pf in variants:
+    for name, biases, pf, prologue in variants:
+        if prologue and stk.w_qkv0 is None:
+            stk.w_qkv0 = synth.device_first_qkv_weight(shape, args.config, "cuda").view(torch.int16)
+        stk.prologue = prologue
         structs = [stk.structs(pf, biases is not None, parity) for parity in (0, 1)]
         step_us, layer_us = [], []
         for s in range(n_steps):
@@ -161,6 +167,8 @@ def bench_stack(args) -> dict:
             stk.set_step_inputs(ins[s], None if biases is None else biases[s])
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(n_layers + 1)]
             st = structs[s % 2]
+            if stk.prologue:
+                stk.launch_step([], sp)          # the prologue alone, outside the per-layer split
             ev[0].record(stream)
             for L in range(n_layers):
                 c, w, io = st[L]

@@ -55,43 +55,55 @@ int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const u
 // [q; k; v] = h W^T for the step's T <= 16 tokens: h bf16 [T][H] (the tokens' embeddings),
 // W bf16 [N][H] with N = qd + 2 kd (layer 0's query, key and value projections stacked); q
 // goes to q_out [T][qd], k and v to the cache rows pos..pos+T-1 ([capacity][kd]).  One
-// workgroup of 4 waves per 16 output columns: the 16 token rows are one MFMA tile, wave w takes
-// the 32-element k-steps w, w+4, ..., and the four partial tiles are summed in LDS in wave
-// order before the single bf16 rounding.  Rows past T are zero.
-__global__ void __launch_bounds__(256) qkv_prologue_kernel(const uint16_t* __restrict__ h,
-                                                           const uint16_t* __restrict__ w, int T, int H,
-                                                           int qd, int kd, uint16_t* __restrict__ q_out,
-                                                           uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
-                                                           int pos) {
-  __shared__ float red[4][16][17];
+// workgroup of 16 waves per 16 output columns: the 16 token rows are one MFMA tile, wave w
+// takes the 32-element k-steps w, w+16, ..., eight of them loaded together, and the 16 partial
+// tiles are summed in LDS in wave order before the single bf16 rounding.  Rows past T are zero.
+constexpr int kPrologueWaves = 16;
+__global__ void __launch_bounds__(64 * kPrologueWaves) qkv_prologue_kernel(
+    const uint16_t* __restrict__ h, const uint16_t* __restrict__ w, int T, int H, int qd, int kd,
+    uint16_t* __restrict__ q_out, uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, int pos) {
+  __shared__ float red[kPrologueWaves][16][17];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 16, ksteps = H / 32;
   const bool xv = nl < T;
   const uint16_t* xrow = h + (size_t)(xv ? nl : 0) * H + 8 * g;
   const uint16_t* wrow = w + (size_t)(n0 + nl) * H + 8 * g;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = wave; s < ksteps; s += 4) {
-    const u32x4 xa = xv ? *(const u32x4*)(xrow + 32 * s) : u32x4{0, 0, 0, 0};
-    acc = mfma_bf16(xa, *(const u32x4*)(wrow + 32 * s), acc);
+  for (int s0 = wave; s0 < ksteps; s0 += 8 * kPrologueWaves) {
+    u32x4 xa[8], wb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int s = s0 + kPrologueWaves * j;
+      const bool ok = s < ksteps;
+      xa[j] = (ok && xv) ? *(const u32x4*)(xrow + 32 * s) : u32x4{0, 0, 0, 0};
+      wb[j] = ok ? *(const u32x4*)(wrow + 32 * s) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (s0 + kPrologueWaves * j < ksteps) acc = mfma_bf16(xa[j], wb[j], acc);
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r) red[wave][4 * g + r][nl] = acc[r];
   __syncthreads();
-  const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
-  if (t < T) {
-    const float v = ((red[0][t][c] + red[1][t][c]) + red[2][t][c]) + red[3][t][c];
-    const uint16_t b = (uint16_t)f2bf(v);
-    const int n = n0 + c;
-    if (n < qd) q_out[(size_t)t * qd + n] = b;
-    else if (n < qd + kd) kc[(size_t)(pos + t) * kd + (n - qd)] = b;
-    else vc[(size_t)(pos + t) * kd + (n - qd - kd)] = b;
+  if (threadIdx.x < 256) {
+    const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (t < T) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < kPrologueWaves; ++q) v += red[q][t][c];
+      const uint16_t b = (uint16_t)f2bf(v);
+      const int n = n0 + c;
+      if (n < qd) q_out[(size_t)t * qd + n] = b;
+      else if (n < qd + kd) kc[(size_t)(pos + t) * kd + (n - qd)] = b;
+      else vc[(size_t)(pos + t) * kd + (n - qd - kd)] = b;
+    }
   }
 }
 
 int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int qd, int kd, uint16_t* q_out,
                         uint16_t* kc, uint16_t* vc, int pos, hipStream_t stream) {
-  hipLaunchKernelGGL(qkv_prologue_kernel, dim3((qd + 2 * kd) / 16), dim3(256), 0, stream, h, w, T, H, qd, kd,
+  hipLaunchKernelGGL(qkv_prologue_kernel, dim3((qd + 2 * kd) / 16), dim3(64 * kPrologueWaves), 0, stream, h, w, T,
+                     H, qd, kd,
                      q_out, kc, vc, pos);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

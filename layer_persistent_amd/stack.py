@@ -5,8 +5,10 @@ layer: orcarouter.ai write-up, "where the kernel boundary sits").
 Layer L's launch reads its own KV cache and writes the tree rows of layer L+1's cache, so the
 next launch finds them in place; h_out / q_next of layer L are h_in / q_in of layer L+1.
 Every fourth layer (0, 4, ..., 60) attends globally and the rest over a 2048-token window
-(46 + 16 of 62).  The last layer has no next-layer projection.  The caller supplies layer 0's
-inputs (queries, residual and its tree K/V rows), standing in for the embedding prologue.
+(46 + 16 of 62).  The last layer has no next-layer projection.  Layer 0's inputs come either
+from the caller (queries, residual and its tree K/V rows) or, with the prologue, from the step
+tokens' embeddings alone: a first launch (mk_qkv_prologue) computes layer 0's queries and
+tree K/V rows, as the pages' first launch differs from the others.
 
 This module only places tensors in HBM and fills the C-ABI structs; all arithmetic runs in
 libmk.so.
@@ -40,9 +42,14 @@ def is_global(layer: int) -> bool:
 
 class Stack:
     def __init__(self, shape: synth.LayerShape, cfg_id: int, n_layers: int = 62, device: str = "cuda",
-                 n_prefetch: int = 14):
+                 n_prefetch: int = 14, prologue: bool = False):
+        """With `prologue`, a step starts from the step tokens' embeddings: before layer 0's
+        launch, mk_qkv_prologue computes layer 0's queries and tree K/V rows from them with
+        layer 0's own qkv projection.  Without it the caller supplies those (stand-ins)."""
         self.shape, self.cfg_id, self.n_layers, self.device = shape, cfg_id, n_layers, device
         self.n_prefetch = n_prefetch
+        self.prologue = prologue
+        self.w_qkv0 = synth.device_first_qkv_weight(shape, cfg_id, device).view(torch.int16) if prologue else None
         sh = shape
         E, I, P, T, k = sh.n_experts, sh.expert_inter, sh.pooled, sh.T, sh.top_k
         u8 = dict(dtype=torch.uint8, device=device)
@@ -82,15 +89,18 @@ class Stack:
 
     def set_step_inputs(self, step_in: dict, bias: np.ndarray | None = None) -> None:
         """Layer 0's inputs for a step (host arrays from synth.stack_step_inputs), written into
-        place: the tree, h_in, q_in, and layer 0's tree K/V rows; router biases [L][T][E]."""
+        place: the tree and h_in (the step tokens' embeddings), and unless the stack runs the
+        prologue, q_in and layer 0's tree K/V rows; router biases [L][T][E]."""
         sh = self.shape
         self.parent.copy_(torch.from_numpy(step_in["parent"].astype(np.int32)))
         self.h[0].copy_(torch.from_numpy(step_in["h_in"].view(np.int16)))
-        self.q[0].copy_(torch.from_numpy(step_in["q_in"].view(np.int16)))
-        k0 = torch.from_numpy(step_in["k_tree"].view(np.int16)).to(self.device)
-        v0 = torch.from_numpy(step_in["v_tree"].view(np.int16)).to(self.device)
-        l0 = self.layers[0]
-        abi.mk_kv_append(l0.k_cache, l0.v_cache, sh.kv_capacity, sh.n_kv_heads, sh.head_dim, sh.ctx, k0, v0, sh.T)
+        if not self.prologue:
+            self.q[0].copy_(torch.from_numpy(step_in["q_in"].view(np.int16)))
+            k0 = torch.from_numpy(step_in["k_tree"].view(np.int16)).to(self.device)
+            v0 = torch.from_numpy(step_in["v_tree"].view(np.int16)).to(self.device)
+            l0 = self.layers[0]
+            abi.mk_kv_append(l0.k_cache, l0.v_cache, sh.kv_capacity, sh.n_kv_heads, sh.head_dim, sh.ctx, k0, v0,
+                             sh.T)
         if bias is not None:
             if self.bias is None:
                 self.bias = torch.empty(bias.shape, dtype=torch.float32, device=self.device)
@@ -120,6 +130,14 @@ class Stack:
         return out
 
     def launch_step(self, structs, stream_ptr) -> None:
+        if self.prologue:
+            sh, l0 = self.shape, self.layers[0]
+            rc = self.lib.mk_qkv_prologue(self.h[0].data_ptr(), self.w_qkv0.data_ptr(), sh.T, sh.hidden,
+                                          sh.n_q_heads, sh.n_kv_heads, sh.head_dim, self.q[0].data_ptr(),
+                                          l0.k_cache.data_ptr(), l0.v_cache.data_ptr(), sh.kv_capacity, sh.ctx,
+                                          stream_ptr)
+            if rc != 0:
+                raise abi.MKError(rc, "mk_qkv_prologue")
         for c, w, io in structs:
             rc = self.lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), stream_ptr)
             if rc != 0:

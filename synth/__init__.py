@@ -21,6 +21,7 @@ import numpy as np
 # tensor ids for np.random.default_rng([base, layer, tensor_id, expert])
 T_HIN, T_QIN, T_KCTX, T_VCTX, T_KTREE, T_VTREE = 0, 1, 2, 3, 4, 5
 T_WO, T_WP, T_WR, T_WU, T_WQKV = 10, 11, 12, 13, 14
+T_WQKV0 = 15        # layer 0's own qkv projection (the embedding prologue of a stack)
 T_W1, T_W2 = 20, 21
 T_TREE, T_BIAS, T_MARKOV, T_KNEXT = 30, 31, 32, 33
 
@@ -229,6 +230,12 @@ def device_layer_weights(shape: LayerShape, cfg_id: int, layer: int, device) -> 
     return dict(w_o=w(T_WO, (H, Hq * d)), w_pool=w(T_WP, (P, H)), w_router=w(T_WR, (E, P)),
                 w_unpool=w(T_WU, (H, P)), w_qkv_next=w(T_WQKV, (shape.qkv_out, H)),
                 w1=w(T_W1, (E, 2 * I, P)), w2=w(T_W2, (E, P, I)))
+
+
+def device_first_qkv_weight(shape: LayerShape, cfg_id: int, device):
+    """Layer 0's own qkv projection [qkv_out][H] bf16, drawn on the device: what a stack's
+    prologue applies to the step tokens' embeddings."""
+    return device_normal_bf16((shape.qkv_out, shape.hidden), 0.02, device, base_seed(cfg_id), 0, T_WQKV0)
 
 
 def device_kv_context(shape: LayerShape, cfg_id: int, layer: int, device):

@@ -167,3 +167,56 @@ def test_stack_step_replayed_as_one_graph():
         for key in eager:
             assert np.array_equal(eager[key], replay[key]), (s, key)
     log("  graph replays bit-identical to the eager launches")
+
+
+def test_stack_step_from_embeddings_with_the_prologue():
+    """A stack run with the first-layer prologue: layer 0's queries and tree K/V rows come
+    from mk_qkv_prologue on the step tokens' embeddings (checked against the oracle), and the
+    whole step, eager and replayed as one graph, equals the plain stack given those same
+    prologue outputs as its step inputs, bit for bit."""
+    sh = SMALL_STACK
+    T, ctx, cap, H, Hq, Hkv, d = sh.T, sh.ctx, sh.kv_capacity, sh.hidden, sh.n_q_heads, sh.n_kv_heads, sh.head_dim
+    stream = torch.cuda.current_stream()
+    stk_p = Stack(sh, CFG_ID, N_LAYERS, prologue=True)
+    step_in = synth.stack_step_inputs(sh, CFG_ID, 4)
+    # the prologue on its own
+    q0 = torch.zeros((T, Hq * d), dtype=torch.int16, device="cuda")
+    kc = torch.zeros((cap, Hkv, d), dtype=torch.int16, device="cuda")
+    vc = torch.zeros((cap, Hkv, d), dtype=torch.int16, device="cuda")
+    mk.mk_qkv_prologue(dt.dev_u16(step_in["h_in"]), stk_p.w_qkv0, T, H, Hq, Hkv, d, q0, kc, vc, cap, ctx)
+    torch.cuda.synchronize()
+    q_ref, k_ref, v_ref, _ = oracle.qkv_project(step_in["h_in"], _host(stk_p.w_qkv0), Hq, Hkv, d)
+    assert_close_bf16("prologue q", _host(q0), q_ref)
+    assert_close_bf16("prologue k", _host(kc)[ctx:ctx + T], k_ref)
+    assert_close_bf16("prologue v", _host(vc)[ctx:ctx + T], v_ref)
+    # the plain stack given the prologue's outputs
+    stk = Stack(sh, CFG_ID, N_LAYERS)
+    stk.set_step_inputs(dict(step_in, q_in=_host(q0), k_tree=_host(kc)[ctx:ctx + T], v_tree=_host(vc)[ctx:ctx + T]))
+    stk.launch_step(stk.structs(False, False), stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk.ws) == 0
+    ref = _step_outputs(stk)
+    # the prologue stack, eager, then replayed as one graph (prologue inside the graph)
+    structs = stk_p.structs(False, False)
+    stk_p.set_step_inputs(step_in)
+    stk_p.launch_step(structs, stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk_p.ws) == 0
+    got = _step_outputs(stk_p)
+    for key in ref:
+        assert np.array_equal(ref[key], got[key]), ("eager", key)
+    g = stk_p.capture_step(structs)
+    for t in stk_p.h + stk_p.q:
+        t.zero_()
+    for lay in stk_p.layers:
+        lay.topk_idx.zero_()
+        lay.k_cache.view(cap, -1)[ctx:ctx + T].zero_()
+        lay.v_cache.view(cap, -1)[ctx:ctx + T].zero_()
+    stk_p.set_step_inputs(step_in)
+    g.replay()
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk_p.ws) == 0
+    got = _step_outputs(stk_p)
+    for key in ref:
+        assert np.array_equal(ref[key], got[key]), ("graph", key)
+    log("  step from embeddings: eager and graph replay bit-identical to the plain stack")
