@@ -261,3 +261,70 @@ def test_qkv_project_matches_exact_per_element_dot_products():
             else:
                 got = v[t].reshape(-1)[n - (Hq + Hkv) * d]
             assert scalar.bits_to_float(int(got)) == ref, (t, n)
+
+
+def _accept_case(g, T, match_p):
+    """A random tree whose siblings carry distinct drafted tokens, and target tokens that
+    match one child with probability match_p."""
+    parent = synth.tree_parents(T, g)
+    draft = np.zeros(T, np.int64)
+    target = g.integers(1000, 2000, T)
+    for i in range(T):
+        kids = [c for c in range(1, T) if parent[c] == i]
+        toks = g.choice(np.arange(100, 200), size=len(kids), replace=False)
+        draft[kids] = toks
+        if kids and g.random() < match_p:
+            target[i] = toks[g.integers(len(kids))]
+    return parent, draft, target
+
+
+def test_tree_accept_is_the_deepest_consistent_node():
+    """Brute force: with distinct sibling tokens, the nodes whose every edge from the root
+    matches (child's draft == target at its parent) form one chain; the accepted path is that
+    chain, and the bonus is the target's token at its end."""
+    g = np.random.default_rng(7)
+    for trial in range(300):
+        T = int(g.integers(1, 17))
+        parent, draft, target = _accept_case(g, T, float(g.random()))
+        def consistent(n):
+            while n != 0:
+                if draft[n] != target[parent[n]]:
+                    return False
+                n = parent[n]
+            return True
+        chain = [n for n in range(T) if consistent(n)]
+        path, bonus = oracle.tree_accept(parent, draft, target)
+        assert path == sorted(chain), (trial, path, chain)
+        assert all(parent[b] == a for a, b in zip(path, path[1:]))
+        assert bonus == target[path[-1]]
+
+
+def test_tree_accept_special_cases():
+    # a chain whose every draft matches: all of it, then the target after the leaf
+    T = 7
+    parent = np.arange(-1, T - 1)
+    target = np.arange(10, 10 + T)
+    draft = np.concatenate([[0], target[:-1]])
+    path, bonus = oracle.tree_accept(parent, draft, target)
+    assert path == list(range(T)) and bonus == target[-1]
+    # nothing matches: the root alone, and its target token
+    path, bonus = oracle.tree_accept(parent, draft + 1, target)
+    assert path == [0] and bonus == target[0]
+    # two siblings with the same token: the lower index is taken
+    parent = np.array([-1, 0, 0])
+    path, _ = oracle.tree_accept(parent, np.array([0, 5, 5]), np.array([5, 1, 2]))
+    assert path == [0, 1]
+
+
+def test_kv_commit_is_a_row_gather():
+    g = np.random.default_rng(8)
+    cap, ctx = 40, 20
+    k = synth.normal_bf16(g, (cap, 2, 8), 1.0)
+    v = synth.normal_bf16(g, (cap, 2, 8), 1.0)
+    path = [0, 2, 5, 9]
+    kc, vc = oracle.kv_commit(k, v, ctx, path)
+    for j, node in enumerate(path):
+        assert np.array_equal(kc[ctx + j], k[ctx + node]) and np.array_equal(vc[ctx + j], v[ctx + node])
+    rest = np.ones(cap, bool)
+    rest[ctx:ctx + len(path)] = False
+    assert np.array_equal(kc[rest], k[rest]) and np.array_equal(vc[rest], v[rest])
