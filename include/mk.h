@@ -173,6 +173,29 @@ int mk_qkv_prologue(const void *h, const void *w_qkv, int T, int hidden, int n_q
                     int head_dim, void *q_out, void *k_cache, void *v_cache, int capacity, int pos,
                     void *stream);
 
+/* Greedy acceptance after a verify step (the pages decode greedily and keep the accepted part
+ * of a 16-token tree: orcarouter.ai, "what the number is and isn't"; the rule itself is not
+ * printed, the plain greedy one is taken).  From the root (node 0), repeatedly follow the
+ * lowest-index child whose drafted token equals the target's greedy token at the current
+ * node; stop when no child does.
+ * parent int32 [T] (as in mk_step_io: parent[0] = -1, parent[i] < i); draft int32 [T] (each
+ * node's token; node 0's is the last accepted token); target int32 [T] (the target model's
+ * greedy token after each node).  Outputs: path int32 [T] (accepted nodes root-first, then -1),
+ * n_path int32 [1] (>= 1), bonus int32 [1] (the target token after the last accepted node).
+ * A malformed tree gives n_path = 0, bonus = -1 and path all -1.  1 <= T <= 64.  Enqueues one
+ * kernel; nothing is read back, so the call can sit in a captured step graph. */
+int mk_tree_accept(const int32_t *parent, const int32_t *draft, const int32_t *target, int T, int32_t *path,
+                   int32_t *n_path, int32_t *bonus, void *stream);
+
+/* KV commit of an accepted path in one layer's cache pair: row ctx + path[j] moves to row
+ * ctx + j for j < *n_path (read on the device; values above T are clamped to T), every other
+ * row untouched.  All source rows are read before any is written.  k_cache, v_cache bf16
+ * [capacity][n_kv_heads][head_dim]; path, n_path as written by mk_tree_accept.  1 <= T <= 64,
+ * 2 T n_kv_heads head_dim <= 16384, ctx + T <= capacity.  Enqueues one kernel per call (one
+ * call per layer). */
+int mk_kv_commit(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int head_dim, int ctx,
+                 const int32_t *path, const int32_t *n_path, int T, void *stream);
+
 /* Router on its own: logits = x . w_router^T (+ bias) in fp32, then the top-k experts per
  * token ordered by (logit desc, index asc) and softmax gates over the k selected logits.
  * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k];

@@ -17,7 +17,7 @@ MK_W_BF16, MK_W_NVFP4 = 0, 1
 MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step",
-            "mk_kv_append", "mk_qkv_prologue", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
+            "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
             "mk_read_status", "mk_strerror"]
 
 
@@ -72,6 +72,8 @@ def lib() -> C.CDLL:
         L.mk_kv_append.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_qkv_prologue.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int,
                                       C.c_int, P]
+        L.mk_tree_accept.argtypes = [P, P, P, C.c_int, P, P, P, P]
+        L.mk_kv_commit.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_route_topk.argtypes = [P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.mk_nvfp4_pack.argtypes = [P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.mk_nvfp4_tile_w1.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P, P]
@@ -81,6 +83,7 @@ def lib() -> C.CDLL:
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_kv_append", "mk_qkv_prologue",
+                     "mk_tree_accept", "mk_kv_commit",
                      "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_read_status"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -144,6 +147,18 @@ def mk_qkv_prologue(h, w_qkv, T, hidden, n_q_heads, n_kv_heads, head_dim, q_out,
     rc = lib().mk_qkv_prologue(_ptr(h), _ptr(w_qkv), T, hidden, n_q_heads, n_kv_heads, head_dim, _ptr(q_out),
                                _ptr(k_cache), _ptr(v_cache), capacity, pos, _stream(stream))
     return _check(rc, "mk_qkv_prologue") if check else rc
+
+
+def mk_tree_accept(parent, draft, target, T, path, n_path, bonus, stream=None, check=True):
+    rc = lib().mk_tree_accept(_ptr(parent), _ptr(draft), _ptr(target), T, _ptr(path), _ptr(n_path), _ptr(bonus),
+                              _stream(stream))
+    return _check(rc, "mk_tree_accept") if check else rc
+
+
+def mk_kv_commit(k_cache, v_cache, capacity, n_kv_heads, head_dim, ctx, path, n_path, T, stream=None, check=True):
+    rc = lib().mk_kv_commit(_ptr(k_cache), _ptr(v_cache), capacity, n_kv_heads, head_dim, ctx, _ptr(path),
+                            _ptr(n_path), T, _stream(stream))
+    return _check(rc, "mk_kv_commit") if check else rc
 
 
 def mk_kv_append(k_cache, v_cache, capacity, n_kv_heads, head_dim, pos, k_new, v_new, n, stream=None, check=True):

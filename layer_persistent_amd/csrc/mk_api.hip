@@ -287,6 +287,26 @@ int mk_qkv_prologue(const void* h, const void* w_qkv, int T, int hidden, int n_q
              ? MK_EHIP : MK_OK;
 }
 
+int mk_tree_accept(const int32_t* parent, const int32_t* draft, const int32_t* target, int T, int32_t* path,
+                   int32_t* n_path, int32_t* bonus, void* stream) {
+  if (!parent || !draft || !target || !path || !n_path || !bonus) return MK_EINVAL;
+  if (T < 1 || T > 64) return MK_ESHAPE;
+  return mk::launch_tree_accept(parent, draft, target, T, path, n_path, bonus, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
+int mk_kv_commit(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int head_dim, int ctx,
+                 const int32_t* path, const int32_t* n_path, int T, void* stream) {
+  if (!k_cache || !v_cache || !path || !n_path) return MK_EINVAL;
+  if (n_kv_heads <= 0 || head_dim <= 0 || (n_kv_heads * head_dim) % 8 || T < 1 || T > 64 ||
+      (size_t)2 * T * n_kv_heads * head_dim * 2 > 65536 || capacity <= 0)
+    return MK_ESHAPE;
+  if (ctx < 0 || ctx + T > capacity) return MK_ECAPACITY;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return MK_EALIGN;
+  return mk::launch_kv_commit((uint16_t*)k_cache, (uint16_t*)v_cache, n_kv_heads * head_dim, ctx, path, n_path, T,
+                              (hipStream_t)stream)
+             ? MK_EHIP : MK_OK;
+}
+
 int mk_route_topk(const void* x, const void* w_router, const float* bias, int T, int P, int E, int k,
                   int32_t* idx, float* gate, float* logits, void* stream) {
   if (!x || !w_router || !idx || !gate) return MK_EINVAL;

@@ -108,6 +108,87 @@ int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int 
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
+// ------------------------------------------------------------------ acceptance and KV commit
+
+// Greedy acceptance along the verified tree, one wave: lane i holds node i's parent, drafted
+// token and target token.  From the root, each round takes the lowest-index child of the
+// current node whose drafted token equals the target token at the current node (a ballot);
+// the walk stops when none does.  path[0..n) = accepted nodes root-first, the rest -1;
+// bonus = the target token at the last accepted node.  A malformed tree accepts nothing
+// (n = 0, bonus = -1).
+__global__ void __launch_bounds__(64) tree_accept_kernel(const int32_t* __restrict__ parent,
+                                                         const int32_t* __restrict__ draft,
+                                                         const int32_t* __restrict__ target, int T,
+                                                         int32_t* __restrict__ path, int32_t* __restrict__ n_path,
+                                                         int32_t* __restrict__ bonus) {
+  const int lane = threadIdx.x;
+  const bool in = lane < T;
+  const int32_t p = in ? parent[lane] : -2;
+  const int32_t dr = in ? draft[lane] : 0;
+  const int32_t tg = in ? target[lane] : 0;
+  const bool ok = !in || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+  const bool bad = __ballot(!ok) != 0;
+  int cur = 0, n = 1;
+  int32_t mine = lane == 0 ? 0 : -1;             // lane j keeps path[j]
+  if (!bad) {
+    for (int r = 1; r < T; ++r) {
+      const int32_t want = __shfl(tg, cur);
+      const uint64_t hit = __ballot(in && lane > 0 && p == cur && dr == want);
+      if (hit == 0) break;
+      cur = __ffsll((unsigned long long)hit) - 1;
+      mine = lane == n ? cur : mine;
+      ++n;
+    }
+  }
+  const int32_t last = __shfl(tg, cur);           // every lane takes part in the shuffle
+  if (in) path[lane] = bad ? -1 : mine;
+  if (lane == 0) {
+    *n_path = bad ? 0 : n;
+    *bonus = bad ? -1 : last;
+  }
+}
+
+// KV commit of an accepted path in one layer's cache pair: row ctx + path[j] -> row ctx + j for
+// j < n (n read on the device).  Every source row is read into LDS before any row is written,
+// so the moves may overlap.  One workgroup; rows are row_elems bf16 (a multiple of 8).
+__global__ void __launch_bounds__(256) kv_commit_kernel(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                                        int row_elems, int ctx, const int32_t* __restrict__ path,
+                                                        const int32_t* __restrict__ n_path, int T) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  u32x4* buf = (u32x4*)lds;                       // [2][T][row_elems / 8]
+  const int n = min(max(*n_path, 0), T);
+  const int per = row_elems / 8, total = n * per;
+  // a path entry outside [0, T) (not one mk_tree_accept writes) moves nothing
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int j = i / per, c = i % per, pj = path[j];
+    if (pj < 0 || pj >= T) continue;
+    const size_t src = (size_t)(ctx + pj) * row_elems + 8 * c;
+    buf[i] = *(const u32x4*)(kc + src);
+    buf[T * per + i] = *(const u32x4*)(vc + src);
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < total; i += blockDim.x) {
+    const int j = i / per, c = i % per, pj = path[j];
+    if (pj < 0 || pj >= T) continue;
+    const size_t dst = (size_t)(ctx + j) * row_elems + 8 * c;
+    *(u32x4*)(kc + dst) = buf[i];
+    *(u32x4*)(vc + dst) = buf[T * per + i];
+  }
+}
+
+int launch_tree_accept(const int32_t* parent, const int32_t* draft, const int32_t* target, int T, int32_t* path,
+                       int32_t* n_path, int32_t* bonus, hipStream_t stream) {
+  hipLaunchKernelGGL(tree_accept_kernel, dim3(1), dim3(64), 0, stream, parent, draft, target, T, path, n_path, bonus);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+int launch_kv_commit(uint16_t* kc, uint16_t* vc, int row_elems, int ctx, const int32_t* path, const int32_t* n_path,
+                     int T, hipStream_t stream) {
+  const size_t lds = (size_t)2 * T * row_elems * 2;
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(1), dim3(256), lds, stream, kc, vc, row_elems, ctx, path, n_path, T);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 // ------------------------------------------------------------------ router top-k
 
 // One workgroup (256 threads) per token: fp32 logits by per-expert dot products, then the

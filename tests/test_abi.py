@@ -102,6 +102,14 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_qkv_prologue(GOOD, GOOD, 16, 4096, 8, 3, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_ESHAPE
     assert mk.mk_qkv_prologue(GOOD, GOOD, 16, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 49, check=False) == mk.MK_ECAPACITY
     assert mk.mk_qkv_prologue(GOOD, BAD, 16, 4096, 8, 1, 128, GOOD, GOOD, GOOD, 64, 0, check=False) == mk.MK_EALIGN
+    assert mk.mk_tree_accept(None, GOOD, GOOD, 16, GOOD, GOOD, GOOD, check=False) == mk.MK_EINVAL
+    assert mk.mk_tree_accept(GOOD, GOOD, GOOD, 65, GOOD, GOOD, GOOD, check=False) == mk.MK_ESHAPE
+    assert mk.mk_tree_accept(GOOD, GOOD, GOOD, 0, GOOD, GOOD, GOOD, check=False) == mk.MK_ESHAPE
+    assert mk.mk_kv_commit(GOOD, GOOD, 64, 1, 128, 0, None, GOOD, 16, check=False) == mk.MK_EINVAL
+    assert mk.mk_kv_commit(GOOD, GOOD, 64, 1, 128, 50, GOOD, GOOD, 16, check=False) == mk.MK_ECAPACITY
+    assert mk.mk_kv_commit(GOOD, GOOD, 64, 1, 60, 0, GOOD, GOOD, 16, check=False) == mk.MK_ESHAPE
+    assert mk.mk_kv_commit(GOOD, GOOD, 4096, 8, 1024, 0, GOOD, GOOD, 16, check=False) == mk.MK_ESHAPE
+    assert mk.mk_kv_commit(BAD, GOOD, 64, 1, 128, 0, GOOD, GOOD, 16, check=False) == mk.MK_EALIGN
     assert mk.mk_route_topk(GOOD, GOOD, None, 16, 2048, 256, 9, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(GOOD, GOOD, None, 65, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(BAD, GOOD, None, 16, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_EALIGN

@@ -146,6 +146,52 @@ def test_qkv_prologue_against_the_oracle(T, H, Hq, Hkv, d, cap, pos):
     assert exact > 0.95
 
 
+def test_tree_accept_and_kv_commit_against_the_oracle():
+    """Greedy acceptance on seeded trees (the verification tree generator, tokens drawn so
+    that the walk stops at every depth) equals the oracle's path and bonus exactly, and the
+    KV commit of that path equals the oracle's row moves bit for bit with every other row
+    untouched; n_path is read on the device.  A malformed tree accepts nothing."""
+    g = np.random.default_rng(31)
+    cap, Hkv, d, ctx = 96, 1, 128, 70
+    dev_i32 = lambda a: torch.from_numpy(np.asarray(a, np.int32)).cuda()
+    path = torch.empty(16, dtype=torch.int32, device="cuda")
+    n_path = torch.empty(1, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(1, dtype=torch.int32, device="cuda")
+    depths = set()
+    for trial in range(40):
+        T = 16 if trial % 4 else int(g.integers(1, 17))
+        parent = synth.tree_parents(T, g) if T > 1 else np.array([-1], np.int32)
+        draft = g.integers(100, 110, T).astype(np.int32)
+        target = g.integers(100, 110, T).astype(np.int32)
+        # make the walk go deep in some trials: copy each first child's token to its parent
+        if trial % 3 == 0:
+            for i in range(T):
+                kids = [c for c in range(1, T) if parent[c] == i]
+                if kids:
+                    target[i] = draft[kids[-1]]
+        mk.mk_tree_accept(dev_i32(parent), dev_i32(draft), dev_i32(target), T, path, n_path, bonus)
+        kc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+        vc = synth.normal_bf16(g, (cap, Hkv, d), 1.0)
+        K, V = dt.dev_u16(kc), dt.dev_u16(vc)
+        mk.mk_kv_commit(K, V, cap, Hkv, d, ctx, path, n_path, T)
+        torch.cuda.synchronize()
+        ref_path, ref_bonus = oracle.tree_accept(parent, draft, target)
+        n = int(n_path.item())
+        assert n == len(ref_path), (trial, n, ref_path)
+        gp = path.cpu().numpy()[:T]
+        assert gp[:n].tolist() == ref_path and np.all(gp[n:] == -1), (trial, gp, ref_path)
+        assert int(bonus.item()) == ref_bonus
+        ek, ev = oracle.kv_commit(kc, vc, ctx, ref_path)
+        assert np.array_equal(dt.host_u16(K), ek) and np.array_equal(dt.host_u16(V), ev), trial
+        depths.add(n)
+    log(f"  accepted path lengths seen: {sorted(depths)}")
+    assert len(depths) >= 4
+    bad = np.array([-1, 0, 3, 1], np.int32)
+    mk.mk_tree_accept(dev_i32(bad), dev_i32([1, 2, 3, 4]), dev_i32([2, 3, 4, 5]), 4, path, n_path, bonus)
+    torch.cuda.synchronize()
+    assert int(n_path.item()) == 0 and int(bonus.item()) == -1 and np.all(path.cpu().numpy()[:4] == -1)
+
+
 def test_route_topk_standalone():
     g = np.random.default_rng(23)
     T, P, E, k = 16, 2048, 256, 8
