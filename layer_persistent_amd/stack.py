@@ -143,6 +143,29 @@ class Stack:
             if rc != 0:
                 raise abi.MKError(rc, "mk_layer_step")
 
+    def accept_and_commit(self, draft: torch.Tensor, target: torch.Tensor, stream_ptr) -> None:
+        """After a verify step: greedy acceptance along the step's tree (mk_tree_accept; draft
+        and target are int32 [T] device tensors, target being the target model's greedy token
+        after each node, which an LM head outside this library produces), then the accepted
+        nodes' K/V rows moved to positions ctx + depth in every layer's cache (mk_kv_commit).
+        The path, its length and the bonus token stay on the device (self.path, self.n_path,
+        self.bonus), so the calls can sit in the step's graph."""
+        sh = self.shape
+        if not hasattr(self, "path"):
+            self.path = torch.full((sh.T,), -1, dtype=torch.int32, device=self.device)
+            self.n_path = torch.zeros(1, dtype=torch.int32, device=self.device)
+            self.bonus = torch.zeros(1, dtype=torch.int32, device=self.device)
+        rc = self.lib.mk_tree_accept(self.parent.data_ptr(), draft.data_ptr(), target.data_ptr(), sh.T,
+                                     self.path.data_ptr(), self.n_path.data_ptr(), self.bonus.data_ptr(), stream_ptr)
+        if rc != 0:
+            raise abi.MKError(rc, "mk_tree_accept")
+        for lay in self.layers:
+            rc = self.lib.mk_kv_commit(lay.k_cache.data_ptr(), lay.v_cache.data_ptr(), sh.kv_capacity, sh.n_kv_heads,
+                                       sh.head_dim, sh.ctx, self.path.data_ptr(), self.n_path.data_ptr(), sh.T,
+                                       stream_ptr)
+            if rc != 0:
+                raise abi.MKError(rc, "mk_kv_commit")
+
     def capture_step(self, structs) -> torch.cuda.CUDAGraph:
         """One step's launches captured once as a HIP graph (the pages switch the stack on per
         server flag and replay each verify step as one graph: orcarouter.ai write-up, "where the

@@ -220,3 +220,44 @@ def test_stack_step_from_embeddings_with_the_prologue():
     for key in ref:
         assert np.array_equal(ref[key], got[key]), ("graph", key)
     log("  step from embeddings: eager and graph replay bit-identical to the plain stack")
+
+
+def test_stack_accept_and_commit_closes_the_step():
+    """After a stack verify step, greedy acceptance with target tokens that follow one branch
+    of the tree, then the KV commit in every layer: each layer's rows ctx..ctx+n-1 hold the
+    accepted nodes' rows (as the step wrote them at ctx + node), the other rows are unchanged,
+    and the path equals the oracle's."""
+    sh = SMALL_STACK
+    T, ctx, cap = sh.T, sh.ctx, sh.kv_capacity
+    stream = torch.cuda.current_stream()
+    stk = Stack(sh, CFG_ID, N_LAYERS)
+    step_in = synth.stack_step_inputs(sh, CFG_ID, 5)
+    stk.set_step_inputs(step_in)
+    stk.launch_step(stk.structs(False, False), stream.cuda_stream)
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk.ws) == 0
+    parent = step_in["parent"].astype(np.int32)
+    g = np.random.default_rng(12)
+    draft = g.integers(0, 1000, T).astype(np.int32)
+    target = g.integers(1000, 2000, T).astype(np.int32)
+    # the target follows the deepest-index child at every node along one branch
+    node = 0
+    while True:
+        kids = [c for c in range(1, T) if parent[c] == node]
+        if not kids:
+            break
+        target[node] = draft[kids[-1]]
+        node = kids[-1]
+    before = [(_host(l.k_cache).reshape(cap, -1).copy(), _host(l.v_cache).reshape(cap, -1).copy()) for l in stk.layers]
+    stk.accept_and_commit(torch.from_numpy(draft).cuda(), torch.from_numpy(target).cuda(), stream.cuda_stream)
+    torch.cuda.synchronize()
+    ref_path, ref_bonus = oracle.tree_accept(parent, draft, target)
+    n = int(stk.n_path.item())
+    assert stk.path.cpu().numpy()[:n].tolist() == ref_path and int(stk.bonus.item()) == ref_bonus
+    assert n >= 2
+    for L, lay in enumerate(stk.layers):
+        k0, v0 = before[L]
+        ek, ev = oracle.kv_commit(k0, v0, ctx, ref_path)
+        assert np.array_equal(_host(lay.k_cache).reshape(cap, -1), ek), L
+        assert np.array_equal(_host(lay.v_cache).reshape(cap, -1), ev), L
+    log(f"  accepted {n} of {T} nodes; committed in all {N_LAYERS} layers")
