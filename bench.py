@@ -507,6 +507,10 @@ def main():
                               "p90": round(float(np.percentile(per, 90)), 2),
                               "note": "an event pair around every launch adds ~3 us per launch"},
         "graph_replay": graph,
+        # 62 launches of this layer per verify step (46 of the pages' layers use this sliding-window
+        # shape; their 16 global layers are slower): a projection, next to the stack workload's
+        # measured step (bench.py --config 4)
+        "projected_62_layer_step_us": round(62 * kern_us, 1),
         "phases_end_us": phases,
         "cpu_baseline": cpu,
     }
