@@ -431,8 +431,9 @@ def main():
         phases["route_tables"] = round(rel(18), 2)
         phases["qkv_end"] = round(rel(19), 2)
         for p, n in enumerate(names, start=1):
-            phases[n + "_poll_done"] = round(rel(20 + p), 2)
-            phases[n + "_loads_issued"] = round(rel(28 + p), 2)
+            if (tsv[:, 20 + p] > 0).any():          # (no grid hand-off follows the attention phase)
+                phases[n + "_poll_done"] = round(rel(20 + p), 2)
+                phases[n + "_loads_issued"] = round(rel(28 + p), 2)
         # per-workgroup work time of each phase (its work end minus its previous hand-off end):
         # median and max over the workgroups
         for p, n in enumerate(names, start=1):
