@@ -24,7 +24,7 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source into layer_persistent_amd/libmk.so; returns its path."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     tmp = LIB + ".tmp"
-    extra = os.environ.get("MK_HIPCC_DEFINES", "").split()   # e.g. "-DMK_SYNC_MODE=0" for experiments
+    extra = os.environ.get("MK_HIPCC_DEFINES", "").split()   # extra -D flags for experiments
     cmd = [HIPCC, *FLAGS, *extra, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)

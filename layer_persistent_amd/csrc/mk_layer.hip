@@ -52,15 +52,6 @@ constexpr int MAXS_P = 16;         // pooler   K = H    <= 4096
 constexpr int MAXS_R = 8;          // router   K = P    <= 2048
 constexpr int MAXS_U = 8;          // unpooler K = P    <= 2048
 constexpr int MAXS_Q = 16;         // qkv      K = H    <= 4096
-#ifndef MK_SYNC_MODE
-#define MK_SYNC_MODE 0
-#endif
-constexpr int SYNC_MODE = MK_SYNC_MODE;   // grid hand-off: 1 sharded counters, 0 per-workgroup flags
-#ifndef MK_SYNC_COUNTERS
-#define MK_SYNC_COUNTERS 8
-#endif
-constexpr int kCounters = MK_SYNC_COUNTERS;   // sharded counters (mode 1), a power of two <= 64
-
 // dynamic LDS layout (byte offsets; phases reuse the same space)
 constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
 constexpr int G1_XS_BYTES = 16 * (2048 + 8) * 2;       // xp rows for GEMM1
@@ -130,7 +121,7 @@ struct Ctl {              // control-wave state shared through LDS
 // ------------------------------------------------------------------ grid hand-off
 
 struct Sync {
-  uint32_t* flags;        // counters / flags of the grid hand-off (see ctl_signal_wait)
+  uint32_t* flags;        // per-workgroup flags of the grid hand-off (see ctl_signal_wait)
   int32_t* status;
   uint32_t base;          // epoch * 64
   int spin_limit;
@@ -145,75 +136,40 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
   const int lane = threadIdx.x & 63;
   const int n = gridDim.x;
   __builtin_amdgcn_s_waitcnt(0);           // this wave's hand-off stores are complete
-  if constexpr (SYNC_MODE == 1) {
-    // kCounters counters (workgroup w adds to counter w % kCounters, 256 bytes apart); each
-    // add is fire-and-forget.  Counter j has grown by (epoch*8 + phase) * n_j once every
-    // member of group j has signalled `phase`, n_j = members of group j.
-    if (lane == 0 && (int)blockIdx.x != s.skip_wg)
-      __hip_atomic_fetch_add(s.flags + (blockIdx.x & (kCounters - 1)) * 64, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-    if (dead) return false;
-    const int j = lane & (kCounters - 1);
-    const uint32_t members = (uint32_t)((n - j + kCounters - 1) / kCounters);
-    const uint32_t target = (s.base / 64u * 8u + (uint32_t)phase) * members;
-    const uint32_t* f = s.flags + j * 64;
-    auto poll = [&]() -> uint32_t { return lane < kCounters ? ld_coh_u32(f) : target; };
-    auto done = [&](uint32_t x) { return __all((int32_t)(x - target) >= 0); };
-    uint32_t a = poll(), b = poll();
-    int polls = 0;
-    while (true) {
-      if (done(a)) break;
-      a = poll();
-      if (done(b)) break;
-      b = poll();
-      polls += 2;
-      if (polls >= s.spin_limit) {
-        if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        return false;
-      }
-      if (polls > 16) __builtin_amdgcn_s_sleep(2);
-      if ((polls & 63) == 0) {
-        const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
-      }
+  // One flag per workgroup, 64 bytes apart; a poll reads all of them (4 loads per lane).
+  const uint32_t target = s.base + (uint32_t)phase;
+  if (lane == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
+  if (dead) return false;
+  const uint32_t* f = s.flags + lane * 16;
+  auto poll = [&]() -> u32x4 {
+    u32x4 x = {target, target, target, target};
+    if (lane < n) x[0] = ld_coh_u32(f);
+    if (lane + 64 < n) x[1] = ld_coh_u32(f + 64 * 16);
+    if (lane + 128 < n) x[2] = ld_coh_u32(f + 128 * 16);
+    if (lane + 192 < n) x[3] = ld_coh_u32(f + 192 * 16);
+    return x;
+  };
+  auto done = [&](u32x4 x) {
+    return __all((int32_t)(x[0] - target) >= 0 && (int32_t)(x[1] - target) >= 0 &&
+                 (int32_t)(x[2] - target) >= 0 && (int32_t)(x[3] - target) >= 0);
+  };
+  u32x4 a = poll(), b = poll();
+  int polls = 0;
+  while (true) {
+    if (done(a)) break;
+    a = poll();
+    if (done(b)) break;
+    b = poll();
+    polls += 2;
+    if (polls >= s.spin_limit) {
+      if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
+      return false;
     }
-  } else {
-    // One flag per workgroup, 64 bytes apart; a poll reads all of them (4 loads per lane).
-    const uint32_t target = s.base + (uint32_t)phase;
-    if (lane == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
-    if (dead) return false;
-    const uint32_t* f = s.flags + lane * 16;
-    auto poll = [&]() -> u32x4 {
-      u32x4 x = {target, target, target, target};
-      if (lane < n) x[0] = ld_coh_u32(f);
-      if (lane + 64 < n) x[1] = ld_coh_u32(f + 64 * 16);
-      if (lane + 128 < n) x[2] = ld_coh_u32(f + 128 * 16);
-      if (lane + 192 < n) x[3] = ld_coh_u32(f + 192 * 16);
-      return x;
-    };
-    auto done = [&](u32x4 x) {
-      return __all((int32_t)(x[0] - target) >= 0 && (int32_t)(x[1] - target) >= 0 &&
-                   (int32_t)(x[2] - target) >= 0 && (int32_t)(x[3] - target) >= 0);
-    };
-    u32x4 a = poll(), b = poll();
-    int polls = 0;
-    while (true) {
-      if (done(a)) break;
-      a = poll();
-      if (done(b)) break;
-      b = poll();
-      polls += 2;
-      if (polls >= s.spin_limit) {
-        if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_s_waitcnt(0);
-        return false;
-      }
-      if (polls > 8) __builtin_amdgcn_s_sleep(4);
-      if ((polls & 63) == 0) {
-        const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
-      }
+    if (polls > 8) __builtin_amdgcn_s_sleep(4);
+    if ((polls & 63) == 0) {
+      const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -2004,13 +1960,6 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     }
     stamp<TS>(a.timestamps, 19);
     if (touched == 0x9E3779B9u) ytile[0] = touched;   // keeps the touch loads alive
-  }
-  // a launch that skipped its phases still advances its counter by the 8 hand-offs, so the
-  // next launch's targets line up
-  if constexpr (SYNC_MODE == 1) {
-    if (tid == kCtl && tr.bad)
-      __hip_atomic_fetch_add(a.flags + (blockIdx.x & (kCounters - 1)) * 64, 8u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
   }
   // the next launch on this workspace uses the next epoch
   if (tid == kCtl) st_coh_u32(a.epoch + blockIdx.x * 16, epoch + 1);
