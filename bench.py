@@ -141,7 +141,8 @@ def bench_stack(args) -> dict:
     else:
         # the step as given (layer 0's queries and tree K/V rows supplied), and the step from the
         # tokens' embeddings with the first-layer prologue in front of layer 0
-        variants = [("stack", None, False, False), ("stack_from_embeddings", None, False, True)]
+        variants = [("stack", None, False, False), ("stack_from_embeddings", None, False, True),
+                    ("decode_step", None, False, True)]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     res = {}
@@ -151,12 +152,22 @@ def bench_stack(args) -> dict:
             stk.w_qkv0 = synth.device_first_qkv_weight(shape, args.config, "cuda").view(torch.int16)
         stk.prologue = prologue
         structs = [stk.structs(pf, biases is not None, parity) for parity in (0, 1)]
+        # the whole decode step: prologue, layers, then greedy acceptance and the KV commit of the
+        # accepted path in every layer.  The target tokens would come from an LM head (outside
+        # this library); synthetic ones accept the tree's chain of depth 6 (7 nodes).
+        accept = None
+        if name == "decode_step":
+            T = shape.T
+            draft = torch.arange(100, 100 + T, dtype=torch.int32, device="cuda")
+            target = torch.full((T,), 999, dtype=torch.int32, device="cuda")
+            target[:6] = draft[1:7]
+            accept = (draft, target)
         step_us, layer_us = [], []
         for s in range(n_steps):
             stk.set_step_inputs(ins[s], None if biases is None else biases[s])
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            stk.launch_step(structs[s % 2], sp)
+            stk.launch_step(structs[s % 2], sp, accept)
             e1.record(stream)
             torch.cuda.synchronize()
             if s >= args.warmup:
@@ -182,7 +193,7 @@ def bench_stack(args) -> dict:
         # prefetch-list parity); the last step's output must equal its eager launches bit for bit
         graph_us = []
         if not args.no_graph:
-            graphs = [stk.capture_step(structs[parity]) for parity in (0, 1)]
+            graphs = [stk.capture_step(structs[parity], accept) for parity in (0, 1)]
             for s in range(n_steps):
                 stk.set_step_inputs(ins[s], None if biases is None else biases[s])
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -195,7 +206,7 @@ def bench_stack(args) -> dict:
             h_graph = stk.h_out().clone()
             s = n_steps - 1
             stk.set_step_inputs(ins[s], None if biases is None else biases[s])
-            stk.launch_step(structs[s % 2], sp)
+            stk.launch_step(structs[s % 2], sp, accept)
             torch.cuda.synchronize()
             if not torch.equal(h_graph, stk.h_out()):
                 raise RuntimeError("stack graph replay differs from the eager launches")
@@ -204,6 +215,8 @@ def bench_stack(args) -> dict:
         lu = np.array(layer_us)
         glob = [L for L in range(n_layers) if is_global(L)]
         swa = [L for L in range(n_layers) if not is_global(L)]
+        if accept is not None and int(stk.n_path.item()) != 7:
+            raise RuntimeError(f"decode step accepted {int(stk.n_path.item())} nodes, expected the chain of 7")
         if n_active is None:
             n_active = [int(len(torch.unique(l.topk_idx))) for l in stk.layers]
         res[name] = dict(step_us_median=round(float(np.median(step_us)), 1),

@@ -196,6 +196,12 @@ int mk_tree_accept(const int32_t *parent, const int32_t *draft, const int32_t *t
 int mk_kv_commit(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int head_dim, int ctx,
                  const int32_t *path, const int32_t *n_path, int T, void *stream);
 
+/* mk_kv_commit for n_layers layers in one launch (one workgroup per layer): k_caches and
+ * v_caches are DEVICE arrays of n_layers cache pointers (8-byte aligned; every cache 16-byte
+ * aligned, all with the same shape).  Same rules and results as n_layers mk_kv_commit calls. */
+int mk_kv_commit_layers(void *const *k_caches, void *const *v_caches, int n_layers, int capacity, int n_kv_heads,
+                        int head_dim, int ctx, const int32_t *path, const int32_t *n_path, int T, void *stream);
+
 /* Router on its own: logits = x . w_router^T (+ bias) in fp32, then the top-k experts per
  * token ordered by (logit desc, index asc) and softmax gates over the k selected logits.
  * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k];

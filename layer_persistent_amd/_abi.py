@@ -17,7 +17,7 @@ MK_W_BF16, MK_W_NVFP4 = 0, 1
 MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step",
-            "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
+            "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
             "mk_read_status", "mk_strerror"]
 
 
@@ -74,6 +74,7 @@ def lib() -> C.CDLL:
                                       C.c_int, P]
         L.mk_tree_accept.argtypes = [P, P, P, C.c_int, P, P, P, P]
         L.mk_kv_commit.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
+        L.mk_kv_commit_layers.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_route_topk.argtypes = [P, P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.mk_nvfp4_pack.argtypes = [P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, P]
         L.mk_nvfp4_tile_w1.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P, P]
@@ -83,7 +84,7 @@ def lib() -> C.CDLL:
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_kv_append", "mk_qkv_prologue",
-                     "mk_tree_accept", "mk_kv_commit",
+                     "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers",
                      "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_read_status"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -159,6 +160,13 @@ def mk_kv_commit(k_cache, v_cache, capacity, n_kv_heads, head_dim, ctx, path, n_
     rc = lib().mk_kv_commit(_ptr(k_cache), _ptr(v_cache), capacity, n_kv_heads, head_dim, ctx, _ptr(path),
                             _ptr(n_path), T, _stream(stream))
     return _check(rc, "mk_kv_commit") if check else rc
+
+
+def mk_kv_commit_layers(k_caches, v_caches, n_layers, capacity, n_kv_heads, head_dim, ctx, path, n_path, T,
+                        stream=None, check=True):
+    rc = lib().mk_kv_commit_layers(_ptr(k_caches), _ptr(v_caches), n_layers, capacity, n_kv_heads, head_dim, ctx,
+                                   _ptr(path), _ptr(n_path), T, _stream(stream))
+    return _check(rc, "mk_kv_commit_layers") if check else rc
 
 
 def mk_kv_append(k_cache, v_cache, capacity, n_kv_heads, head_dim, pos, k_new, v_new, n, stream=None, check=True):

@@ -302,8 +302,21 @@ int mk_kv_commit(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int
     return MK_ESHAPE;
   if (ctx < 0 || ctx + T > capacity) return MK_ECAPACITY;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return MK_EALIGN;
-  return mk::launch_kv_commit((uint16_t*)k_cache, (uint16_t*)v_cache, n_kv_heads * head_dim, ctx, path, n_path, T,
-                              (hipStream_t)stream)
+  return mk::launch_kv_commit((uint16_t*)k_cache, (uint16_t*)v_cache, nullptr, nullptr, 1, n_kv_heads * head_dim, ctx,
+                              path, n_path, T, (hipStream_t)stream)
+             ? MK_EHIP : MK_OK;
+}
+
+int mk_kv_commit_layers(void* const* k_caches, void* const* v_caches, int n_layers, int capacity, int n_kv_heads,
+                        int head_dim, int ctx, const int32_t* path, const int32_t* n_path, int T, void* stream) {
+  if (!k_caches || !v_caches || !path || !n_path) return MK_EINVAL;
+  if (n_layers < 1 || n_layers > 65535 || n_kv_heads <= 0 || head_dim <= 0 || (n_kv_heads * head_dim) % 8 || T < 1 ||
+      T > 64 || (size_t)2 * T * n_kv_heads * head_dim * 2 > 65536 || capacity <= 0)
+    return MK_ESHAPE;
+  if (ctx < 0 || ctx + T > capacity) return MK_ECAPACITY;
+  if (((uintptr_t)k_caches & 7u) || ((uintptr_t)v_caches & 7u)) return MK_EALIGN;
+  return mk::launch_kv_commit(nullptr, nullptr, (uint16_t* const*)k_caches, (uint16_t* const*)v_caches, n_layers,
+                              n_kv_heads * head_dim, ctx, path, n_path, T, (hipStream_t)stream)
              ? MK_EHIP : MK_OK;
 }
 

@@ -151,10 +151,18 @@ __global__ void __launch_bounds__(64) tree_accept_kernel(const int32_t* __restri
 // KV commit of an accepted path in one layer's cache pair: row ctx + path[j] -> row ctx + j for
 // j < n (n read on the device).  Every source row is read into LDS before any row is written,
 // so the moves may overlap.  One workgroup; rows are row_elems bf16 (a multiple of 8).
+// Workgroup y commits layer y of n_layers: its cache pair is kcs[y], vcs[y] when the pointer
+// arrays are given (device memory), else kc, vc.
 __global__ void __launch_bounds__(256) kv_commit_kernel(uint16_t* __restrict__ kc, uint16_t* __restrict__ vc,
+                                                        uint16_t* const* __restrict__ kcs,
+                                                        uint16_t* const* __restrict__ vcs,
                                                         int row_elems, int ctx, const int32_t* __restrict__ path,
                                                         const int32_t* __restrict__ n_path, int T) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  if (kcs) {
+    kc = kcs[blockIdx.x];
+    vc = vcs[blockIdx.x];
+  }
   u32x4* buf = (u32x4*)lds;                       // [2][T][row_elems / 8]
   const int n = min(max(*n_path, 0), T);
   const int per = row_elems / 8, total = n * per;
@@ -182,10 +190,11 @@ int launch_tree_accept(const int32_t* parent, const int32_t* draft, const int32_
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-int launch_kv_commit(uint16_t* kc, uint16_t* vc, int row_elems, int ctx, const int32_t* path, const int32_t* n_path,
-                     int T, hipStream_t stream) {
+int launch_kv_commit(uint16_t* kc, uint16_t* vc, uint16_t* const* kcs, uint16_t* const* vcs, int n_layers,
+                     int row_elems, int ctx, const int32_t* path, const int32_t* n_path, int T, hipStream_t stream) {
   const size_t lds = (size_t)2 * T * row_elems * 2;
-  hipLaunchKernelGGL(kv_commit_kernel, dim3(1), dim3(256), lds, stream, kc, vc, row_elems, ctx, path, n_path, T);
+  hipLaunchKernelGGL(kv_commit_kernel, dim3(n_layers), dim3(256), lds, stream, kc, vc, kcs, vcs, row_elems, ctx, path,
+                     n_path, T);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

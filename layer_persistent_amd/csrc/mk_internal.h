@@ -70,8 +70,8 @@ int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int 
                         uint16_t* kc, uint16_t* vc, int pos, hipStream_t stream);
 int launch_tree_accept(const int32_t* parent, const int32_t* draft, const int32_t* target, int T, int32_t* path,
                        int32_t* n_path, int32_t* bonus, hipStream_t stream);
-int launch_kv_commit(uint16_t* kc, uint16_t* vc, int row_elems, int ctx, const int32_t* path, const int32_t* n_path,
-                     int T, hipStream_t stream);
+int launch_kv_commit(uint16_t* kc, uint16_t* vc, uint16_t* const* kcs, uint16_t* const* vcs, int n_layers,
+                     int row_elems, int ctx, const int32_t* path, const int32_t* n_path, int T, hipStream_t stream);
 int launch_route_topk(const uint16_t* x, const uint16_t* w, const float* bias, int T, int P, int E,
                       int k, int32_t* idx, float* gate, float* logits, hipStream_t stream);
 int launch_nvfp4_pack(const void* w, int is_fp32, int batch, int N, int K, uint8_t* codes,

@@ -1600,18 +1600,13 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
 // the wave partials (weights of the first tile already in `wf` when `have_pref`), the control
 // wave sums them and runs `epi(n0, red, it)`.  Two reduction buffers alternate so a tile needs
 // one workgroup barrier.  Called by all threads.
-struct NoHook {
-  __device__ void operator()() const {}
-};
-
-// `after` runs on the compute threads once their last tile's partials are in LDS (registers of
-// this phase's weights are free then), while the control wave stores the last tile: loads for
-// the next phase can start there.  (Issued before the tile's barrier instead, they made the
-// compiler wait for them at that barrier.)
-template <int MAXS, class Epi, class After = NoHook>
+// Loads for the next phase are not issued here but inside the hand-off wait that follows
+// (phase_end's `pf`): issued before the hand-off, a large tile's loads hold the issuing waves
+// until the CU's load queue drains, and the grid waits for them at the barrier.
+template <int MAXS, class Epi>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
                             const uint16_t* x, int K, int N, int off, float* red2, Epi epi,
-                            const char* wlds = nullptr, After after = After()) {
+                            const char* wlds = nullptr) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
@@ -1631,7 +1626,6 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
     wg_sync();
     if (threadIdx.x >= kCompute) epi(t * 16, red, it);
   }
-  if (threadIdx.x < kCompute) after();
 }
 
 // End of a phase: compute waves run `pf` (loads for a later phase, left in flight) while the

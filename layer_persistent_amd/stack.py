@@ -129,7 +129,14 @@ class Stack:
             out.append((lay.cfg, lay.w.struct(), io))
         return out
 
-    def launch_step(self, structs, stream_ptr) -> None:
+    def launch_step(self, structs, stream_ptr, accept=None) -> None:
+        """One verify step: [the prologue,] every layer's launch, and with `accept` = (draft,
+        target) the acceptance and KV commit after the last layer."""
+        self._launch_layers(structs, stream_ptr)
+        if accept is not None:
+            self.accept_and_commit(accept[0], accept[1], stream_ptr)
+
+    def _launch_layers(self, structs, stream_ptr) -> None:
         if self.prologue:
             sh, l0 = self.shape, self.layers[0]
             rc = self.lib.mk_qkv_prologue(self.h[0].data_ptr(), self.w_qkv0.data_ptr(), sh.T, sh.hidden,
@@ -147,7 +154,8 @@ class Stack:
         """After a verify step: greedy acceptance along the step's tree (mk_tree_accept; draft
         and target are int32 [T] device tensors, target being the target model's greedy token
         after each node, which an LM head outside this library produces), then the accepted
-        nodes' K/V rows moved to positions ctx + depth in every layer's cache (mk_kv_commit).
+        nodes' K/V rows moved to positions ctx + depth in every layer's cache (mk_kv_commit_layers,
+        one launch for all layers).
         The path, its length and the bonus token stay on the device (self.path, self.n_path,
         self.bonus), so the calls can sit in the step's graph."""
         sh = self.shape
@@ -159,14 +167,17 @@ class Stack:
                                      self.path.data_ptr(), self.n_path.data_ptr(), self.bonus.data_ptr(), stream_ptr)
         if rc != 0:
             raise abi.MKError(rc, "mk_tree_accept")
-        for lay in self.layers:
-            rc = self.lib.mk_kv_commit(lay.k_cache.data_ptr(), lay.v_cache.data_ptr(), sh.kv_capacity, sh.n_kv_heads,
-                                       sh.head_dim, sh.ctx, self.path.data_ptr(), self.n_path.data_ptr(), sh.T,
-                                       stream_ptr)
-            if rc != 0:
-                raise abi.MKError(rc, "mk_kv_commit")
+        if not hasattr(self, "kv_ptrs"):
+            # device arrays of every layer's cache pointers, for the one-launch commit
+            self.kv_ptrs = [torch.tensor([getattr(l, f).data_ptr() for l in self.layers], dtype=torch.int64,
+                                         device=self.device) for f in ("k_cache", "v_cache")]
+        rc = self.lib.mk_kv_commit_layers(self.kv_ptrs[0].data_ptr(), self.kv_ptrs[1].data_ptr(), self.n_layers,
+                                          sh.kv_capacity, sh.n_kv_heads, sh.head_dim, sh.ctx, self.path.data_ptr(),
+                                          self.n_path.data_ptr(), sh.T, stream_ptr)
+        if rc != 0:
+            raise abi.MKError(rc, "mk_kv_commit_layers")
 
-    def capture_step(self, structs) -> torch.cuda.CUDAGraph:
+    def capture_step(self, structs, accept=None) -> torch.cuda.CUDAGraph:
         """One step's launches captured once as a HIP graph (the pages switch the stack on per
         server flag and replay each verify step as one graph: orcarouter.ai write-up, "where the
         5.9 ms still goes").  A replay runs the same launches on the stream it is replayed on;
@@ -175,8 +186,11 @@ class Stack:
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
+        if accept is not None and not hasattr(self, "path"):
+            self.accept_and_commit(accept[0], accept[1], torch.cuda.current_stream().cuda_stream)   # buffers
+            torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=side):
-            self.launch_step(structs, torch.cuda.current_stream().cuda_stream)
+            self.launch_step(structs, torch.cuda.current_stream().cuda_stream, accept)
         torch.cuda.current_stream().wait_stream(side)
         return g
 

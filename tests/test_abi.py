@@ -110,6 +110,9 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_kv_commit(GOOD, GOOD, 64, 1, 60, 0, GOOD, GOOD, 16, check=False) == mk.MK_ESHAPE
     assert mk.mk_kv_commit(GOOD, GOOD, 4096, 8, 1024, 0, GOOD, GOOD, 16, check=False) == mk.MK_ESHAPE
     assert mk.mk_kv_commit(BAD, GOOD, 64, 1, 128, 0, GOOD, GOOD, 16, check=False) == mk.MK_EALIGN
+    assert mk.mk_kv_commit_layers(None, GOOD, 62, 64, 1, 128, 0, GOOD, GOOD, 16, check=False) == mk.MK_EINVAL
+    assert mk.mk_kv_commit_layers(GOOD, GOOD, 0, 64, 1, 128, 0, GOOD, GOOD, 16, check=False) == mk.MK_ESHAPE
+    assert mk.mk_kv_commit_layers(GOOD, GOOD, 62, 64, 1, 128, 60, GOOD, GOOD, 16, check=False) == mk.MK_ECAPACITY
     assert mk.mk_route_topk(GOOD, GOOD, None, 16, 2048, 256, 9, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(GOOD, GOOD, None, 65, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_route_topk(BAD, GOOD, None, 16, 2048, 256, 8, GOOD, GOOD, check=False) == mk.MK_EALIGN
