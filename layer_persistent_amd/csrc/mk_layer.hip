@@ -129,8 +129,9 @@ struct Sync {
 };
 
 // Control wave only: signal this workgroup's flag for `phase`, then wait until every
-// workgroup's flag has reached it.  Four polls stay in flight so that a flag landing is
-// seen about a quarter of a round trip later.  Returns false when the wait expired or the
+// workgroup's flag has reached it.  Two polls (of every flag) stay in flight, back to back with
+// no sleep between them (sleeping after a few polls measured 0.35 us slower per layer), so that
+// a flag landing is seen about half a round trip later.  Returns false when the wait expired or the
 // launch was aborted (status word set).
 __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead) {
   const int lane = threadIdx.x & 63;
@@ -166,7 +167,6 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
       __builtin_amdgcn_s_waitcnt(0);
       return false;
     }
-    if (polls > 8) __builtin_amdgcn_s_sleep(4);
     if ((polls & 63) == 0) {
       const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
