@@ -57,7 +57,7 @@ int check_cfg(const mk_layer_cfg* c, int T) {
 }
 
 struct Layout {
-  size_t status, epoch, flags, part_o, part_ml, attn, h1, h_frag, xp, logits, act, y, total;
+  size_t status, epoch, flags, part_o, part_ml, attn, h1, h_frag, xp, logits, act, y, qkv_part, qkv_cnt, total;
   int n_wg, items, chunks_per_head, attn_lo, ck, rw, nrb, part_slots;
 };
 
@@ -123,6 +123,9 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   const size_t act_q = (size_t)T * k * (I / 16) * 16, act_b = (size_t)T * k * I * 2;
   L.act = o; o = up256(o + (act_q > act_b ? act_q : act_b));
   L.y = o; o = up256(o + (size_t)16 * P * 2);
+  // split-K qkv: at most one (tile, part) per workgroup
+  L.qkv_part = o; o = up256(o + (size_t)n_wg * 64 * 4 * 4);
+  L.qkv_cnt = o; o = up256(o + (size_t)n_wg * 64);
   L.total = o;
   return L;
 }
@@ -256,6 +259,8 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.act_q = (uint32_t*)(ws + L.act);
   a.act_bf = (uint16_t*)(ws + L.act);
   a.y = (uint16_t*)(ws + L.y);
+  a.qkv_part = (float*)(ws + L.qkv_part);
+  a.qkv_cnt = (uint32_t*)(ws + L.qkv_cnt);
   a.timestamps = io->timestamps;
   return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
 }

@@ -44,6 +44,8 @@ struct KArgs {
   uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes lo, codes hi, scale byte, 0
   uint16_t* act_bf;     // bf16 intermediate [T*k][I]
   uint16_t* y;                // fragment order
+  float* qkv_part;            // split-K qkv partials [tile][part][64 lanes][4]
+  uint32_t* qkv_cnt;          // split-K qkv arrival counters, one per tile, 64 bytes apart
   uint64_t* timestamps;
 };
 

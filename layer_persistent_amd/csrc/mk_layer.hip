@@ -28,7 +28,8 @@
 //   7 GEMM2  per 8-column slice of P: every active expert's down projection, then the combine
 //            y = bf16(sum over the token's slots, in slot order, of gate * out)
 //   8 UNPOOL h_out = bf16(h1 + y Wu^T)
-//     QKV    [q; k; v] = h_out Wqkv^T -> q_next, KV rows of the next layer
+//     QKV    [q; k; v] = h_out Wqkv^T -> q_next, KV rows of the next layer (K split over up to
+//            4 workgroups per tile; the last part to arrive adds the partials)
 //
 // Cross-workgroup hand-off: data is written with device-coherent (write-through) stores; the
 // writer waits for them, then stores its per-phase flag; readers poll all flags with coherent
@@ -190,11 +191,12 @@ struct WFrag {
 // (weights) and 1 KB (fragment-order x) apart and fit the load instructions' immediate offsets.
 __device__ __forceinline__ int kblock(int ksteps) { return (ksteps + 7) >> 3; }
 
+// `ld` is the row stride in elements when the K columns are part of a longer row (0: K).
 template <int MAXS>
-__device__ __forceinline__ void wfrag_load(WFrag<MAXS>& f, const uint16_t* __restrict__ W, int K, int n0) {
+__device__ __forceinline__ void wfrag_load(WFrag<MAXS>& f, const uint16_t* __restrict__ W, int K, int n0, int ld = 0) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ksteps = K >> 5, J = kblock(ksteps);
-  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * K + (lane >> 4) * 8 + wave * J * 32;
+  const uint16_t* row = W + (size_t)(n0 + (lane & 15)) * (ld > 0 ? ld : K) + (lane >> 4) * 8 + wave * J * 32;
 #pragma unroll
   for (int j = 0; j < MAXS; ++j) {
     const int s = wave * J + j;
@@ -1654,6 +1656,70 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
   return *dead_sh == 0;
 }
 
+// ------------------------------------------------------------------ split-K qkv
+
+// The next layer's qkv projection has few 16-column tiles (N = (Hq + 2 Hkv) d) but a long K
+// (= H), and every tile reads all of x, so with one workgroup per tile a few workgroups would
+// each pull 2 x 16 K bf16 bytes while the rest idle.  Instead each tile's K is cut into
+// `np` parts of `ps` k-steps (a multiple of 8, so the 8 waves get equal blocks) on np
+// workgroups.  Each part's control wave stores its fp32 partial (64 lanes x 4 values, the
+// epilogue's layout) and counts itself in on the tile's counter; the part that arrives last
+// adds the np partials in part order, so the sum does not depend on the arrival order, writes
+// q, k and v, and clears the counter for the next launch.
+struct QkvSplit {
+  int np, ps;
+};
+
+__device__ __forceinline__ QkvSplit qkv_split(int ksteps, int ntiles, int nwg) {
+  QkvSplit q{1, ksteps};
+  if (ntiles <= 0) return q;
+  int np = nwg / ntiles;
+  np = np > 4 ? 4 : np;
+  if (np < 2) return q;
+  const int ps = ((ksteps + np - 1) / np + 7) & ~7;
+  np = (ksteps + ps - 1) / ps;
+  if (np < 2 || ps > 64) return q;
+  q.np = np;
+  q.ps = ps;
+  return q;
+}
+
+// Control wave of a workgroup holding part `part` of tile `tile`: the part's sums from the
+// waves' partials in `red`, the exchange, and (last part only) the tile's outputs.
+__device__ __forceinline__ void qkv_split_epilogue(const KArgs& a, const float* red, int tile, int part, int np,
+                                                   int crow, int cc0, bool crv) {
+  const int lane = threadIdx.x & 63;
+  float v[4];
+  ctl_tile_vals(red, crow, cc0, v);
+  float* mine = a.qkv_part + ((size_t)(tile * np + part) * 64 + lane) * 4;
+  st_coh_u64(mine, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32));
+  st_coh_u64(mine + 2, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32));
+  __builtin_amdgcn_s_waitcnt(0);           // the partial is complete before it is counted
+  uint32_t old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(a.qkv_cnt + tile * 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __shfl(old, 0);
+  if (old != (uint32_t)(np - 1)) return;
+  if (lane == 0) st_coh_u32(a.qkv_cnt + tile * 16, 0u);
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < np; ++p) {
+    float u[4] = {v[0], v[1], v[2], v[3]};
+    if (p != part) {
+      const uint32_t* o = (const uint32_t*)(a.qkv_part + ((size_t)(tile * np + p) * 64 + lane) * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u[j] = __uint_as_float(ld_coh_u32(o + j));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[j] += u[j];
+  }
+  if (!crv) return;
+  const int qd = a.Hq * a.d, kd = a.Hkv * a.d, n = tile * 16 + cc0;
+  uint16_t* dst;
+  if (n < qd) dst = a.q_next + (size_t)crow * qd + n;
+  else if (n < qd + kd) dst = a.kn + (size_t)(a.ctx + crow) * kd + (n - qd);
+  else dst = a.vn + (size_t)(a.ctx + crow) * kd + (n - qd - kd);
+  *(uint64_t*)dst = pack4_bf16(sum);
+}
+
 // ------------------------------------------------------------------ kernel
 
 // SPEC 1: the shard shape of the pages' model on one GPU (hidden 4096, 8 q heads / 1 kv head
@@ -1694,6 +1760,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   WFrag<MAXS_R> wr;
   WFrag<MAXS_U> wu;
   WFrag<MAXS_Q> wq;
+  WFrag<SPEC == 1 ? 6 : 8> wqs;       // a split-K part's fragments
   // pooler tiles run on the last P/16 workgroups, away from the attention items, so that
   // those workgroups can hold their tile in LDS from launch start
   const int off_p = nwg > a.P / 16 ? nwg - a.P / 16 : 0;
@@ -1703,8 +1770,18 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   const int qkv_n = (a.Hq + 2 * a.Hkv) * a.d;
   // the stack's last layer (no next-layer weights) ends after the unpooler
   const bool has_qkv = a.w_qkv != nullptr;
+  // qkv: K split over np workgroups per tile when the grid has room (item t_q is part
+  // t_q / ntiles of tile t_q % ntiles), else one workgroup per tile over the full K
+  // (shard shape: 80 tiles x 3 parts of 48, 48 and 32 k-steps; the host launches it on >= 240
+  // workgroups)
+  const QkvSplit qs = SPEC == 1 ? QkvSplit{3, 48} : qkv_split(a.H >> 5, qkv_n / 16, nwg);
+  const bool q_split = has_qkv && qs.np > 1;
+  const int q_nt = qkv_n / 16 > 0 ? qkv_n / 16 : 1;
+  const int q_tile = t_q % q_nt, q_part = t_q / q_nt;
+  const int q_s0 = q_part * qs.ps, q_ns = min(qs.ps, (a.H >> 5) - q_s0);
+  const bool p_qs = q_split && q_part < qs.np;
   const bool p_o = t_o < a.H / 16, p_p = t_p < a.P / 16, p_r = t_r < a.E / 16, p_u = t_u < a.H / 16,
-             p_q = has_qkv && t_q < qkv_n / 16;
+             p_q = has_qkv && !q_split && t_q < qkv_n / 16;
   // the pooler tile sits in LDS; a workgroup with an attention item fills it afterwards
   const bool pool_lds = p_p && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
   const bool pool_dma = pool_lds && (int)blockIdx.x < a.attn_items;
@@ -1930,11 +2007,18 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // the qkv tile's weights load while the grid hands off.  (Issued before the hand-off, the
     // 128 KB per workgroup kept the issuing waves from the barrier until the CU's load queue
     // drained, and the unpooler's hand-off ended about 2.5 us later on those workgroups.)
-    alive = phase_end<TS>(a, s, 8, &dead_sh, [&] { if (alive && p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16); }) && alive;
+    alive = phase_end<TS>(a, s, 8, &dead_sh, [&] {
+      if (alive && p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
+      if (alive && p_qs) wfrag_load(wqs, a.w_qkv + q_s0 * 32, q_ns * 32, q_tile * 16, a.H);
+    }) && alive;
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
-      if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_frag, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+      if (q_split) {
+        if (cw && p_qs) red_store(red2, wfrag_mma(wqs, a.h_frag + (size_t)q_s0 * 512, a.T, q_ns * 32));
+        wg_sync();
+        if (!cw && p_qs) qkv_split_epilogue(a, red2, q_tile, q_part, qs.np, crow, cc0, crv);
+      } else if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_frag, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
@@ -1972,7 +2056,7 @@ int layer_lds_bytes() { return LDS_BYTES; }
 
 static bool is_spec1(const KArgs& a) {
   return a.H == 4096 && a.Hq == 8 && a.Hkv == 1 && a.d == 128 && a.P == 2048 && a.E == 256 && a.topk == 8 &&
-         a.I == 192 && a.fmt == 1 && a.T == 16;
+         a.I == 192 && a.fmt == 1 && a.T == 16 && a.n_wg >= 240;
 }
 
 int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream) {

@@ -25,6 +25,9 @@ SMALL_RW4 = synth.LayerShape("small-global-ctx8100-nvfp4", 256, 8, 1, 64, 256, 1
 # pooled 1152: nine 128-wide k-steps per W1 row, split 5 + 4 over two pieces (the second
 # piece's scale bytes start at 40, not at half the row)
 SMALL_P1152 = synth.LayerShape("small-p1152-nvfp4", 256, 4, 1, 64, 1152, 16, 4, 64, 128, 300, 16, True)
+# hidden 1280 (40 k-steps of 32) with 24 qkv tiles: on a 256-CU device the next-layer qkv
+# splits each tile's K over three workgroups, 16 + 16 + 8 k-steps
+SMALL_H1280 = synth.LayerShape("small-h1280-splitk-nvfp4", 1280, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
 
 
 @pytest.fixture(autouse=True)
@@ -267,7 +270,7 @@ def _check_layer(inp, out, n_sample_pairs=None):
 
 
 @pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83),
-                                           (SMALL_RW4, 84), (SMALL_P1152, 85)])
+                                           (SMALL_RW4, 84), (SMALL_P1152, 85), (SMALL_H1280, 88)])
 def test_layer_small_shapes(shape, cfg_id):
     log(f"[layer parity] {shape.name}")
     inp = synth.make_layer_inputs(shape, cfg_id)
