@@ -1765,7 +1765,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   // those workgroups can hold their tile in LDS from launch start
   const int off_p = nwg > a.P / 16 ? nwg - a.P / 16 : 0;
   const int t_o = first_tile(0), t_p = first_tile(off_p), t_u = first_tile(0);
-  const int off_r = nwg - a.E / 16, off_q = a.P / 16 < nwg ? a.P / 16 : 0;
+  // router tiles: on workgroups with neither a pooler tile nor an attention item, just below
+  // the pooler's, when there are enough; those hold their tile in LDS (where a pooler tile
+  // would sit) from launch start.  Otherwise on the last workgroups, loaded into registers
+  // during the pooler hand-off.
+  const bool router_room = off_p - a.attn_items >= a.E / 16 && POOL_LDS_OFF + 32 * a.P <= LDS_BYTES;
+  const int off_r = router_room ? off_p - a.E / 16 : nwg - a.E / 16, off_q = a.P / 16 < nwg ? a.P / 16 : 0;
   const int t_r = first_tile(off_r), t_q = first_tile(off_q);
   const int qkv_n = (a.Hq + 2 * a.Hkv) * a.d;
   // the stack's last layer (no next-layer weights) ends after the unpooler
@@ -1785,6 +1790,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   // the pooler tile sits in LDS; a workgroup with an attention item fills it afterwards
   const bool pool_lds = p_p && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
   const bool pool_dma = pool_lds && (int)blockIdx.x < a.attn_items;
+  const bool router_lds = router_room && p_r;
   u32x2 res = {0, 0};
   if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
 
@@ -1883,6 +1889,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       attn_item_run(it, r, qf, false);
     }
     if (pool_lds && !pool_dma) lds_tile_fill(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF);
+    if (router_lds) lds_tile_fill(a.w_router, a.P, t_r * 16, smem + POOL_LDS_OFF);
     // workgroups without an attention item pull the previous step's most-used experts into
     // the device-side caches before the routing of this step is known.  (The unpooler and
     // qkv tiles are not touched here: that traffic slows the attention phase more than it
@@ -1945,10 +1952,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         st_coh_u64(a.xp + frag_off(crow, n0 + cc0), pack4_bf16(v));
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
-    alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
+    alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r && !router_lds) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
     if (alive) {
-      dense_phase(a, wr, p_r, a.w_router, a.xp, a.P, a.E, off_r, red2, [&](int n0, const float* red, int) {
+      dense_phase(a, wr, p_r && !router_lds, a.w_router, a.xp, a.P, a.E, off_r, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
@@ -1959,7 +1966,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         st_coh_u128(a.logits + (size_t)crow * a.E + n0 + cc0,
                     u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
         if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)crow * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
-      });
+      }, router_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     // GEMM1's input rows are fetched while the grid waits for the router (piece maxima go to
     // the LDS area GEMM1 later uses for scales, which the routing tables leave alone)
