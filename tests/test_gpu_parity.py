@@ -342,12 +342,16 @@ def test_expert_prefetch_lists_and_changes_no_output(shape, cfg_id, n):
     log(f"  prefetch list {got[:n].tolist()}")
 
 
-def test_repeated_steps_on_one_workspace():
-    """Successive launches on one workspace (as layer after layer / step after step)."""
+@pytest.mark.parametrize("shape,cfg_id", [(SMALL_NVFP4, 85), (SMALL_H1280, 89)])
+def test_repeated_steps_on_one_workspace(shape, cfg_id):
+    """Successive launches on one workspace (as layer after layer / step after step); the
+    hidden-1280 shape splits the next-layer qkv over workgroups, whose arrival counters must
+    start every launch at zero."""
+    log(f"[repeated steps] {shape.name}")
     dw = None
     st = None
     for step in range(4):
-        inp = synth.make_layer_inputs(SMALL_NVFP4, 85, step=step)
+        inp = synth.make_layer_inputs(shape, cfg_id, step=step)
         if dw is None:
             dw = dt.upload_weights(inp)
             st = dt.make_step(inp)
@@ -364,6 +368,11 @@ def test_repeated_steps_on_one_workspace():
         assert out["status"] == 0
         assert_close_bf16(f"step {step} h_out", out["h_out"], ref["h_out"])
         assert_close_bf16(f"step {step} q_next", out["q_next"], ref["q_next"])
+        ctx, T = shape.ctx, shape.T
+        kn = out["k_cache_next"].reshape(shape.kv_capacity, -1)
+        vn = out["v_cache_next"].reshape(shape.kv_capacity, -1)
+        assert_close_bf16(f"step {step} k_new", kn[ctx:ctx + T], ref["k_new"].reshape(T, -1))
+        assert_close_bf16(f"step {step} v_new", vn[ctx:ctx + T], ref["v_new"].reshape(T, -1))
 
 
 def test_bad_tree_reports_status():
