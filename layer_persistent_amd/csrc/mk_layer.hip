@@ -1660,9 +1660,9 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
 
 // The next layer's qkv projection has few 16-column tiles (N = (Hq + 2 Hkv) d) but a long K
 // (= H), and every tile reads all of x, so with one workgroup per tile a few workgroups would
-// each pull 2 x 16 K bf16 bytes while the rest idle.  Instead each tile's K is cut into
-// `np` parts of `ps` k-steps (a multiple of 8, so the 8 waves get equal blocks) on np
-// workgroups.  Each part's control wave stores its fp32 partial (64 lanes x 4 values, the
+// each pull a 16 x K weight tile and all of x (32 K bytes each) while the rest idle.  Instead
+// each tile's K is cut into `np` parts of `ps` k-steps (a multiple of 8, so the 8 waves get
+// equal blocks) on np workgroups.  Each part's control wave stores its fp32 partial (64 lanes x 4 values, the
 // epilogue's layout) and counts itself in on the tile's counter; the part that arrives last
 // adds the np partials in part order, so the sum does not depend on the arrival order, writes
 // q, k and v, and clears the counter for the next launch.
@@ -2011,9 +2011,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         st_coh_u64(a.h_frag + frag_off(crow, n0 + cc0), hv);          // the qkv phase's x
       }, wu_lds ? smem + WU_LDS_OFF : nullptr);
     }
-    // the qkv tile's weights load while the grid hands off.  (Issued before the hand-off, the
-    // 128 KB per workgroup kept the issuing waves from the barrier until the CU's load queue
-    // drained, and the unpooler's hand-off ended about 2.5 us later on those workgroups.)
+    // the qkv weights (a whole tile, or one K part of it) load while the grid hands off.
+    // (Issued before the hand-off, a whole tile's 128 KB kept the issuing waves from the barrier
+    // until the CU's load queue drained, and the unpooler's hand-off ended about 2.5 us later on
+    // those workgroups.)
     alive = phase_end<TS>(a, s, 8, &dead_sh, [&] {
       if (alive && p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
       if (alive && p_qs) wfrag_load(wqs, a.w_qkv + q_s0 * 32, q_ns * 32, q_tile * 16, a.H);
