@@ -43,9 +43,14 @@
 
 namespace mk {
 
+
 constexpr int kThreads = 576;      // 8 compute waves + 1 control wave
 constexpr int kCompute = 512;
 constexpr int kCtl = 512;          // first thread of the control wave
+// The pooler (P/16 tiles) and the router (E/16 tiles) leave most workgroups without work; those
+// sleep this long before polling (measured: the pooler's work then ends ~0.6 us sooner, and the
+// layer ~0.9 us; longer sleeps, or sleeps in the attention and merge hand-offs, gained nothing).
+constexpr int kIdleSleepUs = 1;
 
 // per-wave MFMA k-steps (32 k each) held in registers for each dense phase
 constexpr int MAXS_O = 4;          // o-proj   K = Hq*d <= 1024
@@ -132,9 +137,11 @@ struct Sync {
 // Control wave only: signal this workgroup's flag for `phase`, then wait until every
 // workgroup's flag has reached it.  Two polls (of every flag) stay in flight, back to back with
 // no sleep between them (sleeping after a few polls measured 0.35 us slower per layer), so that
-// a flag landing is seen about half a round trip later.  Returns false when the wait expired or the
-// launch was aborted (status word set).
-__device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead) {
+// a flag landing is seen about half a round trip later.  `idle_us` (about 1 us each) delays the
+// first poll of a workgroup that had no work in a phase where the others work for ~2 us: its polls
+// of the flags would only add memory traffic while they work.  Returns false when the wait
+// expired or the launch was aborted (status word set).
+__device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead, int idle_us = 0) {
   const int lane = threadIdx.x & 63;
   const int n = gridDim.x;
   __builtin_amdgcn_s_waitcnt(0);           // this wave's hand-off stores are complete
@@ -142,6 +149,7 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
   const uint32_t target = s.base + (uint32_t)phase;
   if (lane == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
   if (dead) return false;
+  for (int i = 0; i < idle_us; ++i) __builtin_amdgcn_s_sleep(37);   // 37 x 64 clocks, ~1 us each
   const uint32_t* f = s.flags + lane * 16;
   auto poll = [&]() -> u32x4 {
     u32x4 x = {target, target, target, target};
@@ -1631,11 +1639,12 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
 }
 
 // End of a phase: compute waves run `pf` (loads for a later phase, left in flight) while the
-// control wave runs `ctlf`, signals and waits for the whole grid.  Returns true when the
-// launch is still alive.  Called by all threads; every compute-wave global store of the phase
-// must be complete before the call.
+// control wave signals and waits for the whole grid (first sleeping `idle_us`, see
+// ctl_signal_wait).  Returns true when the launch is still alive.  Called by all threads; every
+// compute-wave global store of the phase must be complete before the call.
 template <bool TS, class PfF>
-__device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int phase, int32_t* dead_sh, PfF pf) {
+__device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int phase, int32_t* dead_sh, PfF pf,
+                                          int idle_us = 0) {
   wg_sync();
   stamp<TS>(a.timestamps, 2 * phase);
   if (threadIdx.x >= kCompute) {
@@ -1644,7 +1653,7 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
       __builtin_amdgcn_s_waitcnt(0);
       stamp<TS>(a.timestamps, 53 + phase);
     }
-    const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0);
+    const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0, idle_us);
     if (!ok && threadIdx.x == kCtl) *dead_sh = 1;
     stamp<TS>(a.timestamps, 20 + phase);
   } else {
@@ -1952,7 +1961,8 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         st_coh_u64(a.xp + frag_off(crow, n0 + cc0), pack4_bf16(v));
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
-    alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r && !router_lds) wfrag_load(wr, a.w_router, a.P, t_r * 16); }) && alive;
+    alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r && !router_lds) wfrag_load(wr, a.w_router, a.P, t_r * 16); },
+                          p_p ? 0 : kIdleSleepUs) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
     if (alive) {
       dense_phase(a, wr, p_r && !router_lds, a.w_router, a.xp, a.P, a.E, off_r, red2, [&](int n0, const float* red, int) {
@@ -1973,7 +1983,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     u32x4 xpv[8];
     alive = phase_end<TS>(a, s, 5, &dead_sh, [&] {
       if (alive) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
-    }) && alive;
+    }, p_r ? 0 : kIdleSleepUs) && alive;
     // ---- 6 ROUTE + GEMM1
     if (alive) {
       route_tables<TS>(a, rt, (float*)smem);
