@@ -1671,10 +1671,10 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
 // (= H), and every tile reads all of x, so with one workgroup per tile a few workgroups would
 // each pull a 16 x K weight tile and all of x (32 K bytes each) while the rest idle.  Instead
 // each tile's K is cut into `np` parts of `ps` k-steps (a multiple of 8, so the 8 waves get
-// equal blocks) on np workgroups.  Each part's control wave stores its fp32 partial (64 lanes x 4 values, the
-// epilogue's layout) and counts itself in on the tile's counter; the part that arrives last
-// adds the np partials in part order, so the sum does not depend on the arrival order, writes
-// q, k and v, and clears the counter for the next launch.
+// equal blocks) on np workgroups.  Each part's control wave stores its fp32 partial (64 lanes
+// x 4 values, the epilogue's layout) and counts itself in on the tile's counter; the part that
+// arrives last adds the np partials in part order, so the sum does not depend on the arrival
+// order, writes q, k and v, and clears the counter for the next launch.
 struct QkvSplit {
   int np, ps;
 };
