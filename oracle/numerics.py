@@ -149,14 +149,14 @@ def nvfp4_decode(codes, scales, ts) -> np.ndarray:
     return e2m1_value(c) * s * np.float64(ts)
 
 
-def fp4_act_quant(a32) -> tuple[np.ndarray, np.ndarray]:
+def fp4_act_quant(a) -> tuple[np.ndarray, np.ndarray]:
     """NVFP4 requantisation of the SwiGLU intermediate before the second expert GEMM
     (the pages gather it "in fp4" after the first GEMM).  Tensor scale 1, one E4M3
-    scale per 16 consecutive elements.  The decision takes fp32 inputs -- the
-    precision the kernel holds the intermediate in -- and compares them exactly with
-    6*mid (scale) and mid*s (code); both thresholds are exact in fp32.
+    scale per 16 consecutive elements.  The decisions are taken on the value itself
+    (fp64 here), compared exactly with 6*mid (scale) and mid*s (code): both thresholds
+    have few significant bits and are exact in fp64 (and in fp32).
     Returns (codes uint8 [M][K/2], scales uint8 [M][K/16])."""
-    a = np.asarray(a32, dtype=np.float32).astype(np.float64)
+    a = np.asarray(a, dtype=np.float64)
     M, K = a.shape
     blocks = a.reshape(M, K // 16, 16)
     bmax = np.abs(blocks).max(-1)

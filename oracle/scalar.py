@@ -76,14 +76,13 @@ def _nearest(v: float, grid: list[float]) -> int:
 
 def act_quant_dequant(a: list[float]) -> list[float]:
     """NVFP4 (tensor scale 1) round trip of one intermediate row, block size 16.
-    Decisions on fp32-rounded inputs, compared exactly (Fractions)."""
-    import struct
-    f32 = [struct.unpack("f", struct.pack("f", x))[0] for x in a]
+    Decisions on the values as given, compared exactly (Fractions)."""
+    vals = list(a)
     e4 = [e4m3(b) for b in range(127)]
     g2 = [e2m1(c) for c in range(8)]
     out = []
-    for b0 in range(0, len(f32), 16):
-        blk = f32[b0:b0 + 16]
+    for b0 in range(0, len(vals), 16):
+        blk = vals[b0:b0 + 16]
         amax = max(abs(x) for x in blk)
         si = _nearest_frac(Fraction(amax) / 6, e4)
         s = e4[si]

@@ -211,6 +211,21 @@ def test_scalar_oracle_equals_vectorised_oracle(shape, cfg_id):
     assert np.allclose(a["stats"], st, rtol=1e-12, atol=0)
 
 
+@pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (TINY_NVFP4, 91), (TINY_GQA2, 92)])
+def test_layer_step_auto_equals_layer_step_with_every_expert_packed(shape, cfg_id):
+    """layer_step_auto packs only the experts its own routing reaches; every output equals the
+    step run with all E experts packed (routing does not depend on the experts)."""
+    inp = synth.make_layer_inputs(shape, cfg_id)
+    a = oracle.layer_step_auto(inp)
+    b = oracle.layer_step(inp, oracle.pack_experts(inp))
+    for key in ("attn", "stats", "h1", "xp", "logits64", "logits32", "idx", "gate", "y", "h_out", "q_next",
+                "k_new", "v_new", "k_cache_next", "v_cache_next", "hist", "top14", "qkv64"):
+        assert np.array_equal(a[key], b[key]), key
+    assert a["inter_q"].keys() == b["inter_q"].keys()
+    for k_ in a["inter_q"]:
+        assert all(np.array_equal(x, y) for x, y in zip(a["inter_q"][k_], b["inter_q"][k_]))
+
+
 def test_usage_top_is_count_desc_index_asc():
     idx = np.array([[3, 1], [1, 7], [7, 3], [2, 5]])
     hist, top = oracle.usage_top(idx, 10, 4)

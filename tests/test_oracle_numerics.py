@@ -156,13 +156,21 @@ def test_nvfp4_decode_error_bound():
     assert np.abs(dec - w).max() / np.abs(w).max() < 0.2
 
 
-def test_fp4_act_quant_matches_scalar_oracle_and_is_exact_in_fp32():
+def test_fp4_act_quant_matches_scalar_oracle_on_fp64_values():
     g = np.random.default_rng(7)
-    a = (g.standard_normal((5, 64)) * 0.7).astype(np.float32)
+    a = g.standard_normal((6, 64)) * 0.7
     a[2, :16] = 0
     a[3, 16:32] = 3000.0  # saturating block
+    # a block whose scale is 1 (amax 6) and whose element sits above the 0 / 0.5 midpoint 0.25
+    # by less than fp32 resolution: the decision is taken on the fp64 value, so it rounds up
+    # to 0.5 (an fp32 copy of it would be the midpoint itself, a tie going to the even code 0)
+    a[5, :16] = 0.0
+    a[5, 0] = 6.0
+    a[5, 1] = 0.25 * (1 + 2.0 ** -40)
+    a[5, 2] = 0.25
     codes, scales = oracle.fp4_act_quant(a)
     dec = oracle.nvfp4_decode(codes, scales, 1.0)
+    assert dec[5, 0] == 6.0 and dec[5, 1] == 0.5 and dec[5, 2] == 0.0
     for r in range(a.shape[0]):
         assert np.array_equal(dec[r], np.array(scalar.act_quant_dequant([float(x) for x in a[r]])))
     # the decision thresholds 6*mid(e4m3) and mid(e2m1)*s are exact fp32 numbers
