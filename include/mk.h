@@ -145,16 +145,25 @@ typedef struct {
 size_t mk_workspace_bytes(const mk_layer_cfg *cfg, int T);
 /* Offsets of the hand-off buffers; returns MK_OK or an mk_status. */
 int mk_workspace_query(const mk_layer_cfg *cfg, int T, mk_workspace_layout *out /* [host] */);
-/* Zero the workspace (a fill kernel, no hipMemset).  Call once before first use and after
- * an MK_ETIMEOUT. */
+/* Zero the workspace (a fill kernel, no hipMemset).  Call once before the workspace's first
+ * use.  Launches on a workspace need no re-initialisation afterwards, also not after an
+ * in-kernel error: the status word carries the launch's epoch, and the per-launch counters
+ * are cleared by the launch that uses them. */
 int mk_workspace_init(void *workspace, size_t bytes, void *stream);
 
 /* One fused decoder-layer step (see the file comment).  Enqueues one kernel. */
 int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
                   const mk_step_io *io /* [host] */, void *stream);
 
-/* Copy n new rows into a KV cache pair at rows pos..pos+n-1 (the rest untouched).
- * k_cache, v_cache: bf16 [capacity][n_kv_heads][head_dim]; k_new, v_new: bf16 [n][n_kv_heads][head_dim]. */
+/* KV-cache write: copy n new rows into a KV cache pair at rows pos..pos+n-1, bit for bit,
+ * every other row untouched.  The pages' launch ends with the next layer's KV write, and the
+ * KV history a layer attends over was written by earlier steps (orcarouter.ai write-up,
+ * "where the kernel boundary sits"); this call places rows that no fused launch produced
+ * (a layer's tree rows supplied by the caller, a commit of accepted tokens).
+ * k_cache, v_cache: bf16 [capacity][n_kv_heads][head_dim] (DEVICE, caller-owned, written);
+ * k_new, v_new: bf16 [n][n_kv_heads][head_dim] (DEVICE, read).  n >= 0 (0 enqueues nothing);
+ * n_kv_heads * head_dim % 8 == 0 else MK_ESHAPE; pos < 0 or pos + n > capacity -> MK_ECAPACITY;
+ * any pointer not 16-byte aligned -> MK_EALIGN.  Enqueues one kernel. */
 int mk_kv_append(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int head_dim, int pos,
                  const void *k_new, const void *v_new, int n, void *stream);
 
@@ -202,14 +211,23 @@ int mk_kv_commit(void *k_cache, void *v_cache, int capacity, int n_kv_heads, int
 int mk_kv_commit_layers(void *const *k_caches, void *const *v_caches, int n_layers, int capacity, int n_kv_heads,
                         int head_dim, int ctx, const int32_t *path, const int32_t *n_path, int T, void *stream);
 
-/* Router on its own: logits = x . w_router^T (+ bias) in fp32, then the top-k experts per
- * token ordered by (logit desc, index asc) and softmax gates over the k selected logits.
- * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k];
- * gate fp32 [T][k]; logits fp32 [T][E] or NULL.  T <= 64, E <= 256, k <= 8, P % 8 == 0. */
+/* Router on its own: the layer's router sends each token to 8 of 256 experts (orcarouter.ai
+ * write-up, "where the kernel boundary sits"; the selection rule and the gates are not
+ * printed: top-k by (logit desc, index asc), softmax over the k selected logits).
+ * logits = x . w_router^T (+ bias) in fp32 with fp32 accumulation, then the top-k experts per
+ * token ordered by (logit desc, index asc) and softmax gates over the k selected logits --
+ * the same selection the fused launch makes.
+ * x bf16 [T][P]; w_router bf16 [E][P]; bias fp32 [T][E] or NULL; idx int32 [T][k] (written);
+ * gate fp32 [T][k] (written); logits fp32 [T][E] or NULL (written); all DEVICE, caller-owned.
+ * 1 <= T <= 64, E <= 256, 1 <= k <= min(8, E), P % 8 == 0, else MK_ESHAPE; x and w_router
+ * 16-byte aligned, else MK_EALIGN.  Enqueues one kernel. */
 int mk_route_topk(const void *x, const void *w_router, const float *bias, int T, int P, int E, int k,
                   int32_t *idx, float *gate, float *logits, void *stream);
 
-/* NVFP4 quantisation of `batch` matrices w [batch][N][K] (bf16 when w_is_fp32 == 0, else
+/* NVFP4 weight packing: the routed experts are stored as 4-bit NVFP4 (orcarouter.ai write-up,
+ * "where the kernel boundary sits"); the format's details are its public definition (E2M1
+ * codes, an E4M3 scale per 16 elements, an fp32 tensor scale).
+ * Quantisation of `batch` matrices w [batch][N][K] (bf16 when w_is_fp32 == 0, else
  * fp32), K % 16 == 0.  Per matrix: tensor scale ts = fp32(amax) / 2688 (1 when amax = 0);
  * per 16-element block: E4M3 scale s = RNE(amax_block / (6 ts)) saturating at 448;
  * per element: E2M1 code = RNE(x / (s ts)) saturating at +-6, ties to the even code, a zero
@@ -232,8 +250,9 @@ int mk_nvfp4_tile_w1(const uint8_t *codes, const uint8_t *scales, int batch, int
 /* Bytes of mk_nvfp4_tile_w1's scales_t, or 0 for an unsupported shape. */
 size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K);
 
-/* Synchronise `stream` and return the status word of the last mk_layer_step on this
- * workspace (MK_OK, MK_EBADTREE or MK_ETIMEOUT), or MK_EHIP if the copy failed. */
+/* Synchronise `stream` and return the in-kernel status of the last mk_layer_step on this
+ * workspace (MK_OK, MK_EBADTREE or MK_ETIMEOUT), or MK_EHIP if a copy failed.  An error of an
+ * earlier launch is not reported once a later launch has run. */
 int mk_read_status(const void *workspace, void *stream);
 
 /* Human-readable name of a status code. */

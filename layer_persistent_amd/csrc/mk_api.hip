@@ -109,8 +109,8 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   const int H = c->hidden, Hq = c->n_q_heads, d = c->head_dim, P = c->pooled, E = c->n_experts,
             k = c->top_k, I = c->expert_inter;
   size_t o = 0;
-  L.status = o; o = up256(o + 4);
-  L.epoch = o; o = up256(o + (size_t)n_wg * 64);
+  L.status = o; o = up256(o + 4);               // mk::kStatusOffset
+  L.epoch = o; o = up256(o + (size_t)n_wg * 64); // mk::kEpochOffset
   L.flags = o; o = up256(o + (size_t)n_wg * 64);
   L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
   L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
@@ -246,7 +246,7 @@ int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_ste
   a.w1_codes = w->w1_codes; a.w1_scales = w->w1_scales; a.w2_codes = w->w2_codes; a.w2_scales = w->w2_scales;
   a.w1_ts = w->w1_tscale; a.w2_ts = w->w2_tscale;
   char* ws = (char*)io->workspace;
-  a.status = (int32_t*)(ws + L.status);
+  a.status = (uint32_t*)(ws + L.status);
   a.epoch = (uint32_t*)(ws + L.epoch);
   a.flags = (uint32_t*)(ws + L.flags);
   a.part_o = (float*)(ws + L.part_o);
@@ -361,9 +361,12 @@ size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K) {
 int mk_read_status(const void* workspace, void* stream) {
   if (!workspace) return MK_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_EHIP;
-  int32_t st = 0;
-  if (hipMemcpy(&st, workspace, 4, hipMemcpyDeviceToHost) != hipSuccess) return MK_EHIP;
-  return st;
+  // the status word and workgroup 0's epoch slot, which the last launch left one past its own
+  uint32_t st = 0, ep = 0;
+  if (hipMemcpy(&st, (const char*)workspace + mk::kStatusOffset, 4, hipMemcpyDeviceToHost) != hipSuccess ||
+      hipMemcpy(&ep, (const char*)workspace + mk::kEpochOffset, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return MK_EHIP;
+  return mk::status_is_error_of(st, ep - 1u) ? mk::status_code(st) : MK_OK;
 }
 
 }  // extern "C"

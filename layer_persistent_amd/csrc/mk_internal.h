@@ -10,6 +10,22 @@
 
 namespace mk {
 
+// The workspace starts with the status word (offset 0) and the per-workgroup epoch slots
+// (offset 256, 64 bytes apart), at these offsets for every configuration.
+constexpr size_t kStatusOffset = 0;
+constexpr size_t kEpochOffset = 256;
+
+// Status word of a launch: the low 24 bits of the launch's epoch above an 8-bit status code
+// (0 = ok).  A code is only acted on (waits abort, mk_read_status reports it) when its epoch
+// is the current launch's, so an error never outlives the launch that raised it.
+__host__ __device__ inline uint32_t status_word(uint32_t epoch, int code) {
+  return ((epoch & 0xFFFFFFu) << 8) | ((uint32_t)code & 0xFFu);
+}
+__host__ __device__ inline bool status_is_error_of(uint32_t word, uint32_t epoch) {
+  return (word & 0xFFu) != 0 && (word >> 8) == (epoch & 0xFFFFFFu);
+}
+__host__ __device__ inline int status_code(uint32_t word) { return (int)(int8_t)(word & 0xFFu); }
+
 // Kernel arguments of one fused layer launch (passed by value).
 struct KArgs {
   // shapes
@@ -35,7 +51,7 @@ struct KArgs {
   const uint8_t *w1_codes, *w1_scales, *w2_codes, *w2_scales;
   const float *w1_ts, *w2_ts;
   // workspace
-  int32_t* status;
+  uint32_t* status;           // status word (status_word)
   uint32_t *epoch, *flags;
   float *part_o, *part_ml;
   uint16_t *attn, *h1, *xp;   // hand-off activations, [16][K] bf16 in MFMA fragment order

@@ -128,7 +128,8 @@ struct Ctl {              // control-wave state shared through LDS
 
 struct Sync {
   uint32_t* flags;        // per-workgroup flags of the grid hand-off (see ctl_signal_wait)
-  int32_t* status;
+  uint32_t* status;       // status word (status_word: epoch-tagged code)
+  uint32_t epoch;         // this launch's epoch
   uint32_t base;          // epoch * 64
   int spin_limit;
   int skip_wg;
@@ -140,7 +141,7 @@ struct Sync {
 // a flag landing is seen about half a round trip later.  `idle_us` (about 1 us each) delays the
 // first poll of a workgroup that had no work in a phase where the others work for ~2 us: its polls
 // of the flags would only add memory traffic while they work.  Returns false when the wait
-// expired or the launch was aborted (status word set).
+// expired or the launch was aborted (this launch's error code in the status word).
 __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead, int idle_us = 0) {
   const int lane = threadIdx.x & 63;
   const int n = gridDim.x;
@@ -172,13 +173,14 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
     b = poll();
     polls += 2;
     if (polls >= s.spin_limit) {
-      if (lane == 0) __hip_atomic_store(s.status, (int32_t)MK_ETIMEOUT_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) __hip_atomic_store(s.status, status_word(s.epoch, MK_ETIMEOUT_DEV), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __builtin_amdgcn_s_waitcnt(0);
       return false;
     }
     if ((polls & 63) == 0) {
-      const int st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__any(st != 0)) { __builtin_amdgcn_s_waitcnt(0); return false; }
+      // only an error raised by this launch aborts it (an earlier launch's code is stale)
+      const uint32_t st = __hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__any(status_is_error_of(st, s.epoch))) { __builtin_amdgcn_s_waitcnt(0); return false; }
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -1674,7 +1676,10 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
 // equal blocks) on np workgroups.  Each part's control wave stores its fp32 partial (64 lanes
 // x 4 values, the epilogue's layout) and counts itself in on the tile's counter; the part that
 // arrives last adds the np partials in part order, so the sum does not depend on the arrival
-// order, writes q, k and v, and clears the counter for the next launch.
+// order, writes q, k and v.  Tile t's counter is cleared at the start of every launch by the
+// control wave of workgroup t, whose store completes before it first signals; every part
+// counts in only after the last grid hand-off, so it always finds the cleared counter (also
+// after an aborted launch left it part-way).
 struct QkvSplit {
   int np, ps;
 };
@@ -1708,7 +1713,6 @@ __device__ __forceinline__ void qkv_split_epilogue(const KArgs& a, const float* 
   if (lane == 0) old = __hip_atomic_fetch_add(a.qkv_cnt + tile * 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old != (uint32_t)(np - 1)) return;
-  if (lane == 0) st_coh_u32(a.qkv_cnt + tile * 16, 0u);
   float sum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < np; ++p) {
     float u[4] = {v[0], v[1], v[2], v[3]};
@@ -1813,6 +1817,8 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (l == 0) {
       epoch_sh = ep;
       dead_sh = 0;
+      // this launch's split-K qkv arrival counter of tile blockIdx.x starts at zero
+      if (q_split && (int)blockIdx.x < q_nt) st_coh_u32(a.qkv_cnt + blockIdx.x * 16, 0u);
     }
   }
   // the first attention item's queries and first K/V batch load during the setup
@@ -1850,7 +1856,8 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (lane == 0) {
       tr.bad = bad;
       if (bad && blockIdx.x == 0)
-        __hip_atomic_store(a.status, (int32_t)MK_EBADTREE_DEV, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.status, status_word(epoch_sh, MK_EBADTREE_DEV), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   wg_sync();
@@ -1859,6 +1866,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   Sync s;
   s.flags = a.flags;
   s.status = a.status;
+  s.epoch = epoch;
   s.base = epoch * 64u;
   s.spin_limit = a.spin_limit;
   s.skip_wg = a.skip_wg;

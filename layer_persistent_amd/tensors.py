@@ -181,5 +181,5 @@ def outputs(st: DeviceStep) -> dict:
         h1=untile_frag(st.ws_u16(L.h1, 16 * c.hidden), sh_T, c.hidden),
         xp=untile_frag(st.ws_u16(L.xp, 16 * c.pooled), sh_T, c.pooled),
         y=untile_frag(st.ws_u16(L.y, 16 * c.pooled), sh_T, c.pooled),
-        status=int(st.ws_f32(L.status, 1).view(np.int32)[0]),
+        status=abi.mk_read_status(st.workspace),
     )

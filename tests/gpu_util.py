@@ -51,6 +51,63 @@ def fp32_dot_bound(x_bits, w_bits) -> np.ndarray:
     return (K * u / (1 - K * u)) * (x @ w.T)
 
 
+# fp32 unit roundoff taken as 2^-23 (not 2^-24) so that the bounds below also hold if an
+# accumulation step truncates instead of rounding to nearest
+U32 = 2.0 ** -23
+U64 = 2.0 ** -53
+MISMATCH_CEILING = 0.005     # at most this fraction of an anchored stage's elements may differ
+
+
+def rounding_band(x_bits, w_bits, residual_bits=None, extra_terms: int = 16):
+    """Exact value v = x . W^T (+ residual) of a dense stage on bf16 inputs, and a rigorous
+    bound B on |fp32 result - v| for any fp32 summation order: every product of two bf16
+    values is exact in fp32, a sum of n terms is within gamma_n sum|x||w| (n = K plus
+    `extra_terms` for partial sums combined afterwards), and the residual add rounds once
+    more.  The fp64 evaluation of v adds its own (tiny) error bound."""
+    x = oracle.bf16_to_f64(x_bits)
+    w = oracle.bf16_to_f64(w_bits)
+    v = x @ w.T
+    if residual_bits is not None:
+        v = v + oracle.bf16_to_f64(residual_bits)
+    n = x.shape[1] + extra_terms
+    g32 = n * U32 / (1 - n * U32)
+    g64 = (n + 2) * U64 / (1 - (n + 2) * U64)
+    mag = np.abs(x) @ np.abs(w).T
+    B = (g32 + g64) * mag
+    if residual_bits is not None:
+        B = B + U32 * (np.abs(v) + B)
+    B = B + 2.0 ** -50 * np.abs(v)
+    return v, B
+
+
+def assert_rounding_exact(name, gpu_bits, x_bits, w_bits, residual_bits=None, ceiling=MISMATCH_CEILING):
+    """An anchored dense stage, bf16(x . W^T (+ residual)) with fp32 accumulation, against the
+    exact value v.  With B the rigorous fp32 error bound (rounding_band), every GPU element
+    must lie between bf16(v - B) and bf16(v + B): it equals the correctly rounded oracle value
+    bit for bit unless v lies within B of a bf16 rounding boundary ("ambiguous"), and even
+    then it is one of the two roundings.  The elements that differ from the oracle's
+    rounding may be at most `ceiling` of the tensor (at least 2): a correct kernel differs
+    only where its accumulation error crosses a boundary, a fraction of a percent."""
+    gpu_bits = np.asarray(gpu_bits, np.uint16)
+    assert not np.any(gpu_bits == 0xFFFF), f"{name}: unwritten (poison) elements"
+    v, B = rounding_band(x_bits, w_bits, residual_bits)
+    assert gpu_bits.shape == v.shape, (name, gpu_bits.shape, v.shape)
+    ref = oracle.bf16_round(v)
+    lo = oracle.bf16_to_f64(oracle.bf16_round(v - B))
+    hi = oracle.bf16_to_f64(oracle.bf16_round(v + B))
+    g = oracle.bf16_to_f64(gpu_bits)
+    outside = ~((g >= lo) & (g <= hi))
+    ambiguous = int(np.count_nonzero(lo != hi))
+    mismatch = int(np.count_nonzero(gpu_bits != ref))
+    limit = max(2, int(ceiling * gpu_bits.size))
+    log(f"  {name}: {gpu_bits.size - mismatch}/{gpu_bits.size} bit-equal to the oracle's rounding, "
+        f"{mismatch} differ (limit {limit}), {ambiguous} within the fp32 bound of a rounding boundary, "
+        f"{int(outside.sum())} outside the bound")
+    assert not outside.any(), f"{name}: {int(outside.sum())} elements outside the rigorous fp32 band"
+    assert mismatch <= limit, f"{name}: {mismatch} elements differ from the oracle's rounding (limit {limit})"
+    return mismatch, ambiguous
+
+
 def check_routing(gpu_logits, gpu_idx, gpu_gate, ref_logits64, bias, k, max_dlogit):
     """Routing parity: (i) indices equal the stable full sort of the GPU's own logits, always;
     (ii) equal the oracle's except where the oracle's k-th / (k+1)-th gap is within the

@@ -14,7 +14,8 @@ if torch.cuda.is_available():
     import layer_persistent_amd as mk
     from layer_persistent_amd import tensors as dt
 
-from gpu_util import (assert_close_bf16, assert_stats, check_routing, fp32_dot_bound, log)
+from gpu_util import (assert_close_bf16, assert_rounding_exact, assert_stats, check_routing, fp32_dot_bound,
+                      log, max_abs_rel)
 
 SMALL_NVFP4 = synth.LayerShape("small-tree-swa-nvfp4", 256, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
 SMALL_GQA = synth.LayerShape("small-tree-gqa2-global-bf16", 256, 8, 2, 64, 128, 32, 3, 64, 0, 200, 16, False)
@@ -137,16 +138,14 @@ def test_qkv_prologue_against_the_oracle(T, H, Hq, Hkv, d, cap, pos):
     torch.cuda.synchronize()
     q_ref, k_ref, v_ref, _ = oracle.qkv_project(h, w, Hq, Hkv, d)
     kg, vg = dt.host_u16(K), dt.host_u16(V)
+    qd, kd = Hq * d, Hkv * d
     assert_close_bf16("prologue q", dt.host_u16(q_out), q_ref)
-    assert_close_bf16("prologue k", kg[pos:pos + T], k_ref)
-    assert_close_bf16("prologue v", vg[pos:pos + T], v_ref)
+    assert_rounding_exact("prologue q", dt.host_u16(q_out), h, w[:qd])
+    assert_rounding_exact("prologue k", kg[pos:pos + T].reshape(T, -1), h, w[qd:qd + kd])
+    assert_rounding_exact("prologue v", vg[pos:pos + T].reshape(T, -1), h, w[qd + kd:])
     rest = np.ones(cap, bool)
     rest[pos:pos + T] = False
     assert np.array_equal(kg[rest], kc[rest]) and np.array_equal(vg[rest], vc[rest])
-    # one rounding of an fp32 sum: nearly every element equals the fp64 oracle's rounding
-    exact = np.mean(dt.host_u16(q_out) == q_ref)
-    log(f"  q equal to the oracle's bf16 bit for bit: {exact:.4f} of elements")
-    assert exact > 0.95
 
 
 def test_tree_accept_and_kv_commit_against_the_oracle():
@@ -223,8 +222,62 @@ def _run(inp, timestamps=False, st=None, dw=None):
     return dw, st, out
 
 
-def _check_layer(inp, out, n_sample_pairs=None):
-    """Stage-local parity (each stage's oracle fed the GPU's own stage inputs) and end-to-end."""
+def _pack_used(inp, gpu_idx):
+    """The layer's experts in storage format, packed by the oracle for every expert that the
+    GPU's routing or the oracle's own (end-to-end) routing selects; the others stay None.
+    oracle.layer_step on these equals oracle.layer_step_auto (which packs the oracle's set)."""
+    sh = inp.shape
+    if not sh.nvfp4:
+        return oracle.pack_experts(inp)
+    attn, _ = oracle.attention(inp.q_in, inp.k_cache, inp.v_cache, inp.parent, sh.ctx, sh.window, sh.n_q_heads,
+                               sh.n_kv_heads, sh.head_dim)
+    xp = oracle.dense(oracle.dense(attn, inp.w_o, inp.h_in), inp.w_pool)
+    _, _, idx, _ = oracle.router(xp, inp.w_router, inp.router_bias, sh.top_k)
+    return oracle.pack_experts(inp, sorted(set(np.unique(idx).tolist()) | set(np.unique(gpu_idx).tolist())))
+
+
+def _end_to_end_reference(inp, out, ex, logit_bound: float) -> dict:
+    """The oracle's layer step from the launch's own inputs, for the end-to-end comparison.
+
+    Upstream roundings (attention's softmax, then each bf16 stage) make the GPU's xp differ
+    from the oracle's in a few low bits, so the two routers' logits differ by at most delta
+    per token (the change those xp differences can cause, plus the fp32 bound).  Where a
+    token's logits are that close, more than one selection (or order of it) is correct.  Rank
+    statistics move by at most delta when every value does, so a correct GPU selection
+    satisfies, at every rank j, |z(gpu's j-th expert) - z(oracle's j-th expert)| <= 2 delta on
+    the oracle's logits z; every token that differs must pass that.  For them the reference
+    takes the GPU's selection (the oracle step anchored on the GPU's indices and gates); every
+    other token's selection is the oracle's own, which the GPU's equals."""
+    sh = inp.shape
+    ref = oracle.layer_step(inp, ex)
+    flip = [t for t in range(sh.T) if list(ref["idx"][t]) != list(out["idx"][t])]
+    dxp = oracle.bf16_to_f64(out["xp"]) - oracle.bf16_to_f64(ref["xp"])
+    dlog = np.abs(dxp) @ np.abs(oracle.bf16_to_f64(inp.w_router)).T
+    log(f"  end-to-end: xp differs from the oracle's in {int(np.count_nonzero(dxp))} of {dxp.size} elements; "
+        f"{len(flip)} token(s) routed differently from the oracle's own routing")
+    for t in flip:
+        z = ref["logits32"][t].astype(np.float64)
+        delta = dlog[t].max() + logit_bound
+        worst = float(np.abs(z[out["idx"][t]] - z[ref["idx"][t]]).max())
+        log(f"    token {t}: gpu {out['idx'][t].tolist()} oracle {ref['idx'][t].tolist()}, "
+            f"largest rank-wise logit difference {worst:.3e} <= 2 delta = {2 * delta:.3e}")
+        assert worst <= 2 * delta, f"token {t}: routing differs end-to-end by {worst} > {2 * delta}"
+    if flip:
+        ref = oracle.layer_step(inp, ex, anchors={"idx": out["idx"], "gate": out["gate"].astype(np.float64)})
+    for key in ("h1", "xp", "y"):
+        log(f"  {key} end-to-end: max-abs-rel {max_abs_rel(out[key], ref[key]):.3e}")
+    return ref
+
+
+def _check_layer(inp, out, last: bool = False):
+    """Stage-local parity (each stage's oracle fed the GPU's own stage inputs) and end-to-end.
+
+    The dense stages (o-proj, pooler, unpooler, next-layer q / k / v and the KV write) are
+    checked rounding-exact (assert_rounding_exact): their bf16 outputs equal the oracle's
+    correctly rounded values except where the exact value lies within the rigorous fp32 bound
+    of a rounding boundary, and only a fraction of a percent may differ at all.  The residual
+    stream's magnitude therefore hides no error in the o-proj or unpooler contributions.
+    `last`: the stack's last layer, which ends after the unpooler (no next-layer q / k / v)."""
     sh = inp.shape
     T, ctx = sh.T, sh.ctx
     assert out["status"] == 0, mk.mk_strerror(out["status"])
@@ -233,8 +286,8 @@ def _check_layer(inp, out, n_sample_pairs=None):
     assert_close_bf16("attn", out["attn"], attn)
     assert_stats("attn stats m", out["stats"][..., 0], stats[..., 0])
     assert_stats("attn stats l", out["stats"][..., 1], stats[..., 1])
-    assert_close_bf16("h1 (anchored on gpu attn)", out["h1"], oracle.dense(out["attn"], inp.w_o, inp.h_in))
-    assert_close_bf16("xp (anchored on gpu h1)", out["xp"], oracle.dense(out["h1"], inp.w_pool))
+    assert_rounding_exact("h1 = o-proj + residual (anchored on gpu attn)", out["h1"], out["attn"], inp.w_o, inp.h_in)
+    assert_rounding_exact("xp = pooler (anchored on gpu h1)", out["xp"], out["h1"], inp.w_pool)
     l64, _, _, _ = oracle.router(out["xp"], inp.w_router, None, sh.top_k)
     bias = inp.router_bias
     bound = fp32_dot_bound(out["xp"], inp.w_router)
@@ -244,25 +297,31 @@ def _check_layer(inp, out, n_sample_pairs=None):
     check_routing(out["logits"], out["idx"], out["gate"], l64, bias, sh.top_k, float(bound.max()))
     hist = np.bincount(out["idx"].reshape(-1), minlength=sh.n_experts)
     assert np.array_equal(out["hist"], hist)
-    used = sorted(set(np.unique(out["idx"]).tolist()))
-    ex = oracle.pack_experts(inp, used)
+    # the experts packed once, for both the anchored check and the end-to-end step: those the
+    # GPU routed to and those the oracle's own routing reaches
+    ex = _pack_used(inp, out["idx"])
     y_ref, _ = oracle.moe(out["xp"], out["idx"], out["gate"].astype(np.float64), ex, sh.expert_inter)
     assert_close_bf16("y (anchored on gpu xp, routing)", out["y"], y_ref)
-    assert_close_bf16("h_out (anchored on gpu y, h1)", out["h_out"], oracle.dense(out["y"], inp.w_unpool, out["h1"]))
-    qkv = oracle.bf16_to_f64(out["h_out"]) @ oracle.bf16_to_f64(inp.w_qkv_next).T
+    assert_rounding_exact("h_out = unpooler + residual (anchored on gpu y, h1)", out["h_out"], out["y"], inp.w_unpool,
+                          out["h1"])
+    ref = _end_to_end_reference(inp, out, ex, float(bound.max()))
+    if last:
+        assert_close_bf16("h_out end-to-end", out["h_out"], ref["h_out"])
+        return
     qd, kd = sh.n_q_heads * sh.head_dim, sh.n_kv_heads * sh.head_dim
-    assert_close_bf16("q_next (anchored on gpu h_out)", out["q_next"], oracle.bf16_round(qkv[:, :qd]))
+    wq = inp.w_qkv_next
     kn = out["k_cache_next"].reshape(sh.kv_capacity, -1)
     vn = out["v_cache_next"].reshape(sh.kv_capacity, -1)
-    assert_close_bf16("k_new (anchored)", kn[ctx:ctx + T], oracle.bf16_round(qkv[:, qd:qd + kd]))
-    assert_close_bf16("v_new (anchored)", vn[ctx:ctx + T], oracle.bf16_round(qkv[:, qd + kd:]))
+    assert_rounding_exact("q_next (anchored on gpu h_out)", out["q_next"], out["h_out"], wq[:qd])
+    # the KV write: rounding-exact against the oracle re-anchored on the GPU's h_out
+    assert_rounding_exact("k_new, KV write (anchored on gpu h_out)", kn[ctx:ctx + T], out["h_out"], wq[qd:qd + kd])
+    assert_rounding_exact("v_new, KV write (anchored on gpu h_out)", vn[ctx:ctx + T], out["h_out"], wq[qd + kd:])
     # every other row of the next layer's cache is untouched, bit for bit
     k0 = inp.k_cache_next.reshape(sh.kv_capacity, -1)
     v0 = inp.v_cache_next.reshape(sh.kv_capacity, -1)
     assert np.array_equal(kn[:ctx], k0[:ctx]) and np.array_equal(kn[ctx + T:], k0[ctx + T:])
     assert np.array_equal(vn[:ctx], v0[:ctx]) and np.array_equal(vn[ctx + T:], v0[ctx + T:])
     # end to end, no anchoring
-    ref = oracle.layer_step_auto(inp)
     assert_close_bf16("h_out end-to-end", out["h_out"], ref["h_out"])
     assert_close_bf16("q_next end-to-end", out["q_next"], ref["q_next"])
     assert_close_bf16("k_new end-to-end", kn[ctx:ctx + T], ref["k_new"].reshape(T, -1))
@@ -375,25 +434,36 @@ def test_repeated_steps_on_one_workspace(shape, cfg_id):
         assert_close_bf16(f"step {step} v_new", vn[ctx:ctx + T], ref["v_new"].reshape(T, -1))
 
 
-def test_bad_tree_reports_status():
+def test_bad_tree_reports_status_and_does_not_outlive_its_launch():
+    """A malformed tree sets MK_EBADTREE for that launch; the next launch on the same workspace
+    (no re-initialisation) runs normally, matches the oracle, and reports MK_OK -- also with a
+    short spin limit, so that any wait that polls the status word sees the stale code."""
     inp = synth.make_layer_inputs(SMALL_NVFP4, 86)
-    inp.parent[5] = 9   # parent after child
+    bad = inp.parent.copy()
+    bad[5] = 9   # parent after child
     dw = dt.upload_weights(inp)
     st = dt.make_step(inp)
+    st.parent.copy_(torch.from_numpy(bad).cuda())
     dt.run_step(dw, st)
     assert mk.mk_read_status(st.workspace) == mk.MK_EBADTREE
+    st.parent.copy_(torch.from_numpy(inp.parent.astype(np.int32)).cuda())
+    dt.run_step(dw, st, spin_limit=4096)
+    out = dt.outputs(st)
+    assert out["status"] == mk.MK_OK and mk.mk_read_status(st.workspace) == mk.MK_OK
+    _check_layer(inp, out)
 
 
 def test_stalled_workgroup_times_out_instead_of_hanging():
-    """A workgroup that never signals (host-set test hook) makes every bounded wait expire."""
-    inp = synth.make_layer_inputs(SMALL_NVFP4, 87)
+    """A workgroup that never signals (host-set test hook) makes every bounded wait expire; the
+    next launches on the same workspace, with no re-initialisation, run normally."""
+    inp = synth.make_layer_inputs(SMALL_H1280, 87)
     dw = dt.upload_weights(inp)
     st = dt.make_step(inp)
     dt.run_step(dw, st, spin_limit=2000, skip_wg=5)
     assert mk.mk_read_status(st.workspace) == mk.MK_ETIMEOUT
-    # after re-initialising the workspace a normal launch works
-    mk.mk_workspace_init(st.workspace, st.workspace.numel())
-    dt.run_step(dw, st)
-    out = dt.outputs(st)
-    assert out["status"] == 0
-    assert_close_bf16("h_out after recovery", out["h_out"], oracle.layer_step_auto(inp)["h_out"])
+    for _ in range(2):
+        st.hist.zero_()                     # the usage histogram accumulates over launches
+        dt.run_step(dw, st)
+        out = dt.outputs(st)
+        assert out["status"] == mk.MK_OK
+        _check_layer(inp, out)

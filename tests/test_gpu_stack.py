@@ -4,6 +4,7 @@ layer against the oracle and, run in one go by the stack runner, bit for bit aga
 layer-by-layer chain, and the stack's verify step replayed as one HIP graph."""
 from __future__ import annotations
 
+import ctypes
 import dataclasses
 
 import numpy as np
@@ -13,10 +14,11 @@ import torch
 import oracle
 import synth
 import layer_persistent_amd as mk
+from layer_persistent_amd import _abi as abi
 from layer_persistent_amd import tensors as dt
 from layer_persistent_amd.stack import Stack, is_global
 
-from gpu_util import assert_close_bf16, log
+from gpu_util import assert_close_bf16, assert_rounding_exact, log
 from test_gpu_parity import SMALL_NVFP4, _check_layer
 
 pytestmark = pytest.mark.gpu
@@ -93,12 +95,7 @@ def test_small_stack_layer_by_layer_and_in_one_go():
         st = dt.make_step(inp)
         dt.run_step(dw, st)
         out = dt.outputs(st)
-        if L + 1 < N_LAYERS:
-            _check_layer(inp, out)
-        else:
-            assert out["status"] == 0
-            ref = oracle.layer_step_auto(inp)
-            assert_close_bf16("last layer h_out end-to-end", out["h_out"], ref["h_out"])
+        _check_layer(inp, out, last=L + 1 == N_LAYERS)
         chain.append(out)
         prev = out
     # the stack runner, all launches back to back on one stream
@@ -186,9 +183,11 @@ def test_stack_step_from_embeddings_with_the_prologue():
     mk.mk_qkv_prologue(dt.dev_u16(step_in["h_in"]), stk_p.w_qkv0, T, H, Hq, Hkv, d, q0, kc, vc, cap, ctx)
     torch.cuda.synchronize()
     q_ref, k_ref, v_ref, _ = oracle.qkv_project(step_in["h_in"], _host(stk_p.w_qkv0), Hq, Hkv, d)
+    w0 = _host(stk_p.w_qkv0)
     assert_close_bf16("prologue q", _host(q0), q_ref)
-    assert_close_bf16("prologue k", _host(kc)[ctx:ctx + T], k_ref)
-    assert_close_bf16("prologue v", _host(vc)[ctx:ctx + T], v_ref)
+    assert_rounding_exact("prologue q", _host(q0), step_in["h_in"], w0[:Hq * d])
+    assert_rounding_exact("prologue k", _host(kc)[ctx:ctx + T].reshape(T, -1), step_in["h_in"], w0[Hq * d:(Hq + Hkv) * d])
+    assert_rounding_exact("prologue v", _host(vc)[ctx:ctx + T].reshape(T, -1), step_in["h_in"], w0[(Hq + Hkv) * d:])
     # the plain stack given the prologue's outputs
     stk = Stack(sh, CFG_ID, N_LAYERS)
     stk.set_step_inputs(dict(step_in, q_in=_host(q0), k_tree=_host(kc)[ctx:ctx + T], v_tree=_host(vc)[ctx:ctx + T]))
@@ -261,3 +260,92 @@ def test_stack_accept_and_commit_closes_the_step():
         assert np.array_equal(_host(lay.k_cache).reshape(cap, -1), ek), L
         assert np.array_equal(_host(lay.v_cache).reshape(cap, -1), ev), L
     log(f"  accepted {n} of {T} nodes; committed in all {N_LAYERS} layers")
+
+
+# ---------------------------------------------------------------- the 62-layer shard-shape stack
+
+STACK62_CHECKED = (0, 1, 3, 61)
+
+
+@pytest.fixture(scope="module")
+def stack62_step0():
+    """Step 0 of the 62-layer stack at one GPU's shard shape (46 SWA-2048 + 16 global layers,
+    ctx 4096, NVFP4 experts), launched layer by layer on one stream as the stack runs it.  For
+    the checked layers, the launch's inputs are copied out before it and its outputs and stage
+    hand-off buffers after it (those launches also return gates, logits, softmax statistics and
+    the usage histogram)."""
+    sh, cfg_id, n_layers = synth.CFG4, 4, 62
+    T, E, k, cap = sh.T, sh.n_experts, sh.top_k, sh.kv_capacity
+    log(f"[stack62] building {n_layers} layers")
+    stk = Stack(sh, cfg_id, n_layers)
+    step_in = synth.stack_step_inputs(sh, cfg_id, 0)
+    stk.set_step_inputs(step_in)
+    structs = stk.structs(False, False)
+    sp = torch.cuda.current_stream().cuda_stream
+    f32 = dict(dtype=torch.float32, device="cuda")
+    snaps = {}
+    for L in range(n_layers):
+        c, w, io = structs[L]
+        lay = stk.layers[L]
+        if L not in STACK62_CHECKED:
+            assert stk.lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io), sp) == 0
+            continue
+        log(f"[stack62] layer {L}: launch and copy out")
+        nxt = stk.layers[L + 1] if L + 1 < n_layers else None
+        snap = dict(h_in=_host(stk.h[L % 2]), q_in=_host(stk.q[L % 2]), k_cache=_host(lay.k_cache),
+                    v_cache=_host(lay.v_cache),
+                    kn=_host(nxt.k_cache) if nxt else None, vn=_host(nxt.v_cache) if nxt else None)
+        gate, logits = torch.zeros((T, k), **f32), torch.zeros((T, E), **f32)
+        stats, hist = torch.zeros((T, sh.n_q_heads, 2), **f32), torch.zeros(E, dtype=torch.int32, device="cuda")
+        io2 = abi.mk_step_io.from_buffer_copy(io)
+        io2.topk_gate, io2.router_logits = gate.data_ptr(), logits.data_ptr()
+        io2.attn_stats, io2.expert_hist = stats.data_ptr(), hist.data_ptr()
+        assert stk.lib.mk_layer_step(ctypes.byref(c), ctypes.byref(w), ctypes.byref(io2), sp) == 0
+        torch.cuda.synchronize()
+        lw = abi.mk_workspace_query(c, T)
+        ws = stk.ws
+        u16 = lambda off, n: ws[off:off + 2 * n].cpu().numpy().view(np.uint16)
+        Hqd = sh.n_q_heads * sh.head_dim
+        snap["out"] = dict(
+            status=mk.mk_read_status(ws), h_out=_host(stk.h[(L + 1) % 2]),
+            q_next=_host(stk.q[(L + 1) % 2]) if nxt else None,
+            k_cache_next=_host(nxt.k_cache) if nxt else None, v_cache_next=_host(nxt.v_cache) if nxt else None,
+            idx=lay.topk_idx.cpu().numpy(), gate=gate.cpu().numpy(), logits=logits.cpu().numpy(),
+            stats=stats.cpu().numpy(), hist=hist.cpu().numpy(),
+            attn=dt.untile_frag(u16(lw.attn, 16 * Hqd), T, Hqd),
+            h1=dt.untile_frag(u16(lw.h1, 16 * sh.hidden), T, sh.hidden),
+            xp=dt.untile_frag(u16(lw.xp, 16 * sh.pooled), T, sh.pooled),
+            y=dt.untile_frag(u16(lw.y, 16 * sh.pooled), T, sh.pooled))
+        snaps[L] = snap
+    torch.cuda.synchronize()
+    assert mk.mk_read_status(stk.ws) == 0
+    del stk
+    torch.cuda.empty_cache()
+    return snaps
+
+
+@pytest.mark.parametrize("L", STACK62_CHECKED)
+def test_stack62_shard_shape_layer_against_the_oracle(stack62_step0, L):
+    """Layers 0, 1, 3 (sliding window) and 61 (the last: no next-layer projection) of step 0
+    of the full 62-layer stack at the shard shape, each against the oracle fed that launch's
+    own inputs: stage by stage (rounding-exact dense stages and KV write) and end to end."""
+    sh0, cfg_id = synth.CFG4, 4
+    sh = dataclasses.replace(sh0, window=0 if is_global(L) else sh0.window)
+    snap = stack62_step0[L]
+    log(f"[stack62 layer {L}] {'global' if is_global(L) else 'swa-2048'}, ctx {sh.ctx}")
+    w = synth.device_layer_weights(sh, cfg_id, L, "cuda")
+    hw = {key: _host(t) for key, t in w.items()}
+    del w
+    torch.cuda.empty_cache()
+    last = L == 61
+    kn = snap["kn"] if not last else np.zeros_like(snap["k_cache"])
+    vn = snap["vn"] if not last else np.zeros_like(snap["v_cache"])
+    parent = synth.stack_step_inputs(sh0, cfg_id, 0)["parent"].astype(np.int32)
+    inp = synth.LayerInputs(sh, parent, snap["h_in"], snap["q_in"], snap["k_cache"], snap["v_cache"], kn, vn,
+                            hw["w_o"], hw["w_pool"], hw["w_router"], hw["w_unpool"], hw["w_qkv_next"], hw["w1"],
+                            hw["w2"], None)
+    out = dict(snap["out"])
+    if last:
+        out["q_next"] = np.zeros((sh.T, sh.n_q_heads * sh.head_dim), np.uint16)
+    _check_layer(inp, out, last=last)
+    log(f"  distinct experts: {len(np.unique(out['idx']))}")
