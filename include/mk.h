@@ -44,7 +44,9 @@ typedef enum {
   MK_ECAPACITY = -4,  /* KV cache or workspace too small                                   */
   MK_EHIP = -5,       /* a HIP runtime call failed (launch, copy, device query)            */
   MK_ETIMEOUT = -6,   /* a bounded in-kernel wait expired (CUs not all available)          */
-  MK_EBADTREE = -7    /* tree_parent malformed: parent[0] != -1 or parent[i] not in [0,i)  */
+  MK_EBADTREE = -7,   /* tree_parent malformed: parent[0] != -1 or parent[i] not in [0,i)  */
+  MK_ESCRATCH = -8    /* mk_layer_step_noalloc: the configuration's workspace exceeds the
+                         static scratch (MK_NOALLOC_SCRATCH_BYTES)                          */
 } mk_status;
 
 typedef enum { MK_W_BF16 = 0, MK_W_NVFP4 = 1 } mk_wfmt;
@@ -155,6 +157,22 @@ int mk_workspace_init(void *workspace, size_t bytes, void *stream);
 int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
                   const mk_step_io *io /* [host] */, void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): mk_layer_step with no caller workspace.  The
+ * launch uses a static device array of the library, MK_NOALLOC_SCRATCH_BYTES on every GPU it
+ * runs on, held until the process ends; io->workspace and io->workspace_bytes are ignored.
+ * Same arguments, checks, kernel and results as mk_layer_step; a configuration whose
+ * mk_workspace_bytes() exceeds the array is rejected with MK_ESCRATCH (at the shard shape that
+ * is a KV capacity above about 90K rows), before anything is enqueued.  The first call on a
+ * device also enqueues one fill kernel that zeroes the array.  No call allocates or frees
+ * memory.  Every call on a GPU shares that GPU's array, which keeps the last call's contents:
+ * calls that overlap on one GPU (concurrent streams, host threads) race and must not be
+ * issued.  mk_read_status(NULL, stream) returns the in-kernel status of the last call on the
+ * current device. */
+#define MK_NOALLOC_SCRATCH_BYTES ((size_t)24 << 20)
+int mk_layer_step_noalloc(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
+                          const mk_step_io *io /* [host] */, void *stream);
+
 /* KV-cache write: copy n new rows into a KV cache pair at rows pos..pos+n-1, bit for bit,
  * every other row untouched.  The pages' launch ends with the next layer's KV write, and the
  * KV history a layer attends over was written by earlier steps (orcarouter.ai write-up,
@@ -252,7 +270,8 @@ size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K);
 
 /* Synchronise `stream` and return the in-kernel status of the last mk_layer_step on this
  * workspace (MK_OK, MK_EBADTREE or MK_ETIMEOUT), or MK_EHIP if a copy failed.  An error of an
- * earlier launch is not reported once a later launch has run. */
+ * earlier launch is not reported once a later launch has run.  workspace NULL: the status of
+ * the last mk_layer_step_noalloc on the current device (MK_EINVAL if there was none). */
 int mk_read_status(const void *workspace, void *stream);
 
 /* Human-readable name of a status code. */

@@ -13,10 +13,12 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK, MK_EINVAL, MK_ESHAPE, MK_EALIGN, MK_ECAPACITY, MK_EHIP, MK_ETIMEOUT, MK_EBADTREE = 0, -1, -2, -3, -4, -5, -6, -7
+MK_ESCRATCH = -8
+MK_NOALLOC_SCRATCH_BYTES = 24 << 20
 MK_W_BF16, MK_W_NVFP4 = 0, 1
 MK_TS_EVENTS = 64
 
-EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step",
+EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
             "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
             "mk_read_status", "mk_strerror"]
 
@@ -69,6 +71,8 @@ def lib() -> C.CDLL:
         L.mk_workspace_query.argtypes = [C.POINTER(mk_layer_cfg), C.c_int, C.POINTER(mk_workspace_layout)]
         L.mk_workspace_init.argtypes = [P, C.c_size_t, P]
         L.mk_layer_step.argtypes = [C.POINTER(mk_layer_cfg), C.POINTER(mk_layer_weights), C.POINTER(mk_step_io), P]
+        L.mk_layer_step_noalloc.argtypes = [C.POINTER(mk_layer_cfg), C.POINTER(mk_layer_weights),
+                                            C.POINTER(mk_step_io), P]
         L.mk_kv_append.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_qkv_prologue.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int,
                                       C.c_int, P]
@@ -83,7 +87,8 @@ def lib() -> C.CDLL:
         L.mk_read_status.argtypes = [P, P]
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
-        for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_kv_append", "mk_qkv_prologue",
+        for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
+                     "mk_kv_append", "mk_qkv_prologue",
                      "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers",
                      "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_read_status"):
             getattr(L, name).restype = C.c_int
@@ -195,6 +200,12 @@ def mk_nvfp4_tile_w1(codes, scales, batch, N, K, codes_t, scales_t, stream=None,
 
 def mk_nvfp4_w1_scales_bytes(batch, N, K) -> int:
     return int(lib().mk_nvfp4_w1_scales_bytes(batch, N, K))
+
+
+def mk_layer_step_noalloc(cfg: mk_layer_cfg, w: mk_layer_weights, io: mk_step_io, stream=None,
+                          check=True) -> int:
+    rc = lib().mk_layer_step_noalloc(C.byref(cfg), C.byref(w), C.byref(io), _stream(stream))
+    return _check(rc, "mk_layer_step_noalloc") if check else rc
 
 
 def mk_read_status(workspace, stream=None) -> int:

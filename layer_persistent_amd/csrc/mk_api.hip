@@ -8,6 +8,11 @@
 #include "../../include/mk.h"
 #include "mk_internal.h"
 
+// The static scratch of mk_layer_step_noalloc (see scratch_ptr): a file-scope device array, one
+// copy on every GPU the library runs on.
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 constexpr int kMaxDevices = 64;
@@ -130,6 +135,130 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   return L;
 }
 
+// Every argument, shape and capacity check of a layer launch, and its kernel arguments apart
+// from the workspace (bind_workspace).  `need_ws`: io->workspace is the workspace (else the
+// caller supplies one of `ws_bytes`).  `*Lout` is the workspace layout once the shape checks
+// have passed.  No HIP call enqueues anything here.
+int build_args(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, bool need_ws,
+               size_t ws_bytes, mk::KArgs* out, Layout* Lout) {
+  memset(Lout, 0, sizeof(*Lout));
+  if (!c || !w || !io) return MK_EINVAL;
+  int rc = check_cfg(c, io->T);
+  if (rc) return rc;
+  const int T = io->T, ctx = io->ctx_len;
+  if (ctx < 0 || ctx + T > c->kv_capacity) return MK_ECAPACITY;
+  if (need_ws && !io->workspace) return MK_EINVAL;
+  const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->h_out,
+                       w->w_o, w->w_pool, w->w_router, w->w_unpool};
+  for (const void* p : req) if (!p) return MK_EINVAL;
+  // the next layer's q/k/v are produced unless this is the stack's last layer (w_qkv_next NULL)
+  if (w->w_qkv_next && (!io->q_next || !io->k_cache_next || !io->v_cache_next)) return MK_EINVAL;
+  if (c->expert_fmt == MK_W_BF16) {
+    if (!w->w1 || !w->w2) return MK_EINVAL;
+  } else {
+    if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales || !w->w1_tscale || !w->w2_tscale)
+      return MK_EINVAL;
+    if (c->pooled % 128) return MK_ESHAPE;
+  }
+  if (io->n_prefetch < 0 || io->n_prefetch > 16) return MK_ESHAPE;
+  if (io->n_prefetch > 0 && !io->prefetch_experts) return MK_EINVAL;
+  if (io->n_prefetch_next < 0 || io->n_prefetch_next > 16) return MK_ESHAPE;
+  if (io->n_prefetch_next > 0 && !io->prefetch_next) return MK_EINVAL;
+  if (io->spin_limit < 0) return MK_EINVAL;
+  const void* al[] = {io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next, io->v_cache_next,
+                      io->h_out, io->q_next, need_ws ? io->workspace : nullptr, io->topk_idx, io->topk_gate,
+                      io->router_logits, io->attn_stats, io->router_bias, w->w_o, w->w_pool,
+                      w->w_router, w->w_unpool, w->w_qkv_next, w->w1, w->w2, w->w1_codes,
+                      w->w1_scales, w->w2_codes, w->w2_scales};
+  for (const void* p : al) if (p && !aligned16(p)) return MK_EALIGN;
+  int n_wg = 0;
+  rc = device_cus(&n_wg);
+  if (rc) return rc;
+  // the workspace must cover the largest context this cache allows, so one workspace serves
+  // every step of a layer
+  Layout L = layout(c, T, c->kv_capacity - T, n_wg);
+  Layout Lc = layout(c, T, ctx, n_wg);
+  *Lout = L;
+  if (ws_bytes < L.total) return MK_ECAPACITY;
+  if (c->n_kv_heads * Lc.chunks_per_head > L.part_slots) return MK_ECAPACITY;
+
+  mk::KArgs& a = *out;
+  memset(&a, 0, sizeof(a));
+  a.H = c->hidden; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.d = c->head_dim; a.P = c->pooled;
+  a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
+  a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
+  a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
+  a.attn_lo = Lc.attn_lo; a.ck = Lc.ck; a.attn_rw = Lc.rw; a.attn_nrb = Lc.nrb;
+  a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
+  a.skip_wg = io->debug_skip_signal_wg;
+  a.parent = io->tree_parent;
+  a.q_in = (const uint16_t*)io->q_in; a.h_in = (const uint16_t*)io->h_in;
+  a.kc = (const uint16_t*)io->k_cache; a.vc = (const uint16_t*)io->v_cache;
+  a.kn = (uint16_t*)io->k_cache_next; a.vn = (uint16_t*)io->v_cache_next;
+  a.h_out = (uint16_t*)io->h_out; a.q_next = (uint16_t*)io->q_next;
+  a.topk_idx = io->topk_idx; a.topk_gate = io->topk_gate; a.router_logits = io->router_logits;
+  a.attn_stats = io->attn_stats; a.hist = io->expert_hist;
+  a.prefetch = io->prefetch_experts; a.n_prefetch = io->n_prefetch; a.bias = io->router_bias;
+  a.prefetch_next = io->prefetch_next; a.n_prefetch_next = io->n_prefetch_next;
+  a.w_o = (const uint16_t*)w->w_o; a.w_pool = (const uint16_t*)w->w_pool;
+  a.w_router = (const uint16_t*)w->w_router; a.w_unpool = (const uint16_t*)w->w_unpool;
+  a.w_qkv = (const uint16_t*)w->w_qkv_next;
+  a.w1 = (const uint16_t*)w->w1; a.w2 = (const uint16_t*)w->w2;
+  a.w1_codes = w->w1_codes; a.w1_scales = w->w1_scales; a.w2_codes = w->w2_codes; a.w2_scales = w->w2_scales;
+  a.w1_ts = w->w1_tscale; a.w2_ts = w->w2_tscale;
+  a.timestamps = io->timestamps;
+  return MK_OK;
+}
+
+// The kernel's workspace regions at `ws` (layout L).
+void bind_workspace(mk::KArgs* ap, const Layout& L, char* ws) {
+  mk::KArgs& a = *ap;
+  a.status = (uint32_t*)(ws + L.status);
+  a.epoch = (uint32_t*)(ws + L.epoch);
+  a.flags = (uint32_t*)(ws + L.flags);
+  a.part_o = (float*)(ws + L.part_o);
+  a.part_ml = (float*)(ws + L.part_ml);
+  a.attn = (uint16_t*)(ws + L.attn);
+  a.h1 = (uint16_t*)(ws + L.h1);
+  a.h_frag = (uint16_t*)(ws + L.h_frag);
+  a.xp = (uint16_t*)(ws + L.xp);
+  a.logits = (float*)(ws + L.logits);
+  a.act_q = (uint32_t*)(ws + L.act);
+  a.act_bf = (uint16_t*)(ws + L.act);
+  a.y = (uint16_t*)(ws + L.y);
+  a.qkv_part = (float*)(ws + L.qkv_part);
+  a.qkv_cnt = (uint32_t*)(ws + L.qkv_cnt);
+}
+
+// ---- static scratch of mk_layer_step_noalloc
+// The workspace of the allocation-free entry point: one file-scope device array per GPU that
+// the library runs on, held until the process ends.  Its device address is taken once per
+// device with hipGetSymbolAddress (the array's name is only a host-side stand-in) and the
+// array is zeroed then by a fill kernel (the epoch slots, flags and status word must start at
+// zero); every later call on that device reuses it as it was left.
+char* g_scratch[kMaxDevices];   // per device: the device address of `scratch`, once set up
+
+int scratch_ptr(hipStream_t stream, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_EHIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MK_EHIP;
+    if (mk::launch_fill_zero(p, kScratchBytes, stream)) return MK_EHIP;
+    g_scratch[dev] = (char*)p;
+  }
+  *out = g_scratch[dev];
+  return MK_OK;
+}
+
+char* scratch_if_set() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_mu);
+  return g_scratch[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -144,6 +273,7 @@ const char* mk_strerror(int s) {
     case MK_EHIP: return "HIP runtime error";
     case MK_ETIMEOUT: return "in-kernel wait timed out";
     case MK_EBADTREE: return "malformed tree_parent";
+    case MK_ESCRATCH: return "configuration needs a larger workspace than the 24 MiB static scratch of mk_layer_step_noalloc";
     default: return "unknown status";
   }
 }
@@ -183,85 +313,23 @@ int mk_workspace_init(void* ws, size_t bytes, void* stream) {
 }
 
 int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, void* stream) {
-  if (!c || !w || !io) return MK_EINVAL;
-  int rc = check_cfg(c, io->T);
-  if (rc) return rc;
-  const int T = io->T, ctx = io->ctx_len;
-  if (ctx < 0 || ctx + T > c->kv_capacity) return MK_ECAPACITY;
-  const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->h_out, io->workspace,
-                       w->w_o, w->w_pool, w->w_router, w->w_unpool};
-  for (const void* p : req) if (!p) return MK_EINVAL;
-  // the next layer's q/k/v are produced unless this is the stack's last layer (w_qkv_next NULL)
-  if (w->w_qkv_next && (!io->q_next || !io->k_cache_next || !io->v_cache_next)) return MK_EINVAL;
-  if (c->expert_fmt == MK_W_BF16) {
-    if (!w->w1 || !w->w2) return MK_EINVAL;
-  } else {
-    if (!w->w1_codes || !w->w1_scales || !w->w2_codes || !w->w2_scales || !w->w1_tscale || !w->w2_tscale)
-      return MK_EINVAL;
-    if (c->pooled % 128) return MK_ESHAPE;
-  }
-  if (io->n_prefetch < 0 || io->n_prefetch > 16) return MK_ESHAPE;
-  if (io->n_prefetch > 0 && !io->prefetch_experts) return MK_EINVAL;
-  if (io->n_prefetch_next < 0 || io->n_prefetch_next > 16) return MK_ESHAPE;
-  if (io->n_prefetch_next > 0 && !io->prefetch_next) return MK_EINVAL;
-  if (io->spin_limit < 0) return MK_EINVAL;
-  const void* al[] = {io->q_in, io->h_in, io->k_cache, io->v_cache, io->k_cache_next, io->v_cache_next,
-                      io->h_out, io->q_next, io->workspace, io->topk_idx, io->topk_gate,
-                      io->router_logits, io->attn_stats, io->router_bias, w->w_o, w->w_pool,
-                      w->w_router, w->w_unpool, w->w_qkv_next, w->w1, w->w2, w->w1_codes,
-                      w->w1_scales, w->w2_codes, w->w2_scales};
-  for (const void* p : al) if (p && !aligned16(p)) return MK_EALIGN;
-  int n_wg = 0;
-  rc = device_cus(&n_wg);
-  if (rc) return rc;
-  // the workspace must cover the largest context this cache allows, so one workspace serves
-  // every step of a layer
-  Layout L = layout(c, T, c->kv_capacity - T, n_wg);
-  Layout Lc = layout(c, T, ctx, n_wg);
-  if (io->workspace_bytes < L.total) return MK_ECAPACITY;
-  if (c->n_kv_heads * Lc.chunks_per_head > L.part_slots) return MK_ECAPACITY;
-
   mk::KArgs a;
-  memset(&a, 0, sizeof(a));
-  a.H = c->hidden; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.d = c->head_dim; a.P = c->pooled;
-  a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
-  a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
-  a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
-  a.attn_lo = Lc.attn_lo; a.ck = Lc.ck; a.attn_rw = Lc.rw; a.attn_nrb = Lc.nrb;
-  a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
-  a.skip_wg = io->debug_skip_signal_wg;
-  a.parent = io->tree_parent;
-  a.q_in = (const uint16_t*)io->q_in; a.h_in = (const uint16_t*)io->h_in;
-  a.kc = (const uint16_t*)io->k_cache; a.vc = (const uint16_t*)io->v_cache;
-  a.kn = (uint16_t*)io->k_cache_next; a.vn = (uint16_t*)io->v_cache_next;
-  a.h_out = (uint16_t*)io->h_out; a.q_next = (uint16_t*)io->q_next;
-  a.topk_idx = io->topk_idx; a.topk_gate = io->topk_gate; a.router_logits = io->router_logits;
-  a.attn_stats = io->attn_stats; a.hist = io->expert_hist;
-  a.prefetch = io->prefetch_experts; a.n_prefetch = io->n_prefetch; a.bias = io->router_bias;
-  a.prefetch_next = io->prefetch_next; a.n_prefetch_next = io->n_prefetch_next;
-  a.w_o = (const uint16_t*)w->w_o; a.w_pool = (const uint16_t*)w->w_pool;
-  a.w_router = (const uint16_t*)w->w_router; a.w_unpool = (const uint16_t*)w->w_unpool;
-  a.w_qkv = (const uint16_t*)w->w_qkv_next;
-  a.w1 = (const uint16_t*)w->w1; a.w2 = (const uint16_t*)w->w2;
-  a.w1_codes = w->w1_codes; a.w1_scales = w->w1_scales; a.w2_codes = w->w2_codes; a.w2_scales = w->w2_scales;
-  a.w1_ts = w->w1_tscale; a.w2_ts = w->w2_tscale;
-  char* ws = (char*)io->workspace;
-  a.status = (uint32_t*)(ws + L.status);
-  a.epoch = (uint32_t*)(ws + L.epoch);
-  a.flags = (uint32_t*)(ws + L.flags);
-  a.part_o = (float*)(ws + L.part_o);
-  a.part_ml = (float*)(ws + L.part_ml);
-  a.attn = (uint16_t*)(ws + L.attn);
-  a.h1 = (uint16_t*)(ws + L.h1);
-  a.h_frag = (uint16_t*)(ws + L.h_frag);
-  a.xp = (uint16_t*)(ws + L.xp);
-  a.logits = (float*)(ws + L.logits);
-  a.act_q = (uint32_t*)(ws + L.act);
-  a.act_bf = (uint16_t*)(ws + L.act);
-  a.y = (uint16_t*)(ws + L.y);
-  a.qkv_part = (float*)(ws + L.qkv_part);
-  a.qkv_cnt = (uint32_t*)(ws + L.qkv_cnt);
-  a.timestamps = io->timestamps;
+  Layout L;
+  int rc = build_args(c, w, io, true, io ? io->workspace_bytes : 0, &a, &L);
+  if (rc) return rc;
+  bind_workspace(&a, L, (char*)io->workspace);
+  return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
+int mk_layer_step_noalloc(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, void* stream) {
+  mk::KArgs a;
+  Layout L;
+  int rc = build_args(c, w, io, false, kScratchBytes, &a, &L);
+  if (rc) return rc == MK_ECAPACITY && L.total > kScratchBytes ? MK_ESCRATCH : rc;
+  char* ws = nullptr;
+  rc = scratch_ptr((hipStream_t)stream, &ws);
+  if (rc) return rc;
+  bind_workspace(&a, L, ws);
   return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
 }
 
@@ -359,6 +427,7 @@ size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K) {
 }
 
 int mk_read_status(const void* workspace, void* stream) {
+  if (!workspace) workspace = scratch_if_set();   // mk_layer_step_noalloc's status
   if (!workspace) return MK_EINVAL;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return MK_EHIP;
   // the status word and workgroup 0's epoch slot, which the last launch left one past its own

@@ -89,6 +89,21 @@ def test_layer_step_rejects_bad_T_capacity_alignment_and_enum():
     assert mk.mk_layer_step(_cfg(), w, _io(), check=False) == mk.MK_EINVAL
 
 
+def test_noalloc_layer_step_validates_like_layer_step_and_ignores_the_workspace():
+    step = mk.mk_layer_step_noalloc
+    for field in ("tree_parent", "q_in", "h_in", "k_cache", "v_cache", "h_out", "q_next"):
+        assert step(_cfg(), _weights(), _io(**{field: None}), check=False) == mk.MK_EINVAL, field
+    assert step(_cfg(hidden=4000), _weights(), _io(workspace=None), check=False) == mk.MK_ESHAPE
+    assert step(_cfg(), _weights(), _io(T=17, workspace=None), check=False) == mk.MK_ESHAPE
+    assert step(_cfg(), _weights(), _io(ctx=8193, workspace=None), check=False) == mk.MK_ECAPACITY
+    assert step(_cfg(), _weights(), _io(h_out=BAD, workspace=None), check=False) == mk.MK_EALIGN
+    # the workspace fields are not used: with no workspace the checks go on to the alignment of
+    # the other pointers (mk_layer_step stops at the missing workspace)
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(workspace=None, h_out=BAD), check=False) == mk.MK_EINVAL
+    assert step(_cfg(), _weights(), _io(workspace=None, h_out=BAD), check=False) == mk.MK_EALIGN
+    assert mk.mk_strerror(mk.MK_ESCRATCH).startswith("configuration needs a larger workspace")
+
+
 def test_small_entry_points_validate_on_host():
     assert mk.mk_kv_append(None, GOOD, 64, 1, 64, 0, GOOD, GOOD, 4, check=False) == mk.MK_EINVAL
     assert mk.mk_kv_append(GOOD, GOOD, 64, 1, 64, 62, GOOD, GOOD, 4, check=False) == mk.MK_ECAPACITY
