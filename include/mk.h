@@ -130,9 +130,12 @@ typedef struct {
  * The bf16 activations (attn, h1, xp, y) hold 16 rows (T padded; rows >= T undefined) of K
  * columns in MFMA fragment order: element (t, c) is at index
  *     ((c / 32) * 64 + ((c / 8) % 4) * 16 + t) * 8 + c % 8,
- * so that one 64-lane operand fetch of 32 columns reads 1 KB contiguously. */
+ * so that one 64-lane operand fetch of 32 columns reads 1 KB contiguously.
+ * The stage buffers exist twice: a launch uses copy (e & 1) of its epoch e, the copy at
+ * offset + (e & 1) * stage_copy, and resets the other copy for the next launch.  After a
+ * launch, the uint32 at offset `epoch` holds e + 1. */
 typedef struct {
-  size_t status;       /* int32 status word                                      */
+  size_t status;       /* uint32 status word (decode with mk_read_status)         */
   size_t attn;         /* bf16 [16][Hq*d]  attention output (fragment order)     */
   size_t h1;           /* bf16 [16][H]     residual after the output projection  */
   size_t xp;           /* bf16 [16][P]     pooler output (fragment order)        */
@@ -141,14 +144,17 @@ typedef struct {
   size_t total;        /* bytes needed                                           */
   int n_wg;            /* workgroups per launch (= CUs of the current device)    */
   int attn_items;      /* attention work items (KV chunks)                       */
+  size_t stage_copy;   /* bytes from copy 0 to copy 1 of the stage buffers       */
+  size_t epoch;        /* uint32 epoch slot of workgroup 0                       */
 } mk_workspace_layout;
 
 /* Workspace bytes for this config on the current device (0 on an unsupported config). */
 size_t mk_workspace_bytes(const mk_layer_cfg *cfg, int T);
 /* Offsets of the hand-off buffers; returns MK_OK or an mk_status. */
 int mk_workspace_query(const mk_layer_cfg *cfg, int T, mk_workspace_layout *out /* [host] */);
-/* Zero the workspace (a fill kernel, no hipMemset).  Call once before the workspace's first
- * use.  Launches on a workspace need no re-initialisation afterwards, also not after an
+/* Initialise a workspace (fill kernels, no hipMemset): its counters to zero, the rest to the
+ * all-ones pattern that marks hand-off data not yet written.  bytes % 16 == 0.  Call once
+ * before the workspace's first use.  Launches on a workspace need no re-initialisation afterwards, also not after an
  * in-kernel error: the status word carries the launch's epoch, and the per-launch counters
  * are cleared by the launch that uses them. */
 int mk_workspace_init(void *workspace, size_t bytes, void *stream);

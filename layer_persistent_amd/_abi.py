@@ -51,7 +51,7 @@ class mk_step_io(C.Structure):
 class mk_workspace_layout(C.Structure):
     _fields_ = [("status", C.c_size_t), ("attn", C.c_size_t), ("h1", C.c_size_t), ("xp", C.c_size_t),
                 ("logits", C.c_size_t), ("y", C.c_size_t), ("total", C.c_size_t), ("n_wg", C.c_int),
-                ("attn_items", C.c_int)]
+                ("attn_items", C.c_int), ("stage_copy", C.c_size_t), ("epoch", C.c_size_t)]
 
 
 _lib = None

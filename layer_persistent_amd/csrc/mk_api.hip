@@ -62,9 +62,18 @@ int check_cfg(const mk_layer_cfg* c, int T) {
 }
 
 struct Layout {
-  size_t status, epoch, flags, part_o, part_ml, attn, h1, h_frag, xp, logits, act, y, qkv_part, qkv_cnt, total;
+  size_t status, epoch, flags, qkv_cnt, zero_end, stage, qkv_part, part_ml, part_o, total;
   int n_wg, items, chunks_per_head, attn_lo, ck, rw, nrb, part_slots;
 };
+
+// The counters at the start of every workspace (status word, epoch slots, flags, qkv arrival
+// counters) start at zero; everything after them starts as the all-ones sentinel.
+size_t zero_bytes(int n_wg) {
+  size_t o = up256(4);                 // status word (mk::kStatusOffset)
+  o = up256(o + (size_t)n_wg * 64);    // epoch slots (mk::kEpochOffset)
+  o = up256(o + (size_t)n_wg * 64);    // flags
+  return up256(o + (size_t)n_wg * 64); // split-K qkv arrival counters
+}
 
 constexpr int kChunkMax = 256;     // keys per attention chunk held in LDS
 
@@ -111,28 +120,30 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
     const int big = c->n_kv_heads * ((keys_max + kChunkMax - 1) / kChunkMax + 1);
     L.part_slots = big > n_wg ? big : n_wg;
   }
-  const int H = c->hidden, Hq = c->n_q_heads, d = c->head_dim, P = c->pooled, E = c->n_experts,
-            k = c->top_k, I = c->expert_inter;
+  const int d = c->head_dim;
   size_t o = 0;
   L.status = o; o = up256(o + 4);               // mk::kStatusOffset
   L.epoch = o; o = up256(o + (size_t)n_wg * 64); // mk::kEpochOffset
   L.flags = o; o = up256(o + (size_t)n_wg * 64);
-  L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
-  L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
-  // hand-off activations: 16 rows (T padded) in MFMA fragment order
-  L.attn = o; o = up256(o + (size_t)16 * Hq * d * 2);
-  L.h1 = o; o = up256(o + (size_t)16 * H * 2);
-  L.h_frag = o; o = up256(o + (size_t)16 * H * 2);
-  L.xp = o; o = up256(o + (size_t)16 * P * 2);
-  L.logits = o; o = up256(o + (size_t)T * E * 4);
-  const size_t act_q = (size_t)T * k * (I / 16) * 16, act_b = (size_t)T * k * I * 2;
-  L.act = o; o = up256(o + (act_q > act_b ? act_q : act_b));
-  L.y = o; o = up256(o + (size_t)16 * P * 2);
+  L.qkv_cnt = o; o = up256(o + (size_t)n_wg * 64);
+  L.zero_end = o;                                // == zero_bytes(n_wg)
+  // the stage buffers, two copies at fixed offsets (mk::kStage*)
+  L.stage = o; o = up256(o + 2 * (size_t)mk::kStageBytes);
   // split-K qkv: at most one (tile, part) per workgroup
   L.qkv_part = o; o = up256(o + (size_t)n_wg * 64 * 4 * 4);
-  L.qkv_cnt = o; o = up256(o + (size_t)n_wg * 64);
+  // attention partials [slot][128 rows]: (m, l), then o
+  L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
+  L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
   L.total = o;
   return L;
+}
+
+// Counters to zero, the rest to the sentinel (fill kernels).
+int init_workspace(char* ws, size_t bytes, int n_wg, hipStream_t stream) {
+  const size_t z = zero_bytes(n_wg) < bytes ? zero_bytes(n_wg) : bytes;
+  if (mk::launch_fill(ws, z, 0u, stream)) return MK_EHIP;
+  if (bytes > z && mk::launch_fill(ws + z, bytes - z, 0xFFFFFFFFu, stream)) return MK_EHIP;
+  return MK_OK;
 }
 
 // Every argument, shape and capacity check of a layer launch, and its kernel arguments apart
@@ -216,16 +227,9 @@ void bind_workspace(mk::KArgs* ap, const Layout& L, char* ws) {
   a.status = (uint32_t*)(ws + L.status);
   a.epoch = (uint32_t*)(ws + L.epoch);
   a.flags = (uint32_t*)(ws + L.flags);
+  a.stage = ws + L.stage;
   a.part_o = (float*)(ws + L.part_o);
   a.part_ml = (float*)(ws + L.part_ml);
-  a.attn = (uint16_t*)(ws + L.attn);
-  a.h1 = (uint16_t*)(ws + L.h1);
-  a.h_frag = (uint16_t*)(ws + L.h_frag);
-  a.xp = (uint16_t*)(ws + L.xp);
-  a.logits = (float*)(ws + L.logits);
-  a.act_q = (uint32_t*)(ws + L.act);
-  a.act_bf = (uint16_t*)(ws + L.act);
-  a.y = (uint16_t*)(ws + L.y);
   a.qkv_part = (float*)(ws + L.qkv_part);
   a.qkv_cnt = (uint32_t*)(ws + L.qkv_cnt);
 }
@@ -238,14 +242,14 @@ void bind_workspace(mk::KArgs* ap, const Layout& L, char* ws) {
 // zero); every later call on that device reuses it as it was left.
 char* g_scratch[kMaxDevices];   // per device: the device address of `scratch`, once set up
 
-int scratch_ptr(hipStream_t stream, char** out) {
+int scratch_ptr(hipStream_t stream, int n_wg, char** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MK_EHIP;
   std::lock_guard<std::mutex> lk(g_mu);
   if (!g_scratch[dev]) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MK_EHIP;
-    if (mk::launch_fill_zero(p, kScratchBytes, stream)) return MK_EHIP;
+    if (init_workspace((char*)p, kScratchBytes, n_wg, stream)) return MK_EHIP;
     g_scratch[dev] = (char*)p;
   }
   *out = g_scratch[dev];
@@ -289,14 +293,16 @@ int mk_workspace_query(const mk_layer_cfg* cfg, int T, mk_workspace_layout* out)
   if (rc) return rc;
   Layout L = layout(cfg, T, cfg->kv_capacity - T > 0 ? cfg->kv_capacity - T : 0, n_wg);
   out->status = L.status;
-  out->attn = L.attn;
-  out->h1 = L.h1;
-  out->xp = L.xp;
-  out->logits = L.logits;
-  out->y = L.y;
+  out->attn = L.stage + mk::kStageAttn;
+  out->h1 = L.stage + mk::kStageH1;
+  out->xp = L.stage + mk::kStageXp;
+  out->logits = L.stage + mk::kStageLogits;
+  out->y = L.stage + mk::kStageY;
   out->total = L.total;
   out->n_wg = L.n_wg;
   out->attn_items = L.items;
+  out->stage_copy = mk::kStageBytes;
+  out->epoch = L.epoch;
   return MK_OK;
 }
 
@@ -308,8 +314,11 @@ size_t mk_workspace_bytes(const mk_layer_cfg* cfg, int T) {
 
 int mk_workspace_init(void* ws, size_t bytes, void* stream) {
   if (!ws || bytes == 0) return MK_EINVAL;
-  if (!aligned16(ws)) return MK_EALIGN;
-  return mk::launch_fill_zero(ws, bytes, (hipStream_t)stream) ? MK_EHIP : MK_OK;
+  if (!aligned16(ws) || bytes % 16) return MK_EALIGN;
+  int n_wg = 0;
+  const int rc = device_cus(&n_wg);
+  if (rc) return rc;
+  return init_workspace((char*)ws, bytes, n_wg, (hipStream_t)stream);
 }
 
 int mk_layer_step(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, void* stream) {
@@ -327,7 +336,7 @@ int mk_layer_step_noalloc(const mk_layer_cfg* c, const mk_layer_weights* w, cons
   int rc = build_args(c, w, io, false, kScratchBytes, &a, &L);
   if (rc) return rc == MK_ECAPACITY && L.total > kScratchBytes ? MK_ESCRATCH : rc;
   char* ws = nullptr;
-  rc = scratch_ptr((hipStream_t)stream, &ws);
+  rc = scratch_ptr((hipStream_t)stream, L.n_wg, &ws);
   if (rc) return rc;
   bind_workspace(&a, L, ws);
   return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;

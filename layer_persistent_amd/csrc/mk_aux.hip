@@ -10,21 +10,25 @@ namespace mk {
 
 // ------------------------------------------------------------------ fill
 
-__global__ void fill_zero_kernel(u32x4* p, size_t n16, uint8_t* tail, size_t ntail) {
+// bytes [0, 16 n16) as 16-byte words of `pattern`, then ntail more bytes of it
+__global__ void fill_kernel(u32x4* p, size_t n16, uint8_t* tail, size_t ntail, uint32_t pattern) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) p[i] = u32x4{0, 0, 0, 0};
-  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = u32x4{pattern, pattern, pattern, pattern};
+  if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = (uint8_t)(pattern >> (8 * (threadIdx.x & 3)));
 }
 
-int launch_fill_zero(void* p, size_t bytes, hipStream_t stream) {
+int launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream) {
   const size_t n16 = bytes / 16, ntail = bytes % 16;
   int grid = (int)((n16 + 255) / 256);
   if (grid < 1) grid = 1;
   if (grid > 4096) grid = 4096;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid), dim3(256), 0, stream, (u32x4*)p, n16,
-                     (uint8_t*)p + n16 * 16, ntail);
+  hipLaunchKernelGGL(fill_kernel, dim3(grid), dim3(256), 0, stream, (u32x4*)p, n16, (uint8_t*)p + n16 * 16,
+                     ntail, pattern);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
+
+int launch_fill_zero(void* p, size_t bytes, hipStream_t stream) { return launch_fill(p, bytes, 0u, stream); }
 
 // ------------------------------------------------------------------ KV append
 

@@ -103,6 +103,24 @@ __device__ __forceinline__ uint32_t ld_coh_u32(const uint32_t* p) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 
+// Hand-off data read as it arrives.  Producers write hand-off data with device-coherent
+// 8-byte stores, and no 8-byte word of it is ever all ones (bf16 and fp32 results are never
+// the all-ones NaN pattern; an NVFP4 intermediate record carries its scale byte, at most
+// 0x7E, in each half); a stage buffer not yet written in this launch holds all ones.  A
+// consumer loads 16 bytes with a device-coherent load -- a raw buffer load with the sc1
+// cache policy, which sees other XCDs' coherent stores -- and takes them once neither
+// 8-byte half is all ones.  Buffer loads outside the resource's range return zero.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 ld_coh16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ bool arrived16(u32x4 v) {
+  return (v[0] & v[1]) != 0xFFFFFFFFu && (v[2] & v[3]) != 0xFFFFFFFFu;
+}
+
 // max / sum across the 4 lanes {l, l^16, l^32, l^48} (the four k-groups of an MFMA column)
 __device__ __forceinline__ float xgroup_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));

@@ -26,6 +26,20 @@ __host__ __device__ inline bool status_is_error_of(uint32_t word, uint32_t epoch
 }
 __host__ __device__ inline int status_code(uint32_t word) { return (int)(int8_t)(word & 0xFFu); }
 
+// Stage (hand-off) buffers between the phases of a launch.  There are two copies; a launch
+// uses copy (epoch & 1) and, at its start, resets the other one to the sentinel for the next
+// launch.  Each buffer sits at a fixed offset inside a copy, sized for the largest supported
+// shapes (T 16, Hq*d 1024, H 4096, P 2048, E 256, top-k 8, I 256), so that one workspace
+// serves every configuration.  A consumer reads them as they arrive: see arrived16().
+constexpr uint32_t kStageAttn = 0;                              // bf16 [16][Hq*d], fragment order
+constexpr uint32_t kStageH1 = kStageAttn + 16 * 1024 * 2;       // bf16 [16][H], fragment order
+constexpr uint32_t kStageHf = kStageH1 + 16 * 4096 * 2;         // bf16 [16][H] h_out, fragment order
+constexpr uint32_t kStageXp = kStageHf + 16 * 4096 * 2;         // bf16 [16][P], fragment order
+constexpr uint32_t kStageLogits = kStageXp + 16 * 2048 * 2;     // fp32 [T][E]
+constexpr uint32_t kStageAct = kStageLogits + 16 * 256 * 4;     // intermediate records / bf16 rows
+constexpr uint32_t kStageY = kStageAct + 16 * 8 * 256 * 2;      // bf16 [16][P], fragment order
+constexpr uint32_t kStageBytes = kStageY + 16 * 2048 * 2;
+
 // Kernel arguments of one fused layer launch (passed by value).
 struct KArgs {
   // shapes
@@ -53,11 +67,14 @@ struct KArgs {
   // workspace
   uint32_t* status;           // status word (status_word)
   uint32_t *epoch, *flags;
+  char* stage;                // stage buffers, copy 0 (copy 1 follows at kStageBytes)
   float *part_o, *part_ml;
+  // this launch's stage buffers (set in the kernel from `stage` and the epoch's parity)
   uint16_t *attn, *h1, *xp;   // hand-off activations, [16][K] bf16 in MFMA fragment order
   uint16_t* h_frag;           // h_out in fragment order (the qkv phase's x)
   float* logits;
-  uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes lo, codes hi, scale byte, 0
+  uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes of elements
+                        // 0-7, scale byte, codes of elements 8-15, scale byte
   uint16_t* act_bf;     // bf16 intermediate [T*k][I]
   uint16_t* y;                // fragment order
   float* qkv_part;            // split-K qkv partials [tile][part][64 lanes][4]
@@ -82,6 +99,8 @@ int layer_lds_bytes();
 int set_layer_kernel_attrs(int lds_bytes);
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+// Fill `bytes` bytes (a multiple of 4) with a 32-bit pattern.
+int launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream);
 int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,
                      const uint16_t* vn, int n, hipStream_t stream);
 int launch_qkv_prologue(const uint16_t* h, const uint16_t* w, int T, int H, int qd, int kd, uint16_t* q_out,

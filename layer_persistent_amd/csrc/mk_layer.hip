@@ -51,6 +51,15 @@ constexpr int kCtl = 512;          // first thread of the control wave
 // sleep this long before polling (measured: the pooler's work then ends ~0.6 us sooner, and the
 // layer ~0.9 us; longer sleeps, or sleeps in the attention and merge hand-offs, gained nothing).
 constexpr int kIdleSleepUs = 1;
+// Polls of stage data that has not arrived are repeated back to back, or after s_sleep
+// MK_POLL_SLEEP (64-clock units)
+#ifndef MK_POLL_SLEEP
+#define MK_POLL_SLEEP 0
+#endif
+// workgroups without a router tile wait about MK_ROUTE_IDLE us before reading the logits
+#ifndef MK_ROUTE_IDLE
+#define MK_ROUTE_IDLE 0
+#endif
 
 // per-wave MFMA k-steps (32 k each) held in registers for each dense phase
 constexpr int MAXS_O = 4;          // o-proj   K = Hq*d <= 1024
@@ -185,6 +194,54 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
   }
   __builtin_amdgcn_s_waitcnt(0);
   return true;
+}
+
+// Reads n 16-byte pieces of a stage buffer as they arrive (arrived16): piece i is at byte
+// offset off(i) of resource r, and use(i, v) consumes it.  This thread takes pieces tid,
+// tid + nthr, ..., NB of them at a time, all loaded together with device-coherent loads; the
+// pieces that have not arrived yet are loaded again, back to back.  Every wait is bounded: after
+// spin_limit rounds this launch's status becomes MK_ETIMEOUT and the workgroup is marked dead
+// (*dead_sh); an error another workgroup raised in this launch ends the wait too.  A dead
+// workgroup's remaining pieces are skipped (the launch's outputs are then unspecified).
+template <int NB, class OffF, class UseF>
+__device__ __forceinline__ void poll_stage(const Sync& s, int32_t* dead_sh, rsrc_t r, int n, int tid, int nthr,
+                                           OffF off, UseF use) {
+  volatile int32_t* dead = dead_sh;
+  for (int base = 0; base < n; base += NB * nthr) {
+    bool need[NB];
+    u32x4 v[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) need[j] = base + j * nthr + tid < n;
+    for (int spins = 0;; ++spins) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        if (need[j]) v[j] = ld_coh16(r, off(base + j * nthr + tid));
+      bool more = false;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        if (need[j] && arrived16(v[j])) {
+          use(base + j * nthr + tid, v[j]);
+          need[j] = false;
+        }
+        more |= need[j];
+      }
+      if (!more || *dead) break;
+#if MK_POLL_SLEEP > 0
+      __builtin_amdgcn_s_sleep(MK_POLL_SLEEP);
+#endif
+      if (spins >= s.spin_limit) {
+        __hip_atomic_store(s.status, status_word(s.epoch, MK_ETIMEOUT_DEV), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *dead = 1;
+        break;
+      }
+      if ((spins & 63) == 63 &&
+          status_is_error_of(__hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), s.epoch)) {
+        *dead = 1;
+        break;
+      }
+    }
+    if (*dead) return;
+  }
 }
 
 // ------------------------------------------------------------------ dense tiles
@@ -818,21 +875,21 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
 // and the dispatch tables.  Every workgroup computes the same tables.  Called by all threads;
 // the work runs on the compute waves.
 template <bool TS>
-__device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* lg) {
+__device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* lg, const Sync& sy, int32_t* dead_sh) {
   const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
   const int npairs = T * K;
   const bool cw = tid < kCompute;
-  // the logits, and (NVFP4) every expert's two tensor scales, in one batch of loads
+  // (NVFP4) every expert's two tensor scales; then the logits, read as they arrive from the
+  // router workgroups
   const int nlg = T * E / 4, nts = a.fmt == 1 ? E / 4 : 0;
-  stage_pieces(nlg + 2 * nts, [&](int i) {
-    if (i < nlg) return (const void*)(a.logits + 4 * i);
-    i -= nlg;
+  stage_pieces(2 * nts, [&](int i) {
     return i < nts ? (const void*)(a.w1_ts + 4 * i) : (const void*)(a.w2_ts + 4 * (i - nts));
   }, [&](int i) {
-    if (i < nlg) return (void*)(lg + 4 * i);
-    i -= nlg;
     return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
   });
+  if (cw)
+    poll_stage<2>(sy, dead_sh, make_rsrc(a.logits, (uint32_t)nlg * 16), nlg, tid, kCompute,
+                  [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) { *(u32x4*)(lg + 4 * i) = v; });
   // scratch after the logits: per expert, a bitmask of the pairs routed there, counts, offsets
   uint32_t* mask = (uint32_t*)(lg + T * E);
   int32_t* ecnt = (int32_t*)(mask + E * 4);
@@ -1055,7 +1112,8 @@ __device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t
   }
 }
 
-// Part 2 (all threads; returns with the workgroup synchronised): the row scales and xs.
+// Part 2 (all threads, after a barrier that follows part 1; returns with the workgroup
+// synchronised): the row scales and xs.
 template <bool TS>
 __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], uint16_t* xs, int xstride,
                                          const uint32_t* pmax, int32_t* xk) {
@@ -1096,9 +1154,17 @@ __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], ui
   wg_sync();
 }
 
+// NVFP4 experts whose local intermediate is a multiple of 64 and at least 128 take gemm2_fp4;
+// the others gemm2_staged
+__device__ __forceinline__ bool g2_fast(const KArgs& a) { return a.fmt == 1 && a.I % 64 == 0 && a.I >= 128; }
+
+// LDS of GEMM1: the input rows xs [T][P + 8] at 0, then 16 P bytes of piece scales (sbuf; the
+// piece maxima while xs is built), then the partial tiles (ubuf).  The routing tables are built
+// in the ubuf area, before GEMM1's first products.
+__device__ __forceinline__ int g1_ubuf_off(int P) { return G1_XS_BYTES + 16 * P; }
+
 template <bool TS>
-__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem, int32_t* xk,
-                                            const u32x4 (&xpv)[8]) {
+__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem, int32_t* xk) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int jblocks = I / 16;
@@ -1107,11 +1173,11 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   const int t_begin = (int)((long)blockIdx.x * ntasks / nwg), t_end = (int)((long)(blockIdx.x + 1) * ntasks / nwg);
   if (t_begin >= t_end) return;                 // uniform over the workgroup
   const int xstride = P + XS_STRIDE_PAD;
-  uint16_t* xs = (uint16_t*)smem;                                  // [T][P + 8] bf16
-  // sbuf: the piece maxima while xs is built, then the wave-private piece-scale buffers (16 rows
-  // x srow_b bytes each, 2 per wave: within 16 P bytes for every P % 128 == 0 up to 2048)
+  const uint16_t* xs = (const uint16_t*)smem;                      // [T][P + 8], built before routing
+  // sbuf: the wave-private piece-scale buffers (16 rows x srow_b bytes each, 2 per wave: within
+  // 16 P bytes for every P % 128 == 0 up to 2048)
   uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // 16 P bytes
-  float* ubuf = (float*)(sbuf + G1_UNITS * 16 * (P / 16));          // [16 units][2 K halves][16][17]
+  float* ubuf = (float*)(smem + g1_ubuf_off(P));                    // [16 units][2 K halves][16][17]
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
   const int lsteps = g1_lsteps(P);
   const int nunits = 2 * (t_end - t_begin);
@@ -1185,22 +1251,22 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
         // codes of columns 8h..8h+7 on lanes q = 2h; the odd lane's half shifted in
         const uint32_t w = c | ((uint32_t)__builtin_amdgcn_update_dpp((int)c, (int)c, 0xB1, 0xF, 0xF, true) << 16);
         const uint32_t w1 = (uint32_t)__builtin_amdgcn_update_dpp((int)w, (int)w, 0x4E, 0xF, 0xF, true);
-        if (valid && q == 0) st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w, w1, sc, 0u});
+        // record: codes of elements 0-7 and the scale byte, codes of 8-15 and the scale byte
+        // (each 8-byte half holds the scale, at most 0x7E, so neither is ever all ones)
+        if (valid && q == 0) st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w, sc, w1, sc});
       } else if (valid) {
         st_coh_u64(a.act_bf + (size_t)pair * I + j0 + 4 * q, pack4_bf16(v));
       }
     }
   };
-  // The first round's first piece is requested before the input rows are built, by every wave
-  // (the control wave's is a dummy).  Nothing useful is in flight here: the explicit wait lets
-  // the compiler's load counters start from zero, so later waits count these loads exactly.
+  // The first round's first piece is requested by every wave (the control wave's is a dummy).
+  // Nothing useful is in flight here: the explicit wait lets the compiler's load counters start
+  // from zero, so later waits count these loads exactly.
   if (a.fmt == 1) {
     __builtin_amdgcn_s_waitcnt(0);
     load_piece(0, wave, cw && wave < nh * min(G1_UNITS, nunits), cA, sA);
   }
   stamp<TS>(a.timestamps, 49, 0);
-  xs_build<TS>(a, xpv, xs, xstride, (const uint32_t*)sbuf, xk);   // sbuf holds the piece maxima here
-  stamp<TS>(a.timestamps, 44, 0);
   for (int u0 = 0; u0 < nunits; u0 += G1_UNITS) {
     const int nu = min(G1_UNITS, nunits - u0);
     if (cw && a.fmt == 1) {
@@ -1294,13 +1360,23 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
 // [grp I/4, (grp+1) I/4) of the reduction: I/8 bytes of codes and I/64 E4M3 block scales,
 // loaded straight into registers (a wave's first G2_UNITS units while the grid waits for
 // GEMM1).  The intermediate is read in the same permuted k order, which MFMA allows.
-// Requires I % 64 == 0.
+// Requires I % 64 == 0 and I >= 128.
 constexpr int G2_UNITS = 4;   // units per register batch
 constexpr int G2_MAXB = 4;    // I/64 <= 4
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 struct G2W {
   u32x2 c[G2_UNITS][G2_MAXB];
-  uint32_t s[G2_UNITS][G2_MAXB];
+  u32x2 s[G2_UNITS];          // an 8-byte window of the row's scale bytes holding the lane's
 };
+
+// The lane's I/64 E4M3 scale bytes of a W2 row (I/16 bytes, I >= 128) come from one 8-byte
+// window inside the row: it starts at the 4-aligned offset g2_swin(I, grp) and the lane's
+// bytes begin g2_sshift(I, grp) bytes into it.
+__device__ __forceinline__ int g2_swin(int I, int grp) { return min((grp * (I / 64)) & ~3, I / 16 - 8); }
+__device__ __forceinline__ int g2_sshift(int I, int grp) { return grp * (I / 64) - g2_swin(I, grp); }
+__device__ __forceinline__ uint32_t g2_sbyte(u32x2 win, int k) {
+  return (uint32_t)((((uint64_t)win[1] << 32) | win[0]) >> (8 * k)) & 0xFFu;
+}
 
 // Loads unit U into register slot `i` of `w` for columns [c0, c0+8).  Compute waves only;
 // `rt` must hold this launch's routing.
@@ -1311,14 +1387,12 @@ __device__ __forceinline__ void g2_load_unit(const KArgs& a, const Route& rt, in
     const int sl = (nl >= 8 && 2 * U + 1 < ns) ? 2 * U + 1 : 2 * U;
     const size_t row = (size_t)rt.slot_expert[sl] * a.P + c0 + (nl & 7);
     const uint8_t* cp = a.w2_codes + row * (I / 2) + grp * (I / 8);   // 8-byte aligned
-    const uint8_t* sp = a.w2_scales + row * (I / 16) + grp * nb;
     // read once per launch, non-temporal as GEMM1's W1 codes (about 1.8 us per layer)
 #pragma unroll
     for (int b = 0; b < G2_MAXB; ++b)
-      if (b < nb) {
-        w.c[i][b] = __builtin_nontemporal_load((const u32x2*)(cp + 8 * b));
-        w.s[i][b] = __builtin_nontemporal_load(sp + b);
-      }
+      if (b < nb) w.c[i][b] = __builtin_nontemporal_load((const u32x2*)(cp + 8 * b));
+    const u32x2_a4 sw = __builtin_nontemporal_load((const u32x2_a4*)(a.w2_scales + row * (I / 16) + g2_swin(I, grp)));
+    w.s[i] = u32x2{sw[0], sw[1]};
   }
 }
 
@@ -1341,12 +1415,13 @@ __device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G
   const uint16_t* arow = actf + (pair_m < 0 ? 0 : pair_m) * astride + grp * (I / 4);
   const int sl = (nl >= 8 && 2 * U + 1 < rt.n_slots) ? 2 * U + 1 : 2 * U;
   const float ts = rt.ts2[rt.slot_expert[sl]];
+  const int sh = g2_sshift(I, grp);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < 2 * G2_MAXB; ++st) {
     if (st < I / 32) {
       const u32x4 x = *(const u32x4*)(arow + 8 * st);
-      acc = mfma_f16(x, fp4x8_to_f16(w.c[i][st / 2][st & 1], e4m3_to_f16x2(w.s[i][st / 2])), acc);
+      acc = mfma_f16(x, fp4x8_to_f16(w.c[i][st / 2][st & 1], e4m3_to_f16x2(g2_sbyte(w.s[i], sh + st / 2))), acc);
     }
   }
   // C lane: weight column nl, token rows 4 grp + r; keep the diagonal blocks
@@ -1361,7 +1436,8 @@ __device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G
 // Called by all threads.  `w0` holds batch 0 of this workgroup's first slice, loaded during
 // the hand-off after GEMM1.
 template <bool TS>
-__device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, G2W& w0) {
+__device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, G2W& w0,
+                                          const Sync& sy, int32_t* dead_sh) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int nwg = gridDim.x, nslices = P / 8;
@@ -1377,30 +1453,23 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
     const int c0 = sl * 8;
     const bool first = sl == (int)blockIdx.x;
     if (first) {
-      // the intermediate: one 16-element block (codes, scale byte) per record, decoded once
-      const int nblk = npairs * (I / 16);                           // <= 2048
-      u32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = j * kCompute + tid;
-        if (cw && i < nblk) v[j] = ld16(a.act_q + (size_t)i * 4);
-      }
       // token-row tables of the units
       for (int e = tid; cw && e < nu * 16; e += kCompute) {
         const int s2 = 2 * (e >> 4) + ((e >> 3) & 1), j = e & 7;
         urow[e] = (s2 < ns && j < rt.slot_cnt[s2]) ? rt.pair_list[rt.slot_off[s2] + j] : -1;
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = j * kCompute + tid;
-        if (cw && i < nblk) {
-          const int pair = i / (I / 16), b = i % (I / 16);
-          const f16x2_t sc = e4m3_to_f16x2(v[j][2]);
-          uint16_t* dst = actf + pair * astride + b * 16;
-          *(u32x4*)dst = fp4x8_to_f16(v[j][0], sc);
-          *(u32x4*)(dst + 8) = fp4x8_to_f16(v[j][1], sc);
-        }
-      }
+      // the intermediate, read as it arrives from GEMM1: one 16-element block (codes and scale
+      // byte) per record, decoded once
+      const int nblk = npairs * (I / 16);                           // <= 2048
+      if (cw)
+        poll_stage<4>(sy, dead_sh, make_rsrc(a.act_q, (uint32_t)nblk * 16), nblk, tid, kCompute,
+                      [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) {
+                        const int pair = i / (I / 16), b = i % (I / 16);
+                        const f16x2_t sc = e4m3_to_f16x2(v[1]);
+                        uint16_t* dst = actf + pair * astride + b * 16;
+                        *(u32x4*)dst = fp4x8_to_f16(v[0], sc);
+                        *(u32x4*)(dst + 8) = fp4x8_to_f16(v[2], sc);
+                      });
     } else if (cw) {
       g2_load(a, rt, c0, 0, w0);
     }
@@ -1457,7 +1526,8 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
 //    ([T][4] dwords of bf16 pairs) for the control wave to store.
 // Called by all threads.
 template <bool TS>
-__device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile) {
+__device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile,
+                                             const Sync& sy, int32_t* dead_sh) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int nwg = gridDim.x;
@@ -1472,33 +1542,24 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
   const int code_bytes = fp4 ? 8 * (I / 2) : 8 * I * 2;             // per expert, per slice
   const int chunk = code_bytes + (fp4 ? 8 * (I / 16) : 0);          // multiple of 16 (I % 32 == 0)
   const int cap = (LDS_BYTES - (int)(wbuf - smem)) / chunk;         // experts per round
-  // decode the intermediate: one 16-element block (fp4) or 8 bf16 per piece
+  // the intermediate, read as it arrives from GEMM1 and decoded: one 16-element block (fp4
+  // record) or 8 bf16 per 16-byte piece
   if (cw) {
     const int nblk = fp4 ? npairs * (I / 16) : npairs * (I / 8);
-    for (int base = 0; base < nblk; base += 4 * kCompute) {
-      u32x4 v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = base + j * kCompute + tid;
-        if (i < nblk) v[j] = fp4 ? ld16(a.act_q + (size_t)i * 4) : ld16(a.act_bf + (size_t)i * 8);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = base + j * kCompute + tid;
-        if (i < nblk) {
-          if (fp4) {
-            const int pair = i / (I / 16), b = i % (I / 16);
-            const float sc = e4m3_to_f32(v[j][2]);
-            uint16_t* dst = actbf + pair * astride + b * 16;
-            *(u32x4*)dst = fp4x8_to_bf16(v[j][0], sc);
-            *(u32x4*)(dst + 8) = fp4x8_to_bf16(v[j][1], sc);
-          } else {
-            const int pair = i / (I / 8), b = i % (I / 8);
-            *(u32x4*)(actbf + pair * astride + b * 8) = v[j];
-          }
-        }
-      }
-    }
+    const void* src = fp4 ? (const void*)a.act_q : (const void*)a.act_bf;
+    poll_stage<4>(sy, dead_sh, make_rsrc(src, (uint32_t)nblk * 16), nblk, tid, kCompute,
+                  [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) {
+                    if (fp4) {
+                      const int pair = i / (I / 16), b = i % (I / 16);
+                      const float sc = e4m3_to_f32(v[1]);
+                      uint16_t* dst = actbf + pair * astride + b * 16;
+                      *(u32x4*)dst = fp4x8_to_bf16(v[0], sc);
+                      *(u32x4*)(dst + 8) = fp4x8_to_bf16(v[2], sc);
+                    } else {
+                      const int pair = i / (I / 8), b = i % (I / 8);
+                      *(u32x4*)(actbf + pair * astride + b * 8) = v;
+                    }
+                  });
   }
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
   const int ksteps = I / 32;
@@ -1863,6 +1924,29 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   wg_sync();
   stamp<TS>(a.timestamps, 1);
   const uint32_t epoch = epoch_sh;
+  // this launch's copy of the stage buffers; the control wave returns this workgroup's share of
+  // the other copy to the sentinel for the next launch (plain stores: the next launch starts
+  // after they are written back)
+  {
+    char* cur = a.stage + (size_t)(epoch & 1u) * kStageBytes;
+    a.attn = (uint16_t*)(cur + kStageAttn);
+    a.h1 = (uint16_t*)(cur + kStageH1);
+    a.h_frag = (uint16_t*)(cur + kStageHf);
+    a.xp = (uint16_t*)(cur + kStageXp);
+    a.logits = (float*)(cur + kStageLogits);
+    a.act_q = (uint32_t*)(cur + kStageAct);
+    a.act_bf = (uint16_t*)(cur + kStageAct);
+    a.y = (uint16_t*)(cur + kStageY);
+    if (!cw) {
+      u32x4* idle = (u32x4*)(a.stage + (size_t)((epoch & 1u) ^ 1u) * kStageBytes);
+      constexpr uint32_t words = kStageBytes / 16;
+      const uint32_t per = (words + nwg - 1) / nwg;
+      for (uint32_t i = lane; i < per; i += 64) {
+        const uint32_t w = blockIdx.x * per + i;
+        if (w < words) idle[w] = u32x4{~0u, ~0u, ~0u, ~0u};
+      }
+    }
+  }
   Sync s;
   s.flags = a.flags;
   s.status = a.status;
@@ -1986,34 +2070,47 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)crow * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
       }, router_lds ? smem + POOL_LDS_OFF : nullptr);
     }
-    // GEMM1's input rows are fetched while the grid waits for the router (piece maxima go to
-    // the LDS area GEMM1 later uses for scales, which the routing tables leave alone)
-    u32x4 xpv[8];
-    alive = phase_end<TS>(a, s, 5, &dead_sh, [&] {
-      if (alive) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
-    }, p_r ? 0 : kIdleSleepUs) && alive;
+    // No grid hand-off after the router: every workgroup reads the logits as they arrive.
+    // GEMM1's input rows are fetched first (xp is complete since the pooler's hand-off; piece
+    // maxima go to the LDS area GEMM1 later uses for scales, which the routing tables leave alone)
+    // GEMM1's input rows (xs, in LDS at 0) are built then, before the routing tables: xp is
+    // complete since the pooler's hand-off, and the rows do not depend on the routing.
+    wg_sync();
+    stamp<TS>(a.timestamps, 10);
+    if (alive) {
+      u32x4 xpv[8];
+      if (cw) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
+      wg_sync();                                // every wave's piece maxima are in LDS
+      xs_build<TS>(a, xpv, (uint16_t*)smem, a.P + XS_STRIDE_PAD, (const uint32_t*)(smem + G1_XS_BYTES), xk_sh);
+    }
+    stamp<TS>(a.timestamps, 11);
     // ---- 6 ROUTE + GEMM1
     if (alive) {
-      route_tables<TS>(a, rt, (float*)smem);
+      if (!p_r)
+        for (int i = 0; i < MK_ROUTE_IDLE; ++i) __builtin_amdgcn_s_sleep(37);
+      route_tables<TS>(a, rt, (float*)(smem + g1_ubuf_off(a.P)), s, &dead_sh);
       stamp<TS>(a.timestamps, 18);
-      gemm1_phase<TS>(a, rt, smem, xk_sh, xpv);
-      if (cw) __builtin_amdgcn_s_waitcnt(0);   // intermediate stores complete
+      alive = dead_sh == 0;                     // (route_tables ends synchronised)
+      if (alive) gemm1_phase<TS>(a, rt, smem, xk_sh);
     }
+    // No grid hand-off after GEMM1 either: GEMM2 reads the intermediate as it arrives.  This
+    // workgroup's first W2 registers are requested now.
     G2W g2w;
-    alive = phase_end<TS>(a, s, 6, &dead_sh, [&] {
-      // this workgroup's first W2 registers (routing is known once phase 6 ran)
-      if (alive && a.fmt == 1 && a.I % 64 == 0 && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
-    }) && alive;
+    wg_sync();
+    stamp<TS>(a.timestamps, 12);
+    alive = alive && dead_sh == 0;
+    if (alive && cw && g2_fast(a) && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
+    stamp<TS>(a.timestamps, 13, 0);
     // ---- 7 GEMM2 + combine
     // NVFP4 experts: GEMM2 leaves LDS above 64 KB free, so the control wave streams the
     // unpooler tile there while the experts run (waited for at this phase's hand-off)
     const int g2_lds_end = ((a.T * a.topk * (a.I + 8) * 2 + 255) & ~255) + 128 * 8 * 4 + 72 * 16 * 4;
-    const bool wu_lds = a.fmt == 1 && a.I % 64 == 0 && p_u && g2_lds_end <= WU_LDS_OFF &&
+    const bool wu_lds = g2_fast(a) && p_u && g2_lds_end <= WU_LDS_OFF &&
                         WU_LDS_OFF + 32 * a.P <= LDS_BYTES;
     if (alive) {
       if (!cw && wu_lds) lds_tile_dma(a.w_unpool, a.P, t_u * 16, smem + WU_LDS_OFF);
-      if (a.fmt == 1 && a.I % 64 == 0) gemm2_fp4<TS>(a, rt, smem, ytile, g2w);
-      else gemm2_staged<TS>(a, rt, smem, ytile);
+      if (g2_fast(a)) gemm2_fp4<TS>(a, rt, smem, ytile, g2w, s, &dead_sh);
+      else gemm2_staged<TS>(a, rt, smem, ytile, s, &dead_sh);
     }
     alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u && !wu_lds) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)

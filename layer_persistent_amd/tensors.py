@@ -166,12 +166,24 @@ def untile_frag(buf: np.ndarray, T: int, K: int) -> np.ndarray:
     return buf.reshape(K // 32, 4, 16, 8).transpose(2, 0, 1, 3).reshape(16, K)[:T].copy()
 
 
+def stage_offset(workspace: torch.Tensor, layout, off: int) -> int:
+    """Byte offset of a stage buffer of the workspace's last launch: copy (epoch & 1) of the
+    launch's epoch, which is one less than the epoch slot of workgroup 0 afterwards."""
+    epoch = int(workspace[layout.epoch:layout.epoch + 4].cpu().numpy().view(np.uint32)[0]) - 1
+    return off + (epoch & 1) * layout.stage_copy
+
+
 def outputs(st: DeviceStep) -> dict:
-    """Copy a step's outputs and stage hand-off buffers to the host."""
+    """Copy a step's outputs and stage hand-off buffers (those of its last launch) to the host."""
     torch.cuda.synchronize()
     sh_T = st.T
-    L = st.layout
+    lay = st.layout
     c = st.cfg
+
+    class _L:      # the stage offsets of the last launch's copy
+        attn, h1, xp, y = (stage_offset(st.workspace, lay, o) for o in (lay.attn, lay.h1, lay.xp, lay.y))
+        status = lay.status
+    L = _L
     return dict(
         h_out=host_u16(st.h_out), q_next=host_u16(st.q_next),
         k_cache_next=host_u16(st.k_next), v_cache_next=host_u16(st.v_next),

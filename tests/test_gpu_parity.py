@@ -29,6 +29,9 @@ SMALL_P1152 = synth.LayerShape("small-p1152-nvfp4", 256, 4, 1, 64, 1152, 16, 4, 
 # hidden 1280 (40 k-steps of 32) with 24 qkv tiles: on a 256-CU device the next-layer qkv
 # splits each tile's K over three workgroups, 16 + 16 + 8 k-steps
 SMALL_H1280 = synth.LayerShape("small-h1280-splitk-nvfp4", 1280, 4, 1, 64, 256, 16, 4, 64, 128, 300, 16, True)
+# local expert intermediates of 128 and 256: the register-fed GEMM2 path (I % 64 == 0, I >= 128)
+SMALL_I128 = synth.LayerShape("small-i128-nvfp4", 256, 4, 1, 64, 256, 16, 4, 128, 128, 300, 16, True)
+SMALL_I256 = synth.LayerShape("small-i256-t9-nvfp4", 256, 8, 2, 64, 512, 32, 8, 256, 0, 500, 9, True)
 
 
 @pytest.fixture(autouse=True)
@@ -329,7 +332,8 @@ def _check_layer(inp, out, last: bool = False):
 
 
 @pytest.mark.parametrize("shape,cfg_id", [(synth.CFG1, 1), (SMALL_NVFP4, 81), (SMALL_GQA, 82), (SMALL_T5, 83),
-                                           (SMALL_RW4, 84), (SMALL_P1152, 85), (SMALL_H1280, 88)])
+                                           (SMALL_RW4, 84), (SMALL_P1152, 85), (SMALL_H1280, 88),
+                                           (SMALL_I128, 93), (SMALL_I256, 94)])
 def test_layer_small_shapes(shape, cfg_id):
     log(f"[layer parity] {shape.name}")
     inp = synth.make_layer_inputs(shape, cfg_id)

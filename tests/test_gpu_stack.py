@@ -304,7 +304,7 @@ def stack62_step0():
         torch.cuda.synchronize()
         lw = abi.mk_workspace_query(c, T)
         ws = stk.ws
-        u16 = lambda off, n: ws[off:off + 2 * n].cpu().numpy().view(np.uint16)
+        u16 = lambda off, n: ws[dt.stage_offset(ws, lw, off):dt.stage_offset(ws, lw, off) + 2 * n].cpu().numpy().view(np.uint16)
         Hqd = sh.n_q_heads * sh.head_dim
         snap["out"] = dict(
             status=mk.mk_read_status(ws), h_out=_host(stk.h[(L + 1) % 2]),
