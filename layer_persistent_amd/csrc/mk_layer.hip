@@ -245,6 +245,98 @@ __device__ __forceinline__ void poll_stage(const Sync& s, int32_t* dead_sh, rsrc
 }
 
 // ------------------------------------------------------------------ dense tiles
+// Bounded-wait bookkeeping of one poll round: true when the wait must end (this workgroup is
+// dead, its spin limit ran out -- this launch's status becomes MK_ETIMEOUT -- or another
+// workgroup raised an error in this launch).
+__device__ __forceinline__ bool poll_give_up(const Sync& s, volatile int32_t* dead, int spins) {
+  if (*dead) return true;
+  if (spins >= s.spin_limit) {
+    __hip_atomic_store(s.status, status_word(s.epoch, MK_ETIMEOUT_DEV), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *dead = 1;
+    return true;
+  }
+  if ((spins & 63) == 63 &&
+      status_is_error_of(__hip_atomic_load(s.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), s.epoch)) {
+    *dead = 1;
+    return true;
+  }
+  return false;
+}
+
+// A stage buffer in MFMA fragment order ([16 rows][K] bf16: k-step s is the 1 KB at 1024 s,
+// lane l's 16 bytes at 16 l).  Read as it arrives (`poll`, device-coherent loads that bypass
+// the XCD's L2), or with plain loads once a grid hand-off has made it complete.  Broadcast
+// data that every workgroup reads in full travels best the second way when it is large: the
+// first workgroup of an XCD to read a line brings it into that XCD's L2 for the others, where
+// polling reads it from the memory side once per workgroup and round.
+struct XSrc {
+  rsrc_t r;
+  const uint16_t* x;
+  const Sync* sy;
+  int32_t* dead;
+  bool poll;
+};
+__device__ __forceinline__ XSrc xsrc(const uint16_t* x, int K, const Sync& sy, int32_t* dead_sh) {
+  return XSrc{make_rsrc(x, (uint32_t)K * 32u), x, &sy, dead_sh, true};
+}
+__device__ __forceinline__ XSrc xplain(const uint16_t* x, const Sync& sy, int32_t* dead_sh) {
+  return XSrc{make_rsrc(x, 0u), x, &sy, dead_sh, false};
+}
+
+// This lane's 16-byte pieces j < NB of a stage buffer (byte offsets off[j]; read when need[j],
+// left zero otherwise), read as they arrive: every round reads all the pieces still missing,
+// back to back (pieces from different producers arrive at different times; reading them one
+// after another would add a round trip each).
+template <int NB>
+__device__ __forceinline__ void poll_pieces(const Sync& sy, int32_t* dead_sh, rsrc_t r, const uint32_t (&off)[NB],
+                                            bool (&need)[NB], u32x4 (&v)[NB]) {
+  volatile int32_t* dead = dead_sh;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) v[j] = u32x4{0, 0, 0, 0};
+  for (int spins = 0;; ++spins) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      if (need[j]) v[j] = ld_coh16(r, off[j]);
+    bool more = false;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      if (need[j] && arrived16(v[j])) need[j] = false;
+      more |= need[j];
+    }
+    if (!more || poll_give_up(sy, dead, spins)) return;
+  }
+}
+
+// This lane's x fragments of k-steps s0 + j, j < NB: read as they arrive when j < cnt and the
+// lane's row is valid (rv), zero otherwise.
+template <int NB>
+__device__ __forceinline__ void x_poll(const XSrc& x, int s0, int cnt, bool rv, u32x4 (&xa)[NB]) {
+  const uint32_t lane16 = (uint32_t)(threadIdx.x & 63) * 16u;
+  if (!x.poll) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+      xa[j] = (rv && j < cnt) ? ld16((const char*)x.x + (size_t)(s0 + j) * 1024 + lane16) : u32x4{0, 0, 0, 0};
+    return;
+  }
+  uint32_t off[NB];
+  bool need[NB];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    off[j] = (uint32_t)(s0 + j) * 1024u + lane16;
+    need[j] = rv && j < cnt;
+  }
+  poll_pieces<NB>(*x.sy, x.dead, x.r, off, need, xa);
+}
+
+// One 8-byte word of a stage buffer, read as it arrives (device-coherent 8-byte loads).
+__device__ __forceinline__ uint64_t poll_u64(const Sync& s, int32_t* dead_sh, const void* p) {
+  volatile int32_t* dead = dead_sh;
+  for (int spins = 0;; ++spins) {
+    const uint64_t v = __hip_atomic_load((uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v != ~0ull || poll_give_up(s, dead, spins)) return v;
+  }
+}
+
 
 // Weight fragments of one wave for one 16-column tile of W [N][K]: MFMA k-steps
 // s = wave + 8j (j < MAXS) hold W[n0 + l%16][32 s + 8 (l/16) .. +8].
@@ -333,23 +425,19 @@ __host__ __device__ __forceinline__ int frag_off(int t, int c) {
 }
 
 // This wave's partial of the tile: x (fragment order; rows >= T are zero) times the fragments.
+// x: the stage buffer, read as it arrives; s_base: its first k-step used here.
 template <int MAXS>
-__device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t* __restrict__ x, int T, int K) {
+__device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const XSrc& x, int s_base, int T, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const bool xv = nl < T;
   const int ksteps = K >> 5, J = kblock(ksteps);
-  const uint16_t* xrow = x + lane * 8 + wave * J * 512;
   constexpr int XB = MAXS < 8 ? MAXS : 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j0 = 0; j0 < MAXS; j0 += XB) {
     u32x4 xa[XB];
-#pragma unroll
-    for (int j = 0; j < XB; ++j) {
-      const int jj = j0 + j, s = wave * J + jj;
-      xa[j] = (xv && jj < J && s < ksteps) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
-    }
+    x_poll<XB>(x, s_base + wave * J + j0, min(J - j0, ksteps - (wave * J + j0)), xv, xa);
 #pragma unroll
     for (int j = 0; j < XB; ++j) {
       const int jj = j0 + j, s = wave * J + jj;
@@ -361,24 +449,21 @@ __device__ __forceinline__ f32x4 wfrag_mma(const WFrag<MAXS>& f, const uint16_t*
 
 // This wave's partial of a tile whose weights are read now (typically from L2 after a touch
 // prefetch): weights and x of 8 k-steps are loaded together, then multiplied.
-__device__ __forceinline__ f32x4 stream_mma(const uint16_t* __restrict__ W, int K, int n0,
-                                           const uint16_t* __restrict__ x, int T) {
+__device__ __forceinline__ f32x4 stream_mma(const uint16_t* __restrict__ W, int K, int n0, const XSrc& x, int T) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const bool xv = nl < T;
   const int ksteps = K >> 5, J = kblock(ksteps);
   const uint16_t* wrow = W + (size_t)(n0 + nl) * K + (lane >> 4) * 8 + wave * J * 32;
-  const uint16_t* xrow = x + lane * 8 + wave * J * 512;   // fragment order
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < J; b += 8) {
     u32x4 w[8], xa[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = b + j, s = wave * J + jj;
-      const bool ok = jj < J && s < ksteps;
-      w[j] = ok ? ld16(wrow + jj * 32) : u32x4{0, 0, 0, 0};
-      xa[j] = (xv && ok) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
+      w[j] = (jj < J && s < ksteps) ? ld16(wrow + jj * 32) : u32x4{0, 0, 0, 0};
     }
+    x_poll<8>(x, wave * J + b, min(J - b, ksteps - (wave * J + b)), xv, xa);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = b + j, s = wave * J + jj;
@@ -426,20 +511,15 @@ __device__ __forceinline__ void lds_tile_dma(const uint16_t* __restrict__ W, int
 
 // This wave's partial of a tile whose weights sit in LDS (lds_tile_fill layout); x rows are
 // loaded 16 k-steps at a time.
-__device__ __forceinline__ f32x4 lds_mma(const char* wl, const uint16_t* __restrict__ x, int T, int K) {
+__device__ __forceinline__ f32x4 lds_mma(const char* wl, const XSrc& x, int T, int K) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15;
   const bool xv = nl < T;
   const int ksteps = K >> 5, J = kblock(ksteps);
-  const uint16_t* xrow = x + lane * 8 + wave * J * 512;   // fragment order
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int b = 0; b < J; b += 16) {
     u32x4 xa[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int jj = b + j, sk = wave * J + jj;
-      xa[j] = (xv && jj < J && sk < ksteps) ? ld16(xrow + jj * 512) : u32x4{0, 0, 0, 0};
-    }
+    x_poll<16>(x, wave * J + b, min(J - b, ksteps - (wave * J + b)), xv, xa);
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int jj = b + j, sk = wave * J + jj;
@@ -1082,7 +1162,7 @@ constexpr int G1_UNITS = 16;                   // units per round (2 per compute
 // (relative effect below 2^-28).  The GEMM1 result is scaled back by 2^-xk[t].  bf16 experts
 // take xs = xp unchanged.
 //
-// Part 1 (compute threads, no barrier; runs while the grid waits for the router): this
+// Part 1 (compute threads, no barrier; xp is complete since the pooler's hand-off): this
 // thread's pieces of xp into registers and, for NVFP4, each piece's largest magnitude into
 // pmax[t][c / 8] (LDS).  xp is in fragment order: piece i (8 bf16, 16 * P / 8 <= 4096 pieces)
 // is row i % 16, columns 8 ((i / 64) * 4 + (i / 16) % 4) .. + 8; pieces of rows >= T are skipped.
@@ -1678,7 +1758,7 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
 // until the CU's load queue drains, and the grid waits for them at the barrier.
 template <int MAXS, class Epi>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
-                            const uint16_t* x, int K, int N, int off, float* red2, Epi epi,
+                            const XSrc& x, int K, int N, int off, float* red2, Epi epi,
                             const char* wlds = nullptr) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
@@ -1692,7 +1772,7 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
         acc = stream_mma(W, K, t * 16, x, a.T);
       } else {
         if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
-        acc = wfrag_mma(wf, x, a.T, K);
+        acc = wfrag_mma(wf, x, 0, a.T, K);
       }
       red_store(red, acc);
     }
@@ -2020,44 +2100,55 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         }
       }
     }
-    // While the grid waits for the merge: the o-proj tile into registers, and the pooler tile of
-    // a workgroup that had an attention item into LDS (the merge and o-proj phases use LDS below
-    // POOL_LDS_OFF only; the loads are waited for before the o-proj hand-off).  Issued during
-    // the attention hand-off instead, each slowed that hand-off by ~2 us (the 8 MB o-proj
-    // prefetch over the grid, and even the 0.5 MB of pooler LDS-DMA on 4 workgroups).
-    alive = phase_end<TS>(a, s, 2, &dead_sh, [&] {
+    // No grid hand-off after the merge: the o-proj reads attn as it arrives.  Meanwhile the
+    // o-proj tile loads into registers and, on a workgroup that had an attention item, the
+    // pooler tile into LDS by LDS-DMA (the merge and o-proj phases use LDS below POOL_LDS_OFF
+    // only; the DMA is waited for before the pooler phase).  Workgroups without a merge unit
+    // first wait about kIdleSleepUs: their polls would only add traffic while the merge runs.
+    wg_sync();
+    stamp<TS>(a.timestamps, 4);
+    if (alive && cw) {
       if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
       if (pool_dma) lds_tile_dma(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF, tid >> 6, kCompute / 64);
-    }) && alive;
-    // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T)
+      if ((int)blockIdx.x >= a.Hkv * a.T * (a.Hq / a.Hkv))
+        for (int i = 0; i < kIdleSleepUs; ++i) __builtin_amdgcn_s_sleep(37);
+    }
+    stamp<TS>(a.timestamps, 5, 0);
+    // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T).  The control wave keeps its first tile's h1
+    // values: the unpooler's tiles are the same (N = H, same order), h1 is its residual.
+    u32x2 res_u = {0, 0};
     if (alive) {
-      dense_phase(a, wo, p_o, a.w_o, a.attn, a.Hq * a.d, a.H, 0, red2, [&](int n0, const float* red, int it) {
+      dense_phase(a, wo, p_o, a.w_o, xsrc(a.attn, a.Hq * a.d, s, &dead_sh), a.Hq * a.d, a.H, 0, red2,
+                  [&](int n0, const float* red, int it) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h_in + (size_t)crow * a.H + n0 + cc0);
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
-        st_coh_u64(a.h1 + frag_off(crow, n0 + cc0), pack4_bf16(v));
+        const uint64_t hv = pack4_bf16(v);
+        st_coh_u64(a.h1 + frag_off(crow, n0 + cc0), hv);
+        if (it == 0) res_u = u32x2{(uint32_t)hv, (uint32_t)(hv >> 32)};
       });
     }
     if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
-    alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive;
+    alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive && dead_sh == 0;
     // ---- 4 POOL: xp = bf16(h1 Wp^T)
     if (alive) {
-      // control wave: the unpooler's residual (h1) for its first tile, needed in phase 8
-      if (!cw && p_u && crv) res = *(const u32x2*)(a.h1 + frag_off(crow, t_u * 16 + cc0));
-      dense_phase(a, wp, false, a.w_pool, a.h1, a.H, a.P, off_p, red2, [&](int n0, const float* red, int) {
+      dense_phase(a, wp, false, a.w_pool, xplain(a.h1, s, &dead_sh), a.H, a.P, off_p, red2,
+                  [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         st_coh_u64(a.xp + frag_off(crow, n0 + cc0), pack4_bf16(v));
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
+    // the router tile loads into registers (unless held in LDS) while the grid hands off
     alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r && !router_lds) wfrag_load(wr, a.w_router, a.P, t_r * 16); },
                           p_p ? 0 : kIdleSleepUs) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
     if (alive) {
-      dense_phase(a, wr, p_r && !router_lds, a.w_router, a.xp, a.P, a.E, off_r, red2, [&](int n0, const float* red, int) {
+      dense_phase(a, wr, p_r && !router_lds, a.w_router, xplain(a.xp, s, &dead_sh), a.P, a.E, off_r, red2,
+                  [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
@@ -2071,10 +2162,8 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       }, router_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     // No grid hand-off after the router: every workgroup reads the logits as they arrive.
-    // GEMM1's input rows are fetched first (xp is complete since the pooler's hand-off; piece
-    // maxima go to the LDS area GEMM1 later uses for scales, which the routing tables leave alone)
-    // GEMM1's input rows (xs, in LDS at 0) are built then, before the routing tables: xp is
-    // complete since the pooler's hand-off, and the rows do not depend on the routing.
+    // GEMM1's input rows (xs, in LDS at 0) are built first, from xp as it arrives (piece maxima
+    // go to the LDS area GEMM1 later uses for scales): they do not depend on the routing.
     wg_sync();
     stamp<TS>(a.timestamps, 10);
     if (alive) {
@@ -2112,36 +2201,47 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       if (g2_fast(a)) gemm2_fp4<TS>(a, rt, smem, ytile, g2w, s, &dead_sh);
       else gemm2_staged<TS>(a, rt, smem, ytile, s, &dead_sh);
     }
-    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u && !wu_lds) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); }) && alive;
+    // the unpooler tile is in LDS (the control wave's LDS-DMA during GEMM2, waited for in the hand-off)
+    // or loads into registers while the grid hands off
+    alive = phase_end<TS>(a, s, 7, &dead_sh, [&] { if (p_u && !wu_lds) wfrag_load(wu, a.w_unpool, a.P, t_u * 16); })
+            && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
-      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool, a.y, a.P, a.H, 0, red2, [&](int n0, const float* red, int it) {
+      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool, xplain(a.y, s, &dead_sh), a.P, a.H, 0, red2,
+                  [&](int n0, const float* red, int it) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h1 + frag_off(crow, n0 + cc0));
+        u32x2 r = res_u;                    // this workgroup's own o-proj output (first tile)
+        if (it > 0) {
+          const uint64_t w = poll_u64(s, &dead_sh, a.h1 + frag_off(crow, n0 + cc0));
+          r = u32x2{(uint32_t)w, (uint32_t)(w >> 32)};
+        }
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
         const uint64_t hv = pack4_bf16(v);
         st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, hv);     // the step's output, row-major
         st_coh_u64(a.h_frag + frag_off(crow, n0 + cc0), hv);          // the qkv phase's x
       }, wu_lds ? smem + WU_LDS_OFF : nullptr);
     }
-    // the qkv weights (a whole tile, or one K part of it) load while the grid hands off.
-    // (Issued before the hand-off, a whole tile's 128 KB kept the issuing waves from the barrier
-    // until the CU's load queue drained, and the unpooler's hand-off ended about 2.5 us later on
-    // those workgroups.)
-    alive = phase_end<TS>(a, s, 8, &dead_sh, [&] {
-      if (alive && p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
-      if (alive && p_qs) wfrag_load(wqs, a.w_qkv + q_s0 * 32, q_ns * 32, q_tile * 16, a.H);
-    }) && alive;
+    // No grid hand-off after the unpooler: the qkv projection reads h_out as it arrives; its
+    // weights (a whole tile, or one K part of it) load meanwhile.
+    wg_sync();
+    stamp<TS>(a.timestamps, 16);
+    if (alive && cw) {
+      if (p_q) wfrag_load(wq, a.w_qkv, a.H, t_q * 16);
+      if (p_qs) wfrag_load(wqs, a.w_qkv + q_s0 * 32, q_ns * 32, q_tile * 16, a.H);
+    }
+    stamp<TS>(a.timestamps, 17, 0);
+    alive = alive && dead_sh == 0;
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
+      const XSrc hx = xsrc(a.h_frag, a.H, s, &dead_sh);
       if (q_split) {
-        if (cw && p_qs) red_store(red2, wfrag_mma(wqs, a.h_frag + (size_t)q_s0 * 512, a.T, q_ns * 32));
+        if (cw && p_qs) red_store(red2, wfrag_mma(wqs, hx, q_s0, a.T, q_ns * 32));
         wg_sync();
         if (!cw && p_qs) qkv_split_epilogue(a, red2, q_tile, q_part, qs.np, crow, cc0, crv);
-      } else if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, a.h_frag, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
+      } else if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, hx, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
         if (!crv) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
