@@ -24,11 +24,22 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = 2500.0           # dense bf16 / fp16 matrix-core peak
 HERE = os.path.dirname(os.path.abspath(__file__))
 # sources that decide what the layer kernel reads and writes
 KERNEL_SOURCES = ["layer_persistent_amd/csrc/mk_layer.hip", "layer_persistent_amd/csrc/mk_device.h",
                   "layer_persistent_amd/csrc/mk_internal.h", "layer_persistent_amd/csrc/mk_api.hip"]
 COPY_CALIB_ELEMS = 1 << 26          # fp32 elements of the copy-calibration kernel (256 MiB each way)
+
+
+# timestamp events the layer kernel records (index, name): phase ends, hand-off ends, and the
+# points inside the routing and expert phases
+PHASE_EVENTS = [(1, "setup"), (2, "attn_work"), (3, "attn_handoff"), (4, "merge_work"), (5, "oproj_weights_issued"),
+                (6, "oproj_work"), (7, "oproj_handoff"), (8, "pool_work"), (9, "pool_handoff"), (10, "router_work"),
+                (11, "xs_built"), (46, "route_logits_in"), (47, "route_topk"), (18, "route_tables"),
+                (49, "gemm1_first_loads"), (45, "gemm1_round1"), (12, "gemm1_work"), (13, "w2_first_issued"),
+                (42, "gemm2_staged"), (48, "gemm2_batch0"), (43, "gemm2_experts"), (14, "gemm2_work"),
+                (15, "gemm2_handoff"), (16, "unpool_work"), (17, "qkv_weights_issued"), (19, "qkv_end")]
 
 
 def kernel_source_sha() -> str:
@@ -74,31 +85,92 @@ def algorithmic_bytes(shape, n_active: int) -> dict:
                 total=kv + dense + experts + acts + kv_write)
 
 
-def cpu_baseline(inp) -> dict:
-    """The oracle (fp64 NumPy) on the host: one full layer step of the same workload.  Expert
-    packing is weight preparation (the GPU side does it with mk_nvfp4_pack outside the timed
-    region) and is excluded here too."""
-    import oracle
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        blas_threads = 1
-    t0 = time.time()
-    ref0 = oracle.layer_step_auto(inp)            # routing + packing of the used experts
-    used = sorted(set(np.unique(ref0["idx"]).tolist()))
-    ex = oracle.pack_experts(inp, used)
-    prep = time.time() - t0
-    t1 = time.perf_counter()
-    oracle.layer_step(inp, ex)
-    dt = time.perf_counter() - t1
+        return 1
+
+
+def cpu_baseline(inputs: dict, reps: int = 3) -> dict:
+    """The oracle (fp64 NumPy) on the host: full layer steps of the single-layer workloads,
+    each timed `reps` times with BLAS limited to one thread and with every thread it has, the
+    median reported.  Expert packing is weight preparation (the GPU side does it with
+    mk_nvfp4_pack outside the timed region) and is done once per workload, untimed.  `inputs`
+    maps a workload id to its inputs; the first one is the headline workload."""
+    import oracle
+    from threadpoolctl import threadpool_limits
     cores = len(os.sched_getaffinity(0))
-    log(f"cpu baseline: oracle layer step {dt:.2f} s (prep {prep:.1f} s), {cores} cores, BLAS threads {blas_threads}")
-    return {"value": round(dt * 1e6, 1), "unit": "us", "cores": int(max(1, min(cores, blas_threads))),
-            "kind": "oracle",
-            "sample": "one full layer step of the same workload (SWA-2048 layer, ctx 8192, 16-token tree, "
-                      f"{len(used)} active NVFP4 experts), fp64 NumPy; expert packing excluded; "
-                      f"{cores} host cores visible, {blas_threads} BLAS threads"}
+    all_threads = _blas_threads()
+    runs = []
+    for cfg, inp in inputs.items():
+        t0 = time.time()
+        ex = oracle.pack_experts(inp, oracle.used_experts(inp))
+        prep = time.time() - t0
+        for threads in (1, all_threads):
+            ts = []
+            with threadpool_limits(limits=threads):
+                for _ in range(reps):
+                    t1 = time.perf_counter()
+                    oracle.layer_step(inp, ex)
+                    ts.append(time.perf_counter() - t1)
+            runs.append({"workload": inp.shape.name, "blas_threads": threads, "median_us": round(float(np.median(ts)) * 1e6, 1),
+                         "all_us": [round(t * 1e6, 1) for t in ts]})
+            log(f"cpu baseline: {inp.shape.name}, {threads} BLAS thread(s): oracle layer step median "
+                f"{np.median(ts):.2f} s of {reps} (prep {prep:.1f} s)")
+    head = [r for r in runs if r["workload"] == next(iter(inputs.values())).shape.name]
+    best = min(head, key=lambda r: r["median_us"])
+    return {"value": best["median_us"], "unit": "us", "cores": int(best["blas_threads"]), "kind": "oracle",
+            "sample": f"one full layer step of each of {', '.join(i.shape.name for i in inputs.values())}, "
+                      f"fp64 NumPy, median of {reps}, with BLAS at 1 thread and at all {all_threads}; value = the "
+                      f"headline workload's faster median; expert packing excluded; {cores} host cores visible",
+            "runs": runs}
+
+
+def algorithmic_flops(shape, parent) -> dict:
+    """Multiply-add work of one layer launch (2 flops each): the dense projections at T rows,
+    attention over the keys each (token, head) can see, and the experts' two GEMMs per routed
+    (token, slot) pair.  All of it runs on the matrix cores (bf16, and fp16 for the experts)."""
+    H, Hq, Hkv, d, P, E, I, T = (shape.hidden, shape.n_q_heads, shape.n_kv_heads, shape.head_dim,
+                                 shape.pooled, shape.n_experts, shape.expert_inter, shape.T)
+    dense = 2 * T * (H * Hq * d + P * H + E * P + H * P + shape.qkv_out * H)
+    depth = np.zeros(T, np.int64)
+    for t in range(1, T):
+        depth[t] = depth[parent[t]] + 1
+    keys = 0
+    for t in range(T):
+        pos = shape.ctx + int(depth[t])
+        lo = max(0, pos - shape.window + 1) if shape.window > 0 else 0
+        keys += (shape.ctx - min(lo, shape.ctx)) + int(depth[t]) + 1
+    attn = 2 * 2 * d * Hq * keys
+    experts = T * shape.top_k * (2 * 2 * I * P + 2 * P * I)
+    return dict(dense=dense, attn=attn, experts=experts, total=dense + attn + experts)
+
+
+def stream_read_gbs(torch, lib_mod, stream) -> dict:
+    """Read rate of the library's plain streaming-read kernel (mk_stream_read) over 2 GiB that
+    no other work touches, for a few grid sizes; best of 5 timed passes per size.  `stream` is
+    the torch stream object (events record on it; the library takes its handle)."""
+    nbytes = 2 << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    buf.fill_(0x01020304)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for blocks in (1024, 2048, 4096, 8192):
+        lib_mod.mk_stream_read(buf, nbytes, blocks, sink, stream.cuda_stream)
+        best = None
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            lib_mod.mk_stream_read(buf, nbytes, blocks, sink, stream.cuda_stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1000.0
+            best = us if best is None else min(best, us)
+        out[blocks] = round(nbytes / (best * 1e-6) / 1e9, 1)
+    del buf
+    return out
 
 
 def stack_bytes(shape, n_active_per_layer) -> int:
@@ -133,16 +205,11 @@ def bench_stack(args) -> dict:
     n_steps = args.warmup + args.steps
     ins = [synth.stack_step_inputs(shape, args.config, s) for s in range(n_steps)]
     if args.config == 5:
-        variants = []
-        for reuse in (0.8, 0.0):
-            b = synth.stack_router_biases(shape, args.config, n_layers, n_steps, reuse)
-            variants += [(f"reuse{int(reuse * 100)}_noprefetch", b, False, False),
-                         (f"reuse{int(reuse * 100)}_prefetch", b, True, False)]
-    else:
-        # the step as given (layer 0's queries and tree K/V rows supplied), and the step from the
-        # tokens' embeddings with the first-layer prologue in front of layer 0
-        variants = [("stack", None, False, False), ("stack_from_embeddings", None, False, True),
-                    ("decode_step", None, False, True)]
+        return bench_reuse(args, stk, ins)
+    # the step as given (layer 0's queries and tree K/V rows supplied), and the step from the
+    # tokens' embeddings with the first-layer prologue in front of layer 0
+    variants = [("stack", None, False, False), ("stack_from_embeddings", None, False, True),
+                ("decode_step", None, False, True)]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     res = {}
@@ -234,6 +301,74 @@ def bench_stack(args) -> dict:
     return dict(results=res, n_active_last_step=n_active, n_layers=n_layers)
 
 
+def routing_stats(stk) -> dict:
+    """Distinct experts and the largest number of (token, slot) pairs on one expert, per layer,
+    from the topk_idx every launch of the last step wrote."""
+    import torch
+    n_act, max_pairs = [], []
+    for lay in stk.layers:
+        idx = lay.topk_idx.reshape(-1).to(torch.int64)
+        cnt = torch.bincount(idx, minlength=stk.shape.n_experts)
+        n_act.append(int((cnt > 0).sum()))
+        max_pairs.append(int(cnt.max()))
+    return dict(n_active_mean=round(float(np.mean(n_act)), 2), n_active_min=int(min(n_act)),
+                n_active_max=int(max(n_act)), max_pairs_mean=round(float(np.mean(max_pairs)), 2),
+                max_pairs_max=int(max(max_pairs))), n_act
+
+
+def bench_reuse(args, stk, ins) -> dict:
+    """Config 5: the stack under Markov routing (each (token, slot) keeps the previous step's
+    expert with probability 0.8, or 0) with and without the speculative expert prefetch.  The
+    four variants run in blocks of warmup + steps verify steps, in the order A B C D D C B A,
+    args.abba rounds of it, so that a drift over the run (clocks, caches, memory placement)
+    weighs on every variant alike; each block reports its median step and the routing it saw."""
+    import torch
+    import synth
+    shape, n_layers = stk.shape, stk.n_layers
+    n_steps = args.warmup + args.steps
+    biases = {r: synth.stack_router_biases(shape, args.config, n_layers, n_steps, r) for r in (0.8, 0.0)}
+    variants = [("reuse80_noprefetch", 0.8, False), ("reuse80_prefetch", 0.8, True),
+                ("reuse0_noprefetch", 0.0, False), ("reuse0_prefetch", 0.0, True)]
+    structs = {n: [stk.structs(pf, True, parity) for parity in (0, 1)] for n, _, pf in variants}
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    steps = {n: [] for n, _, _ in variants}
+    blocks = {n: [] for n, _, _ in variants}
+    routing, per_layer = {}, {}
+    order = (variants + variants[::-1]) * args.abba
+    for name, reuse, _ in order:
+        b = biases[reuse]
+        times = []
+        for s in range(n_steps):
+            stk.set_step_inputs(ins[s], b[s])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            stk.launch_step(structs[name][s % 2], sp)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if s >= args.warmup:
+                times.append(e0.elapsed_time(e1) * 1000.0)
+        mk_read_status_ok(stk)
+        steps[name] += times
+        blocks[name].append(round(float(np.median(times)), 1))
+        routing[name], per_layer[name] = routing_stats(stk)
+        log(f"{name}: block median {blocks[name][-1]} us; routing {routing[name]}")
+    res = {}
+    for name, _, _ in variants:
+        res[name] = dict(step_us_median=round(float(np.median(steps[name])), 1),
+                         step_us_p10=round(float(np.percentile(steps[name], 10)), 1),
+                         step_us_p90=round(float(np.percentile(steps[name], 90)), 1),
+                         layer_us_mean=round(float(np.median(steps[name])) / n_layers, 2),
+                         block_medians_us=blocks[name], **routing[name])
+    # the prefetch's effect, block by block: the two blocks of one ABBA round sit symmetrically
+    # around its middle, so their mean difference cancels a linear drift
+    for r in ("reuse80", "reuse0"):
+        d = np.array(blocks[f"{r}_noprefetch"]) - np.array(blocks[f"{r}_prefetch"])
+        res[f"{r}_prefetch_saving_us"] = dict(mean=round(float(d.mean()), 1), per_block=[round(float(x), 1) for x in d])
+    log("reuse workload: " + json.dumps(res))
+    return dict(results=res, n_active_last_step=per_layer["reuse80_prefetch"], n_layers=n_layers)
+
+
 def mk_read_status_ok(stk) -> int:
     import layer_persistent_amd as mk
     s = mk.mk_read_status(stk.ws)
@@ -252,6 +387,7 @@ def main():
                     help="workload id (2: SWA layer ctx 8192, 3: global layer ctx 32768, "
                          "4: 62-layer stack ctx 4096, 5: stack with expert reuse and prefetch)")
     ap.add_argument("--layers", type=int, default=62, help="stack depth for configs 4 and 5")
+    ap.add_argument("--abba", type=int, default=2, help="config 5: rounds of the A B C D D C B A variant order")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--dump-timestamps", default=None,
@@ -397,20 +533,19 @@ def main():
     log(f"algorithmic bytes {ab['total'] / 1e6:.2f} MB ({n_active} active experts) -> {achieved:.0f} GB/s "
         f"= {achieved / HBM_PEAK_GBS:.3f} of {HBM_PEAK_GBS:.0f} GB/s")
 
-    # achievable streaming-read bandwidth in this run (1 GiB sum, cold)
-    big = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-    big.fill_(1.0)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    big.sum()
-    e0.record(stream)
-    for _ in range(5):
-        big.sum()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    read_gbs = 5 * big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del big
-    log(f"achievable streaming read (torch sum over 1 GiB): {read_gbs:.0f} GB/s")
+    # matrix-core work per launch against the bf16/fp16 dense peak
+    fl = algorithmic_flops(shape, inp.parent)
+    tflops = fl["total"] / (kern_us * 1e-6) / 1e12
+    mfma = {"flops_per_launch": int(fl["total"]), "dense": int(fl["dense"]), "attn": int(fl["attn"]),
+            "experts": int(fl["experts"]), "achieved_tflops": round(tflops, 2), "peak_tflops": MFMA_PEAK_TFLOPS,
+            "frac": round(tflops / MFMA_PEAK_TFLOPS, 5)}
+    log(f"matrix-core work {fl['total'] / 1e9:.3f} GFLOP per launch -> {tflops:.1f} TFLOP/s "
+        f"= {tflops / MFMA_PEAK_TFLOPS:.4f} of {MFMA_PEAK_TFLOPS:.0f}")
+
+    # achievable streaming-read rate in this run: the library's plain read kernel over 2 GiB
+    sweep = stream_read_gbs(torch, mk, stream)
+    read_gbs = max(sweep.values())
+    log(f"streaming read (mk_stream_read over 2 GiB), GB/s by workgroup count: {sweep}")
 
     if args.copy_calibration:
         src = torch.ones(COPY_CALIB_ELEMS, dtype=torch.float32, device="cuda")
@@ -431,70 +566,42 @@ def main():
         tsv = ts_step.timestamps.cpu().numpy().astype(np.int64)
         if args.dump_timestamps:
             np.save(args.dump_timestamps, tsv)
-        # events: 0 start, 1 setup done, 2p work of phase p done, 2p+1 its grid hand-off done
-        # (p = 1 attn, 2 merge, 3 oproj, 4 pool, 5 router, 6 gemm1, 7 gemm2, 8 unpool),
-        # 18 routing tables built, 19 qkv done; ticks of the 100 MHz wall clock
+        # timestamp events (ticks of the 100 MHz wall clock, per workgroup), in launch order
         t0 = tsv[:, 0].min()
-        rel = lambda ev: float((tsv[:, ev].max() - t0) / 100.0)
-        names = ["attn", "merge", "oproj", "pool", "router", "gemm1", "gemm2", "unpool"]
-        phases = {"setup": round(rel(1), 2)}
-        for p, n in enumerate(names, start=1):
-            phases[n + "_work"] = round(rel(2 * p), 2)
-            phases[n + "_sync"] = round(rel(2 * p + 1), 2)
-        phases["route_tables"] = round(rel(18), 2)
-        phases["qkv_end"] = round(rel(19), 2)
-        for p, n in enumerate(names, start=1):
-            if (tsv[:, 20 + p] > 0).any():          # (no grid hand-off follows the attention phase)
-                phases[n + "_poll_done"] = round(rel(20 + p), 2)
-                phases[n + "_loads_issued"] = round(rel(28 + p), 2)
-        # per-workgroup work time of each phase (its work end minus its previous hand-off end):
-        # median and max over the workgroups
-        for p, n in enumerate(names, start=1):
-            dur = (tsv[:, 2 * p] - tsv[:, 2 * p - 1 if p > 1 else 1]) / 100.0
-            phases[n + "_wg_p50_max"] = [round(float(np.median(dur)), 2), round(float(dur.max()), 2)]
-        for p, n in enumerate(names, start=1):
-            if (tsv[:, 53 + p] > 0).any():
-                phases[n + "_stores_done"] = round(rel(53 + p), 2)
+        phases = {}
+        for ev, name in PHASE_EVENTS:
+            m = tsv[:, ev] > 0
+            if m.any():
+                v = (tsv[m, ev] - t0) / 100.0
+                phases[name] = [round(float(np.median(v)), 2), round(float(v.max()), 2)]
+        # the four grid hand-offs left (flag waits): last arrival to last release
+        for p, n in ((1, "attn"), (3, "oproj"), (4, "pool"), (7, "gemm2")):
+            phases[n + "_handoff_us"] = round(float((tsv[:, 2 * p + 1].max() - tsv[:, 2 * p].max()) / 100.0), 2)
         starts = (tsv[:, 0] - t0) / 100.0
         phases["wg_start_spread"] = round(float(starts.max()), 2)
+        d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
         items = tsv[:, 37] > 0
         if items.any():
-            phases["attn_stage_us_max"] = round(float(((tsv[items, 37] - tsv[items, 1]) / 100.0).max()), 2)
-            phases["attn_compute_us_max"] = round(float(((tsv[items, 38] - tsv[items, 37]) / 100.0).max()), 2)
-            phases["attn_setup_end_max"] = round(float(((tsv[items, 1] - t0) / 100.0).max()), 2)
-            if (tsv[items, 39] > 0).all():
-                phases["attn_keyloop_us_max"] = round(float(((tsv[items, 39] - tsv[items, 37]) / 100.0).max()), 2)
-                phases["attn_combine_us_max"] = round(float(((tsv[items, 38] - tsv[items, 39]) / 100.0).max()), 2)
-        g2 = tsv[:, 42] > 0
-        if g2.any():
-            d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
-            phases["gemm2_staged_after_sync"] = d(42, 13, g2)
-            phases["gemm2_experts_after_staged"] = d(43, 42, g2)
-        d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
+            phases["attn_stage_us_max"] = d(37, 1, items)
+            phases["attn_compute_us_max"] = d(38, 37, items)
         rtm = tsv[:, 46] > 0
         if rtm.any():
-            phases["route_staged_after_sync"] = d(46, 11, rtm)
-            phases["route_topk"] = d(47, 46, rtm)
-            phases["route_rest"] = d(18, 47, rtm)
-        g2b = tsv[:, 48] > 0
-        if g2b.any():
-            phases["gemm2_batch0"] = d(48, 42, g2b)
-            phases["gemm2_batch1"] = d(43, 48, g2b)
-        g1e = tsv[:, 49] > 0
-        if g1e.any():
-            phases["gemm1_first_loads_issued"] = d(49, 18, g1e)
-            phases["gemm1_xs_rowmax"] = d(50, 49, g1e)
-            phases["gemm1_xs_convert"] = d(44, 50, g1e)
-        g1 = tsv[:, 45] > 0
-        if g1.any():
-            d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
-            phases["gemm1_xs_after_routes"] = d(44, 18, g1)
-            phases["gemm1_batch1_after_xs"] = d(45, 44, g1)
-        log("phase end times (us after the first workgroup starts, timestamp build): " + json.dumps(phases))
+            phases["route_logits_wait_us_max"] = d(46, 11, rtm)
+            phases["route_topk_us_max"] = d(47, 46, rtm)
+            phases["route_rest_us_max"] = d(18, 47, rtm)
+        phases["gemm1_us_p50_max"] = [round(float(np.median((tsv[:, 12] - tsv[:, 18]) / 100.0)), 2), d(12, 18, tsv[:, 12] > 0)]
+        g2 = tsv[:, 43] > 0
+        if g2.any():
+            phases["gemm2_us_p50_max"] = [round(float(np.median((tsv[g2, 43] - tsv[g2, 13]) / 100.0)), 2), d(43, 13, g2)]
+        log("event times, [median, max] over workgroups in us after the first workgroup starts "
+            "(timestamp build): " + json.dumps(phases))
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp)
+        inputs = {args.config: inp}
+        if args.config == 2:                      # the global-attention layer as well
+            inputs[3] = synth.make_layer_inputs(synth.CONFIGS[3], 3)
+        cpu = cpu_baseline(inputs)
 
     res = {
         "metric": "us per fused decoder layer (16-token verify, 1 GPU)",
@@ -516,7 +623,9 @@ def main():
                    "active_experts": n_active, "replicas": args.replicas, "launches_per_layer": 1},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counted_traffic(shape.name),
-                     "bytes_per_launch": ab["total"], "achievable_read_gbs": round(read_gbs, 1)},
+                     "bytes_per_launch": ab["total"], "achievable_read_gbs": round(read_gbs, 1),
+                     "frac_of_achievable": round(achieved / read_gbs, 4), "stream_read_sweep_gbs": sweep},
+        "mfma": mfma,
         "evented_launch_us": {"median": round(med_us, 2), "p10": round(float(np.percentile(per, 10)), 2),
                               "p90": round(float(np.percentile(per, 90)), 2),
                               "note": "an event pair around every launch adds ~3 us per launch"},

@@ -280,6 +280,17 @@ size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K);
  * the last mk_layer_step_noalloc on the current device (MK_EINVAL if there was none). */
 int mk_read_status(const void *workspace, void *stream);
 
+/* Streaming-read probe: reads `bytes` bytes of src once, in coalesced 16-byte non-temporal
+ * loads with 8 per thread in flight, over n_blocks workgroups of 256 threads (0 = 8 per CU),
+ * and computes nothing else.  The time it takes gives the HBM read rate that a plain stream
+ * reaches on this device, the practical ceiling for the weight streams of mk_layer_step (the
+ * pages price a decode layer by the bytes it must bring from HBM: alphasignal.ai, "Launch
+ * boundaries leave hardware idle").  src DEVICE, 16-byte aligned, bytes % 16 == 0, else
+ * MK_EALIGN; sink DEVICE uint32 [1], 4-byte aligned: the XOR of every 32-bit word read is
+ * XORed into it atomically (a checksum: zero it first to obtain the data's XOR).  n_blocks in
+ * [0, 2^20], else MK_ESHAPE.  Enqueues one kernel. */
+int mk_stream_read(const void *src, size_t bytes, int n_blocks, uint32_t *sink, void *stream);
+
 /* Human-readable name of a status code. */
 const char *mk_strerror(int status);
 

@@ -9,4 +9,4 @@ from ._abi import (MK_OK, MK_EINVAL, MK_ESHAPE, MK_EALIGN, MK_ECAPACITY, MK_EHIP
                    mk_strerror, mk_workspace_bytes, mk_workspace_query, mk_workspace_init,
                    mk_layer_step, mk_layer_step_noalloc, mk_kv_append, mk_qkv_prologue, mk_tree_accept, mk_kv_commit, mk_kv_commit_layers,
                    mk_route_topk, mk_nvfp4_pack, mk_nvfp4_tile_w1,
-                   mk_nvfp4_w1_scales_bytes, mk_read_status)
+                   mk_nvfp4_w1_scales_bytes, mk_stream_read, mk_read_status)

@@ -20,7 +20,7 @@ MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
             "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
-            "mk_read_status", "mk_strerror"]
+            "mk_stream_read", "mk_read_status", "mk_strerror"]
 
 
 class mk_layer_cfg(C.Structure):
@@ -84,13 +84,14 @@ def lib() -> C.CDLL:
         L.mk_nvfp4_tile_w1.argtypes = [P, P, C.c_int, C.c_int, C.c_int, P, P, P]
         L.mk_nvfp4_w1_scales_bytes.argtypes = [C.c_int, C.c_int, C.c_int]
         L.mk_nvfp4_w1_scales_bytes.restype = C.c_size_t
+        L.mk_stream_read.argtypes = [P, C.c_size_t, C.c_int, P, P]
         L.mk_read_status.argtypes = [P, P]
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
                      "mk_kv_append", "mk_qkv_prologue",
                      "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers",
-                     "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_read_status"):
+                     "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_stream_read", "mk_read_status"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -206,6 +207,11 @@ def mk_layer_step_noalloc(cfg: mk_layer_cfg, w: mk_layer_weights, io: mk_step_io
                           check=True) -> int:
     rc = lib().mk_layer_step_noalloc(C.byref(cfg), C.byref(w), C.byref(io), _stream(stream))
     return _check(rc, "mk_layer_step_noalloc") if check else rc
+
+
+def mk_stream_read(src, nbytes, n_blocks, sink, stream=None, check=True) -> int:
+    rc = lib().mk_stream_read(_ptr(src), nbytes, n_blocks, _ptr(sink), _stream(stream))
+    return _check(rc, "mk_stream_read") if check else rc
 
 
 def mk_read_status(workspace, stream=None) -> int:

@@ -435,6 +435,19 @@ size_t mk_nvfp4_w1_scales_bytes(int batch, int N, int K) {
   return (size_t)batch * N * mk::g1_scale_row_bytes(K);
 }
 
+int mk_stream_read(const void* src, size_t bytes, int n_blocks, uint32_t* sink, void* stream) {
+  if (!src || !sink) return MK_EINVAL;
+  if (n_blocks < 0 || n_blocks > (1 << 20)) return MK_ESHAPE;
+  if (bytes % 16 != 0 || ((uintptr_t)src & 15) != 0 || ((uintptr_t)sink & 3) != 0) return MK_EALIGN;
+  if (bytes == 0) return MK_OK;
+  if (n_blocks == 0) {
+    int cus = 0;
+    if (device_cus(&cus) != 0) return MK_EHIP;
+    n_blocks = 8 * cus;
+  }
+  return mk::launch_stream_read(src, bytes, n_blocks, sink, (hipStream_t)stream) == 0 ? MK_OK : MK_EHIP;
+}
+
 int mk_read_status(const void* workspace, void* stream) {
   if (!workspace) workspace = scratch_if_set();   // mk_layer_step_noalloc's status
   if (!workspace) return MK_EINVAL;

@@ -30,6 +30,38 @@ int launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream) {
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t stream) { return launch_fill(p, bytes, 0u, stream); }
 
+// ------------------------------------------------------------------ streaming read
+
+// Reads bytes [0, 16 n16) of src once, 16 bytes per load, U loads in flight per thread: each
+// workgroup takes consecutive 256 * 16 * U-byte blocks, one contiguous 16-byte piece per thread
+// and load (coalesced).  The XOR of every 32-bit word read is folded per wave and XORed into
+// sink[0] by one atomic per wave: a checksum that keeps the loads alive and lets a test see
+// that every piece was read exactly once.
+template <int U>
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4* __restrict__ src, size_t n16, uint32_t* sink) {
+  constexpr size_t kBlock = (size_t)256 * U;
+  uint32_t acc = 0;
+  for (size_t b = (size_t)blockIdx.x * kBlock; b < n16; b += (size_t)gridDim.x * kBlock) {
+    u32x4 v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const size_t i = b + (size_t)j * 256 + threadIdx.x;
+      v[j] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+  if ((threadIdx.x & 63) == 0 && acc != 0) atomicXor(sink, acc);
+}
+
+int launch_stream_read(const void* src, size_t bytes, int n_blocks, uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(stream_read_kernel<8>, dim3(n_blocks), dim3(256), 0, stream, (const u32x4*)src, bytes / 16,
+                     sink);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
 // ------------------------------------------------------------------ KV append
 
 // rows pos..pos+n-1 of both caches <- k_new / v_new; row_elems = n_kv_heads * head_dim (bf16)

@@ -99,6 +99,7 @@ int layer_lds_bytes();
 int set_layer_kernel_attrs(int lds_bytes);
 
 int launch_fill_zero(void* p, size_t bytes, hipStream_t stream);
+int launch_stream_read(const void* src, size_t bytes, int n_blocks, uint32_t* sink, hipStream_t stream);
 // Fill `bytes` bytes (a multiple of 4) with a 32-bit pattern.
 int launch_fill(void* p, size_t bytes, uint32_t pattern, hipStream_t stream);
 int launch_kv_append(uint16_t* kc, uint16_t* vc, int row_elems, int pos, const uint16_t* kn,

@@ -112,6 +112,9 @@ class Stack:
         launch writes its layer's most-used experts into list 1 - parity; with `prefetch` it
         prefetches the experts of list `parity` (the previous step's), so steps alternate."""
         sh = self.shape
+        if use_bias and self.bias is None:
+            # the structs hold the bias buffer's address: it must exist before they are built
+            self.bias = torch.zeros((self.n_layers, sh.T, sh.n_experts), dtype=torch.float32, device=self.device)
         out = []
         for L, lay in enumerate(self.layers):
             nxt = self.layers[L + 1] if L + 1 < self.n_layers else None
@@ -124,7 +127,7 @@ class Stack:
                 p(lay.topk_idx), None, None, None, None,
                 p(lay.prefetch[parity]) if prefetch else None, self.n_prefetch if prefetch else 0,
                 p(lay.prefetch[1 - parity]), self.n_prefetch,
-                p(self.bias[L]) if (use_bias and self.bias is not None) else None,
+                p(self.bias[L]) if use_bias else None,
                 p(self.ws), self.ws_bytes, None, 0, -1)
             out.append((lay.cfg, lay.w.struct(), io))
         return out

@@ -13,10 +13,10 @@ module both sides use is ``synth`` (seeded inputs, no layer arithmetic).
 from .numerics import (bf16_round, bf16_to_f64, e2m1_value, e4m3_value, e4m3_rne_scale,
                        nvfp4_pack, nvfp4_decode, fp4_act_quant, E2M1_GRID, E4M3_POS)
 from .layer import (tree_masks, visible_keys, attention, dense, router, moe, silu, qkv_project,
-                    layer_step, layer_step_auto, pack_experts, usage_top)
+                    layer_step, layer_step_auto, used_experts, pack_experts, usage_top)
 from .accept import tree_accept, kv_commit
 
 __all__ = ["bf16_round", "bf16_to_f64", "e2m1_value", "e4m3_value", "e4m3_rne_scale",
            "nvfp4_pack", "nvfp4_decode", "fp4_act_quant", "E2M1_GRID", "E4M3_POS",
            "tree_masks", "visible_keys", "attention", "dense", "router", "moe", "silu", "qkv_project",
-           "layer_step", "layer_step_auto", "pack_experts", "usage_top", "tree_accept", "kv_commit"]
+           "layer_step", "layer_step_auto", "used_experts", "pack_experts", "usage_top", "tree_accept", "kv_commit"]

@@ -244,18 +244,22 @@ def pack_experts(inp, which=None) -> dict:
     return {"fmt": "nvfp4", "w1": w1, "w2": w2}
 
 
-def layer_step_auto(inp, anchors=None) -> dict:
-    """Layer step that packs only the experts the routing reaches (the full pack of
-    256 experts is slow in plain NumPy)."""
+def used_experts(inp, anchors=None) -> set:
+    """The experts the step's routing reaches: attention, o-proj, pooler and router as in
+    layer_step (routing does not depend on the experts), with the same anchors."""
     sh = inp.shape
-    if not sh.nvfp4:
-        return layer_step(inp, pack_experts(inp), anchors)
-    # route first (routing does not depend on the experts), then pack what is used
     a = anchors or {}
     attn, _ = attention(inp.q_in, inp.k_cache, inp.v_cache, inp.parent, sh.ctx, sh.window,
                         sh.n_q_heads, sh.n_kv_heads, sh.head_dim)
     h1 = dense(a.get("attn", attn), inp.w_o, inp.h_in)
     xp = dense(a.get("h1", h1), inp.w_pool)
     _, _, idx, _ = router(a.get("xp", xp), inp.w_router, inp.router_bias, sh.top_k)
-    used = set(np.unique(np.asarray(a.get("idx", idx))).tolist())
-    return layer_step(inp, pack_experts(inp, used), anchors)
+    return set(np.unique(np.asarray(a.get("idx", idx))).tolist())
+
+
+def layer_step_auto(inp, anchors=None) -> dict:
+    """Layer step that packs only the experts the routing reaches (the full pack of
+    256 experts is slow in plain NumPy)."""
+    if not inp.shape.nvfp4:
+        return layer_step(inp, pack_experts(inp), anchors)
+    return layer_step(inp, pack_experts(inp, used_experts(inp, anchors)), anchors)

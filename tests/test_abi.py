@@ -140,6 +140,12 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 24, 128, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 16, 192, GOOD, GOOD, check=False) == mk.MK_ESHAPE
     assert mk.mk_nvfp4_tile_w1(GOOD, GOOD, 1, 16, 128, BAD, GOOD, check=False) == mk.MK_EALIGN
+    assert mk.mk_stream_read(None, 16, 256, GOOD, check=False) == mk.MK_EINVAL
+    assert mk.mk_stream_read(GOOD, 16, 256, None, check=False) == mk.MK_EINVAL
+    assert mk.mk_stream_read(GOOD, 16, -1, GOOD, check=False) == mk.MK_ESHAPE
+    assert mk.mk_stream_read(GOOD, 24, 256, GOOD, check=False) == mk.MK_EALIGN
+    assert mk.mk_stream_read(BAD, 16, 256, GOOD, check=False) == mk.MK_EALIGN
+    assert mk.mk_stream_read(GOOD, 0, 256, GOOD, check=False) == mk.MK_OK      # nothing to read: no launch
 
 
 def test_w1_scale_bytes_follow_the_piece_rule():

@@ -217,6 +217,23 @@ def test_route_topk_standalone():
     assert idx[2, 0].item() == 77
 
 
+@pytest.mark.parametrize("n_words,blocks", [(4 * (1 << 20) + 4 * 37, 256), (4 * 1000 + 4, 3), (4, 2048)])
+def test_stream_read_reads_every_byte_once(n_words, blocks):
+    """The streaming-read probe XORs every 32-bit word it reads into the sink: on random data
+    the result equals the host's XOR of the whole buffer (a piece skipped or read twice would
+    change it), and a second call XORs the same value in again, back to zero."""
+    g = np.random.default_rng(31)
+    w = g.integers(0, 1 << 32, n_words, dtype=np.uint64).astype(np.uint32)
+    src = torch.from_numpy(w.view(np.int32)).cuda()
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mk.mk_stream_read(src, 4 * n_words, blocks, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == int(np.bitwise_xor.reduce(w)), (n_words, blocks)
+    mk.mk_stream_read(src, 4 * n_words, blocks, sink)
+    torch.cuda.synchronize()
+    assert int(sink.cpu().numpy().view(np.uint32)[0]) == 0
+
+
 def _run(inp, timestamps=False, st=None, dw=None):
     dw = dw or dt.upload_weights(inp)
     st = st or dt.make_step(inp, timestamps=timestamps)
