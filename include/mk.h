@@ -179,6 +179,46 @@ int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *
 int mk_layer_step_noalloc(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
                           const mk_step_io *io /* [host] */, void *stream);
 
+/* One rank's share of the N-sharded expert layout.  The pages shard both expert GEMMs on
+ * their output dimension across the R tensor-parallel ranks, with an fp4 all-gather of the
+ * intermediate after the first and a bf16 all-gather of the expert output after the second,
+ * a layout bitwise-consistent with expert parallelism (orcarouter.ai write-up, "where the
+ * kernel boundary sits"); receivers poll the payload against a sentinel that no result can
+ * take, instead of a flag (alphasignal.ai, "Four mechanisms keep work moving").  On one GPU
+ * this is rank `rank`'s part of the step, with the two gathered buffers supplied by the caller
+ * (the other ranks' parts arrive there as data):
+ *  - GEMM1 computes this rank's I = cfg.expert_inter intermediate channels (w1_* as in
+ *    mk_layer_step: the full expert's gate and up rows of those channels) and writes them as
+ *    records r I/16 .. (r+1) I/16 - 1 of each pair's row of act_recv;
+ *  - GEMM2 multiplies the gathered rows (K2 = n_ranks I) by this rank's rows of the full down
+ *    projection -- w2_codes uint8 [E][P/R][K2/2], w2_scales uint8 [E][P/R][K2/16] (row-major,
+ *    mk_nvfp4_pack layout, whole-matrix tensor scales in w2_tscale) -- for output columns
+ *    [r P/R, (r+1) P/R), combines the top-k slots locally and writes those columns of y_recv;
+ *  - the unpooler reads all of y_recv.
+ * act_recv: [T*top_k][K2/16] records of 16 bytes, pair p = t*top_k + slot; record q holds
+ *   elements 16q..16q+15 of the pair's intermediate: uint32 codes of elements 0-7 (element j in
+ *   bits 4j..4j+3, E2M1), uint32 E4M3 scale byte (bits 0-7, other bits 0), uint32 codes of
+ *   elements 8-15, the scale again; the tensor scale is 1.  A record not yet delivered holds
+ *   all ones (a real record never does: its scale word is at most 0x7E).
+ * y_recv: bf16 [16][P] in fragment order (as mk_workspace_layout describes), rows >= T
+ *   unused; columns not yet delivered hold 0xFFFF (a bf16 result never does).
+ * Before the launch the caller sets this rank's records and this rank's y_recv columns to all
+ * ones; the other ranks' records and columns hold their data or all ones (the kernel then
+ * waits for them, bounded by spin_limit: a slot that never arrives ends in MK_ETIMEOUT).  The
+ * launch writes this rank's records and columns and reads everything else.  Both buffers are
+ * DEVICE, caller-owned, 16-byte aligned (else MK_EALIGN), NULL -> MK_EINVAL.
+ * Shapes: everything mk_layer_step needs, expert_fmt MK_W_NVFP4 (else MK_EINVAL),
+ * 2 <= n_ranks <= 8 and 0 <= rank < n_ranks, pooled % (8 n_ranks) == 0 and
+ * (n_ranks expert_inter) % 256 == 0, else MK_ESHAPE.  Enqueues one kernel. */
+typedef struct {
+  int rank;            /* this rank r                                                  */
+  int n_ranks;         /* R                                                            */
+  void *act_recv;      /* gathered intermediate records (DEVICE)                       */
+  void *y_recv;        /* gathered expert output, bf16 fragment order (DEVICE)         */
+} mk_nshard;
+int mk_layer_step_nshard(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *w /* [host] */,
+                         const mk_step_io *io /* [host] */, const mk_nshard *ns /* [host] */, void *stream);
+
 /* KV-cache write: copy n new rows into a KV cache pair at rows pos..pos+n-1, bit for bit,
  * every other row untouched.  The pages' launch ends with the next layer's KV write, and the
  * KV history a layer attends over was written by earlier steps (orcarouter.ai write-up,

@@ -19,8 +19,13 @@ MK_W_BF16, MK_W_NVFP4 = 0, 1
 MK_TS_EVENTS = 64
 
 EXPORTED = ["mk_workspace_bytes", "mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
+            "mk_layer_step_nshard",
             "mk_kv_append", "mk_qkv_prologue", "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers", "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_nvfp4_w1_scales_bytes",
             "mk_stream_read", "mk_read_status", "mk_strerror"]
+
+
+class mk_nshard(C.Structure):
+    _fields_ = [("rank", C.c_int), ("n_ranks", C.c_int), ("act_recv", C.c_void_p), ("y_recv", C.c_void_p)]
 
 
 class mk_layer_cfg(C.Structure):
@@ -73,6 +78,8 @@ def lib() -> C.CDLL:
         L.mk_layer_step.argtypes = [C.POINTER(mk_layer_cfg), C.POINTER(mk_layer_weights), C.POINTER(mk_step_io), P]
         L.mk_layer_step_noalloc.argtypes = [C.POINTER(mk_layer_cfg), C.POINTER(mk_layer_weights),
                                             C.POINTER(mk_step_io), P]
+        L.mk_layer_step_nshard.argtypes = [C.POINTER(mk_layer_cfg), C.POINTER(mk_layer_weights),
+                                           C.POINTER(mk_step_io), C.POINTER(mk_nshard), P]
         L.mk_kv_append.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, P, P, C.c_int, P]
         L.mk_qkv_prologue.argtypes = [P, P, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, P, P, P, C.c_int,
                                       C.c_int, P]
@@ -89,6 +96,7 @@ def lib() -> C.CDLL:
         L.mk_strerror.argtypes = [C.c_int]
         L.mk_strerror.restype = C.c_char_p
         for name in ("mk_workspace_query", "mk_workspace_init", "mk_layer_step", "mk_layer_step_noalloc",
+                     "mk_layer_step_nshard",
                      "mk_kv_append", "mk_qkv_prologue",
                      "mk_tree_accept", "mk_kv_commit", "mk_kv_commit_layers",
                      "mk_route_topk", "mk_nvfp4_pack", "mk_nvfp4_tile_w1", "mk_stream_read", "mk_read_status"):
@@ -212,6 +220,12 @@ def mk_layer_step_noalloc(cfg: mk_layer_cfg, w: mk_layer_weights, io: mk_step_io
 def mk_stream_read(src, nbytes, n_blocks, sink, stream=None, check=True) -> int:
     rc = lib().mk_stream_read(_ptr(src), nbytes, n_blocks, _ptr(sink), _stream(stream))
     return _check(rc, "mk_stream_read") if check else rc
+
+
+def mk_layer_step_nshard(cfg: mk_layer_cfg, w: mk_layer_weights, io: mk_step_io, ns: mk_nshard, stream=None,
+                         check=True) -> int:
+    rc = lib().mk_layer_step_nshard(C.byref(cfg), C.byref(w), C.byref(io), C.byref(ns), _stream(stream))
+    return _check(rc, "mk_layer_step_nshard") if check else rc
 
 
 def mk_read_status(workspace, stream=None) -> int:

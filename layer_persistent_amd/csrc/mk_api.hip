@@ -342,6 +342,29 @@ int mk_layer_step_noalloc(const mk_layer_cfg* c, const mk_layer_weights* w, cons
   return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
 }
 
+int mk_layer_step_nshard(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_io* io, const mk_nshard* ns,
+                         void* stream) {
+  if (!ns || !c) return MK_EINVAL;
+  if (c->expert_fmt != MK_W_NVFP4) return MK_EINVAL;
+  if (ns->n_ranks < 2 || ns->n_ranks > 8 || ns->rank < 0 || ns->rank >= ns->n_ranks) return MK_ESHAPE;
+  if (c->pooled % (8 * ns->n_ranks) || (ns->n_ranks * c->expert_inter) % 256) return MK_ESHAPE;
+  if (!ns->act_recv || !ns->y_recv) return MK_EINVAL;
+  if (!aligned16(ns->act_recv) || !aligned16(ns->y_recv)) return MK_EALIGN;
+  mk::KArgs a;
+  Layout L;
+  int rc = build_args(c, w, io, true, io ? io->workspace_bytes : 0, &a, &L);
+  if (rc) return rc;
+  // a workgroup's GEMM2 tasks must span at most two units: the grid covers the column blocks
+  // and the units (at most T k / 2)
+  if (c->pooled / (8 * ns->n_ranks) > a.n_wg || (io->T * c->top_k + 1) / 2 > a.n_wg) return MK_ESHAPE;
+  a.ns_r = ns->rank;
+  a.ns_R = ns->n_ranks;
+  a.act_recv = (uint32_t*)ns->act_recv;
+  a.y_recv = (uint16_t*)ns->y_recv;
+  bind_workspace(&a, L, (char*)io->workspace);
+  return mk::launch_layer(a, mk::layer_lds_bytes(), (hipStream_t)stream) ? MK_EHIP : MK_OK;
+}
+
 int mk_kv_append(void* k_cache, void* v_cache, int capacity, int n_kv_heads, int head_dim, int pos,
                  const void* k_new, const void* v_new, int n, void* stream) {
   if (!k_cache || !v_cache || !k_new || !v_new) return MK_EINVAL;

@@ -38,7 +38,10 @@ constexpr uint32_t kStageXp = kStageHf + 16 * 4096 * 2;         // bf16 [16][P],
 constexpr uint32_t kStageLogits = kStageXp + 16 * 2048 * 2;     // fp32 [T][E]
 constexpr uint32_t kStageAct = kStageLogits + 16 * 256 * 4;     // intermediate records / bf16 rows
 constexpr uint32_t kStageY = kStageAct + 16 * 8 * 256 * 2;      // bf16 [16][P], fragment order
-constexpr uint32_t kStageBytes = kStageY + 16 * 2048 * 2;
+// the N-sharded layout's GEMM2 products before gates, fp32 [T*k][P/R], P/R <= 1024 (reset with
+// the rest of the idle copy by every launch, so that the two layouts may share a workspace)
+constexpr uint32_t kStagePart = kStageY + 16 * 2048 * 2;
+constexpr uint32_t kStageBytes = kStagePart + 16 * 8 * 1024 * 4;
 
 // Kernel arguments of one fused layer launch (passed by value).
 struct KArgs {
@@ -77,6 +80,13 @@ struct KArgs {
                         // 0-7, scale byte, codes of elements 8-15, scale byte
   uint16_t* act_bf;     // bf16 intermediate [T*k][I]
   uint16_t* y;                // fragment order
+  // N-sharded expert layout (rank ns_r of ns_R; ns_R == 0: the ordinary layout): the gathered
+  // intermediate records [T*k][ns_R*I/16][4 dwords], the gathered y (bf16 [16][P], fragment
+  // order), and GEMM2's products before gates (stage, [T*k][P/ns_R] fp32)
+  int ns_r, ns_R;
+  uint32_t* act_recv;
+  uint16_t* y_recv;
+  float* g2_part;
   float* qkv_part;            // split-K qkv partials [tile][part][64 lanes][4]
   uint32_t* qkv_cnt;          // split-K qkv arrival counters, one per tile, 64 bytes apart
   uint64_t* timestamps;

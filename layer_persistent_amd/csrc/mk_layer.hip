@@ -1333,7 +1333,10 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
         const uint32_t w1 = (uint32_t)__builtin_amdgcn_update_dpp((int)w, (int)w, 0x4E, 0xF, 0xF, true);
         // record: codes of elements 0-7 and the scale byte, codes of 8-15 and the scale byte
         // (each 8-byte half holds the scale, at most 0x7E, so neither is ever all ones)
-        if (valid && q == 0) st_coh_u128(a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4, u32x4{w, sc, w1, sc});
+        // (N-sharded layout: this rank's slice of the pair's gathered row)
+        uint32_t* dst = a.ns_R ? a.act_recv + ((size_t)pair * (a.ns_R * I / 16) + a.ns_r * (I / 16) + j0 / 16) * 4
+                               : a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4;
+        if (valid && q == 0) st_coh_u128(dst, u32x4{w, sc, w1, sc});
       } else if (valid) {
         st_coh_u64(a.act_bf + (size_t)pair * I + j0 + 4 * q, pack4_bf16(v));
       }
@@ -1587,6 +1590,160 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
     if (tid >= kCompute && (tid - kCompute) < T) {
       const int t = tid - kCompute;
       uint16_t* dst = a.y + frag_off(t, c0);            // 8 columns: 16 contiguous bytes
+      st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
+      st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
+    }
+  }
+}
+
+// ---- GEMM2 of the N-sharded expert layout: rank r of R computes output columns
+// [r P/R, (r+1) P/R) over the gathered intermediate (K2 = R I, the R ranks' NVFP4 slices in
+// rank order, read from the receive buffer as they arrive), then combines its columns locally
+// and writes them into the gathered y, where the other ranks' columns arrive the same way.
+//
+// Work: the unit tiles of gemm2_fp4 (two slots of <= 8 pairs, 8 columns each), dealt out as
+// tasks (unit U, column block cb of 8 of the P/R columns), task U (P/(8R)) + cb, in contiguous
+// ranges per workgroup: a workgroup's tasks span at most two units (the host checks that the
+// grid covers P/(8R) blocks and T k / 2 units), so it decodes only those units' gathered rows
+// (<= 32 rows of K2) into LDS.  Lane (nl, grp) holds W2 row c0 + nl % 8 of its slot's expert
+// for the quarter [grp K2/4, (grp+1) K2/4) of the reduction, streamed in chunks of 64 values
+// (32 code bytes, 4 scale bytes; NS_CH chunks in flight per wave); the intermediate is read in
+// the same permuted k order.  Each task writes its products before gates as fp32 partials
+// part[pair][c]; a combine step per column block then sums the 8 slots per token in slot order,
+// reading the partials as they arrive.  Requires K2 % 256 == 0 and P % (8 R) == 0.
+constexpr int NS_CH = 4;
+
+template <bool TS>
+__device__ __forceinline__ void gemm2_ns(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, const Sync& sy,
+                                         int32_t* dead_sh) {
+  const int R = a.ns_R, K2 = R * a.I, N2 = a.P / R, K = a.topk, T = a.T, tid = threadIdx.x;
+  const bool cw = tid < kCompute;
+  const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, grp = lane >> 4;
+  const int nblk = N2 / 8, ns = rt.n_slots, npairs = T * K;
+  const long nt = (long)((ns + 1) / 2) * nblk;
+  const int tb = (int)(nt * blockIdx.x / gridDim.x), te = (int)(nt * (blockIdx.x + 1) / gridDim.x);
+  const int Ub = tb / nblk, nloc = te > tb ? (te - 1) / nblk - Ub + 1 : 0;      // <= 2
+  const int astride = K2 + 8;
+  uint16_t* actf = (uint16_t*)smem;                                   // [32][K2 + 8] fp16
+  const int actb = 32 * astride * 2;
+  float* outp = (float*)(smem + actb);                                // [pairs][8] (combine)
+  int32_t* urow = (int32_t*)(smem + actb + 128 * 8 * 4);              // [32]: pair or -1
+  int32_t* vrow = urow + 32;                                          // local rows with a pair
+  int32_t* nvrow = vrow + 32;
+  // local row (U - Ub) 16 + m: slot 2U's m-th pair (m < 8) or slot 2U+1's (m - 8)-th
+  if (tid < 64) {
+    const int lr = tid, U = Ub + (lr >> 4), m = lr & 15, s2 = 2 * U + (m >> 3), j = m & 7;
+    const int pr = (lr < 16 * nloc && s2 < ns && j < rt.slot_cnt[s2]) ? rt.pair_list[rt.slot_off[s2] + j] : -1;
+    const uint64_t has = __ballot(lr < 32 && pr >= 0);
+    if (lr < 32) urow[lr] = pr;
+    if (lr < 32 && pr >= 0) vrow[__popcll(has & ((1ull << lr) - 1ull))] = lr;
+    if (lr == 0) *nvrow = __popcll(has);
+  }
+  wg_sync();
+  // the units' gathered intermediate rows, as they arrive, decoded once into actf
+  const int RB = K2 / 16, nrec = *nvrow * RB;
+  if (cw && nrec > 0)
+    poll_stage<4>(sy, dead_sh, make_rsrc(a.act_recv, (uint32_t)(npairs * RB) * 16u), nrec, tid, kCompute,
+                  [&](int i) { return (uint32_t)(urow[vrow[i / RB]] * RB + i % RB) * 16u; }, [&](int i, u32x4 v) {
+                    const f16x2_t sc = e4m3_to_f16x2(v[1]);
+                    uint16_t* dst = actf + vrow[i / RB] * astride + (i % RB) * 16;
+                    *(u32x4*)dst = fp4x8_to_f16(v[0], sc);
+                    *(u32x4*)(dst + 8) = fp4x8_to_f16(v[2], sc);
+                  });
+  wg_sync();
+  stamp<TS>(a.timestamps, 42, 0);
+  const int kq = K2 / 4, nch = kq / 64;
+  float* part = a.g2_part;
+  if (cw && *dead_sh == 0) {
+    const int my = te - tb > wave ? (te - tb - wave + 7) / 8 : 0;     // this wave's tasks
+    const int nflat = my * nch;                                       // (task, chunk) in order
+    u32x4 c0b[NS_CH], c1b[NS_CH];
+    uint32_t scb[NS_CH];
+    auto task_of = [&](int f, int& U, int& c0, int& e) {
+      const int tau = tb + wave + 8 * (f / nch);
+      U = tau / nblk;
+      c0 = (tau % nblk) * 8;
+      const int sl = (nl >= 8 && 2 * U + 1 < ns) ? 2 * U + 1 : 2 * U;
+      e = rt.slot_expert[sl];
+    };
+    auto load_chunk = [&](int f, u32x4& x0, u32x4& x1, uint32_t& sv) {
+      if (f < nflat) {
+        int U, c0, e;
+        task_of(f, U, c0, e);
+        const int c = f % nch;
+        const size_t row = (size_t)e * N2 + c0 + (nl & 7);
+        const uint8_t* cp = a.w2_codes + row * (K2 / 2) + grp * (K2 / 8) + 32 * c;
+        x0 = __builtin_nontemporal_load((const u32x4*)cp);
+        x1 = __builtin_nontemporal_load((const u32x4*)(cp + 16));
+        sv = __builtin_nontemporal_load((const uint32_t*)(a.w2_scales + row * (K2 / 16) + grp * (K2 / 64) + 4 * c));
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < NS_CH; ++q) load_chunk(q, c0b[q], c1b[q], scb[q]);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int f0 = 0; f0 < nflat; f0 += NS_CH) {
+#pragma unroll
+      for (int q = 0; q < NS_CH; ++q) {
+        const int f = f0 + q;
+        if (f < nflat) {
+          int U, c0, e;
+          task_of(f, U, c0, e);
+          const int c = f % nch, lb = (U - Ub) * 16;
+          // a local row without a pair holds stale LDS: its products land in discarded rows
+          const uint16_t* arow = actf + (lb + nl) * astride + grp * kq + 64 * c;
+#pragma unroll
+          for (int st = 0; st < 8; ++st) {
+            const u32x4 x = *(const u32x4*)(arow + 8 * st);
+            const uint32_t cw4 = st < 4 ? c0b[q][st] : c1b[q][st - 4];
+            acc = mfma_f16(x, fp4x8_to_f16(cw4, e4m3_to_f16x2((scb[q] >> (8 * (st / 2))) & 0xFFu)), acc);
+          }
+          if (c == nch - 1) {
+            // C lane: weight column nl, token rows 4 grp + r; the diagonal blocks hold this
+            // unit's (pair, column) products.  Even lanes store theirs with the odd neighbour's.
+            const float ts = rt.ts2[e];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = acc[r] * ts;
+              const float vn = dpp_f32<0xF5>(v);                    // lane nl + 1 (quad_perm 1,1,3,3)
+              const int row = 4 * grp + r, pair = urow[lb + row];
+              if (pair >= 0 && (row >> 3) == (nl >> 3) && (nl & 1) == 0)
+                st_coh_u64(part + (size_t)pair * N2 + c0 + (nl & 7),
+                           (uint64_t)__float_as_uint(v) | ((uint64_t)__float_as_uint(vn) << 32));
+            }
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+        load_chunk(f + NS_CH, c0b[q], c1b[q], scb[q]);
+      }
+    }
+  }
+  wg_sync();
+  stamp<TS>(a.timestamps, 43, 0);
+  // combine: column blocks cb = blockIdx.x, + grid, ...: every pair's 8 partials, as they arrive
+  for (int cb = blockIdx.x; cb < nblk && *dead_sh == 0; cb += gridDim.x) {
+    const int c0 = cb * 8;
+    if (cw)
+      poll_stage<1>(sy, dead_sh, make_rsrc(part, (uint32_t)(npairs * N2) * 4u), 2 * npairs, tid, kCompute,
+                    [&](int i) { return (uint32_t)((i >> 1) * N2 + c0 + 4 * (i & 1)) * 4u; },
+                    [&](int i, u32x4 v) { *(u32x4*)(outp + (i >> 1) * 8 + 4 * (i & 1)) = v; });
+    wg_sync();
+    if (tid < T) {
+      float y[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) y[c] = 0.f;
+      for (int j = 0; j < K; ++j) {
+        const float gt = rt.gate[tid * K + j];
+        const float* o = outp + (tid * K + j) * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) y[c] += gt * o[c];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ytile[tid * 4 + q] = pack_bf2(y[2 * q], y[2 * q + 1]);
+    }
+    wg_sync();
+    if (tid >= kCompute && (tid - kCompute) < T) {
+      const int t = tid - kCompute;
+      uint16_t* dst = a.y_recv + frag_off(t, a.ns_r * N2 + c0);     // 8 columns: 16 contiguous bytes
       st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
       st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
     }
@@ -1879,13 +2036,16 @@ __device__ __forceinline__ void qkv_split_epilogue(const KArgs& a, const float* 
 // SPEC 1: the shard shape of the pages' model on one GPU (hidden 4096, 8 q heads / 1 kv head
 // of 128, pooled 2048, 256 experts top-8, NVFP4 experts with local intermediate 192, a
 // 16-token tree) with every shape a compile-time constant; SPEC 0 takes shapes at run time.
-template <bool TS, int SPEC>
+// NS: the N-sharded expert layout (a separate instantiation, so that the ordinary layout's
+// code does not carry its registers).
+template <bool TS, int SPEC, bool NS>
 __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   KArgs a = a_in;
   if constexpr (SPEC == 1) {
     a.H = 4096; a.Hq = 8; a.Hkv = 1; a.d = 128; a.P = 2048; a.E = 256; a.topk = 8; a.I = 192;
     a.fmt = 1; a.T = 16;
   }
+  if constexpr (!NS) a.ns_R = 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ Route rt;
   __shared__ Tree tr;
@@ -2017,6 +2177,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     a.act_q = (uint32_t*)(cur + kStageAct);
     a.act_bf = (uint16_t*)(cur + kStageAct);
     a.y = (uint16_t*)(cur + kStageY);
+    a.g2_part = (float*)(cur + kStagePart);
     if (!cw) {
       u32x4* idle = (u32x4*)(a.stage + (size_t)((epoch & 1u) ^ 1u) * kStageBytes);
       constexpr uint32_t words = kStageBytes / 16;
@@ -2188,17 +2349,18 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     wg_sync();
     stamp<TS>(a.timestamps, 12);
     alive = alive && dead_sh == 0;
-    if (alive && cw && g2_fast(a) && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
+    if (alive && cw && !a.ns_R && g2_fast(a) && (int)blockIdx.x < a.P / 8) g2_load(a, rt, blockIdx.x * 8, 0, g2w);
     stamp<TS>(a.timestamps, 13, 0);
     // ---- 7 GEMM2 + combine
     // NVFP4 experts: GEMM2 leaves LDS above 64 KB free, so the control wave streams the
     // unpooler tile there while the experts run (waited for at this phase's hand-off)
     const int g2_lds_end = ((a.T * a.topk * (a.I + 8) * 2 + 255) & ~255) + 128 * 8 * 4 + 72 * 16 * 4;
-    const bool wu_lds = g2_fast(a) && p_u && g2_lds_end <= WU_LDS_OFF &&
+    const bool wu_lds = !a.ns_R && g2_fast(a) && p_u && g2_lds_end <= WU_LDS_OFF &&
                         WU_LDS_OFF + 32 * a.P <= LDS_BYTES;
     if (alive) {
       if (!cw && wu_lds) lds_tile_dma(a.w_unpool, a.P, t_u * 16, smem + WU_LDS_OFF);
-      if (g2_fast(a)) gemm2_fp4<TS>(a, rt, smem, ytile, g2w, s, &dead_sh);
+      if (a.ns_R) gemm2_ns<TS>(a, rt, smem, ytile, s, &dead_sh);
+      else if (g2_fast(a)) gemm2_fp4<TS>(a, rt, smem, ytile, g2w, s, &dead_sh);
       else gemm2_staged<TS>(a, rt, smem, ytile, s, &dead_sh);
     }
     // the unpooler tile is in LDS (the control wave's LDS-DMA during GEMM2, waited for in the hand-off)
@@ -2207,7 +2369,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
             && alive;
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
-      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool, xplain(a.y, s, &dead_sh), a.P, a.H, 0, red2,
+      // (N-sharded layout: the gathered y, the other ranks' columns read as they arrive)
+      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool,
+                  a.ns_R ? xsrc(a.y_recv, a.P, s, &dead_sh) : xplain(a.y, s, &dead_sh), a.P, a.H, 0, red2,
                   [&](int n0, const float* red, int it) {
         if (!crv) return;
         float v[4];
@@ -2270,10 +2434,14 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
 }
 
-template __global__ void layer_kernel<false, 0>(KArgs);
-template __global__ void layer_kernel<true, 0>(KArgs);
-template __global__ void layer_kernel<false, 1>(KArgs);
-template __global__ void layer_kernel<true, 1>(KArgs);
+template __global__ void layer_kernel<false, 0, false>(KArgs);
+template __global__ void layer_kernel<true, 0, false>(KArgs);
+template __global__ void layer_kernel<false, 1, false>(KArgs);
+template __global__ void layer_kernel<true, 1, false>(KArgs);
+template __global__ void layer_kernel<false, 0, true>(KArgs);
+template __global__ void layer_kernel<true, 0, true>(KArgs);
+template __global__ void layer_kernel<false, 1, true>(KArgs);
+template __global__ void layer_kernel<true, 1, true>(KArgs);
 
 int layer_lds_bytes() { return LDS_BYTES; }
 
@@ -2282,21 +2450,29 @@ static bool is_spec1(const KArgs& a) {
          a.I == 192 && a.fmt == 1 && a.T == 16 && a.n_wg >= 240;
 }
 
-int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream) {
+template <bool NS>
+void launch_ns(const KArgs& a, int lds_bytes, hipStream_t stream) {
   const dim3 g(a.n_wg), b(kThreads);
   if (is_spec1(a)) {
-    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 1>), g, b, lds_bytes, stream, a);
-    else hipLaunchKernelGGL((layer_kernel<false, 1>), g, b, lds_bytes, stream, a);
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 1, NS>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 1, NS>), g, b, lds_bytes, stream, a);
   } else {
-    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 0>), g, b, lds_bytes, stream, a);
-    else hipLaunchKernelGGL((layer_kernel<false, 0>), g, b, lds_bytes, stream, a);
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 0, NS>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 0, NS>), g, b, lds_bytes, stream, a);
   }
+}
+
+int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream) {
+  if (a.ns_R) launch_ns<true>(a, lds_bytes, stream);
+  else launch_ns<false>(a, lds_bytes, stream);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 int set_layer_kernel_attrs(int lds_bytes) {
-  const void* fns[] = {(const void*)layer_kernel<false, 0>, (const void*)layer_kernel<true, 0>,
-                       (const void*)layer_kernel<false, 1>, (const void*)layer_kernel<true, 1>};
+  const void* fns[] = {(const void*)layer_kernel<false, 0, false>, (const void*)layer_kernel<true, 0, false>,
+                       (const void*)layer_kernel<false, 1, false>, (const void*)layer_kernel<true, 1, false>,
+                       (const void*)layer_kernel<false, 0, true>, (const void*)layer_kernel<true, 0, true>,
+                       (const void*)layer_kernel<false, 1, true>, (const void*)layer_kernel<true, 1, true>};
   for (const void* f : fns)
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess) return -5;
   return 0;

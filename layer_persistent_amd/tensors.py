@@ -166,6 +166,35 @@ def untile_frag(buf: np.ndarray, T: int, K: int) -> np.ndarray:
     return buf.reshape(K // 32, 4, 16, 8).transpose(2, 0, 1, 3).reshape(16, K)[:T].copy()
 
 
+def tile_frag(rows: np.ndarray, K: int) -> np.ndarray:
+    """Row-major [T <= 16][K] bf16 into MFMA fragment order [16 * K] (rows >= T all ones, the
+    hand-off sentinel): the inverse of untile_frag."""
+    full = np.full((16, K), 0xFFFF, np.uint16)
+    full[:rows.shape[0]] = rows
+    return full.reshape(16, K // 32, 4, 8).transpose(1, 2, 0, 3).reshape(-1).copy()
+
+
+def nvfp4_records(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """NVFP4 rows (codes uint8 [M][K/2], element 2j in the low nibble; E4M3 scales uint8
+    [M][K/16]) as the kernel's 16-byte intermediate records, uint32 [M][K/16][4]: the 4 code
+    bytes of elements 0-7, the scale byte, the 4 code bytes of elements 8-15, the scale byte."""
+    M, K2 = codes.shape[0], codes.shape[1] * 2
+    c = np.ascontiguousarray(codes).reshape(M, K2 // 16, 2, 4).view(np.uint32).reshape(M, K2 // 16, 2)
+    rec = np.empty((M, K2 // 16, 4), np.uint32)
+    rec[:, :, 0] = c[:, :, 0]
+    rec[:, :, 2] = c[:, :, 1]
+    rec[:, :, 1] = scales
+    rec[:, :, 3] = scales
+    return rec
+
+
+def nvfp4_from_records(rec: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Inverse of nvfp4_records: (codes uint8 [M][K/2], scales uint8 [M][K/16])."""
+    M, nb = rec.shape[0], rec.shape[1]
+    c = np.stack([rec[:, :, 0], rec[:, :, 2]], axis=2).astype(np.uint32).view(np.uint8).reshape(M, nb * 8)
+    return c.copy(), (rec[:, :, 1] & 0xFF).astype(np.uint8)
+
+
 def stage_offset(workspace: torch.Tensor, layout, off: int) -> int:
     """Byte offset of a stage buffer of the workspace's last launch: copy (epoch & 1) of the
     launch's epoch, which is one less than the epoch slot of workgroup 0 afterwards."""

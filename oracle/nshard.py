@@ -79,8 +79,6 @@ def moe_rank(xp_bits, idx, gate, w1_rank: dict, w2_shard: dict, I: int, R: int, 
     for e in set(np.asarray(idx).reshape(-1).tolist()):
         dec1[e] = nvfp4_decode(*w1_rank[e])
         dec2[e] = nvfp4_decode(*w2_shard[e])
-    n_own = next(iter(dec2.values())).shape[0]
-    comb = np.zeros((T, n_own))
     for t in range(T):
         for j in range(k):
             e = int(idx[t, j])
@@ -88,9 +86,22 @@ def moe_rank(xp_bits, idx, gate, w1_rank: dict, w2_shard: dict, I: int, R: int, 
             c, s = intermediate_slice(xp[t], dec1[e], I)
             codes_all[p, r * I // 2:(r + 1) * I // 2] = c
             scales_all[p, r * I // 16:(r + 1) * I // 16] = s
+    return gemm2_rank(idx, gate, codes_all, scales_all, dec2), codes_all, scales_all
+
+
+def gemm2_rank(idx, gate, codes_all, scales_all, w2_dec: dict):
+    """Rank r's second GEMM and combine from the gathered rows as given: y_own[t] =
+    sum over slots j (in slot order) of gate[t, j] * (decoded row of pair t k + j) . W2_e^T,
+    with w2_dec {e: decoded [P/R][R I] fp64}; one bf16 rounding.  Returns bf16 [T][P/R]."""
+    T, k = np.asarray(idx).shape
+    n_own = next(iter(w2_dec.values())).shape[0]
+    comb = np.zeros((T, n_own))
+    for t in range(T):
+        for j in range(k):
+            p = t * k + j
             a_full = nvfp4_decode(codes_all[p][None, :], scales_all[p][None, :], 1.0)[0]
-            comb[t] += gate[t, j] * (a_full @ dec2[e].T)
-    return bf16_round(comb), codes_all, scales_all
+            comb[t] += gate[t, j] * (a_full @ w2_dec[int(idx[t, j])].T)
+    return bf16_round(comb)
 
 
 def gathered_y(y_peers_bits, y_own_bits, R: int, r: int):

@@ -24,6 +24,7 @@ T_WO, T_WP, T_WR, T_WU, T_WQKV = 10, 11, 12, 13, 14
 T_WQKV0 = 15        # layer 0's own qkv projection (the embedding prologue of a stack)
 T_W1, T_W2 = 20, 21
 T_TREE, T_BIAS, T_MARKOV, T_KNEXT = 30, 31, 32, 33
+T_W2SHARD, T_PEER_CODES, T_PEER_SCALES, T_PEER_Y = 40, 41, 42, 43
 
 
 @dataclasses.dataclass(frozen=True)
@@ -275,3 +276,23 @@ def stack_router_biases(shape: LayerShape, cfg_id: int, n_layers: int, n_steps: 
             out[s, L] = bias
             prev = np.stack([np.flatnonzero(bias[t]) for t in range(shape.T)])
     return out
+
+
+# ---------------------------------------------------------------- N-sharded expert layout
+
+def nshard_inputs(shape: LayerShape, cfg_id: int, R: int, r: int) -> dict:
+    """What rank r of R needs beyond the layer's inputs in the N-sharded expert layout, drawn
+    at random: its rows of the full down projections, w2_shard bf16 [E][P/R][R I] (N(0, 0.02)
+    like every weight); what the other ranks deliver -- the gathered intermediate rows as
+    NVFP4 codes uint8 [T k][R I / 2] (any byte) and E4M3 scale bytes [T k][R I / 16] (0x10 ..
+    0x30: 2^-5 .. 2^-1, so that decoded values stay below 3, near the size of a real
+    intermediate), and y columns bf16 [T][P] (N(0, 0.1)).  Rank r's own parts of the last two
+    are filled in by whoever computes them; their draws here are discarded."""
+    b = base_seed(cfg_id)
+    P, E, I, T, k = shape.pooled, shape.n_experts, shape.expert_inter, shape.T, shape.top_k
+    w2 = np.stack([normal_bf16(rng(b, r, T_W2SHARD, e), (P // R, R * I), 0.02) for e in range(E)])
+    g = rng(b, r, T_PEER_CODES, 0)
+    codes = g.integers(0, 256, (T * k, R * I // 2), dtype=np.uint8)
+    scales = rng(b, r, T_PEER_SCALES, 0).integers(0x10, 0x31, (T * k, R * I // 16), dtype=np.uint8)
+    y = normal_bf16(rng(b, r, T_PEER_Y, 0), (T, P), 0.1)
+    return dict(w2_shard=w2, peer_codes=codes, peer_scales=scales, peer_y=y)

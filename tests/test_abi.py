@@ -148,6 +148,28 @@ def test_small_entry_points_validate_on_host():
     assert mk.mk_stream_read(GOOD, 0, 256, GOOD, check=False) == mk.MK_OK      # nothing to read: no launch
 
 
+def test_nshard_entry_validates_on_host():
+    c, w, io = _cfg(), _weights(), _io()
+    ns = lambda **kw: mk.mk_nshard(*[kw.get(f, d) for f, d in (("rank", 3), ("n_ranks", 8), ("act_recv", GOOD),
+                                                                  ("y_recv", GOOD))])
+    call = lambda cfg, n: mk.mk_layer_step_nshard(cfg, w, io, n, check=False)
+    assert call(_cfg(expert_fmt=mk.MK_W_BF16), ns()) == mk.MK_EINVAL
+    assert call(c, ns(n_ranks=1, rank=0)) == mk.MK_ESHAPE
+    assert call(c, ns(n_ranks=9)) == mk.MK_ESHAPE
+    assert call(c, ns(rank=8)) == mk.MK_ESHAPE
+    assert call(c, ns(rank=-1)) == mk.MK_ESHAPE
+    assert call(c, ns(n_ranks=3)) == mk.MK_ESHAPE                     # 2048 % 24 != 0
+    assert call(c, ns(n_ranks=2)) == mk.MK_ESHAPE                     # 2 * 192 % 256 != 0
+    assert call(c, ns(act_recv=None)) == mk.MK_EINVAL
+    assert call(c, ns(y_recv=BAD)) == mk.MK_EALIGN
+    assert mk.lib().mk_layer_step_nshard(ctypes_byref(c), ctypes_byref(w), ctypes_byref(io), None, None) == mk.MK_EINVAL
+
+
+def ctypes_byref(x):
+    import ctypes
+    return ctypes.byref(x)
+
+
 def test_w1_scale_bytes_follow_the_piece_rule():
     # L = K/128 k-steps; 2 pieces when L > 8; 8 * ceil(L / pieces) bytes per piece and row
     assert mk.mk_nvfp4_w1_scales_bytes(1, 16, 2048) == 16 * 128       # L = 16: 2 x 64 = K/16
