@@ -93,6 +93,13 @@ def _blas_threads() -> int:
         return 1
 
 
+def batch_bytes(shape, n_active: int, B: int) -> int:
+    """Compulsory bytes of a launch of B sequences: the weights and the active experts once,
+    each sequence's visible KV rows, activations and KV writes."""
+    ab = algorithmic_bytes(shape, n_active)
+    return ab["dense"] + ab["experts"] + B * (ab["kv"] + ab["acts"] + ab["kv_write"])
+
+
 def cpu_baseline(inputs: dict, reps: int = 3) -> dict:
     """The oracle (fp64 NumPy) on the host: full layer steps of the single-layer workloads,
     each timed `reps` times with BLAS limited to one thread and with every thread it has, the
@@ -369,6 +376,103 @@ def bench_reuse(args, stk, ins) -> dict:
     return dict(results=res, n_active_last_step=per_layer["reuse80_prefetch"], n_layers=n_layers)
 
 
+def bench_nshard(inp, args, R: int = 8, r: int = 3) -> dict:
+    """The same layer in the pages' N-sharded expert layout (rank r of R; mk_layer_step_nshard):
+    the other ranks' intermediate slices and y columns are delivered by the host into a fresh
+    pair of receive buffers per launch before the timed region (so that every launch polls
+    real arrivals, not leftovers), and the K launches run back to back."""
+    import torch
+    import synth
+    import layer_persistent_amd as mk
+    from layer_persistent_amd import tensors as dt
+    sh = inp.shape
+    E, P, I, T, k = sh.n_experts, sh.pooled, sh.expert_inter, sh.T, sh.top_k
+    K2, N2 = R * I, P // R
+    ns = synth.nshard_inputs(sh, args.config, R, r)
+    dw = dt.upload_weights(inp)
+    u8 = dict(dtype=torch.uint8, device="cuda")
+    dw.w2_codes = torch.empty((E, N2, K2 // 2), **u8)
+    dw.w2_scales = torch.empty((E, N2, K2 // 16), **u8)
+    dw.w2_ts = torch.empty(E, dtype=torch.float32, device="cuda")
+    mk.mk_nvfp4_pack(dt.dev_u16(ns["w2_shard"]), 0, E, N2, K2, dw.w2_codes, dw.w2_scales, dw.w2_ts)
+    st = dt.make_step(inp)
+    rec = dt.nvfp4_records(ns["peer_codes"], ns["peer_scales"])
+    rec[:, r * I // 16:(r + 1) * I // 16, :] = 0xFFFFFFFF
+    yr = ns["peer_y"].copy()
+    yr[:, r * N2:(r + 1) * N2] = 0xFFFF
+    n = args.warmup + args.steps
+    act = torch.from_numpy(rec.view(np.int32)).cuda().unsqueeze(0).repeat(n, 1, 1, 1).contiguous()
+    yrv = torch.from_numpy(dt.tile_frag(yr, P).view(np.int16)).cuda().unsqueeze(0).repeat(n, 1).contiguous()
+    lib = mk.lib()
+    stream = torch.cuda.current_stream()
+    cfg, w, io = st.cfg, dw.struct(), st.struct()
+    args_ns = [mk.mk_nshard(r, R, act[i].data_ptr(), yrv[i].data_ptr()) for i in range(n)]
+    call = lambda i: lib.mk_layer_step_nshard(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io),
+                                              ctypes.byref(args_ns[i]), stream.cuda_stream)
+    for i in range(args.warmup):
+        if call(i) != 0:
+            raise RuntimeError("mk_layer_step_nshard failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.warmup, n):
+        call(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s_ = mk.mk_read_status(st.workspace)
+    if s_ != 0:
+        raise RuntimeError(f"nshard in-kernel status {mk.mk_strerror(s_)}")
+    us = e0.elapsed_time(e1) * 1000.0 / args.steps
+    log(f"N-sharded expert layout (rank {r} of {R}, GEMM2 K = {K2} -> {N2} columns): {us:.2f} us per launch")
+    return {"us_per_launch": round(us, 2), "ranks": R, "rank": r, "gemm2_k": K2, "gemm2_n": N2,
+            "launches": args.steps}
+
+
+def bench_batch2(inp, args, n_rep: int = 3) -> dict:
+    """Two sequences verified in one launch (mk_step_io.batch = 2): the workload's sequence and a
+    second one with its own tree, queries, residual and KV rows (another seed) over the same
+    weights; `n_rep` replicas of weights and steps rotate so that a launch's weights are not
+    served from the previous launch's cache."""
+    import dataclasses
+    import torch
+    import synth
+    import layer_persistent_amd as mk
+    from layer_persistent_amd import tensors as dt
+    sh = inp.shape
+    s1 = synth.make_layer_inputs(sh, args.config + 1000, step=1)
+    weights = ("w_o", "w_pool", "w_router", "w_unpool", "w_qkv_next", "w1", "w2")
+    s1 = dataclasses.replace(s1, **{w: getattr(inp, w) for w in weights})
+    reps = []
+    for _ in range(n_rep):
+        dw = dt.upload_weights(inp)
+        st = dt.make_step_batch([inp, s1])
+        reps.append((dw, st, st.cfg, dw.struct(), st.struct()))
+    lib = mk.lib()
+    stream = torch.cuda.current_stream()
+    call = lambda i: lib.mk_layer_step(ctypes.byref(reps[i % n_rep][2]), ctypes.byref(reps[i % n_rep][3]),
+                                       ctypes.byref(reps[i % n_rep][4]), stream.cuda_stream)
+    for i in range(args.warmup):
+        if call(i) != 0:
+            raise RuntimeError("mk_layer_step (batch 2) failed")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(args.warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    for _, st, _, _, _ in reps:
+        s_ = mk.mk_read_status(st.workspace)
+        if s_ != 0:
+            raise RuntimeError(f"batch 2 in-kernel status {mk.mk_strerror(s_)}")
+    us = e0.elapsed_time(e1) * 1000.0 / args.steps
+    n_active = int(len(np.unique(reps[0][1].topk_idx.cpu().numpy())))
+    log(f"two sequences per launch (32 tokens, {n_active} active experts): {us:.2f} us per launch")
+    return {"us_per_launch": round(us, 2), "sequences": 2, "tokens": 2 * sh.T, "active_experts": n_active,
+            "bytes_per_launch": batch_bytes(sh, n_active, 2),
+            "launches": args.steps}
+
+
 def mk_read_status_ok(stk) -> int:
     import layer_persistent_amd as mk
     s = mk.mk_read_status(stk.ws)
@@ -392,6 +496,8 @@ def main():
     ap.add_argument("--no-phases", action="store_true")
     ap.add_argument("--dump-timestamps", default=None,
                     help="save the timing build's per-workgroup event ticks ([n_wg][64] int64, .npy)")
+    ap.add_argument("--no-nshard", action="store_true", help="skip the N-sharded expert layout's timing")
+    ap.add_argument("--no-batch2", action="store_true", help="skip the two-sequence launch's timing")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip the graph-replay timing of the same K launches")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -557,6 +663,9 @@ def main():
         log(f"copy calibration: 3 x torch.neg over {COPY_CALIB_ELEMS * 4} B read + {COPY_CALIB_ELEMS * 4} B written")
         del src, dst
 
+    nshard_res = None if args.no_nshard else bench_nshard(inp, args)
+    batch2_res = None if args.no_batch2 else bench_batch2(inp, args)
+
     phases = None
     if not args.no_phases:
         dw0 = reps[0][0]
@@ -635,6 +744,8 @@ def main():
         # measured step (bench.py --config 4)
         "projected_62_layer_step_us": round(62 * kern_us, 1),
         "phases_end_us": phases,
+        "nshard_layout": nshard_res,
+        "batch2": batch2_res,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

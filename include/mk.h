@@ -122,6 +122,17 @@ typedef struct {
   int spin_limit;              /* [host] 0 = default; else max polls of each in-kernel wait  */
   int debug_skip_signal_wg;    /* [host] -1 normally; test hook: this workgroup never signals,
                                   so the others' bounded waits must end in MK_ETIMEOUT        */
+  int batch;                   /* [host] 0 or 1: one sequence.  2: two sequences verified in
+                                  one launch (the pages name batch one as the present limit:
+                                  alphasignal.ai, "Batch one defines the current limit"), each
+                                  a tree of T = 16 over its own KV cache at the same ctx_len;
+                                  every weight is read once for both.  Then tree_parent is
+                                  [2][16]; q_in, h_in, h_out, q_next, topk_idx, topk_gate,
+                                  router_logits, attn_stats and router_bias hold 32 rows,
+                                  sequence b on rows 16b..16b+15; the four KV caches are
+                                  [2][cap][Hkv][d] (sequence b at b*cap rows).  Needs NVFP4
+                                  experts with expert_inter a multiple of 64 in [128, 192];
+                                  not with mk_layer_step_nshard.  Else MK_ESHAPE.            */
 } mk_step_io;
 
 #define MK_TS_EVENTS 64
@@ -148,7 +159,10 @@ typedef struct {
   size_t epoch;        /* uint32 epoch slot of workgroup 0                       */
 } mk_workspace_layout;
 
-/* Workspace bytes for this config on the current device (0 on an unsupported config). */
+/* Workspace bytes for this config on the current device (0 on an unsupported config); for
+ * T = 16 the size also covers launches of two sequences (mk_step_io.batch = 2).  The stage
+ * buffers hold one 16-row tile per sequence: sequence b's tile of a buffer at offset
+ * + b * 16 * K * 2 bytes (K its column count). */
 size_t mk_workspace_bytes(const mk_layer_cfg *cfg, int T);
 /* Offsets of the hand-off buffers; returns MK_OK or an mk_status. */
 int mk_workspace_query(const mk_layer_cfg *cfg, int T, mk_workspace_layout *out /* [host] */);

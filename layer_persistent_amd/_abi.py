@@ -50,7 +50,7 @@ class mk_step_io(C.Structure):
                 ("prefetch_experts", C.c_void_p), ("n_prefetch", C.c_int),
                 ("prefetch_next", C.c_void_p), ("n_prefetch_next", C.c_int), ("router_bias", C.c_void_p),
                 ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t), ("timestamps", C.c_void_p),
-                ("spin_limit", C.c_int), ("debug_skip_signal_wg", C.c_int)]
+                ("spin_limit", C.c_int), ("debug_skip_signal_wg", C.c_int), ("batch", C.c_int)]
 
 
 class mk_workspace_layout(C.Structure):

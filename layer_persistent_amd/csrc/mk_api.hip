@@ -108,17 +108,22 @@ void attn_split(const mk_layer_cfg* c, int T, int ctx, int n_wg, Layout* L) {
   }
 }
 
-Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
+// `B` sequences of T tokens share the launch: each sequence's attention is split exactly as in
+// a launch of its own (so that a sequence's results do not depend on the batch it is in), and
+// its items follow the previous sequence's.  The attention partials and the split-K qkv
+// partials take B times the room; every offset before them does not depend on B.
+Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg, int B = 1) {
   Layout L;
   memset(&L, 0, sizeof(L));
   L.n_wg = n_wg;
   attn_split(c, T, ctx, n_wg, &L);
-  // partial slots [kv head][chunk]: a split within one round has at most n_wg of them;
-  // beyond, chunks are kChunkMax keys and their count grows with the context
+  L.items *= B;
+  // partial slots [sequence][kv head][chunk]: a split within one round has at most n_wg of
+  // them; beyond, chunks are kChunkMax keys and their count grows with the context
   {
     const int keys_max = ctx - (c->window > 0 && ctx - c->window + 1 > 0 ? ctx - c->window + 1 : 0);
     const int big = c->n_kv_heads * ((keys_max + kChunkMax - 1) / kChunkMax + 1);
-    L.part_slots = big > n_wg ? big : n_wg;
+    L.part_slots = B * (big > n_wg ? big : n_wg);
   }
   const int d = c->head_dim;
   size_t o = 0;
@@ -129,8 +134,8 @@ Layout layout(const mk_layer_cfg* c, int T, int ctx, int n_wg) {
   L.zero_end = o;                                // == zero_bytes(n_wg)
   // the stage buffers, two copies at fixed offsets (mk::kStage*)
   L.stage = o; o = up256(o + 2 * (size_t)mk::kStageBytes);
-  // split-K qkv: at most one (tile, part) per workgroup
-  L.qkv_part = o; o = up256(o + (size_t)n_wg * 64 * 4 * 4);
+  // split-K qkv: at most one (tile, part) per workgroup, one partial per sequence
+  L.qkv_part = o; o = up256(o + (size_t)n_wg * B * 64 * 4 * 4);
   // attention partials [slot][128 rows]: (m, l), then o
   L.part_ml = o; o = up256(o + (size_t)L.part_slots * 128 * 2 * 4);
   L.part_o = o; o = up256(o + (size_t)L.part_slots * 128 * d * 4);
@@ -157,6 +162,11 @@ int build_args(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_i
   int rc = check_cfg(c, io->T);
   if (rc) return rc;
   const int T = io->T, ctx = io->ctx_len;
+  const int B = io->batch <= 1 ? 1 : io->batch;
+  if (io->batch < 0 || B > 2) return MK_ESHAPE;
+  if (B > 1 && (T != 16 || c->expert_fmt != MK_W_NVFP4 || c->expert_inter % 64 || c->expert_inter < 128 ||
+                c->expert_inter > 192))
+    return MK_ESHAPE;
   if (ctx < 0 || ctx + T > c->kv_capacity) return MK_ECAPACITY;
   if (need_ws && !io->workspace) return MK_EINVAL;
   const void* req[] = {io->tree_parent, io->q_in, io->h_in, io->k_cache, io->v_cache, io->h_out,
@@ -187,17 +197,17 @@ int build_args(const mk_layer_cfg* c, const mk_layer_weights* w, const mk_step_i
   if (rc) return rc;
   // the workspace must cover the largest context this cache allows, so one workspace serves
   // every step of a layer
-  Layout L = layout(c, T, c->kv_capacity - T, n_wg);
-  Layout Lc = layout(c, T, ctx, n_wg);
+  Layout L = layout(c, T, c->kv_capacity - T, n_wg, B);
+  Layout Lc = layout(c, T, ctx, n_wg, B);
   *Lout = L;
   if (ws_bytes < L.total) return MK_ECAPACITY;
-  if (c->n_kv_heads * Lc.chunks_per_head > L.part_slots) return MK_ECAPACITY;
+  if (B * c->n_kv_heads * Lc.chunks_per_head > L.part_slots) return MK_ECAPACITY;
 
   mk::KArgs& a = *out;
   memset(&a, 0, sizeof(a));
   a.H = c->hidden; a.Hq = c->n_q_heads; a.Hkv = c->n_kv_heads; a.d = c->head_dim; a.P = c->pooled;
   a.E = c->n_experts; a.topk = c->top_k; a.I = c->expert_inter; a.window = c->window;
-  a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T; a.ctx = ctx;
+  a.fmt = c->expert_fmt; a.cap = c->kv_capacity; a.T = T * B; a.ctx = ctx; a.B = B; a.Ts = T;
   a.n_wg = n_wg; a.attn_items = Lc.items; a.attn_chunks_per_head = Lc.chunks_per_head;
   a.attn_lo = Lc.attn_lo; a.ck = Lc.ck; a.attn_rw = Lc.rw; a.attn_nrb = Lc.nrb;
   a.spin_limit = io->spin_limit > 0 ? io->spin_limit : kDefaultSpin;
@@ -291,7 +301,9 @@ int mk_workspace_query(const mk_layer_cfg* cfg, int T, mk_workspace_layout* out)
   int n_wg = 0;
   rc = device_cus(&n_wg);
   if (rc) return rc;
-  Layout L = layout(cfg, T, cfg->kv_capacity - T > 0 ? cfg->kv_capacity - T : 0, n_wg);
+  // T = 16 may also run two sequences (mk_step_io.batch = 2): the size covers that
+  const int B = T == 16 ? 2 : 1;
+  Layout L = layout(cfg, T, cfg->kv_capacity - T > 0 ? cfg->kv_capacity - T : 0, n_wg, B);
   out->status = L.status;
   out->attn = L.stage + mk::kStageAttn;
   out->h1 = L.stage + mk::kStageH1;
@@ -350,6 +362,7 @@ int mk_layer_step_nshard(const mk_layer_cfg* c, const mk_layer_weights* w, const
   if (c->pooled % (8 * ns->n_ranks) || (ns->n_ranks * c->expert_inter) % 256) return MK_ESHAPE;
   if (!ns->act_recv || !ns->y_recv) return MK_EINVAL;
   if (!aligned16(ns->act_recv) || !aligned16(ns->y_recv)) return MK_EALIGN;
+  if (io && io->batch > 1) return MK_ESHAPE;
   mk::KArgs a;
   Layout L;
   int rc = build_args(c, w, io, true, io ? io->workspace_bytes : 0, &a, &L);

@@ -29,24 +29,29 @@ __host__ __device__ inline int status_code(uint32_t word) { return (int)(int8_t)
 // Stage (hand-off) buffers between the phases of a launch.  There are two copies; a launch
 // uses copy (epoch & 1) and, at its start, resets the other one to the sentinel for the next
 // launch.  Each buffer sits at a fixed offset inside a copy, sized for the largest supported
-// shapes (T 16, Hq*d 1024, H 4096, P 2048, E 256, top-k 8, I 256), so that one workspace
-// serves every configuration.  A consumer reads them as they arrive: see arrived16().
-constexpr uint32_t kStageAttn = 0;                              // bf16 [16][Hq*d], fragment order
-constexpr uint32_t kStageH1 = kStageAttn + 16 * 1024 * 2;       // bf16 [16][H], fragment order
-constexpr uint32_t kStageHf = kStageH1 + 16 * 4096 * 2;         // bf16 [16][H] h_out, fragment order
-constexpr uint32_t kStageXp = kStageHf + 16 * 4096 * 2;         // bf16 [16][P], fragment order
-constexpr uint32_t kStageLogits = kStageXp + 16 * 2048 * 2;     // fp32 [T][E]
-constexpr uint32_t kStageAct = kStageLogits + 16 * 256 * 4;     // intermediate records / bf16 rows
-constexpr uint32_t kStageY = kStageAct + 16 * 8 * 256 * 2;      // bf16 [16][P], fragment order
+// shapes (32 rows -- two sequences of 16 --, Hq*d 1024, H 4096, P 2048, E 256, top-k 8, I 256),
+// so that one workspace serves every configuration.  Row-tiled activations hold one 16-row
+// MFMA fragment tile per sequence, tile b at b * 16 K elements.  A consumer reads them as they
+// arrive: see arrived16().
+constexpr int kMaxRowTiles = 2;
+constexpr uint32_t kStageAttn = 0;                                         // bf16 [tiles][16][Hq*d], fragment order
+constexpr uint32_t kStageH1 = kStageAttn + kMaxRowTiles * 16 * 1024 * 2;   // bf16 [tiles][16][H], fragment order
+constexpr uint32_t kStageHf = kStageH1 + kMaxRowTiles * 16 * 4096 * 2;     // bf16 h_out, fragment order
+constexpr uint32_t kStageXp = kStageHf + kMaxRowTiles * 16 * 4096 * 2;     // bf16 [tiles][16][P], fragment order
+constexpr uint32_t kStageLogits = kStageXp + kMaxRowTiles * 16 * 2048 * 2; // fp32 [rows][E]
+constexpr uint32_t kStageAct = kStageLogits + kMaxRowTiles * 16 * 256 * 4; // intermediate records / bf16 rows
+constexpr uint32_t kStageY = kStageAct + kMaxRowTiles * 16 * 8 * 256 * 2;  // bf16 [tiles][16][P], fragment order
 // the N-sharded layout's GEMM2 products before gates, fp32 [T*k][P/R], P/R <= 1024 (reset with
 // the rest of the idle copy by every launch, so that the two layouts may share a workspace)
-constexpr uint32_t kStagePart = kStageY + 16 * 2048 * 2;
+constexpr uint32_t kStagePart = kStageY + kMaxRowTiles * 16 * 2048 * 2;
 constexpr uint32_t kStageBytes = kStagePart + 16 * 8 * 1024 * 4;
 
 // Kernel arguments of one fused layer launch (passed by value).
 struct KArgs {
   // shapes
-  int H, Hq, Hkv, d, P, E, topk, I, window, fmt, cap, T, ctx;
+  // T: rows of the launch (every token of every sequence); B sequences of Ts tokens each
+  // (B > 1: Ts = 16, sequence b on rows 16 b .. 16 b + 15)
+  int H, Hq, Hkv, d, P, E, topk, I, window, fmt, cap, T, ctx, B, Ts;
   // launch geometry
   int n_wg, attn_items, attn_chunks_per_head, attn_lo, ck;
   int attn_rw, attn_nrb;     // row tiles per attention item, row blocks per chunk
@@ -72,21 +77,18 @@ struct KArgs {
   uint32_t *epoch, *flags;
   char* stage;                // stage buffers, copy 0 (copy 1 follows at kStageBytes)
   float *part_o, *part_ml;
-  // this launch's stage buffers (set in the kernel from `stage` and the epoch's parity)
-  uint16_t *attn, *h1, *xp;   // hand-off activations, [16][K] bf16 in MFMA fragment order
-  uint16_t* h_frag;           // h_out in fragment order (the qkv phase's x)
-  float* logits;
-  uint32_t* act_q;      // NVFP4 intermediate records [T*k][I/16][4 dwords]: codes of elements
-                        // 0-7, scale byte, codes of elements 8-15, scale byte
-  uint16_t* act_bf;     // bf16 intermediate [T*k][I]
-  uint16_t* y;                // fragment order
+  // this launch's copy of the stage buffers (set in the kernel from `stage` and the epoch's
+  // parity); the buffers at the kStage* offsets: attn, h1, xp, y hand-off activations ([16][K]
+  // bf16 tiles in MFMA fragment order), h_out in fragment order (the qkv phase's x), logits,
+  // the NVFP4 intermediate records [T*k][I/16][4 dwords] (codes of elements 0-7, scale byte,
+  // codes of elements 8-15, scale byte) or bf16 rows [T*k][I], GEMM2 partials
+  char* cur;
   // N-sharded expert layout (rank ns_r of ns_R; ns_R == 0: the ordinary layout): the gathered
   // intermediate records [T*k][ns_R*I/16][4 dwords], the gathered y (bf16 [16][P], fragment
   // order), and GEMM2's products before gates (stage, [T*k][P/ns_R] fp32)
   int ns_r, ns_R;
   uint32_t* act_recv;
   uint16_t* y_recv;
-  float* g2_part;
   float* qkv_part;            // split-K qkv partials [tile][part][64 lanes][4]
   uint32_t* qkv_cnt;          // split-K qkv arrival counters, one per tile, 64 bytes apart
   uint64_t* timestamps;

@@ -69,7 +69,7 @@ constexpr int MAXS_U = 8;          // unpooler K = P    <= 2048
 constexpr int MAXS_Q = 16;         // qkv      K = H    <= 4096
 // dynamic LDS layout (byte offsets; phases reuse the same space)
 constexpr int XS_STRIDE_PAD = 8;                       // bf16 elements of padding per xp row
-constexpr int G1_XS_BYTES = 16 * (2048 + 8) * 2;       // xp rows for GEMM1
+constexpr int G1_XS_BYTES = 32 * (1024 + 8) * 2;       // xp rows for GEMM1: 16 x (2048 + 8) or 32 x (1024 + 8)
 constexpr int LDS_BYTES = 148 * 1024;                  // >= every phase's use (GEMM1: 136.5 KB)
 // A pooler tile (16 x K <= 4096 bf16 = 128 KB) held in LDS from launch start, above the 17 KB of
 // dense-phase reduction buffers and the merge scratch
@@ -79,6 +79,18 @@ static_assert(POOL_LDS_OFF + 16 * 4096 * 2 <= LDS_BYTES, "pooler tile in LDS");
 constexpr int WU_LDS_OFF = 64 * 1024;
 static_assert(WU_LDS_OFF + 16 * 2048 * 2 <= LDS_BYTES, "unpooler tile in LDS");
 static_assert(G1_XS_BYTES + 16 * 16 * 128 + 2 * 16 * 16 * 17 * 4 <= LDS_BYTES, "GEMM1 LDS");
+
+// This launch's stage buffers (copy `a.cur`), computed where they are used rather than held:
+// nine pointers kept live through the launch would crowd the scalar registers.
+__device__ __forceinline__ uint16_t* st_attn(const KArgs& a) { return (uint16_t*)(a.cur + kStageAttn); }
+__device__ __forceinline__ uint16_t* st_h1(const KArgs& a) { return (uint16_t*)(a.cur + kStageH1); }
+__device__ __forceinline__ uint16_t* st_h_frag(const KArgs& a) { return (uint16_t*)(a.cur + kStageHf); }
+__device__ __forceinline__ uint16_t* st_xp(const KArgs& a) { return (uint16_t*)(a.cur + kStageXp); }
+__device__ __forceinline__ float* st_logits(const KArgs& a) { return (float*)(a.cur + kStageLogits); }
+__device__ __forceinline__ uint32_t* st_act_q(const KArgs& a) { return (uint32_t*)(a.cur + kStageAct); }
+__device__ __forceinline__ uint16_t* st_act_bf(const KArgs& a) { return (uint16_t*)(a.cur + kStageAct); }
+__device__ __forceinline__ uint16_t* st_y(const KArgs& a) { return (uint16_t*)(a.cur + kStageY); }
+__device__ __forceinline__ float* st_g2_part(const KArgs& a) { return (float*)(a.cur + kStagePart); }
 
 __device__ __forceinline__ void wg_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -106,26 +118,32 @@ __device__ __forceinline__ void stamp(uint64_t* ts, int ev, int who = kCtl) {
 
 // ------------------------------------------------------------------ shared state
 
-struct Route {            // routing tables, identical in every workgroup
-  int32_t idx[16 * 8];    // [T][k]
-  float gate[16 * 8];
+// Routing tables, identical in every workgroup, for up to NRT * 16 rows of k <= 8 pairs (16-bit
+// entries keep the two-sequence tables within the LDS budget).
+template <int NRT>
+struct RouteT {
+  static constexpr int kPairs = NRT * 16 * 8;
+  int16_t idx[kPairs];    // [rows][k]
+  float gate[kPairs];
+  // GEMM1 entries: the active experts in ascending order, an expert with more than 16 pairs as
+  // several entries of <= 16 (one 16-row MFMA tile each)
   int32_t n_active;
-  int32_t act_expert[128];
-  int32_t act_off[128];
-  int32_t act_cnt[128];
-  int32_t pair_list[128]; // pair id t*k + slot, grouped by expert (ascending), then by pair id
+  int16_t act_expert[256 + kPairs / 17];
+  int16_t act_off[256 + kPairs / 17];
+  int16_t act_cnt[256 + kPairs / 17];
+  int16_t pair_list[kPairs];  // pair id row*k + slot, grouped by expert (ascending), then by pair id
   float ts1[256], ts2[256];  // NVFP4 tensor scales of every expert (W1, W2)
-  // GEMM2 slots: each active expert's first (up to) 8 pairs, then the rest of every expert
-  // with more than 8 pairs; a slot holds at most 8 pairs
+  // GEMM2 slots: each GEMM1 entry's first (up to) 8 pairs, then the rest of every entry with
+  // more than 8 pairs; a slot holds at most 8 pairs
   int32_t n_slots;
-  int32_t slot_expert[144];
-  int32_t slot_off[144];  // into pair_list
-  int32_t slot_cnt[144];
+  int16_t slot_expert[kPairs];
+  int16_t slot_off[kPairs];  // into pair_list
+  int16_t slot_cnt[kPairs];
 };
 
-struct Tree {
-  uint32_t anc[16];
-  int32_t lo[16];         // first visible context row per token
+struct Tree {              // per row (sequence b's tokens on rows b Ts ..; ancestors within it)
+  uint32_t anc[32];
+  int32_t lo[32];         // first visible context row per token
   int32_t bad;
 };
 
@@ -281,6 +299,13 @@ __device__ __forceinline__ XSrc xsrc(const uint16_t* x, int K, const Sync& sy, i
 }
 __device__ __forceinline__ XSrc xplain(const uint16_t* x, const Sync& sy, int32_t* dead_sh) {
   return XSrc{make_rsrc(x, 0u), x, &sy, dead_sh, false};
+}
+// Row tile r of a row-tiled stage buffer with K columns (tiles 16 K elements apart).
+__device__ __forceinline__ XSrc xtile(const XSrc& x, int r, int K) {
+  XSrc y = x;
+  y.x = x.x + (size_t)r * 16 * K;
+  y.r = make_rsrc(y.x, x.poll ? (uint32_t)K * 32u : 0u);
+  return y;
 }
 
 // This lane's 16-byte pieces j < NB of a stage buffer (byte offsets off[j]; read when need[j],
@@ -593,25 +618,27 @@ __device__ __forceinline__ void stage_pieces(int n, SrcF piece, DstF dst) {
 // puts keys on the MFMA M axis so that the probabilities land in exactly the B-operand layout
 // the P.V product needs.
 struct AttnItem {
-  int g, chunk, rb, kb, nk;
+  int b, g, chunk, rb, kb, nk;      // b: the sequence (its KV cache, queries and tree)
   bool tree;
 };
 __device__ __forceinline__ AttnItem attn_item(const KArgs& a, int item) {
   AttnItem t;
   const int per_g = a.attn_chunks_per_head * a.attn_nrb;
+  t.b = a.B == 1 ? 0 : item / (a.Hkv * per_g);   // (one sequence: a constant, no scalar registers)
+  item -= t.b * a.Hkv * per_g;
   t.g = item / per_g;
   const int r = item % per_g;
   t.chunk = r / a.attn_nrb;
   t.rb = r % a.attn_nrb;
   t.tree = t.chunk == a.attn_chunks_per_head - 1;
   t.kb = t.tree ? a.ctx : a.attn_lo + t.chunk * a.ck;
-  t.nk = t.tree ? a.T : min(a.ck, a.ctx - t.kb);
+  t.nk = t.tree ? a.Ts : min(a.ck, a.ctx - t.kb);
   return t;
 }
 
 // This lane's query fragments (B operand of S^T): row = 16 tile + l%16, d = 32 s + 8 (l/16).
 __device__ __forceinline__ void attention_q(const KArgs& a, const AttnItem& it, u32x4 qf[4]) {
-  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G;
+  const int d = a.d, G = a.Hq / a.Hkv, R = a.Ts * G;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = (it.rb * a.attn_rw + wave % a.attn_rw) * 16 + (lane & 15), grp = lane >> 4;
   const bool rv = threadIdx.x < kCompute && row < R;
@@ -619,7 +646,7 @@ __device__ __forceinline__ void attention_q(const KArgs& a, const AttnItem& it, 
   // every lane loads, unconditionally (conditional loads would leave join copies that wait for
   // every load in flight): a row outside the item reads row 0, whose finite values only reach
   // scores that are masked for that row; k-steps past d/32 are never used
-  const uint16_t* q = a.q_in + (size_t)tok * a.Hq * d + head * d + grp * 8;
+  const uint16_t* q = a.q_in + (size_t)(it.b * a.Ts + tok) * a.Hq * d + head * d + grp * 8;
 #pragma unroll
   for (int s = 0; s < 4; ++s) qf[s] = ld16(q + (s < d / 32 ? s : 0) * 32);
 }
@@ -644,8 +671,9 @@ __device__ __forceinline__ void stage_load(const KArgs& a, const AttnItem& it, i
   const int d = a.d, per_row = d / 8, nkp = a.ck / 2;
   const int kpieces = a.ck * per_row, vpieces = nkp * per_row;
   const size_t rstride = (size_t)a.Hkv * d;
-  const uint16_t* kbase = a.kc + ((size_t)it.kb * a.Hkv + it.g) * d;
-  const uint16_t* vbase = a.vc + ((size_t)it.kb * a.Hkv + it.g) * d;
+  const size_t seq = (size_t)it.b * a.cap * a.Hkv * d;           // sequence it.b's cache
+  const uint16_t* kbase = a.kc + seq + ((size_t)it.kb * a.Hkv + it.g) * d;
+  const uint16_t* vbase = a.vc + seq + ((size_t)it.kb * a.Hkv + it.g) * d;
   // Every piece is loaded unconditionally from a valid address (a key past the chunk's rows
   // reads its last row, a piece past the chunk reads piece 0); stage_store zeroes or skips
   // those.  Conditional loads would leave join copies that wait for every load in flight.
@@ -709,7 +737,7 @@ __device__ __forceinline__ void stage_store(const KArgs& a, const AttnItem& it, 
 template <int RW, bool TS>
 __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr, const AttnItem& it, char* smem,
                                                   const u32x4 qf[4]) {
-  const int d = a.d, G = a.Hq / a.Hkv, R = a.T * G, ck = a.ck;
+  const int d = a.d, G = a.Hq / a.Hkv, R = a.Ts * G, ck = a.ck;
   constexpr int rw = RW, nkw = 8 / RW;
   const int ks_stride = d + 8, vs = vt_stride(ck);
   const uint16_t* Ks = (const uint16_t*)smem;
@@ -730,9 +758,10 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
   const int k0 = kg * kpg, k1 = min(k0 + kpg, it.nk);
   // visibility of chunk key kl for this lane's row: kl in [vis_lo, nk) for context chunks
   // (sliding-window lower bound), the ancestor mask for the tree chunk
-  const int vis_lo = rv ? max(0, tr.lo[tok] - it.kb) : 0;
+  const int trow = it.b * a.Ts + tok;           // the token's row (its sequence's tree bits at b Ts)
+  const int vis_lo = rv ? max(0, tr.lo[trow] - it.kb) : 0;
   const int vis_hi = rv ? it.nk : 0;
-  const uint32_t anc_m = rv ? tr.anc[tok] : 0u;
+  const uint32_t anc_m = rv ? tr.anc[trow] >> (it.b * a.Ts) : 0u;
   float m = -INFINITY, lpart = 0.f;
   f32x4 o[8];
 #pragma unroll
@@ -819,7 +848,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
   }
   stamp<TS>(a.timestamps, 39, 0);
   const float lsum = xgroup_sum(lpart);
-  const int slot = it.g * a.attn_chunks_per_head + it.chunk;
+  const int slot = (it.b * a.Hkv + it.g) * a.attn_chunks_per_head + it.chunk;
   if (nkw == 1) {
     if (rv) {
       float* po = a.part_o + ((size_t)slot * 128 + row) * d;
@@ -889,8 +918,10 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
 // and its stats go to LDS `outrow` for the control wave to store.  Called by all threads.
 __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scratch, uint32_t* outrow) {
   const int d = a.d;
-  const int G = a.Hq / a.Hkv, R = a.T * G;
-  const int g_kv = unit / R, row = unit % R;
+  const int G = a.Hq / a.Hkv, R = a.Ts * G;
+  const int b = a.B == 1 ? 0 : unit / (a.Hkv * R);       // the sequence
+  unit -= b * a.Hkv * R;
+  const int g_kv = b * a.Hkv + unit / R, row = unit % R;    // (partial slots are per sequence)
   const int nchunks = a.attn_chunks_per_head;
   const int quads = d / 4;
   const int ngroups = kCompute / 32;
@@ -954,8 +985,8 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
 // Top-k per token from the logits (value desc, index asc), softmax gates over the selected,
 // and the dispatch tables.  Every workgroup computes the same tables.  Called by all threads;
 // the work runs on the compute waves.
-template <bool TS>
-__device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* lg, const Sync& sy, int32_t* dead_sh) {
+template <bool TS, class RT>
+__device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, float* lg, const Sync& sy, int32_t* dead_sh) {
   const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
   const int npairs = T * K;
   const bool cw = tid < kCompute;
@@ -968,13 +999,15 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
   });
   if (cw)
-    poll_stage<2>(sy, dead_sh, make_rsrc(a.logits, (uint32_t)nlg * 16), nlg, tid, kCompute,
+    poll_stage<2>(sy, dead_sh, make_rsrc(st_logits(a), (uint32_t)nlg * 16), nlg, tid, kCompute,
                   [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) { *(u32x4*)(lg + 4 * i) = v; });
-  // scratch after the logits: per expert, a bitmask of the pairs routed there, counts, offsets
+  // scratch after the logits: per expert, a bitmask of the pairs routed there (kMW words),
+  // counts, offsets
+  constexpr int kMW = RT::kPairs / 32;
   uint32_t* mask = (uint32_t*)(lg + T * E);
-  int32_t* ecnt = (int32_t*)(mask + E * 4);
+  int32_t* ecnt = (int32_t*)(mask + E * kMW);
   int32_t* efirst = ecnt + E;
-  for (int i = tid; cw && i < E * 4; i += kCompute) mask[i] = 0u;
+  for (int i = tid; cw && i < E * kMW; i += kCompute) mask[i] = 0u;
   wg_sync();
   stamp<TS>(a.timestamps, 46, 0);
   const int lane = tid & 63, wave = tid >> 6;
@@ -1049,19 +1082,24 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
   }
   wg_sync();
   stamp<TS>(a.timestamps, 47, 0);
-  for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&mask[rt.idx[p] * 4 + (p >> 5)], 1u << (p & 31));
+  for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&mask[rt.idx[p] * kMW + (p >> 5)], 1u << (p & 31));
   wg_sync();
-  for (int e = tid; cw && e < E; e += kCompute)
-    ecnt[e] = __popc(mask[e * 4]) + __popc(mask[e * 4 + 1]) + __popc(mask[e * 4 + 2]) + __popc(mask[e * 4 + 3]);
+  for (int e = tid; cw && e < E; e += kCompute) {
+    int c = 0;
+#pragma unroll
+    for (int q = 0; q < kMW; ++q) c += __popc(mask[e * kMW + q]);
+    ecnt[e] = c;
+  }
   wg_sync();
   if (tid < 64) {
-    // exclusive scans over experts: lane handles 4 consecutive experts
+    // exclusive scans over experts: lane handles 4 consecutive experts; an expert takes
+    // ceil(count / 16) GEMM1 entries
     int cnt[4], act[4], sumc = 0, suma = 0;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
       cnt[q] = e < E ? ecnt[e] : 0;
-      act[q] = cnt[q] > 0;
+      act[q] = (cnt[q] + 15) / 16;
       sumc += cnt[q];
       suma += act[q];
     }
@@ -1076,10 +1114,10 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
       if (e < E) efirst[e] = pc;
-      if (act[q]) {
+      for (int j = 0; j < act[q]; ++j) {
         rt.act_expert[pa] = e;
-        rt.act_off[pa] = pc;
-        rt.act_cnt[pa] = cnt[q];
+        rt.act_off[pa] = pc + 16 * j;
+        rt.act_cnt[pa] = min(16, cnt[q] - 16 * j);
         ++pa;
       }
       pc += cnt[q];
@@ -1132,7 +1170,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, Route& rt, float* l
   }
   for (int p = tid; cw && p < npairs; p += kCompute) {
     const int e = rt.idx[p];
-    const uint32_t* m = mask + e * 4;
+    const uint32_t* m = mask + e * kMW;
     const int w = p >> 5;
     int r = __popc(m[w] & ((1u << (p & 31)) - 1u));
     for (int q = 0; q < w; ++q) r += __popc(m[q]);
@@ -1173,7 +1211,7 @@ __device__ __forceinline__ void xp_fetch(const KArgs& a, u32x4 (&v)[8], uint32_t
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int i = j * kCompute + tid;
-    if (i < n && piece_row(i) < a.T) v[j] = ld16(a.xp + (size_t)i * 8);
+    if (i < n && piece_row(i) < a.T) v[j] = ld16(st_xp(a) + (size_t)i * 8);
   }
   if (a.fmt != 1) return;
 #pragma unroll
@@ -1234,6 +1272,71 @@ __device__ __forceinline__ void xs_build(const KArgs& a, const u32x4 (&v)[8], ui
   wg_sync();
 }
 
+// Two sequences (32 rows, NVFP4 experts): the row scales from all of xp's two 16-row tiles
+// (piece maxima in `pmax`, [32][P/8]), then GEMM1's input rows for columns [c_lo, c_lo + ncol)
+// (all of them, or one K half when 32 rows of P do not fit), reloaded from xp.  Called by all
+// threads; both return synchronised.
+template <bool TS>
+__device__ __forceinline__ void xs_rowscale2(const KArgs& a, uint32_t* pmax, int32_t* xk) {
+  const int tid = threadIdx.x, per_row = a.P / 8, n = 16 * per_row;
+  const bool cw = tid < kCompute;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int r = 0; r < 2; ++r) {
+    u32x4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = j * kCompute + tid;
+      if (cw && i < n) v[j] = ld16(st_xp(a) + (size_t)r * 16 * a.P + (size_t)i * 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = j * kCompute + tid;
+      if (cw && i < n) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w = v[j][q] & 0x7FFF7FFFu;
+          m = max(m, max(w & 0xFFFFu, w >> 16));
+        }
+        pmax[(16 * r + piece_row(i)) * per_row + piece_col8(i)] = m;
+      }
+    }
+  }
+  wg_sync();
+  for (int t = wave; cw && t < 32; t += 8) {
+    uint32_t m = 0;
+    for (int i = lane; i < per_row; i += 64) m = max(m, pmax[t * per_row + i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    if (lane == 0) xk[t] = m == 0 ? 0 : min(126, max(-126, 141 - (int)(m >> 7)));
+  }
+  wg_sync();
+}
+__device__ __forceinline__ void xs_fill2(const KArgs& a, uint16_t* xs, int xstride, int c_lo, int ncol,
+                                         const int32_t* xk) {
+  const int tid = threadIdx.x, per_row = a.P / 8, n = 16 * per_row;
+  if (tid >= kCompute) return;
+  for (int r = 0; r < 2; ++r) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = j * kCompute + tid;
+      const int c = piece_col8(i) * 8;
+      if (i < n && c >= c_lo && c < c_lo + ncol) {
+        const int t = 16 * r + piece_row(i);
+        const u32x4 v = ld16(st_xp(a) + (size_t)r * 16 * a.P + (size_t)i * 8);
+        const float f = __uint_as_float((uint32_t)(127 + xk[t]) << 23);   // 2^xk[t], exact
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(v[q] << 16) * f, hi = __uint_as_float(v[q] & 0xFFFF0000u) * f;
+          o[q] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+        }
+        *(u32x4*)(xs + t * xstride + (c - c_lo)) = o;
+      }
+    }
+  }
+}
+
 // NVFP4 experts whose local intermediate is a multiple of 64 and at least 128 take gemm2_fp4;
 // the others gemm2_staged
 __device__ __forceinline__ bool g2_fast(const KArgs& a) { return a.fmt == 1 && a.I % 64 == 0 && a.I >= 128; }
@@ -1243,8 +1346,8 @@ __device__ __forceinline__ bool g2_fast(const KArgs& a) { return a.fmt == 1 && a
 // in the ubuf area, before GEMM1's first products.
 __device__ __forceinline__ int g1_ubuf_off(int P) { return G1_XS_BYTES + 16 * P; }
 
-template <bool TS>
-__device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, char* smem, int32_t* xk) {
+template <bool TS, class RT>
+__device__ __forceinline__ void gemm1_phase(const KArgs& a, const RT& rt, char* smem, int32_t* xk) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int jblocks = I / 16;
@@ -1252,8 +1355,16 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   const int nwg = gridDim.x;
   const int t_begin = (int)((long)blockIdx.x * ntasks / nwg), t_end = (int)((long)(blockIdx.x + 1) * ntasks / nwg);
   if (t_begin >= t_end) return;                 // uniform over the workgroup
-  const int xstride = P + XS_STRIDE_PAD;
-  const uint16_t* xs = (const uint16_t*)smem;                      // [T][P + 8], built before routing
+  const int nh = g1_pieces(P);                                   // pieces per unit
+  const int hsteps = g1_hsteps(P);                               // load steps per piece (<= 8)
+  // Two sequences of 16 with two pieces per unit: 32 rows of P do not fit, so xs holds one K
+  // half -- the columns of pieces hf -- at a time (half 0 built before routing): a round runs
+  // every half-0 piece, swaps in half 1 between two barriers, then runs the half-1 pieces, with
+  // pieces dealt half-major (piece pc: unit pc % nu, half pc / nu).
+  constexpr int NRT = RT::kPairs / 128;
+  const bool kh = NRT == 2 && nh == 2;
+  const int xstride = (kh ? hsteps * 128 : P) + XS_STRIDE_PAD;
+  uint16_t* xs = (uint16_t*)smem;                                  // [T][cols + 8], built before routing
   // sbuf: the wave-private piece-scale buffers (16 rows x srow_b bytes each, 2 per wave: within
   // 16 P bytes for every P % 128 == 0 up to 2048)
   uint8_t* sbuf = (uint8_t*)(smem + G1_XS_BYTES);                  // 16 P bytes
@@ -1265,9 +1376,23 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   // round-robin (piece pc: unit pc / nh, half pc % nh), so the waves carry equal work.  A wave
   // streams its pieces with the next piece's codes and block scales in flight while the
   // current one is multiplied; each piece leaves its partial tile in ubuf[unit][half].
-  const int nh = g1_pieces(P);                                   // pieces per unit
-  const int hsteps = g1_hsteps(P);                               // load steps per piece (<= 8)
   const int srow_b = g1_sb(P);                                   // scale bytes per row and piece
+  auto piece_uh = [&](int u0, int pc, int& u, int& hf) {
+    if (kh) {
+      const int nu = min(G1_UNITS, nunits - u0);
+      u = pc % nu;
+      hf = pc / nu;
+    } else {
+      u = pc / nh;
+      hf = pc % nh;
+    }
+  };
+  // (two K halves) all threads: xs becomes the columns of pieces `h`
+  auto xs_swap = [&](int h) {
+    wg_sync();
+    xs_fill2(a, xs, xstride, h * hsteps * 128, hsteps * 128, xk);
+    wg_sync();
+  };
   u32x4 cA[8], cB[8], sA, sB;
   // Piece pc of the round at unit u0 into cd / sv.  A piece that does not exist (`real` false)
   // loads the first bytes of W1 at one address for all lanes instead: a few cache lines whose
@@ -1276,7 +1401,8 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   // while the next one stays in flight.  Past-the-end k-steps of a piece load its last k-step.
   auto load_piece = [&](int u0, int pc, bool real, u32x4 (&cd)[8], u32x4& sv) {
     const int pcr = real ? pc : 0;
-    const int u = pcr / nh, hf = pcr % nh;
+    int u, hf;
+    piece_uh(u0, pcr, u, hf);
     const int task = t_begin + (u0 + u) / 2, half = (u0 + u) & 1;
     const int ai = task / jblocks, j0 = (task % jblocks) * 16;
     // W1 is in GEMM1's operand order: k-step ls of the 16-row tile is 1 KB, lane l's 16 B at
@@ -1335,10 +1461,10 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
         // (each 8-byte half holds the scale, at most 0x7E, so neither is ever all ones)
         // (N-sharded layout: this rank's slice of the pair's gathered row)
         uint32_t* dst = a.ns_R ? a.act_recv + ((size_t)pair * (a.ns_R * I / 16) + a.ns_r * (I / 16) + j0 / 16) * 4
-                               : a.act_q + ((size_t)pair * (I / 16) + j0 / 16) * 4;
+                               : st_act_q(a) + ((size_t)pair * (I / 16) + j0 / 16) * 4;
         if (valid && q == 0) st_coh_u128(dst, u32x4{w, sc, w1, sc});
       } else if (valid) {
-        st_coh_u64(a.act_bf + (size_t)pair * I + j0 + 4 * q, pack4_bf16(v));
+        st_coh_u64(st_act_bf(a) + (size_t)pair * I + j0 + 4 * q, pack4_bf16(v));
       }
     }
   };
@@ -1352,6 +1478,8 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
   stamp<TS>(a.timestamps, 49, 0);
   for (int u0 = 0; u0 < nunits; u0 += G1_UNITS) {
     const int nu = min(G1_UNITS, nunits - u0);
+    if (kh && u0 > 0) xs_swap(0);                 // (the last round ended on half 1)
+    bool swapped = false;
     if (cw && a.fmt == 1) {
       const int npc = nh * nu;
       const int my = wave < npc ? (npc - 1 - wave) / 8 + 1 : 0;     // this wave's pieces
@@ -1360,7 +1488,9 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
       // piece jj of this wave (pc = wave + 8 jj) from cd / sv into ubuf[unit][half]; x picks
       // the wave's scale buffer
       auto piece_mma = [&](int jj, const u32x4 (&cd)[8], const u32x4& sv, int x) {
-        const int pc = wave + 8 * jj, u = pc / nh, hf = pc % nh;
+        const int pc = wave + 8 * jj;
+        int u, hf;
+        piece_uh(u0, pc, u, hf);
         const int task = t_begin + (u0 + u) / 2;
         const int ai = task / jblocks;
         const int cnt = rt.act_cnt[ai], off = rt.act_off[ai];
@@ -1379,7 +1509,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
             const f16x2_t s0 = e4m3_to_f16x2(sc & 0xFF), s1 = e4m3_to_f16x2(sc >> 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const u32x4 xa = *(const u32x4*)(xrow + ls * 128 + q * 8);
+              const u32x4 xa = *(const u32x4*)(xrow + (kh ? k : ls) * 128 + q * 8);
               acc = mfma_f16(xa, fp4x8_to_f16(cd[k][q], q < 2 ? s0 : s1), acc);
             }
           }
@@ -1393,12 +1523,25 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
       };
       // two pieces per trip, each loaded one piece ahead; the loads do not depend on which
       // pieces exist, only the products do
+      // (two K halves: the swap to half 1 before this wave's first half-1 piece)
+      auto maybe_swap = [&](int jj) {
+        if (kh && !swapped && wave + 8 * jj >= nu) {
+          xs_swap(1);
+          swapped = true;
+        }
+      };
 #pragma unroll 1
       for (int j = 0; j < mmax; j += 2) {
         load_piece(u0, wave + 8 * (j + 1), j + 1 < my, cB, sB);
-        if (j < my) piece_mma(j, cA, sA, 0);
+        if (j < my) {
+          maybe_swap(j);
+          piece_mma(j, cA, sA, 0);
+        }
         load_piece(u0, wave + 8 * (j + 2), j + 2 < my, cA, sA);
-        if (j + 1 < my) piece_mma(j + 1, cB, sB, 1);
+        if (j + 1 < my) {
+          maybe_swap(j + 1);
+          piece_mma(j + 1, cB, sB, 1);
+        }
       }
     } else if (cw) {
       // bf16 experts: rows loaded as they are used
@@ -1426,6 +1569,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const Route& rt, cha
         }
       }
     }
+    if (kh && !swapped) xs_swap(1);               // every wave takes part in the swap once
     wg_sync();
     if (u0 == 0) stamp<TS>(a.timestamps, 45, 0);
     swiglu_round(u0, nu);
@@ -1463,7 +1607,8 @@ __device__ __forceinline__ uint32_t g2_sbyte(u32x2 win, int k) {
 
 // Loads unit U into register slot `i` of `w` for columns [c0, c0+8).  Compute waves only;
 // `rt` must hold this launch's routing.
-__device__ __forceinline__ void g2_load_unit(const KArgs& a, const Route& rt, int c0, int U, G2W& w, int i) {
+template <class RT>
+__device__ __forceinline__ void g2_load_unit(const KArgs& a, const RT& rt, int c0, int U, G2W& w, int i) {
   const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
   const int I = a.I, nb = I / 64, ns = rt.n_slots;
   if (2 * U < ns) {                                              // uniform over the wave
@@ -1480,7 +1625,8 @@ __device__ __forceinline__ void g2_load_unit(const KArgs& a, const Route& rt, in
 }
 
 // Batch `batch` of this wave: units wave + 8 (G2_UNITS batch + i), i < G2_UNITS.
-__device__ __forceinline__ void g2_load(const KArgs& a, const Route& rt, int c0, int batch, G2W& w) {
+template <class RT>
+__device__ __forceinline__ void g2_load(const KArgs& a, const RT& rt, int c0, int batch, G2W& w) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < G2_UNITS; ++i) g2_load_unit(a, rt, c0, wave + 8 * (G2_UNITS * batch + i), w, i);
@@ -1488,7 +1634,8 @@ __device__ __forceinline__ void g2_load(const KArgs& a, const Route& rt, int c0,
 
 // One unit from register slot `i` of `w`.  urow[U][m] is the pair on token row m (-1: none).
 // Writes the expert outputs (before gates) to outp[pair][8].
-__device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G2W& w, int i, int U,
+template <class RT>
+__device__ __forceinline__ void g2_unit(const KArgs& a, const RT& rt, const G2W& w, int i, int U,
                                         const int32_t* urow, const uint16_t* actf, int astride, float* outp) {
   const int lane = threadIdx.x & 63, nl = lane & 15, grp = lane >> 4;
   const int I = a.I;
@@ -1518,8 +1665,8 @@ __device__ __forceinline__ void g2_unit(const KArgs& a, const Route& rt, const G
 
 // Called by all threads.  `w0` holds batch 0 of this workgroup's first slice, loaded during
 // the hand-off after GEMM1.
-template <bool TS>
-__device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, G2W& w0,
+template <bool TS, class RT>
+__device__ __forceinline__ void gemm2_fp4(const KArgs& a, const RT& rt, char* smem, uint32_t* ytile, G2W& w0,
                                           const Sync& sy, int32_t* dead_sh) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
@@ -1530,7 +1677,7 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
   uint16_t* actf = (uint16_t*)smem;                                 // [pairs][I + 8]
   const int actb = (npairs * astride * 2 + 255) & ~255;
   float* outp = (float*)(smem + actb);                              // [pairs][8]
-  int32_t* urow = (int32_t*)(smem + actb + 128 * 8 * 4);            // [units][16]
+  int32_t* urow = (int32_t*)(smem + actb + RT::kPairs * 8 * 4);     // [units][16]
   const int wave = tid >> 6;
   for (int sl = blockIdx.x; sl < nslices; sl += nwg) {
     const int c0 = sl * 8;
@@ -1543,9 +1690,9 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
       }
       // the intermediate, read as it arrives from GEMM1: one 16-element block (codes and scale
       // byte) per record, decoded once
-      const int nblk = npairs * (I / 16);                           // <= 2048
+      const int nblk = npairs * (I / 16);                           // <= 4096
       if (cw)
-        poll_stage<4>(sy, dead_sh, make_rsrc(a.act_q, (uint32_t)nblk * 16), nblk, tid, kCompute,
+        poll_stage<4>(sy, dead_sh, make_rsrc(st_act_q(a), (uint32_t)nblk * 16), nblk, tid, kCompute,
                       [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) {
                         const int pair = i / (I / 16), b = i % (I / 16);
                         const f16x2_t sc = e4m3_to_f16x2(v[1]);
@@ -1589,7 +1736,7 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
     wg_sync();
     if (tid >= kCompute && (tid - kCompute) < T) {
       const int t = tid - kCompute;
-      uint16_t* dst = a.y + frag_off(t, c0);            // 8 columns: 16 contiguous bytes
+      uint16_t* dst = st_y(a) + (size_t)(t >> 4) * 16 * a.P + frag_off(t & 15, c0);   // 8 columns: 16 contiguous bytes
       st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
       st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
     }
@@ -1613,8 +1760,8 @@ __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const Route& rt, char*
 // reading the partials as they arrive.  Requires K2 % 256 == 0 and P % (8 R) == 0.
 constexpr int NS_CH = 4;
 
-template <bool TS>
-__device__ __forceinline__ void gemm2_ns(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile, const Sync& sy,
+template <bool TS, class RT>
+__device__ __forceinline__ void gemm2_ns(const KArgs& a, const RT& rt, char* smem, uint32_t* ytile, const Sync& sy,
                                          int32_t* dead_sh) {
   const int R = a.ns_R, K2 = R * a.I, N2 = a.P / R, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
@@ -1653,7 +1800,7 @@ __device__ __forceinline__ void gemm2_ns(const KArgs& a, const Route& rt, char* 
   wg_sync();
   stamp<TS>(a.timestamps, 42, 0);
   const int kq = K2 / 4, nch = kq / 64;
-  float* part = a.g2_part;
+  float* part = st_g2_part(a);
   if (cw && *dead_sh == 0) {
     const int my = te - tb > wave ? (te - tb - wave + 7) / 8 : 0;     // this wave's tasks
     const int nflat = my * nch;                                       // (task, chunk) in order
@@ -1762,8 +1909,8 @@ __device__ __forceinline__ void gemm2_ns(const KArgs& a, const Route& rt, char* 
 //  * Per token, the gate-weighted sum over its slots in slot order goes to LDS `ytile`
 //    ([T][4] dwords of bf16 pairs) for the control wave to store.
 // Called by all threads.
-template <bool TS>
-__device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, char* smem, uint32_t* ytile,
+template <bool TS, class RT>
+__device__ __forceinline__ void gemm2_staged(const KArgs& a, const RT& rt, char* smem, uint32_t* ytile,
                                              const Sync& sy, int32_t* dead_sh) {
   const int P = a.P, I = a.I, K = a.topk, T = a.T, tid = threadIdx.x;
   const bool cw = tid < kCompute;
@@ -1783,7 +1930,7 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
   // record) or 8 bf16 per 16-byte piece
   if (cw) {
     const int nblk = fp4 ? npairs * (I / 16) : npairs * (I / 8);
-    const void* src = fp4 ? (const void*)a.act_q : (const void*)a.act_bf;
+    const void* src = fp4 ? (const void*)st_act_q(a) : (const void*)st_act_bf(a);
     poll_stage<4>(sy, dead_sh, make_rsrc(src, (uint32_t)nblk * 16), nblk, tid, kCompute,
                   [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) {
                     if (fp4) {
@@ -1897,7 +2044,7 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
     wg_sync();
     if (tid >= kCompute && (tid - kCompute) < T) {
       const int t = tid - kCompute;
-      uint16_t* dst = a.y + frag_off(t, c0);            // 8 columns: 16 contiguous bytes
+      uint16_t* dst = st_y(a) + (size_t)(t >> 4) * 16 * a.P + frag_off(t & 15, c0);   // 8 columns: 16 contiguous bytes
       st_coh_u64(dst, (uint64_t)ytile[t * 4] | ((uint64_t)ytile[t * 4 + 1] << 32));
       st_coh_u64(dst + 4, (uint64_t)ytile[t * 4 + 2] | ((uint64_t)ytile[t * 4 + 3] << 32));
     }
@@ -1913,28 +2060,34 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const Route& rt, ch
 // Loads for the next phase are not issued here but inside the hand-off wait that follows
 // (phase_end's `pf`): issued before the hand-off, a large tile's loads hold the issuing waves
 // until the CU's load queue drains, and the grid waits for them at the barrier.
-template <int MAXS, class Epi>
+template <int NRT, int MAXS, class Epi>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
                             const XSrc& x, int K, int N, int off, float* red2, Epi epi,
                             const char* wlds = nullptr) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
-    float* red = red2 + (it & 1) * (8 * 16 * 17);
-    if (threadIdx.x < kCompute) {
-      f32x4 acc;
-      if (wlds && it == 0) {
-        acc = lds_mma(wlds, x, a.T, K);                // the first tile's weights are in LDS
-      } else if constexpr (MAXS == 0) {
-        acc = stream_mma(W, K, t * 16, x, a.T);
-      } else {
-        if (!(have_pref && it == 0)) wfrag_load(wf, W, K, t * 16);
-        acc = wfrag_mma(wf, x, 0, a.T, K);
+    // every row tile (sequence) with the same weights: registers or LDS, loaded once
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) {
+      float* red = red2 + ((it * NRT + r) & 1) * (8 * 16 * 17);
+      if (threadIdx.x < kCompute) {
+        const XSrc xr = NRT == 1 ? x : xtile(x, r, K);
+        const int Tr = min(16, a.T - 16 * r);
+        f32x4 acc;
+        if (wlds && it == 0) {
+          acc = lds_mma(wlds, xr, Tr, K);                // the first tile's weights are in LDS
+        } else if constexpr (MAXS == 0) {
+          acc = stream_mma(W, K, t * 16, xr, Tr);
+        } else {
+          if (!(have_pref && it == 0) && r == 0) wfrag_load(wf, W, K, t * 16);
+          acc = wfrag_mma(wf, xr, 0, Tr, K);
+        }
+        red_store(red, acc);
       }
-      red_store(red, acc);
+      wg_sync();
+      if (threadIdx.x >= kCompute) epi(t * 16, red, it, r);
     }
-    wg_sync();
-    if (threadIdx.x >= kCompute) epi(t * 16, red, it);
   }
 }
 
@@ -1996,39 +2149,50 @@ __device__ __forceinline__ QkvSplit qkv_split(int ksteps, int ntiles, int nwg) {
   return q;
 }
 
-// Control wave of a workgroup holding part `part` of tile `tile`: the part's sums from the
-// waves' partials in `red`, the exchange, and (last part only) the tile's outputs.
+// Control wave of a workgroup holding part `part` of tile `tile`: the part's sums of every row
+// tile r from the waves' partials in red + r * (8 * 16 * 17), the exchange, and (last part
+// only) the tile's outputs.
+template <int NRT>
 __device__ __forceinline__ void qkv_split_epilogue(const KArgs& a, const float* red, int tile, int part, int np,
-                                                   int crow, int cc0, bool crv) {
+                                                   int crow, int cc0) {
   const int lane = threadIdx.x & 63;
-  float v[4];
-  ctl_tile_vals(red, crow, cc0, v);
-  float* mine = a.qkv_part + ((size_t)(tile * np + part) * 64 + lane) * 4;
-  st_coh_u64(mine, (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32));
-  st_coh_u64(mine + 2, (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32));
-  __builtin_amdgcn_s_waitcnt(0);           // the partial is complete before it is counted
+  float v[NRT][4];
+#pragma unroll
+  for (int r = 0; r < NRT; ++r) {
+    ctl_tile_vals(red + r * (8 * 16 * 17), crow, cc0, v[r]);
+    float* mine = a.qkv_part + (((size_t)(tile * np + part) * NRT + r) * 64 + lane) * 4;
+    st_coh_u64(mine, (uint64_t)__float_as_uint(v[r][0]) | ((uint64_t)__float_as_uint(v[r][1]) << 32));
+    st_coh_u64(mine + 2, (uint64_t)__float_as_uint(v[r][2]) | ((uint64_t)__float_as_uint(v[r][3]) << 32));
+  }
+  __builtin_amdgcn_s_waitcnt(0);           // the partials are complete before they are counted
   uint32_t old = 0;
   if (lane == 0) old = __hip_atomic_fetch_add(a.qkv_cnt + tile * 16, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   old = __shfl(old, 0);
   if (old != (uint32_t)(np - 1)) return;
-  float sum[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int p = 0; p < np; ++p) {
-    float u[4] = {v[0], v[1], v[2], v[3]};
-    if (p != part) {
-      const uint32_t* o = (const uint32_t*)(a.qkv_part + ((size_t)(tile * np + p) * 64 + lane) * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u[j] = __uint_as_float(ld_coh_u32(o + j));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sum[j] += u[j];
-  }
-  if (!crv) return;
   const int qd = a.Hq * a.d, kd = a.Hkv * a.d, n = tile * 16 + cc0;
-  uint16_t* dst;
-  if (n < qd) dst = a.q_next + (size_t)crow * qd + n;
-  else if (n < qd + kd) dst = a.kn + (size_t)(a.ctx + crow) * kd + (n - qd);
-  else dst = a.vn + (size_t)(a.ctx + crow) * kd + (n - qd - kd);
-  *(uint64_t*)dst = pack4_bf16(sum);
+#pragma unroll
+  for (int r = 0; r < NRT; ++r) {
+    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < np; ++p) {
+      float u[4] = {v[r][0], v[r][1], v[r][2], v[r][3]};
+      if (p != part) {
+        const uint32_t* o = (const uint32_t*)(a.qkv_part + (((size_t)(tile * np + p) * NRT + r) * 64 + lane) * 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) u[j] = __uint_as_float(ld_coh_u32(o + j));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum[j] += u[j];
+    }
+    const int row = 16 * r + crow;
+    if (row >= a.T) continue;
+    const int sq = row / a.Ts, tok = row - sq * a.Ts;
+    const size_t kvs = (size_t)sq * a.cap * kd;              // sequence sq's next-layer cache
+    uint16_t* dst;
+    if (n < qd) dst = a.q_next + (size_t)row * qd + n;
+    else if (n < qd + kd) dst = a.kn + kvs + (size_t)(a.ctx + tok) * kd + (n - qd);
+    else dst = a.vn + kvs + (size_t)(a.ctx + tok) * kd + (n - qd - kd);
+    *(uint64_t*)dst = pack4_bf16(sum);
+  }
 }
 
 // ------------------------------------------------------------------ kernel
@@ -2037,24 +2201,33 @@ __device__ __forceinline__ void qkv_split_epilogue(const KArgs& a, const float* 
 // of 128, pooled 2048, 256 experts top-8, NVFP4 experts with local intermediate 192, a
 // 16-token tree) with every shape a compile-time constant; SPEC 0 takes shapes at run time.
 // NS: the N-sharded expert layout (a separate instantiation, so that the ordinary layout's
-// code does not carry its registers).
-template <bool TS, int SPEC, bool NS>
+// code does not carry its registers).  NRT: 16-row tiles of the launch (1: one sequence of
+// T <= 16 tokens; 2: two sequences of 16), SPEC 1 the shard shape at either.
+template <bool TS, int SPEC, bool NS, int NRT>
 __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   KArgs a = a_in;
   if constexpr (SPEC == 1) {
     a.H = 4096; a.Hq = 8; a.Hkv = 1; a.d = 128; a.P = 2048; a.E = 256; a.topk = 8; a.I = 192;
-    a.fmt = 1; a.T = 16;
+    a.fmt = 1; a.T = 16 * NRT;
+  }
+  if constexpr (NRT == 1) {
+    a.B = 1;
+    a.Ts = a.T;
+  } else {
+    a.B = NRT;
+    a.Ts = 16;
+    a.T = 16 * NRT;
   }
   if constexpr (!NS) a.ns_R = 0;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ Route rt;
+  __shared__ RouteT<NRT> rt;
   __shared__ Tree tr;
   __shared__ int32_t dead_sh;
   __shared__ uint32_t epoch_sh;
-  __shared__ int32_t par_sh[16];
-  __shared__ int32_t xk_sh[16];     // GEMM1 input row scales (NVFP4 experts)
+  __shared__ int32_t par_sh[32];
+  __shared__ int32_t xk_sh[16 * NRT];   // GEMM1 input row scales (NVFP4 experts)
   __shared__ uint32_t outrow[68];
-  __shared__ uint32_t ytile[16 * 4];
+  __shared__ uint32_t ytile[16 * NRT * 4];
   const int tid = threadIdx.x;
   const bool cw = tid < kCompute;
   const int lane = tid & 63;
@@ -2064,9 +2237,10 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
   stamp<TS>(a.timestamps, 0);
 
-  // control lanes: row / columns of the 4 outputs they store in a dense tile epilogue
+  // control lanes: row (within a 16-row tile) / columns of the 4 outputs they store in a dense
+  // tile epilogue; row tile r covers rows 16 r .. 16 r + 15
   const int crow = lane >> 2, cc0 = (lane & 3) * 4;
-  const bool crv = crow < a.T;
+  auto crv = [&](int r) { return 16 * r + crow < a.T; };
 
   // weights of the o-proj tile, and (control wave) its residual, fetched at launch
   WFrag<MAXS_O> wo;
@@ -2105,8 +2279,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   const bool pool_lds = p_p && POOL_LDS_OFF + 16 * a.H * 2 <= LDS_BYTES;
   const bool pool_dma = pool_lds && (int)blockIdx.x < a.attn_items;
   const bool router_lds = router_room && p_r;
-  u32x2 res = {0, 0};
-  if (!cw && p_o && crv) res = *(const u32x2*)(a.h_in + (size_t)crow * a.H + t_o * 16 + cc0);
+  u32x2 res[NRT];
+#pragma unroll
+  for (int r = 0; r < NRT; ++r) {
+    res[r] = u32x2{0, 0};
+    if (!cw && p_o && crv(r)) res[r] = *(const u32x2*)(a.h_in + (size_t)(16 * r + crow) * a.H + t_o * 16 + cc0);
+  }
 
   // the control wave reads the tree and this workgroup's epoch, both loads in flight together
   // (wave 0 issues its attention loads meanwhile)
@@ -2132,14 +2310,15 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
   wg_sync();
   if (tid < 64) {
-    // lanes i < T: ancestor-or-self set by pointer jumping (4 rounds cover depth <= 15);
-    // depth = |ancestors| - 1
+    // lanes i < T (rows; sequence b's tree on lanes b Ts ..): ancestor-or-self set by pointer
+    // jumping (4 rounds cover depth <= 15); depth = |ancestors| - 1
     const int lane = tid;
+    const int sq = a.B == 1 ? 0 : lane / a.Ts, node = lane - sq * a.Ts;
     const int p = lane < a.T ? par_sh[lane] : -1;
-    const bool ok = lane >= a.T || (lane == 0 ? p == -1 : (p >= 0 && p < lane));
+    const bool ok = lane >= a.T || (node == 0 ? p == -1 : (p >= 0 && p < node));
     const bool bad = __ballot(!ok) != 0;
     uint32_t anc = lane < a.T ? 1u << lane : 0u;
-    int jump = (lane < a.T && lane > 0 && ok) ? p : -1;
+    int jump = (lane < a.T && node > 0 && ok) ? sq * a.Ts + p : -1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t aj = __shfl(anc, jump < 0 ? lane : jump);
@@ -2168,16 +2347,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   // the other copy to the sentinel for the next launch (plain stores: the next launch starts
   // after they are written back)
   {
-    char* cur = a.stage + (size_t)(epoch & 1u) * kStageBytes;
-    a.attn = (uint16_t*)(cur + kStageAttn);
-    a.h1 = (uint16_t*)(cur + kStageH1);
-    a.h_frag = (uint16_t*)(cur + kStageHf);
-    a.xp = (uint16_t*)(cur + kStageXp);
-    a.logits = (float*)(cur + kStageLogits);
-    a.act_q = (uint32_t*)(cur + kStageAct);
-    a.act_bf = (uint16_t*)(cur + kStageAct);
-    a.y = (uint16_t*)(cur + kStageY);
-    a.g2_part = (float*)(cur + kStagePart);
+    a.cur = a.stage + (size_t)(epoch & 1u) * kStageBytes;
     if (!cw) {
       u32x4* idle = (u32x4*)(a.stage + (size_t)((epoch & 1u) ^ 1u) * kStageBytes);
       constexpr uint32_t words = kStageBytes / 16;
@@ -2244,19 +2414,20 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     });
     // ---- 2 MERGE
     if (alive) {
-      const int units = a.Hkv * a.T * (a.Hq / a.Hkv);
-      const int G = a.Hq / a.Hkv, R = a.T * G;
+      const int G = a.Hq / a.Hkv, R = a.Ts * G;
+      const int units = a.B * a.Hkv * R;
       for (int u = blockIdx.x; u < units; u += nwg) {
         merge_unit(a, u, (float*)smem, outrow);
         wg_sync();
         if (!cw) {
-          const int g_kv = u / R, row = u % R, tok = row / G, head = g_kv * G + row % G;
+          const int sq = u / (a.Hkv * R), ul = u % (a.Hkv * R);
+          const int g_kv = ul / R, row = ul % R, tok = row / G, head = g_kv * G + row % G;
           if (lane < a.d / 4)
-            st_coh_u64(a.attn + frag_off(tok, head * a.d + lane * 4),
+            st_coh_u64(st_attn(a) + (size_t)sq * 16 * a.Hq * a.d + frag_off(tok, head * a.d + lane * 4),
                        (uint64_t)outrow[2 * lane] | ((uint64_t)outrow[2 * lane + 1] << 32));
           if (lane == 0 && a.attn_stats) {
-            a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 0] = __uint_as_float(outrow[64]);
-            a.attn_stats[((size_t)tok * a.Hq + head) * 2 + 1] = __uint_as_float(outrow[65]);
+            a.attn_stats[((size_t)(sq * a.Ts + tok) * a.Hq + head) * 2 + 0] = __uint_as_float(outrow[64]);
+            a.attn_stats[((size_t)(sq * a.Ts + tok) * a.Hq + head) * 2 + 1] = __uint_as_float(outrow[65]);
           }
         }
       }
@@ -2271,36 +2442,39 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (alive && cw) {
       if (p_o) wfrag_load(wo, a.w_o, a.Hq * a.d, t_o * 16);
       if (pool_dma) lds_tile_dma(a.w_pool, a.H, t_p * 16, smem + POOL_LDS_OFF, tid >> 6, kCompute / 64);
-      if ((int)blockIdx.x >= a.Hkv * a.T * (a.Hq / a.Hkv))
+      if ((int)blockIdx.x >= a.B * a.Hkv * a.Ts * (a.Hq / a.Hkv))
         for (int i = 0; i < kIdleSleepUs; ++i) __builtin_amdgcn_s_sleep(37);
     }
     stamp<TS>(a.timestamps, 5, 0);
     // ---- 3 OPROJ: h1 = bf16(h_in + attn Wo^T).  The control wave keeps its first tile's h1
     // values: the unpooler's tiles are the same (N = H, same order), h1 is its residual.
-    u32x2 res_u = {0, 0};
+    u32x2 res_u[NRT];
+#pragma unroll
+    for (int r = 0; r < NRT; ++r) res_u[r] = u32x2{0, 0};
     if (alive) {
-      dense_phase(a, wo, p_o, a.w_o, xsrc(a.attn, a.Hq * a.d, s, &dead_sh), a.Hq * a.d, a.H, 0, red2,
-                  [&](int n0, const float* red, int it) {
-        if (!crv) return;
+      dense_phase<NRT>(a, wo, p_o, a.w_o, xsrc(st_attn(a), a.Hq * a.d, s, &dead_sh), a.Hq * a.d, a.H, 0, red2,
+                       [&](int n0, const float* red, int it, int rr) {
+        if (!crv(rr)) return;
+        const int row = 16 * rr + crow;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        const u32x2 r = it == 0 ? res : *(const u32x2*)(a.h_in + (size_t)crow * a.H + n0 + cc0);
+        const u32x2 r = it == 0 ? res[rr] : *(const u32x2*)(a.h_in + (size_t)row * a.H + n0 + cc0);
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
         const uint64_t hv = pack4_bf16(v);
-        st_coh_u64(a.h1 + frag_off(crow, n0 + cc0), hv);
-        if (it == 0) res_u = u32x2{(uint32_t)hv, (uint32_t)(hv >> 32)};
+        st_coh_u64(st_h1(a) + (size_t)rr * 16 * a.H + frag_off(crow, n0 + cc0), hv);
+        if (it == 0) res_u[rr] = u32x2{(uint32_t)hv, (uint32_t)(hv >> 32)};
       });
     }
     if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
     alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive && dead_sh == 0;
     // ---- 4 POOL: xp = bf16(h1 Wp^T)
     if (alive) {
-      dense_phase(a, wp, false, a.w_pool, xplain(a.h1, s, &dead_sh), a.H, a.P, off_p, red2,
-                  [&](int n0, const float* red, int) {
-        if (!crv) return;
+      dense_phase<NRT>(a, wp, false, a.w_pool, xplain(st_h1(a), s, &dead_sh), a.H, a.P, off_p, red2,
+                       [&](int n0, const float* red, int, int rr) {
+        if (!crv(rr)) return;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        st_coh_u64(a.xp + frag_off(crow, n0 + cc0), pack4_bf16(v));
+        st_coh_u64(st_xp(a) + (size_t)rr * 16 * a.P + frag_off(crow, n0 + cc0), pack4_bf16(v));
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     // the router tile loads into registers (unless held in LDS) while the grid hands off
@@ -2308,18 +2482,19 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
                           p_p ? 0 : kIdleSleepUs) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
     if (alive) {
-      dense_phase(a, wr, p_r && !router_lds, a.w_router, xplain(a.xp, s, &dead_sh), a.P, a.E, off_r, red2,
-                  [&](int n0, const float* red, int) {
-        if (!crv) return;
+      dense_phase<NRT>(a, wr, p_r && !router_lds, a.w_router, xplain(st_xp(a), s, &dead_sh), a.P, a.E, off_r, red2,
+                       [&](int n0, const float* red, int, int rr) {
+        if (!crv(rr)) return;
+        const int row = 16 * rr + crow;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         if (a.bias) {
-          const f32x4 b = *(const f32x4*)(a.bias + (size_t)crow * a.E + n0 + cc0);
+          const f32x4 b = *(const f32x4*)(a.bias + (size_t)row * a.E + n0 + cc0);
           v[0] += b[0]; v[1] += b[1]; v[2] += b[2]; v[3] += b[3];
         }
-        st_coh_u128(a.logits + (size_t)crow * a.E + n0 + cc0,
+        st_coh_u128(st_logits(a) + (size_t)row * a.E + n0 + cc0,
                     u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
-        if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)crow * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
+        if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)row * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
       }, router_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     // No grid hand-off after the router: every workgroup reads the logits as they arrive.
@@ -2328,10 +2503,18 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     wg_sync();
     stamp<TS>(a.timestamps, 10);
     if (alive) {
-      u32x4 xpv[8];
-      if (cw) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
-      wg_sync();                                // every wave's piece maxima are in LDS
-      xs_build<TS>(a, xpv, (uint16_t*)smem, a.P + XS_STRIDE_PAD, (const uint32_t*)(smem + G1_XS_BYTES), xk_sh);
+      if constexpr (NRT == 1) {
+        u32x4 xpv[8];
+        if (cw) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
+        wg_sync();                              // every wave's piece maxima are in LDS
+        xs_build<TS>(a, xpv, (uint16_t*)smem, a.P + XS_STRIDE_PAD, (const uint32_t*)(smem + G1_XS_BYTES), xk_sh);
+      } else {
+        // two sequences: all 32 rows, or (two pieces per unit) the first K half of them
+        xs_rowscale2<TS>(a, (uint32_t*)(smem + G1_XS_BYTES), xk_sh);
+        const int cols = g1_pieces(a.P) == 2 ? g1_hsteps(a.P) * 128 : a.P;
+        xs_fill2(a, (uint16_t*)smem, cols + XS_STRIDE_PAD, 0, cols, xk_sh);
+        wg_sync();
+      }
     }
     stamp<TS>(a.timestamps, 11);
     // ---- 6 ROUTE + GEMM1
@@ -2370,21 +2553,22 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- 8 UNPOOL: h_out = bf16(h1 + y Wu^T)
     if (alive) {
       // (N-sharded layout: the gathered y, the other ranks' columns read as they arrive)
-      dense_phase(a, wu, p_u && !wu_lds, a.w_unpool,
-                  a.ns_R ? xsrc(a.y_recv, a.P, s, &dead_sh) : xplain(a.y, s, &dead_sh), a.P, a.H, 0, red2,
-                  [&](int n0, const float* red, int it) {
-        if (!crv) return;
+      dense_phase<NRT>(a, wu, p_u && !wu_lds, a.w_unpool,
+                       a.ns_R ? xsrc(a.y_recv, a.P, s, &dead_sh) : xplain(st_y(a), s, &dead_sh), a.P, a.H, 0, red2,
+                       [&](int n0, const float* red, int it, int rr) {
+        if (!crv(rr)) return;
+        const int row = 16 * rr + crow;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
-        u32x2 r = res_u;                    // this workgroup's own o-proj output (first tile)
+        u32x2 r = res_u[rr];                // this workgroup's own o-proj output (first tile)
         if (it > 0) {
-          const uint64_t w = poll_u64(s, &dead_sh, a.h1 + frag_off(crow, n0 + cc0));
+          const uint64_t w = poll_u64(s, &dead_sh, st_h1(a) + (size_t)rr * 16 * a.H + frag_off(crow, n0 + cc0));
           r = u32x2{(uint32_t)w, (uint32_t)(w >> 32)};
         }
         v[0] += bf2f(r[0] & 0xFFFF); v[1] += bf2f(r[0] >> 16); v[2] += bf2f(r[1] & 0xFFFF); v[3] += bf2f(r[1] >> 16);
         const uint64_t hv = pack4_bf16(v);
-        st_coh_u64(a.h_out + (size_t)crow * a.H + n0 + cc0, hv);     // the step's output, row-major
-        st_coh_u64(a.h_frag + frag_off(crow, n0 + cc0), hv);          // the qkv phase's x
+        st_coh_u64(a.h_out + (size_t)row * a.H + n0 + cc0, hv);                        // the output, row-major
+        st_coh_u64(st_h_frag(a) + (size_t)rr * 16 * a.H + frag_off(crow, n0 + cc0), hv);  // the qkv phase's x
       }, wu_lds ? smem + WU_LDS_OFF : nullptr);
     }
     // No grid hand-off after the unpooler: the qkv projection reads h_out as it arrives; its
@@ -2400,20 +2584,28 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     // ---- QKV + KV write
     if (alive) {
       const int qd = a.Hq * a.d, kd = a.Hkv * a.d;
-      const XSrc hx = xsrc(a.h_frag, a.H, s, &dead_sh);
+      const XSrc hx = xsrc(st_h_frag(a), a.H, s, &dead_sh);
       if (q_split) {
-        if (cw && p_qs) red_store(red2, wfrag_mma(wqs, hx, q_s0, a.T, q_ns * 32));
+        // every row tile's part with the same weight registers, each into its own buffer
+#pragma unroll
+        for (int r = 0; r < NRT; ++r)
+          if (cw && p_qs)
+            red_store(red2 + r * (8 * 16 * 17), wfrag_mma(wqs, NRT == 1 ? hx : xtile(hx, r, a.H), q_s0,
+                                                          min(16, a.T - 16 * r), q_ns * 32));
         wg_sync();
-        if (!cw && p_qs) qkv_split_epilogue(a, red2, q_tile, q_part, qs.np, crow, cc0, crv);
-      } else if (has_qkv) dense_phase(a, wq, p_q, a.w_qkv, hx, a.H, qkv_n, off_q, red2, [&](int n0, const float* red, int) {
-        if (!crv) return;
+        if (!cw && p_qs) qkv_split_epilogue<NRT>(a, red2, q_tile, q_part, qs.np, crow, cc0);
+      } else if (has_qkv) dense_phase<NRT>(a, wq, p_q, a.w_qkv, hx, a.H, qkv_n, off_q, red2,
+                                           [&](int n0, const float* red, int, int rr) {
+        if (!crv(rr)) return;
+        const int row = 16 * rr + crow, sq = row / a.Ts, tok = row - sq * a.Ts;
         float v[4];
         ctl_tile_vals(red, crow, cc0, v);
         const int n = n0 + cc0;
+        const size_t kvs = (size_t)sq * a.cap * kd;           // sequence sq's next-layer cache
         uint16_t* dst;
-        if (n < qd) dst = a.q_next + (size_t)crow * qd + n;
-        else if (n < qd + kd) dst = a.kn + (size_t)(a.ctx + crow) * kd + (n - qd);
-        else dst = a.vn + (size_t)(a.ctx + crow) * kd + (n - qd - kd);
+        if (n < qd) dst = a.q_next + (size_t)row * qd + n;
+        else if (n < qd + kd) dst = a.kn + kvs + (size_t)(a.ctx + tok) * kd + (n - qd);
+        else dst = a.vn + kvs + (size_t)(a.ctx + tok) * kd + (n - qd - kd);
         *(uint64_t*)dst = pack4_bf16(v);
       });
       if (blockIdx.x == 0) {
@@ -2434,45 +2626,52 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
 }
 
-template __global__ void layer_kernel<false, 0, false>(KArgs);
-template __global__ void layer_kernel<true, 0, false>(KArgs);
-template __global__ void layer_kernel<false, 1, false>(KArgs);
-template __global__ void layer_kernel<true, 1, false>(KArgs);
-template __global__ void layer_kernel<false, 0, true>(KArgs);
-template __global__ void layer_kernel<true, 0, true>(KArgs);
-template __global__ void layer_kernel<false, 1, true>(KArgs);
-template __global__ void layer_kernel<true, 1, true>(KArgs);
+template __global__ void layer_kernel<false, 0, false, 1>(KArgs);
+template __global__ void layer_kernel<true, 0, false, 1>(KArgs);
+template __global__ void layer_kernel<false, 1, false, 1>(KArgs);
+template __global__ void layer_kernel<true, 1, false, 1>(KArgs);
+template __global__ void layer_kernel<false, 0, true, 1>(KArgs);
+template __global__ void layer_kernel<true, 0, true, 1>(KArgs);
+template __global__ void layer_kernel<false, 1, true, 1>(KArgs);
+template __global__ void layer_kernel<true, 1, true, 1>(KArgs);
+template __global__ void layer_kernel<false, 0, false, 2>(KArgs);
+template __global__ void layer_kernel<true, 0, false, 2>(KArgs);
+template __global__ void layer_kernel<false, 1, false, 2>(KArgs);
+template __global__ void layer_kernel<true, 1, false, 2>(KArgs);
 
 int layer_lds_bytes() { return LDS_BYTES; }
 
 static bool is_spec1(const KArgs& a) {
   return a.H == 4096 && a.Hq == 8 && a.Hkv == 1 && a.d == 128 && a.P == 2048 && a.E == 256 && a.topk == 8 &&
-         a.I == 192 && a.fmt == 1 && a.T == 16 && a.n_wg >= 240;
+         a.I == 192 && a.fmt == 1 && a.T == 16 * a.B && a.n_wg >= 240;
 }
 
-template <bool NS>
-void launch_ns(const KArgs& a, int lds_bytes, hipStream_t stream) {
+template <bool NS, int NRT>
+void launch_v(const KArgs& a, int lds_bytes, hipStream_t stream) {
   const dim3 g(a.n_wg), b(kThreads);
   if (is_spec1(a)) {
-    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 1, NS>), g, b, lds_bytes, stream, a);
-    else hipLaunchKernelGGL((layer_kernel<false, 1, NS>), g, b, lds_bytes, stream, a);
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 1, NS, NRT>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 1, NS, NRT>), g, b, lds_bytes, stream, a);
   } else {
-    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 0, NS>), g, b, lds_bytes, stream, a);
-    else hipLaunchKernelGGL((layer_kernel<false, 0, NS>), g, b, lds_bytes, stream, a);
+    if (a.timestamps) hipLaunchKernelGGL((layer_kernel<true, 0, NS, NRT>), g, b, lds_bytes, stream, a);
+    else hipLaunchKernelGGL((layer_kernel<false, 0, NS, NRT>), g, b, lds_bytes, stream, a);
   }
 }
 
 int launch_layer(const KArgs& a, int lds_bytes, hipStream_t stream) {
-  if (a.ns_R) launch_ns<true>(a, lds_bytes, stream);
-  else launch_ns<false>(a, lds_bytes, stream);
+  if (a.B == 2) launch_v<false, 2>(a, lds_bytes, stream);     // (the host admits no N-sharded batch)
+  else if (a.ns_R) launch_v<true, 1>(a, lds_bytes, stream);
+  else launch_v<false, 1>(a, lds_bytes, stream);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
 int set_layer_kernel_attrs(int lds_bytes) {
-  const void* fns[] = {(const void*)layer_kernel<false, 0, false>, (const void*)layer_kernel<true, 0, false>,
-                       (const void*)layer_kernel<false, 1, false>, (const void*)layer_kernel<true, 1, false>,
-                       (const void*)layer_kernel<false, 0, true>, (const void*)layer_kernel<true, 0, true>,
-                       (const void*)layer_kernel<false, 1, true>, (const void*)layer_kernel<true, 1, true>};
+  const void* fns[] = {(const void*)layer_kernel<false, 0, false, 1>, (const void*)layer_kernel<true, 0, false, 1>,
+                       (const void*)layer_kernel<false, 1, false, 1>, (const void*)layer_kernel<true, 1, false, 1>,
+                       (const void*)layer_kernel<false, 0, true, 1>, (const void*)layer_kernel<true, 0, true, 1>,
+                       (const void*)layer_kernel<false, 1, true, 1>, (const void*)layer_kernel<true, 1, true, 1>,
+                       (const void*)layer_kernel<false, 0, false, 2>, (const void*)layer_kernel<true, 0, false, 2>,
+                       (const void*)layer_kernel<false, 1, false, 2>, (const void*)layer_kernel<true, 1, false, 2>};
   for (const void* f : fns)
     if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes) != hipSuccess) return -5;
   return 0;

@@ -111,6 +111,7 @@ class DeviceStep:
     workspace: torch.Tensor
     layout: abi.mk_workspace_layout
     timestamps: torch.Tensor | None = None
+    batch: int = 1                          # sequences of T tokens (rows: batch * T)
     prefetch: torch.Tensor | None = None
     n_prefetch: int = 0
     prefetch_next: torch.Tensor | None = None
@@ -123,7 +124,7 @@ class DeviceStep:
                               p(self.topk_idx), p(self.topk_gate), p(self.logits), p(self.stats), p(self.hist),
                               p(self.prefetch), self.n_prefetch, p(self.prefetch_next), self.n_prefetch_next,
                               p(self.bias), p(self.workspace),
-                              self.workspace.numel(), p(self.timestamps), spin_limit, skip_wg)
+                              self.workspace.numel(), p(self.timestamps), spin_limit, skip_wg, self.batch)
 
     def ws_u16(self, off: int, n: int) -> np.ndarray:
         return self.workspace[off:off + 2 * n].cpu().numpy().view(np.uint16)
@@ -153,6 +154,33 @@ def make_step(inp, device="cuda", timestamps: bool = False, stream=None) -> Devi
     if timestamps:
         st.timestamps = torch.zeros((lay.n_wg, abi.MK_TS_EVENTS), dtype=torch.int64, device=device)
     return st
+
+
+def make_step_batch(inps, device="cuda") -> DeviceStep:
+    """Two sequences in one launch: their trees, queries, residuals, caches and outputs stacked
+    (sequence b on rows 16 b .., its caches at b * capacity rows).  The sequences must share the
+    layer's weights and shape (T = 16, same ctx)."""
+    sh = inps[0].shape
+    B = len(inps)
+    assert B == 2 and sh.T == 16 and all(i.shape == sh for i in inps)
+    cfg = layer_cfg(sh)
+    T, E, k = sh.T, sh.n_experts, sh.top_k
+    R = B * T
+    f32 = dict(dtype=torch.float32, device=device)
+    i32 = dict(dtype=torch.int32, device=device)
+    lay = abi.mk_workspace_query(cfg, T)
+    ws = torch.empty(lay.total, dtype=torch.uint8, device=device)
+    abi.mk_workspace_init(ws, lay.total, None)
+    cat = lambda name: np.concatenate([getattr(i, name) for i in inps], axis=0)
+    bias = None if inps[0].router_bias is None else torch.from_numpy(cat("router_bias")).to(device)
+    return DeviceStep(cfg, T, sh.ctx, torch.from_numpy(cat("parent").astype(np.int32)).to(device),
+                      dev_u16(cat("q_in"), device), dev_u16(cat("h_in"), device), dev_u16(cat("k_cache"), device),
+                      dev_u16(cat("v_cache"), device), dev_u16(cat("k_cache_next"), device),
+                      dev_u16(cat("v_cache_next"), device),
+                      torch.zeros((R, sh.hidden), dtype=torch.int16, device=device),
+                      torch.zeros((R, sh.n_q_heads * sh.head_dim), dtype=torch.int16, device=device),
+                      torch.full((R, k), -1, **i32), torch.zeros((R, k), **f32), torch.zeros((R, E), **f32),
+                      torch.zeros((R, sh.n_q_heads, 2), **f32), torch.zeros(E, **i32), bias, ws, lay, None, B)
 
 
 def run_step(dw: DeviceWeights, st: DeviceStep, stream=None, spin_limit: int = 0, skip_wg: int = -1) -> int:
@@ -203,7 +231,8 @@ def stage_offset(workspace: torch.Tensor, layout, off: int) -> int:
 
 
 def outputs(st: DeviceStep) -> dict:
-    """Copy a step's outputs and stage hand-off buffers (those of its last launch) to the host."""
+    """Copy a step's outputs and stage hand-off buffers (those of its last launch) to the host
+    (stage buffers: one 16-row fragment tile per sequence, rows stacked)."""
     torch.cuda.synchronize()
     sh_T = st.T
     lay = st.layout
@@ -213,6 +242,17 @@ def outputs(st: DeviceStep) -> dict:
         attn, h1, xp, y = (stage_offset(st.workspace, lay, o) for o in (lay.attn, lay.h1, lay.xp, lay.y))
         status = lay.status
     L = _L
+
+    def tiles(off, K):
+        return np.concatenate([untile_frag(st.ws_u16(off + 2 * b * 16 * K, 16 * K), sh_T, K) for b in range(st.batch)])
+    if st.batch > 1:
+        return dict(
+            h_out=host_u16(st.h_out), q_next=host_u16(st.q_next),
+            k_cache_next=host_u16(st.k_next), v_cache_next=host_u16(st.v_next),
+            idx=st.topk_idx.cpu().numpy(), gate=st.topk_gate.cpu().numpy(), logits=st.logits.cpu().numpy(),
+            stats=st.stats.cpu().numpy(), hist=st.hist.cpu().numpy(),
+            attn=tiles(L.attn, c.n_q_heads * c.head_dim), h1=tiles(L.h1, c.hidden), xp=tiles(L.xp, c.pooled),
+            y=tiles(L.y, c.pooled), status=abi.mk_read_status(st.workspace))
     return dict(
         h_out=host_u16(st.h_out), q_next=host_u16(st.q_next),
         k_cache_next=host_u16(st.k_next), v_cache_next=host_u16(st.v_next),

@@ -49,7 +49,7 @@ def _io(T=16, ctx=8192, ptr=GOOD, **kw):
     io = mk.mk_step_io()
     for f, _ in mk.mk_step_io._fields_:
         if f not in ("T", "ctx_len", "n_prefetch", "n_prefetch_next", "workspace_bytes", "spin_limit",
-                     "debug_skip_signal_wg"):
+                     "debug_skip_signal_wg", "batch"):
             setattr(io, f, ptr)
     io.T, io.ctx_len, io.workspace_bytes, io.debug_skip_signal_wg = T, ctx, 1 << 30, -1
     io.prefetch_experts = None
@@ -70,6 +70,18 @@ def test_layer_step_rejects_null_inputs(field):
                                 dict(n_q_heads=16)])
 def test_layer_step_rejects_bad_shapes(kw):
     assert mk.mk_layer_step(_cfg(**kw), _weights(), _io(), check=False) == mk.MK_ESHAPE
+
+
+def test_batch_is_validated_on_host():
+    ok = dict(check=False)
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(batch=3), **ok) == mk.MK_ESHAPE
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(batch=-1), **ok) == mk.MK_ESHAPE
+    assert mk.mk_layer_step(_cfg(), _weights(), _io(batch=2, T=9), **ok) == mk.MK_ESHAPE       # trees of 16
+    assert mk.mk_layer_step(_cfg(expert_fmt=mk.MK_W_BF16), _weights(), _io(batch=2), **ok) == mk.MK_ESHAPE
+    assert mk.mk_layer_step(_cfg(expert_inter=256), _weights(), _io(batch=2), **ok) == mk.MK_ESHAPE
+    assert mk.mk_layer_step(_cfg(expert_inter=96), _weights(), _io(batch=2), **ok) == mk.MK_ESHAPE
+    ns = mk.mk_nshard(3, 8, GOOD, GOOD)
+    assert mk.mk_layer_step_nshard(_cfg(), _weights(), _io(batch=2), ns, check=False) == mk.MK_ESHAPE
 
 
 def test_layer_step_rejects_bad_T_capacity_alignment_and_enum():
