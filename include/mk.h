@@ -181,10 +181,10 @@ int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *
  * loops, harnesses that forbid allocation): mk_layer_step with no caller workspace.  The
  * launch uses a static device array of the library, MK_NOALLOC_SCRATCH_BYTES on every GPU it
  * runs on, held until the process ends; io->workspace and io->workspace_bytes are ignored.
- * Same arguments, checks, kernel and results as mk_layer_step; a configuration whose
- * mk_workspace_bytes() exceeds the array is rejected with MK_ESCRATCH (at the shard shape that
- * is a KV capacity above about 90K rows), before anything is enqueued.  The first call on a
- * device also enqueues one fill kernel that zeroes the array.  No call allocates or frees
+ * Same arguments, checks, kernel and results as mk_layer_step; a launch whose workspace
+ * exceeds the array is rejected with MK_ESCRATCH before anything is enqueued (at the shard
+ * shape: a global-attention context above about 83K tokens, or batch two).  The first call on
+ * a device also enqueues one fill kernel that zeroes the array.  No call allocates or frees
  * memory.  Every call on a GPU shares that GPU's array, which keeps the last call's contents:
  * calls that overlap on one GPU (concurrent streams, host threads) race and must not be
  * issued.  mk_read_status(NULL, stream) returns the in-kernel status of the last call on the
