@@ -184,8 +184,8 @@ int mk_layer_step(const mk_layer_cfg *cfg /* [host] */, const mk_layer_weights *
  * Same arguments, checks, kernel and results as mk_layer_step; a launch whose workspace
  * exceeds the array is rejected with MK_ESCRATCH before anything is enqueued (at the shard
  * shape: a global-attention context above about 83K tokens, or batch two).  The first call on
- * a device also enqueues one fill kernel that zeroes the array.  No call allocates or frees
- * memory.  Every call on a GPU shares that GPU's array, which keeps the last call's contents:
+ * a device also enqueues the fill kernels of mk_workspace_init on the array (counters to zero,
+ * the rest to the all-ones sentinel).  No call allocates or frees memory.  Every call on a GPU shares that GPU's array, which keeps the last call's contents:
  * calls that overlap on one GPU (concurrent streams, host threads) race and must not be
  * issued.  mk_read_status(NULL, stream) returns the in-kernel status of the last call on the
  * current device. */

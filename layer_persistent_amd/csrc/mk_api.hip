@@ -248,8 +248,9 @@ void bind_workspace(mk::KArgs* ap, const Layout& L, char* ws) {
 // The workspace of the allocation-free entry point: one file-scope device array per GPU that
 // the library runs on, held until the process ends.  Its device address is taken once per
 // device with hipGetSymbolAddress (the array's name is only a host-side stand-in) and the
-// array is zeroed then by a fill kernel (the epoch slots, flags and status word must start at
-// zero); every later call on that device reuses it as it was left.
+// array is initialised then as mk_workspace_init does (the status word, epoch slots, flags and
+// counters to zero, the stage buffers to the sentinel); every later call on that device reuses
+// it as it was left.
 char* g_scratch[kMaxDevices];   // per device: the device address of `scratch`, once set up
 
 int scratch_ptr(hipStream_t stream, int n_wg, char** out) {

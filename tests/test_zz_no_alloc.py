@@ -1,6 +1,7 @@
 """The allocation-free entry point (mk_layer_step_noalloc): its static scratch against the
 caller-workspace entry point (mk_layer_step), through the C ABI, on two calls in a row -- the
-second on a smaller layer -- and its rejection of a configuration too large for the scratch."""
+second on a smaller layer --, with two sequences per launch, and its rejection of a
+configuration too large for the scratch."""
 from __future__ import annotations
 
 import numpy as np
@@ -68,3 +69,32 @@ def test_noalloc_rejects_a_configuration_larger_than_its_scratch():
     io.workspace, io.workspace_bytes = None, 0
     assert mk.mk_layer_step_noalloc(cfg, dw.struct(), io, check=False) == mk.MK_ESCRATCH
     log(f"  a {need >> 20} MiB workspace is rejected: {mk.mk_strerror(mk.MK_ESCRATCH)}")
+
+
+def test_noalloc_batch_two():
+    """Two sequences per launch: bit-identical to mk_layer_step's batched launch at a small shape;
+    at the shard shape the batched workspace exceeds the scratch and is rejected."""
+    from test_gpu_batch import _two_sequences
+    from test_gpu_parity import SMALL_I128
+    seqs = _two_sequences(SMALL_I128, 124)
+    dw = dt.upload_weights(seqs[0])
+    ref_st = dt.make_step_batch(seqs)
+    dt.run_step(dw, ref_st)
+    ref = dt.outputs(ref_st)
+    assert ref["status"] == mk.MK_OK
+    st = dt.make_step_batch(seqs)
+    io = st.struct()
+    io.workspace, io.workspace_bytes = None, 0
+    assert mk.mk_layer_step_noalloc(st.cfg, dw.struct(), io) == mk.MK_OK
+    got = dt.outputs(st)
+    assert mk.mk_read_status(None) == mk.MK_OK
+    for key in ("h_out", "q_next", "k_cache_next", "v_cache_next", "idx", "gate", "logits", "stats"):
+        assert np.array_equal(ref[key], got[key]), key
+    log("  two sequences: outputs bit-identical to mk_layer_step")
+    big = _two_sequences(synth.CFG2, 125)
+    dwb = dt.upload_weights(big[0])
+    stb = dt.make_step_batch(big)
+    iob = stb.struct()
+    iob.workspace, iob.workspace_bytes = None, 0
+    assert mk.mk_layer_step_noalloc(stb.cfg, dwb.struct(), iob, check=False) == mk.MK_ESCRATCH
+    log("  two sequences at the shard shape: rejected with MK_ESCRATCH")
