@@ -5,36 +5,39 @@
 // "Muse Spark Open" megakernel (orcarouter.ai write-up, "where the kernel boundary sits").
 // The grid is one workgroup per CU (the dynamic LDS request keeps a second one off any CU);
 // the workgroups stay resident for the whole layer and hand work between phases through
-// device-side flags, the role the pages give to device-side counters (alphasignal.ai, "A
-// 12-warp pipeline takes over scheduling").
+// device-side flags or through the data itself, the role the pages give to device-side
+// counters (alphasignal.ai, "A 12-warp pipeline takes over scheduling").
 //
 // Workgroup = 9 waves.  Waves 0..7 compute (MFMA, attention, routing, experts).  Wave 8 is
 // the control wave: it stores each dense phase's output tile, signals this workgroup's flag
-// and polls everyone else's.  Because compute waves never wait for their own global stores
-// at a hand-off, the weight loads they issue for a later phase stay in flight across the
-// grid-wide wait -- the pages' "weights do not depend on the previous output, so fetch the
+// and polls everyone else's at a grid hand-off.  Because compute waves never wait for their
+// own global stores at a hand-off, the weight loads they issue for a later phase stay in
+// flight across the grid-wide wait -- the pages' "weights do not depend on the previous output, so fetch the
 // next operation's weights while the current one runs" (alphasignal.ai, "Four mechanisms
 // keep work moving"), with the register file as the staging buffer.
 //
-// Phases (each ends in a grid-wide hand-off):
-//   1 ATTN   tree-masked GQA attention over KV chunks -> per-chunk partial (m, l, o)
-//   2 MERGE  merge partials per (token, head) -> attn (bf16), stats (m, l)
-//   3 OPROJ  h1 = bf16(h_in + attn Wo^T)
-//   4 POOL   xp = bf16(h1 Wp^T)
-//   5 ROUTER logits = xp Wr^T (+ bias), fp32
+// Phases (G: a grid-wide hand-off follows; D: the next phase reads the output as it arrives):
+//   1 ATTN   tree-masked GQA attention over KV chunks -> per-chunk partial (m, l, o)      G
+//   2 MERGE  merge partials per (token, head) -> attn (bf16), stats (m, l)              D
+//   3 OPROJ  h1 = bf16(h_in + attn Wo^T)                                                 G
+//   4 POOL   xp = bf16(h1 Wp^T)                                                          G
+//   5 ROUTER logits = xp Wr^T (+ bias), fp32                                             D
 //   6 GEMM1  every workgroup: top-k, gates and dispatch from the logits (identical everywhere);
 //            then (expert, 16-column block) tasks: u = xp W1^T ts1, a = silu(u_gate) u_up,
-//            NVFP4 requantisation of a (bf16 for bf16 experts)
+//            NVFP4 requantisation of a (bf16 for bf16 experts)                           D
 //   7 GEMM2  per 8-column slice of P: every active expert's down projection, then the combine
-//            y = bf16(sum over the token's slots, in slot order, of gate * out)
-//   8 UNPOOL h_out = bf16(h1 + y Wu^T)
+//            y = bf16(sum over the token's slots, in slot order, of gate * out)          G
+//   8 UNPOOL h_out = bf16(h1 + y Wu^T)                                                   D
 //     QKV    [q; k; v] = h_out Wqkv^T -> q_next, KV rows of the next layer (K split over up to
 //            4 workgroups per tile; the last part to arrive adds the partials)
 //
-// Cross-workgroup hand-off: data is written with device-coherent (write-through) stores; the
+// Cross-workgroup hand-off, G: data is written with device-coherent (write-through) stores; the
 // writer waits for them, then stores its per-phase flag; readers poll all flags with coherent
-// loads and then read the data with ordinary loads.  Each hand-off buffer is written once per
-// launch before any workgroup of the launch first reads it, so no cache can hold a stale copy.
+// loads and then read the data with ordinary loads.  D: the stage buffer holds all ones until
+// written (no written 8-byte word ever does), and readers take 16-byte pieces with
+// device-coherent loads as they arrive (arrived16).  Large broadcasts that every workgroup
+// reads in full go by G, small ones by D.  Each hand-off buffer is written once per launch
+// before any workgroup of the launch first reads it, so no cache can hold a stale copy.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,7 +52,7 @@ constexpr int kCompute = 512;
 constexpr int kCtl = 512;          // first thread of the control wave
 // The pooler (P/16 tiles) and the router (E/16 tiles) leave most workgroups without work; those
 // sleep this long before polling (measured: the pooler's work then ends ~0.6 us sooner, and the
-// layer ~0.9 us; longer sleeps, or sleeps in the attention and merge hand-offs, gained nothing).
+// layer ~0.9 us; longer sleeps, or sleeps in the attention hand-off too, gained nothing).
 constexpr int kIdleSleepUs = 1;
 // Polls of stage data that has not arrived are repeated back to back, or after s_sleep
 // MK_POLL_SLEEP (64-clock units)
@@ -1585,8 +1588,8 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const RT& rt, char* 
 // 2U+1, and the off-diagonal blocks are discarded.  Wave w takes units w, w+8, ...  Lane
 // (nl, grp) holds weight row c0 + nl % 8 of its column's expert for the quarter k in
 // [grp I/4, (grp+1) I/4) of the reduction: I/8 bytes of codes and I/64 E4M3 block scales,
-// loaded straight into registers (a wave's first G2_UNITS units while the grid waits for
-// GEMM1).  The intermediate is read in the same permuted k order, which MFMA allows.
+// loaded straight into registers (a wave's first G2_UNITS units as soon as its workgroup's
+// GEMM1 work ends).  The intermediate is read in the same permuted k order, which MFMA allows.
 // Requires I % 64 == 0 and I >= 128.
 constexpr int G2_UNITS = 4;   // units per register batch
 constexpr int G2_MAXB = 4;    // I/64 <= 4
@@ -1663,8 +1666,8 @@ __device__ __forceinline__ void g2_unit(const KArgs& a, const RT& rt, const G2W&
   }
 }
 
-// Called by all threads.  `w0` holds batch 0 of this workgroup's first slice, loaded during
-// the hand-off after GEMM1.
+// Called by all threads.  `w0` holds batch 0 of this workgroup's first slice, requested as
+// soon as this workgroup's GEMM1 work ended.
 template <bool TS, class RT>
 __device__ __forceinline__ void gemm2_fp4(const KArgs& a, const RT& rt, char* smem, uint32_t* ytile, G2W& w0,
                                           const Sync& sy, int32_t* dead_sh) {
