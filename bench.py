@@ -718,6 +718,9 @@ def main():
             phases[n + "_handoff_us"] = round(float((tsv[:, 2 * p + 1].max() - tsv[:, 2 * p].max()) / 100.0), 2)
         starts = (tsv[:, 0] - t0) / 100.0
         phases["wg_start_spread"] = round(float(starts.max()), 2)
+        # first workgroup start to last workgroup end of the timestamped launch, next to the
+        # per-launch time from HIP events (the rest is dispatch and end-of-kernel work)
+        phases["launch_span_us"] = round(float((tsv[:, 19].max() - t0) / 100.0), 2)
         d = lambda e1, e0, m: round(float(((tsv[m, e1] - tsv[m, e0]) / 100.0).max()), 2)
         items = tsv[:, 37] > 0
         if items.any():
