@@ -172,7 +172,8 @@ struct Sync {
 // first poll of a workgroup that had no work in a phase where the others work for ~2 us: its polls
 // of the flags would only add memory traffic while they work.  Returns false when the wait
 // expired or the launch was aborted (this launch's error code in the status word).
-__device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead, int idle_us = 0) {
+__device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead, int idle_us = 0,
+                                                bool wait = true) {
   const int lane = threadIdx.x & 63;
   const int n = gridDim.x;
   __builtin_amdgcn_s_waitcnt(0);           // this wave's hand-off stores are complete
@@ -180,6 +181,7 @@ __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool d
   const uint32_t target = s.base + (uint32_t)phase;
   if (lane == 0 && (int)blockIdx.x != s.skip_wg) st_coh_u32(s.flags + blockIdx.x * 16, target);
   if (dead) return false;
+  if (!wait) return true;
   for (int i = 0; i < idle_us; ++i) __builtin_amdgcn_s_sleep(37);   // 37 x 64 clocks, ~1 us each
   const uint32_t* f = s.flags + lane * 16;
   auto poll = [&]() -> u32x4 {
@@ -2100,7 +2102,7 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
 // compute-wave global store of the phase must be complete before the call.
 template <bool TS, class PfF>
 __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int phase, int32_t* dead_sh, PfF pf,
-                                          int idle_us = 0) {
+                                          int idle_us = 0, bool wait = true) {
   wg_sync();
   stamp<TS>(a.timestamps, 2 * phase);
   if (threadIdx.x >= kCompute) {
@@ -2109,7 +2111,7 @@ __device__ __forceinline__ bool phase_end(const KArgs& a, const Sync& s, int pha
       __builtin_amdgcn_s_waitcnt(0);
       stamp<TS>(a.timestamps, 53 + phase);
     }
-    const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0, idle_us);
+    const bool ok = ctl_signal_wait(s, phase, *dead_sh != 0, idle_us, wait);
     if (!ok && threadIdx.x == kCtl) *dead_sh = 1;
     stamp<TS>(a.timestamps, 20 + phase);
   } else {
@@ -2412,9 +2414,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (cw && (int)blockIdx.x >= a.attn_items && a.n_prefetch > 0 && nwg > a.attn_items)
       touched ^= expert_touch(a, blockIdx.x - a.attn_items, nwg - a.attn_items);
     if (cw) __builtin_amdgcn_s_waitcnt(0);   // partial stores complete
+    // only the workgroups with a merge unit read the attention partials: the others raise their
+    // flag and go on (the o-proj reads the merged rows as they arrive)
+    const bool merge_wg = (int)blockIdx.x < a.B * a.Hkv * a.Ts * (a.Hq / a.Hkv);
     alive = phase_end<TS>(a, s, 1, &dead_sh, [&] {
       if (p_p && !pool_lds) touched ^= touch_tile<2>(a.w_pool, a.H, t_p * 16);
-    });
+    }, 0, merge_wg);
     // ---- 2 MERGE
     if (alive) {
       const int G = a.Hq / a.Hkv, R = a.Ts * G;
@@ -2469,7 +2474,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       });
     }
     if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
-    alive = phase_end<TS>(a, s, 3, &dead_sh, nop) && alive && dead_sh == 0;
+    // only the pooler's workgroups read h1 now; the others raise their flag and go on to the
+    // pooler's hand-off
+    alive = phase_end<TS>(a, s, 3, &dead_sh, nop, 0, p_p) && alive && dead_sh == 0;
     // ---- 4 POOL: xp = bf16(h1 Wp^T)
     if (alive) {
       dense_phase<NRT>(a, wp, false, a.w_pool, xplain(st_h1(a), s, &dead_sh), a.H, a.P, off_p, red2,
