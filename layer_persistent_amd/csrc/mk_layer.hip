@@ -170,8 +170,11 @@ struct Sync {
 // no sleep between them (sleeping after a few polls measured 0.35 us slower per layer), so that
 // a flag landing is seen about half a round trip later.  `idle_us` (about 1 us each) delays the
 // first poll of a workgroup that had no work in a phase where the others work for ~2 us: its polls
-// of the flags would only add memory traffic while they work.  Returns false when the wait
-// expired or the launch was aborted (this launch's error code in the status word).
+// of the flags would only add memory traffic while they work.  A workgroup that does not read
+// the phase's output (`wait` false) raises its flag and goes on: flags only grow, so the next
+// wait it takes part in still covers it, and the others poll against less traffic.  Returns
+// false when the wait expired or the launch was aborted (this launch's error code in the
+// status word).
 __device__ __forceinline__ bool ctl_signal_wait(const Sync& s, int phase, bool dead, int idle_us = 0,
                                                 bool wait = true) {
   const int lane = threadIdx.x & 63;
