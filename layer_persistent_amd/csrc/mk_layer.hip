@@ -50,10 +50,12 @@ namespace mk {
 constexpr int kThreads = 576;      // 8 compute waves + 1 control wave
 constexpr int kCompute = 512;
 constexpr int kCtl = 512;          // first thread of the control wave
-// The pooler (P/16 tiles) and the router (E/16 tiles) leave most workgroups without work; those
-// sleep this long before polling (measured: the pooler's work then ends ~0.6 us sooner, and the
-// layer ~0.9 us; longer sleeps, or sleeps in the attention hand-off too, gained nothing).
-constexpr int kIdleSleepUs = 1;
+// The merge (one unit per (token, head) row) and the pooler (P/16 tiles) leave about half the
+// workgroups without work, and those skip the grid wait before it; they sleep this long before
+// their first poll, so that their polls do not load the memory side while the others work
+// (measured: without it the layer is ~0.9 us slower; 2 us beats 1 by ~0.1 us, and 4 or 5 us
+// before the o-proj cost 0.3 and 1.0 us).
+constexpr int kIdleSleepUs = 2;
 // Polls of stage data that has not arrived are repeated back to back, or after s_sleep
 // MK_POLL_SLEEP (64-clock units)
 #ifndef MK_POLL_SLEEP
