@@ -50,11 +50,11 @@ namespace mk {
 constexpr int kThreads = 576;      // 8 compute waves + 1 control wave
 constexpr int kCompute = 512;
 constexpr int kCtl = 512;          // first thread of the control wave
-// The merge (one unit per (token, head) row) and the pooler (P/16 tiles) leave about half the
-// workgroups without work, and those skip the grid wait before it; they sleep this long before
-// their first poll, so that their polls do not load the memory side while the others work
-// (measured: without it the layer is ~0.9 us slower; 2 us beats 1 by ~0.1 us, and 4 or 5 us
-// before the o-proj cost 0.3 and 1.0 us).
+// The merge (one unit per (token, head) row) leaves about half the workgroups without work, and
+// those skip the attention hand-off; they sleep this long before their first poll of the merged
+// rows, so that their polls do not load the memory side while the merge runs (measured: 2 us
+// beats 1 by ~0.1 us per layer; 4 or 5 us cost 0.3 and 1.0 us).  The pooler's idle workgroups
+// sleep longer (see its hand-off).
 constexpr int kIdleSleepUs = 2;
 // Polls of stage data that has not arrived are repeated back to back, or after s_sleep
 // MK_POLL_SLEEP (64-clock units)
@@ -2493,8 +2493,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       }, pool_lds ? smem + POOL_LDS_OFF : nullptr);
     }
     // the router tile loads into registers (unless held in LDS) while the grid hands off
+    // The workgroups without a pooler tile reach this wait right after their o-proj tile (they
+    // skip the o-proj's wait) and sleep through the o-proj hand-off and the pooler's work, both
+    // proportional to H: 1 + H/1024 us (5 at H = 4096, where 3, 4, 5, 6, 7, 8 us measured -0.09,
+    // -0.18, -0.35, -0.34, -0.14, +0.36 us per layer against 2).
     alive = phase_end<TS>(a, s, 4, &dead_sh, [&] { if (p_r && !router_lds) wfrag_load(wr, a.w_router, a.P, t_r * 16); },
-                          p_p ? 0 : kIdleSleepUs) && alive;
+                          p_p ? 0 : 1 + a.H / 1024) && alive;
     // ---- 5 ROUTER: logits = xp Wr^T (+ bias)
     if (alive) {
       dense_phase<NRT>(a, wr, p_r && !router_lds, a.w_router, xplain(st_xp(a), s, &dead_sh), a.P, a.E, off_r, red2,
