@@ -34,9 +34,11 @@ COPY_CALIB_ELEMS = 1 << 26          # fp32 elements of the copy-calibration kern
 
 # timestamp events the layer kernel records (index, name): phase ends, hand-off ends, and the
 # points inside the routing and expert phases
-PHASE_EVENTS = [(1, "setup"), (2, "attn_work"), (3, "attn_handoff"), (4, "merge_work"), (5, "oproj_weights_issued"),
+PHASE_EVENTS = [(1, "setup"), (2, "attn_work"), (3, "attn_handoff"), (61, "merge_loaded"),
+                (63, "merge_reduced"), (4, "merge_work"), (5, "oproj_weights_issued"),
                 (6, "oproj_work"), (7, "oproj_handoff"), (8, "pool_work"), (9, "pool_handoff"), (10, "router_work"),
-                (11, "xs_built"), (46, "route_logits_in"), (47, "route_topk"), (18, "route_tables"),
+                (11, "xs_built"), (51, "route_logits_in"), (52, "route_published"), (46, "route_in"),
+                (18, "route_tables"),
                 (49, "gemm1_first_loads"), (45, "gemm1_round1"), (12, "gemm1_work"), (13, "w2_first_issued"),
                 (42, "gemm2_staged"), (48, "gemm2_batch0"), (43, "gemm2_experts"), (14, "gemm2_work"),
                 (15, "gemm2_handoff"), (16, "unpool_work"), (17, "qkv_weights_issued"), (19, "qkv_end")]
@@ -726,11 +728,16 @@ def main():
         if items.any():
             phases["attn_stage_us_max"] = d(37, 1, items)
             phases["attn_compute_us_max"] = d(38, 37, items)
+        mg = tsv[:, 63] > 0
+        if mg.any():
+            phases["merge_reduce_us_max"] = d(63, 61, mg)
         rtm = tsv[:, 46] > 0
         if rtm.any():
-            phases["route_logits_wait_us_max"] = d(46, 11, rtm)
-            phases["route_topk_us_max"] = d(47, 46, rtm)
-            phases["route_rest_us_max"] = d(18, 47, rtm)
+            phases["route_wait_us_max"] = d(46, 11, rtm)
+            phases["route_tables_us_max"] = d(18, 46, rtm)
+        pub = tsv[:, 52] > 0
+        if pub.any():
+            phases["route_topk_us_max"] = d(52, 51, pub)
         phases["gemm1_us_p50_max"] = [round(float(np.median((tsv[:, 12] - tsv[:, 18]) / 100.0)), 2), d(12, 18, tsv[:, 12] > 0)]
         g2 = tsv[:, 43] > 0
         if g2.any():

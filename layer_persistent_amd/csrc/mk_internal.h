@@ -44,7 +44,10 @@ constexpr uint32_t kStageY = kStageAct + kMaxRowTiles * 16 * 8 * 256 * 2;  // bf
 // the N-sharded layout's GEMM2 products before gates, fp32 [T*k][P/R], P/R <= 1024 (reset with
 // the rest of the idle copy by every launch, so that the two layouts may share a workspace)
 constexpr uint32_t kStagePart = kStageY + kMaxRowTiles * 16 * 2048 * 2;
-constexpr uint32_t kStageBytes = kStagePart + 16 * 8 * 1024 * 4;
+// each row's routing, published once by one workgroup: 8 slots of (expert int32, gate fp32),
+// slots past top-k zero
+constexpr uint32_t kStageRoute = kStagePart + 16 * 8 * 1024 * 4;
+constexpr uint32_t kStageBytes = kStageRoute + kMaxRowTiles * 16 * 8 * 8;
 
 // Kernel arguments of one fused layer launch (passed by value).
 struct KArgs {
@@ -81,7 +84,7 @@ struct KArgs {
   // parity); the buffers at the kStage* offsets: attn, h1, xp, y hand-off activations ([16][K]
   // bf16 tiles in MFMA fragment order), h_out in fragment order (the qkv phase's x), logits,
   // the NVFP4 intermediate records [T*k][I/16][4 dwords] (codes of elements 0-7, scale byte,
-  // codes of elements 8-15, scale byte) or bf16 rows [T*k][I], GEMM2 partials
+  // codes of elements 8-15, scale byte) or bf16 rows [T*k][I], GEMM2 partials, the routing
   char* cur;
   // N-sharded expert layout (rank ns_r of ns_R; ns_R == 0: the ordinary layout): the gathered
   // intermediate records [T*k][ns_R*I/16][4 dwords], the gathered y (bf16 [16][P], fragment

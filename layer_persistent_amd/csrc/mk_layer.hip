@@ -21,10 +21,11 @@
 //   2 MERGE  merge partials per (token, head) -> attn (bf16), stats (m, l)              D
 //   3 OPROJ  h1 = bf16(h_in + attn Wo^T)                                                 G
 //   4 POOL   xp = bf16(h1 Wp^T)                                                          G
-//   5 ROUTER logits = xp Wr^T (+ bias), fp32                                             D
-//   6 GEMM1  every workgroup: top-k, gates and dispatch from the logits (identical everywhere);
-//            then (expert, 16-column block) tasks: u = xp W1^T ts1, a = silu(u_gate) u_up,
-//            NVFP4 requantisation of a (bf16 for bf16 experts)                           D
+//   5 ROUTER logits = xp Wr^T (+ bias), fp32; the control wave of workgroup t reads row t as
+//            it arrives and publishes its top-k experts and gates                        D
+//   6 GEMM1  every workgroup: dispatch tables from the published routing (identical
+//            everywhere); then (expert, 16-column block) tasks: u = xp W1^T ts1,
+//            a = silu(u_gate) u_up, NVFP4 requantisation of a (bf16 for bf16 experts)    D
 //   7 GEMM2  per 8-column slice of P: every active expert's down projection, then the combine
 //            y = bf16(sum over the token's slots, in slot order, of gate * out)          G
 //   8 UNPOOL h_out = bf16(h1 + y Wu^T)                                                   D
@@ -61,7 +62,7 @@ constexpr int kIdleSleepUs = 2;
 #ifndef MK_POLL_SLEEP
 #define MK_POLL_SLEEP 0
 #endif
-// workgroups without a router tile wait about MK_ROUTE_IDLE us before reading the logits
+// workgroups without a router tile wait about MK_ROUTE_IDLE us before reading the routing
 #ifndef MK_ROUTE_IDLE
 #define MK_ROUTE_IDLE 0
 #endif
@@ -96,6 +97,7 @@ __device__ __forceinline__ uint32_t* st_act_q(const KArgs& a) { return (uint32_t
 __device__ __forceinline__ uint16_t* st_act_bf(const KArgs& a) { return (uint16_t*)(a.cur + kStageAct); }
 __device__ __forceinline__ uint16_t* st_y(const KArgs& a) { return (uint16_t*)(a.cur + kStageY); }
 __device__ __forceinline__ float* st_g2_part(const KArgs& a) { return (float*)(a.cur + kStagePart); }
+__device__ __forceinline__ uint64_t* st_route(const KArgs& a) { return (uint64_t*)(a.cur + kStageRoute); }
 
 __device__ __forceinline__ void wg_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -926,6 +928,7 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
 // Merge of the per-chunk partials of one (kv head, row), flash-decoding style rescale.
 // Compute waves: 16 chunk groups x 32 threads (4 d values each).  The merged row (bf16)
 // and its stats go to LDS `outrow` for the control wave to store.  Called by all threads.
+template <bool TS>
 __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scratch, uint32_t* outrow) {
   const int d = a.d;
   const int G = a.Hq / a.Hkv, R = a.Ts * G;
@@ -963,22 +966,31 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
       }
     }
   }
+  stamp<TS>(a.timestamps, 61, 0);
+  // The row's maximum over the groups' maxima (the threads of a group share theirs); every
+  // thread rescales its group's sums to it, and the first 32 threads add the groups up in
+  // group order.  LDS: the group maxima after 5 components x 16 groups x 32 threads.
+  float* gmax = scratch + 5 * 16 * 32;
+  if (threadIdx.x < kCompute && tq == 0) gmax[cg] = M;
+  wg_sync();
+  stamp<TS>(a.timestamps, 62, 0);
+  float Mt = -INFINITY;
   if (threadIdx.x < kCompute) {
-    float* me = scratch + (cg * 32 + tq) * 6;
-    me[0] = M; me[1] = L; me[2] = O[0]; me[3] = O[1]; me[4] = O[2]; me[5] = O[3];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) Mt = fmaxf(Mt, gmax[q]);
+    const float s = M == -INFINITY ? 0.f : __expf(M - Mt);
+    scratch[cg * 32 + tq] = L * s;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) scratch[((1 + j) * 16 + cg) * 32 + tq] = O[j] * s;
   }
   wg_sync();
   if (threadIdx.x < quads) {
-    float Mt = -INFINITY;
-    for (int q = 0; q < ngroups; ++q) Mt = fmaxf(Mt, scratch[(q * 32 + threadIdx.x) * 6]);
     float Lt = 0.f, Ot[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < ngroups; ++q) {
-      const float* e = scratch + (q * 32 + threadIdx.x) * 6;
-      if (e[0] == -INFINITY) continue;
-      const float s = __expf(e[0] - Mt);
-      Lt += e[1] * s;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) Ot[j] += e[2 + j] * s;
+    for (int q = 0; q < 16; ++q) {
+      Lt += scratch[q * 32 + threadIdx.x];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Ot[j] += scratch[((1 + j) * 16 + q) * 32 + threadIdx.x];
     }
     const float inv = 1.0f / Lt;
     outrow[2 * threadIdx.x] = pack_bf2(Ot[0] * inv, Ot[1] * inv);
@@ -988,60 +1000,36 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
       outrow[65] = __float_as_uint(Lt);
     }
   }
+  stamp<TS>(a.timestamps, 63, 0);
 }
 
 // ------------------------------------------------------------------ routing
 
-// Top-k per token from the logits (value desc, index asc), softmax gates over the selected,
-// and the dispatch tables.  Every workgroup computes the same tables.  Called by all threads;
-// the work runs on the compute waves.
-template <bool TS, class RT>
-__device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, float* lg, const Sync& sy, int32_t* dead_sh) {
-  const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
-  const int npairs = T * K;
-  const bool cw = tid < kCompute;
-  // (NVFP4) every expert's two tensor scales; then the logits, read as they arrive from the
-  // router workgroups
-  const int nlg = T * E / 4, nts = a.fmt == 1 ? E / 4 : 0;
-  stage_pieces(2 * nts, [&](int i) {
-    return i < nts ? (const void*)(a.w1_ts + 4 * i) : (const void*)(a.w2_ts + 4 * (i - nts));
-  }, [&](int i) {
-    return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
-  });
-  if (cw)
-    poll_stage<2>(sy, dead_sh, make_rsrc(st_logits(a), (uint32_t)nlg * 16), nlg, tid, kCompute,
-                  [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) { *(u32x4*)(lg + 4 * i) = v; });
-  // scratch after the logits: per expert, a bitmask of the pairs routed there (kMW words),
-  // counts, offsets
-  constexpr int kMW = RT::kPairs / 32;
-  uint32_t* mask = (uint32_t*)(lg + T * E);
-  int32_t* ecnt = (int32_t*)(mask + E * kMW);
-  int32_t* efirst = ecnt + E;
-  for (int i = tid; cw && i < E * kMW; i += kCompute) mask[i] = 0u;
-  wg_sync();
-  stamp<TS>(a.timestamps, 46, 0);
-  const int lane = tid & 63, wave = tid >> 6;
-  // Top-k per token.  Wave w takes tokens w (lanes 0-31) and w + 8 (lanes 32-63), so one DPP
-  // reduction serves both.  Lane l of a half holds experts 8 (l % 32) .. + 7, sorted by (logit
-  // desc, index asc); each round a half's largest head wins (the lowest lane on ties, which
-  // holds the lowest index) and its lane pops it.  Lane j of the wave keeps round j's logits
-  // and experts of both tokens.
-  for (int tA = wave; cw && tA < T; tA += 16) {
-    const int tB = tA + 8;
-    const bool hi = lane >= 32;
-    const int t = hi ? tB : tA;
-    const bool tv = t < T;
+// Top-k of one row of the logits (value desc, index asc) and softmax gates over the selected,
+// published for every workgroup.  One wave per row: the control wave of workgroup t takes rows
+// t, t + grid, ...  It reads the row as it arrives from the router workgroups, then writes the
+// row's 8 routing slots (expert, gate bits) with coherent stores, zero past top-k.
+template <bool TS>
+__device__ __forceinline__ void publish_route(const KArgs& a, const Sync& sy, int32_t* dead_sh) {
+  const int E = a.E, K = a.topk, lane = threadIdx.x & 63;
+  for (int t = blockIdx.x; t < a.T; t += gridDim.x) {
+    // lane l holds experts 4 l .. 4 l + 3
+    u32x4 v = u32x4{0, 0, 0, 0};
+    poll_stage<1>(sy, dead_sh, make_rsrc(st_logits(a) + (size_t)t * E, (uint32_t)E * 4), E / 4, lane, 64,
+                  [](int i) { return (uint32_t)i * 16u; }, [&](int, u32x4 x) { v = x; });
+    if (*(volatile int32_t*)dead_sh) return;
+    stamp<TS>(a.timestamps, 51);
     // Each candidate is one 64-bit word: the logit's order-preserving integer with its sign bit
     // flipped (exact, so ties stay ties) above 0xFFFF - expert, so that a larger word comes
     // first in (logit desc, index asc) order; 0 stands for no expert.  One unsigned compare
     // then orders two candidates, with no branch on ties.
-    uint64_t w[8];
+    uint64_t w[4];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int e = 8 * (lane & 31) + q;
-      w[q] = (tv && e < E) ? ((uint64_t)((uint32_t)f32_order_key(lg[t * E + e]) ^ 0x80000000u) << 32) |
-                                 (uint32_t)(0xFFFF - e)
-                           : 0ull;
+    for (int q = 0; q < 4; ++q) {
+      const int e = 4 * lane + q;
+      w[q] = e < E ? ((uint64_t)((uint32_t)f32_order_key(__uint_as_float(v[q])) ^ 0x80000000u) << 32) |
+                         (uint32_t)(0xFFFF - e)
+                   : 0ull;
     }
     auto cswap = [&](int i, int j) {
       const bool sw = w[j] > w[i];
@@ -1049,49 +1037,65 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, float* lg, 
       w[i] = sw ? y : x;
       w[j] = sw ? x : y;
     };
-    // Batcher's odd-even merge sort of 8 (19 comparators)
-    cswap(0, 1); cswap(2, 3); cswap(4, 5); cswap(6, 7);
-    cswap(0, 2); cswap(1, 3); cswap(4, 6); cswap(5, 7);
-    cswap(1, 2); cswap(5, 6);
-    cswap(0, 4); cswap(1, 5); cswap(2, 6); cswap(3, 7);
-    cswap(2, 4); cswap(3, 5);
-    cswap(1, 2); cswap(3, 4); cswap(5, 6);
-    int32_t kA = 0, kB = 0, eA = 0, eB = 0;
+    cswap(0, 1); cswap(2, 3); cswap(0, 2); cswap(1, 3); cswap(1, 2);
+    // each round the largest head wins (the lowest lane on ties, which holds the lowest index)
+    // and its lane pops it; lane j keeps round j's logit key and expert
+    int32_t kj = 0, ej = 0;
     for (int j = 0; j < K; ++j) {
-      const int32_t head = (int32_t)((uint32_t)(w[0] >> 32) ^ 0x80000000u);   // the logit's key
-      const int32_t m = half_max_i32(head);
-      const int32_t xA = __builtin_amdgcn_readlane(m, 31), xB = __builtin_amdgcn_readlane(m, 63);
-      const uint64_t bal = __ballot(head == (hi ? xB : xA));
-      const int lA = __ffs((unsigned)bal) - 1, lB = 32 + __ffs((unsigned)(bal >> 32)) - 1;
-      const int lo = (int)(uint32_t)w[0];
-      const int beA = 0xFFFF - __builtin_amdgcn_readlane(lo, lA), beB = 0xFFFF - __builtin_amdgcn_readlane(lo, lB);
-      const bool take = lane == lA || lane == lB;
+      const int32_t head = (int32_t)((uint32_t)(w[0] >> 32) ^ 0x80000000u);
+      const int32_t m = wave_max_i32(head);
+      const int lw = __ffsll((unsigned long long)__ballot(head == m)) - 1;
+      const int be = 0xFFFF - __builtin_amdgcn_readlane((int)(uint32_t)w[0], lw);
+      const bool take = lane == lw;
 #pragma unroll
-      for (int q = 0; q < 7; ++q) w[q] = take ? w[q + 1] : w[q];
-      w[7] = take ? 0ull : w[7];
-      kA = lane == j ? xA : kA;
-      eA = lane == j ? beA : eA;
-      kB = lane == j ? xB : kB;
-      eB = lane == j ? beB : eB;
+      for (int q = 0; q < 3; ++q) w[q] = take ? w[q + 1] : w[q];
+      w[3] = take ? 0ull : w[3];
+      kj = lane == j ? m : kj;
+      ej = lane == j ? be : ej;
     }
-    const bool hasB = tB < T;                                    // uniform over the wave
-    const float mA = f32_from_order_key(kA), mB = f32_from_order_key(kB);
-    // gates: softmax over the k selected logits, summed in slot order (lane reads, no LDS)
+    // gates: softmax over the k selected logits, summed in slot order
     auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
-    const float zA = __expf(mA - rl(mA, 0)), zB = __expf(mB - rl(mB, 0));
-    float sA = 0.f, sB = 0.f;
-    for (int j = 0; j < K; ++j) { sA += rl(zA, j); sB += rl(zB, j); }
-    if (lane < K) {
-      rt.idx[tA * K + lane] = eA;
-      rt.gate[tA * K + lane] = zA / sA;
-      if (hasB) {
-        rt.idx[tB * K + lane] = eB;
-        rt.gate[tB * K + lane] = zB / sB;
-      }
-    }
+    const float mj = f32_from_order_key(kj);
+    const float z = __expf(mj - rl(mj, 0));
+    float sum = 0.f;
+    for (int j = 0; j < K; ++j) sum += rl(z, j);
+    if (lane < 8)
+      st_coh_u64(st_route(a) + (size_t)t * 8 + lane,
+                 lane < K ? (uint64_t)(uint32_t)ej | ((uint64_t)__float_as_uint(z / sum) << 32) : 0ull);
+    stamp<TS>(a.timestamps, 52);
   }
+}
+
+// The dispatch tables, from the published routing.  Every workgroup computes the same tables.
+// Called by all threads; the work runs on the compute waves.
+template <bool TS, class RT>
+__device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* lds, const Sync& sy, int32_t* dead_sh) {
+  const int T = a.T, E = a.E, K = a.topk, tid = threadIdx.x;
+  const int npairs = T * K;
+  const bool cw = tid < kCompute;
+  // (NVFP4) every expert's two tensor scales; then the routing, read as it arrives (one 16-byte
+  // piece holds two slots)
+  const int nts = a.fmt == 1 ? E / 4 : 0;
+  stage_pieces(2 * nts, [&](int i) {
+    return i < nts ? (const void*)(a.w1_ts + 4 * i) : (const void*)(a.w2_ts + 4 * (i - nts));
+  }, [&](int i) {
+    return i < nts ? (void*)(rt.ts1 + 4 * i) : (void*)(rt.ts2 + 4 * (i - nts));
+  });
+  if (cw)
+    poll_stage<1>(sy, dead_sh, make_rsrc(st_route(a), (uint32_t)T * 64), T * 4, tid, kCompute,
+                  [](int i) { return (uint32_t)i * 16u; }, [&](int i, u32x4 v) {
+      const int t = i >> 2, j = (i & 3) * 2;
+      if (j < K) { rt.idx[t * K + j] = (int16_t)v[0]; rt.gate[t * K + j] = __uint_as_float(v[1]); }
+      if (j + 1 < K) { rt.idx[t * K + j + 1] = (int16_t)v[2]; rt.gate[t * K + j + 1] = __uint_as_float(v[3]); }
+    });
+  // per expert, a bitmask of the pairs routed there (kMW words), counts, offsets
+  constexpr int kMW = RT::kPairs / 32;
+  uint32_t* mask = lds;
+  int32_t* ecnt = (int32_t*)(mask + E * kMW);
+  int32_t* efirst = ecnt + E;
+  for (int i = tid; cw && i < E * kMW; i += kCompute) mask[i] = 0u;
   wg_sync();
-  stamp<TS>(a.timestamps, 47, 0);
+  stamp<TS>(a.timestamps, 46, 0);
   for (int p = tid; cw && p < npairs; p += kCompute) atomicOr(&mask[rt.idx[p] * kMW + (p >> 5)], 1u << (p & 31));
   wg_sync();
   for (int e = tid; cw && e < E; e += kCompute) {
@@ -2430,7 +2434,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       const int G = a.Hq / a.Hkv, R = a.Ts * G;
       const int units = a.B * a.Hkv * R;
       for (int u = blockIdx.x; u < units; u += nwg) {
-        merge_unit(a, u, (float*)smem, outrow);
+        merge_unit<TS>(a, u, (float*)smem, outrow);
         wg_sync();
         if (!cw) {
           const int sq = u / (a.Hkv * R), ul = u % (a.Hkv * R);
@@ -2516,8 +2520,9 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         if (a.router_logits) *(f32x4*)(a.router_logits + (size_t)row * a.E + n0 + cc0) = f32x4{v[0], v[1], v[2], v[3]};
       }, router_lds ? smem + POOL_LDS_OFF : nullptr);
     }
-    // No grid hand-off after the router: every workgroup reads the logits as they arrive.
-    // GEMM1's input rows (xs, in LDS at 0) are built first, from xp as it arrives (piece maxima
+    // No grid hand-off after the router: the control waves of the first T workgroups read the
+    // logits as they arrive and publish each row's routing, which every workgroup reads as it
+    // arrives.  Meanwhile GEMM1's input rows (xs, in LDS at 0) are built from xp (piece maxima
     // go to the LDS area GEMM1 later uses for scales): they do not depend on the routing.
     wg_sync();
     stamp<TS>(a.timestamps, 10);
@@ -2525,10 +2530,12 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
       if constexpr (NRT == 1) {
         u32x4 xpv[8];
         if (cw) xp_fetch(a, xpv, (uint32_t*)(smem + G1_XS_BYTES));
+        else publish_route<TS>(a, s, &dead_sh);
         wg_sync();                              // every wave's piece maxima are in LDS
         xs_build<TS>(a, xpv, (uint16_t*)smem, a.P + XS_STRIDE_PAD, (const uint32_t*)(smem + G1_XS_BYTES), xk_sh);
       } else {
         // two sequences: all 32 rows, or (two pieces per unit) the first K half of them
+        if (!cw) publish_route<TS>(a, s, &dead_sh);
         xs_rowscale2<TS>(a, (uint32_t*)(smem + G1_XS_BYTES), xk_sh);
         const int cols = g1_pieces(a.P) == 2 ? g1_hsteps(a.P) * 128 : a.P;
         xs_fill2(a, (uint16_t*)smem, cols + XS_STRIDE_PAD, 0, cols, xk_sh);
@@ -2540,7 +2547,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     if (alive) {
       if (!p_r)
         for (int i = 0; i < MK_ROUTE_IDLE; ++i) __builtin_amdgcn_s_sleep(37);
-      route_tables<TS>(a, rt, (float*)(smem + g1_ubuf_off(a.P)), s, &dead_sh);
+      route_tables<TS>(a, rt, (uint32_t*)(smem + g1_ubuf_off(a.P)), s, &dead_sh);
       stamp<TS>(a.timestamps, 18);
       alive = dead_sh == 0;                     // (route_tables ends synchronised)
       if (alive) gemm1_phase<TS>(a, rt, smem, xk_sh);
