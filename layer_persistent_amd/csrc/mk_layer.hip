@@ -926,15 +926,17 @@ __device__ __forceinline__ void attention_compute(const KArgs& a, const Tree& tr
 }
 
 // Merge of the per-chunk partials of one (kv head, row), flash-decoding style rescale.
-// Compute waves: 16 chunk groups x 32 threads (4 d values each).  The merged row (bf16)
-// and its stats go to LDS `outrow` for the control wave to store.  Called by all threads.
+// Compute waves: 16 chunk groups x 32 threads (4 d values each).  The first d/4 threads
+// store the merged row (bf16, read by the o-proj as it arrives) and its stats.  Called by all
+// threads; the caller synchronises before LDS `scratch` is used again.
 template <bool TS>
-__device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scratch, uint32_t* outrow) {
+__device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scratch) {
   const int d = a.d;
   const int G = a.Hq / a.Hkv, R = a.Ts * G;
   const int b = a.B == 1 ? 0 : unit / (a.Hkv * R);       // the sequence
   unit -= b * a.Hkv * R;
   const int g_kv = b * a.Hkv + unit / R, row = unit % R;    // (partial slots are per sequence)
+  const int tok = row / G, head = (unit / R) * G + row % G;
   const int nchunks = a.attn_chunks_per_head;
   const int quads = d / 4;
   const int ngroups = kCompute / 32;
@@ -993,11 +995,11 @@ __device__ __forceinline__ void merge_unit(const KArgs& a, int unit, float* scra
       for (int j = 0; j < 4; ++j) Ot[j] += scratch[((1 + j) * 16 + q) * 32 + threadIdx.x];
     }
     const float inv = 1.0f / Lt;
-    outrow[2 * threadIdx.x] = pack_bf2(Ot[0] * inv, Ot[1] * inv);
-    outrow[2 * threadIdx.x + 1] = pack_bf2(Ot[2] * inv, Ot[3] * inv);
-    if (threadIdx.x == 0) {
-      outrow[64] = __float_as_uint(Mt);
-      outrow[65] = __float_as_uint(Lt);
+    st_coh_u64(st_attn(a) + (size_t)b * 16 * a.Hq * d + frag_off(tok, head * d + threadIdx.x * 4),
+               (uint64_t)pack_bf2(Ot[0] * inv, Ot[1] * inv) | ((uint64_t)pack_bf2(Ot[2] * inv, Ot[3] * inv) << 32));
+    if (threadIdx.x == 0 && a.attn_stats) {
+      a.attn_stats[((size_t)(b * a.Ts + tok) * a.Hq + head) * 2 + 0] = Mt;
+      a.attn_stats[((size_t)(b * a.Ts + tok) * a.Hq + head) * 2 + 1] = Lt;
     }
   }
   stamp<TS>(a.timestamps, 63, 0);
@@ -2074,10 +2076,10 @@ __device__ __forceinline__ void gemm2_staged(const KArgs& a, const RT& rt, char*
 // Loads for the next phase are not issued here but inside the hand-off wait that follows
 // (phase_end's `pf`): issued before the hand-off, a large tile's loads hold the issuing waves
 // until the CU's load queue drains, and the grid waits for them at the barrier.
-template <int NRT, int MAXS, class Epi>
+template <int NRT, bool TS = false, int MAXS, class Epi>
 __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, bool have_pref, const uint16_t* W,
                             const XSrc& x, int K, int N, int off, float* red2, Epi epi,
-                            const char* wlds = nullptr) {
+                            const char* wlds = nullptr, int ev = -1) {
   const int n = gridDim.x, ntiles = N / 16;
   int it = 0;
   for (int t = first_tile(off); t < ntiles; t += n, ++it) {
@@ -2097,6 +2099,7 @@ __device__ __forceinline__ void dense_phase(const KArgs& a, WFrag<MAXS>& wf, boo
           if (!(have_pref && it == 0) && r == 0) wfrag_load(wf, W, K, t * 16);
           acc = wfrag_mma(wf, xr, 0, Tr, K);
         }
+        if (ev >= 0 && it == 0 && r == 0) stamp<TS>(a.timestamps, ev, 0);
         red_store(red, acc);
       }
       wg_sync();
@@ -2240,7 +2243,6 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   __shared__ uint32_t epoch_sh;
   __shared__ int32_t par_sh[32];
   __shared__ int32_t xk_sh[16 * NRT];   // GEMM1 input row scales (NVFP4 experts)
-  __shared__ uint32_t outrow[68];
   __shared__ uint32_t ytile[16 * NRT * 4];
   const int tid = threadIdx.x;
   const bool cw = tid < kCompute;
@@ -2431,22 +2433,11 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
     }, 0, merge_wg);
     // ---- 2 MERGE
     if (alive) {
-      const int G = a.Hq / a.Hkv, R = a.Ts * G;
-      const int units = a.B * a.Hkv * R;
+      const int units = a.B * a.Hkv * a.Ts * (a.Hq / a.Hkv);
       for (int u = blockIdx.x; u < units; u += nwg) {
-        merge_unit<TS>(a, u, (float*)smem, outrow);
-        wg_sync();
-        if (!cw) {
-          const int sq = u / (a.Hkv * R), ul = u % (a.Hkv * R);
-          const int g_kv = ul / R, row = ul % R, tok = row / G, head = g_kv * G + row % G;
-          if (lane < a.d / 4)
-            st_coh_u64(st_attn(a) + (size_t)sq * 16 * a.Hq * a.d + frag_off(tok, head * a.d + lane * 4),
-                       (uint64_t)outrow[2 * lane] | ((uint64_t)outrow[2 * lane + 1] << 32));
-          if (lane == 0 && a.attn_stats) {
-            a.attn_stats[((size_t)(sq * a.Ts + tok) * a.Hq + head) * 2 + 0] = __uint_as_float(outrow[64]);
-            a.attn_stats[((size_t)(sq * a.Ts + tok) * a.Hq + head) * 2 + 1] = __uint_as_float(outrow[65]);
-          }
-        }
+        if (u != (int)blockIdx.x) wg_sync();     // LDS scratch reused
+        merge_unit<TS>(a, u, (float*)smem);
+        stamp<TS>(a.timestamps, 53, 0);
       }
     }
     // No grid hand-off after the merge: the o-proj reads attn as it arrives.  Meanwhile the
@@ -2469,7 +2460,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
 #pragma unroll
     for (int r = 0; r < NRT; ++r) res_u[r] = u32x2{0, 0};
     if (alive) {
-      dense_phase<NRT>(a, wo, p_o, a.w_o, xsrc(st_attn(a), a.Hq * a.d, s, &dead_sh), a.Hq * a.d, a.H, 0, red2,
+      dense_phase<NRT, TS>(a, wo, p_o, a.w_o, xsrc(st_attn(a), a.Hq * a.d, s, &dead_sh), a.Hq * a.d, a.H, 0, red2,
                        [&](int n0, const float* red, int it, int rr) {
         if (!crv(rr)) return;
         const int row = 16 * rr + crow;
@@ -2480,7 +2471,7 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
         const uint64_t hv = pack4_bf16(v);
         st_coh_u64(st_h1(a) + (size_t)rr * 16 * a.H + frag_off(crow, n0 + cc0), hv);
         if (it == 0) res_u[rr] = u32x2{(uint32_t)hv, (uint32_t)(hv >> 32)};
-      });
+      }, nullptr, 47);
     }
     if (cw && pool_dma) __builtin_amdgcn_s_waitcnt(0);   // the pooler tile is in LDS
     // only the pooler's workgroups read h1 now; the others raise their flag and go on to the
