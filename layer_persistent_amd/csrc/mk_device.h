@@ -172,6 +172,28 @@ __device__ __forceinline__ int32_t half_max_i32(int32_t v) {
   v = dpp_max_i32<0x140, 0xF>(v);       // row_mirror
   return dpp_max_i32<0x142, 0xA>(v);    // row_bcast:15 into rows 1 and 3
 }
+// wave_max_i32 with each exchange folded into the max (one DPP instruction per step)
+__device__ __forceinline__ int32_t wave_max_i32_folded(int32_t v) {
+  v = dpp_max_i32<0xB1, 0xF>(v);        // quad_perm [1,0,3,2]
+  v = dpp_max_i32<0x4E, 0xF>(v);        // quad_perm [2,3,0,1]
+  v = dpp_max_i32<0x141, 0xF>(v);       // row_half_mirror
+  v = dpp_max_i32<0x140, 0xF>(v);       // row_mirror
+  v = dpp_max_i32<0x142, 0xA>(v);       // row_bcast:15 into rows 1 and 3
+  v = dpp_max_i32<0x143, 0xC>(v);       // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
+}
+// Inclusive prefix sum over the 64 lanes of a wave (all lanes active): shifts right by 1, 2,
+// 4 and 8 lanes inside each row of 16 (lanes with no source add 0), then row broadcasts add
+// the preceding rows' totals (lane 15 into rows 1 and 3, then lane 31 into rows 2 and 3).
+__device__ __forceinline__ int32_t wave_incl_scan_i32(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return v;
+}
 __device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
   v = max(v, dpp_i32<0xB1, 0xF>(v));    // quad_perm [1,0,3,2]
   v = max(v, dpp_i32<0x4E, 0xF>(v));    // quad_perm [2,3,0,1]

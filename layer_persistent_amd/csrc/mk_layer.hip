@@ -1045,7 +1045,7 @@ __device__ __forceinline__ void publish_route(const KArgs& a, const Sync& sy, in
     int32_t kj = 0, ej = 0;
     for (int j = 0; j < K; ++j) {
       const int32_t head = (int32_t)((uint32_t)(w[0] >> 32) ^ 0x80000000u);
-      const int32_t m = wave_max_i32(head);
+      const int32_t m = wave_max_i32_folded(head);
       const int lw = __ffsll((unsigned long long)__ballot(head == m)) - 1;
       const int be = 0xFFFF - __builtin_amdgcn_readlane((int)(uint32_t)w[0], lw);
       const bool take = lane == lw;
@@ -1107,6 +1107,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* l
     ecnt[e] = c;
   }
   wg_sync();
+  stamp<TS>(a.timestamps, 20, 0);
   if (tid < 64) {
     // exclusive scans over experts: lane handles 4 consecutive experts; an expert takes
     // ceil(count / 16) GEMM1 entries
@@ -1119,17 +1120,13 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* l
       sumc += cnt[q];
       suma += act[q];
     }
-    int sc = sumc, sa = suma;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int oc = __shfl_up(sc, off), oa = __shfl_up(sa, off);
-      if (tid >= off) { sc += oc; sa += oa; }
-    }
+    const int sc = wave_incl_scan_i32(sumc), sa = wave_incl_scan_i32(suma);
     int pc = sc - sumc, pa = sa - suma;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid * 4 + q;
       if (e < E) efirst[e] = pc;
+#pragma unroll 1      // (kept small: this code runs once per launch, from a cold instruction cache)
       for (int j = 0; j < act[q]; ++j) {
         rt.act_expert[pa] = e;
         rt.act_off[pa] = pc + 16 * j;
@@ -1141,6 +1138,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* l
     if (tid == 63) rt.n_active = sa;
   }
   wg_sync();
+  stamp<TS>(a.timestamps, 22, 0);
   if (blockIdx.x == 0 && a.hist)
     for (int e = tid; e < E; e += kThreads) a.hist[e] += ecnt[e];
   if (!cw) {
@@ -1166,6 +1164,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* l
       nsplit += __popcll(split);
     }
     if (lane == 0) rt.n_slots = na + nsplit;
+    stamp<TS>(a.timestamps, 25);
     // workgroup 0: this step's most-used experts, the next step's prefetch list, by a
     // tournament over keys (count, then lower index) that are unique per expert
     if (blockIdx.x == 0 && a.prefetch_next && a.n_prefetch_next > 0) {
@@ -1192,6 +1191,7 @@ __device__ __forceinline__ void route_tables(const KArgs& a, RT& rt, uint32_t* l
     for (int q = 0; q < w; ++q) r += __popc(m[q]);
     rt.pair_list[efirst[e] + r] = p;
   }
+  stamp<TS>(a.timestamps, 26, 0);
   wg_sync();
 }
 
