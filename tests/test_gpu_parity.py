@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -355,6 +357,30 @@ def test_layer_small_shapes(shape, cfg_id):
     log(f"[layer parity] {shape.name}")
     inp = synth.make_layer_inputs(shape, cfg_id)
     _, _, out = _run(inp)
+    _check_layer(inp, out)
+
+
+def test_layer_router_ties():
+    """Router weight rows repeated in threes (experts 3j, 3j+1, 3j+2 share a row), so every
+    logit occurs three times and ties fall inside the top-k and across its k-th / (k+1)-th
+    boundary.  The published selection must be the stable sort (logit desc, expert index asc)
+    of the GPU's own logits -- the tie rule of the routing -- and the rest of the layer must
+    pass the usual checks."""
+    log("[layer parity] router rows tied in threes")
+    inp = synth.make_layer_inputs(SMALL_NVFP4, 95)
+    assert inp.router_bias is None
+    wr = inp.w_router.copy()
+    for e in range(wr.shape[0]):
+        wr[e] = wr[3 * (e // 3)]
+    inp = dataclasses.replace(inp, w_router=wr)
+    _, _, out = _run(inp)
+    lg, k = out["logits"], SMALL_NVFP4.top_k
+    for e in range(lg.shape[1]):
+        assert np.array_equal(lg[:, e], lg[:, 3 * (e // 3)]), f"expert {e}: tied logits differ"
+    srt = -np.sort(-lg.astype(np.float64), axis=1)
+    boundary = int(np.sum(srt[:, k - 1] == srt[:, k]))
+    log(f"  {boundary}/{lg.shape[0]} tokens with a tie across the top-{k} boundary")
+    assert boundary > 0
     _check_layer(inp, out)
 
 
