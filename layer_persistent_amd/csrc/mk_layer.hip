@@ -1604,7 +1604,7 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const RT& rt, char* 
 // loaded straight into registers (a wave's first G2_UNITS units as soon as its workgroup's
 // GEMM1 work ends).  The intermediate is read in the same permuted k order, which MFMA allows.
 // Requires I % 64 == 0 and I >= 128.
-constexpr int G2_UNITS = 4;   // units per register batch
+constexpr int G2_UNITS = 2;   // units per register batch (4 and 3 measured slower)
 constexpr int G2_MAXB = 4;    // I/64 <= 4
 typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
 struct G2W {
@@ -2643,9 +2643,21 @@ __global__ void __launch_bounds__(kThreads) layer_kernel(KArgs a_in) {
   }
 }
 
+// Code placement.  The time per launch of the one-sequence shard-shape kernel depends on where
+// its code sits in the code object: identical code measured up to ~1.4 us per launch apart
+// between offsets 256 bytes apart, and 0x69400 was the best of the offsets measured for two
+// versions of the kernel.  So it is emitted first, behind a kernel that is never launched and
+// holds MK_CODE_PAD bytes of s_nop, which puts its code at that offset whatever the size of
+// the other kernels (llvm-readelf -s on the device code object shows the offset).
+#ifndef MK_CODE_PAD
+#define MK_CODE_PAD 406784
+#endif
+#if MK_CODE_PAD > 0
+__global__ void code_pad() { asm volatile(".fill %0, 4, 0xBF800000" ::"i"(MK_CODE_PAD / 4)); }
+#endif
+template __global__ void layer_kernel<false, 1, false, 1>(KArgs);
 template __global__ void layer_kernel<false, 0, false, 1>(KArgs);
 template __global__ void layer_kernel<true, 0, false, 1>(KArgs);
-template __global__ void layer_kernel<false, 1, false, 1>(KArgs);
 template __global__ void layer_kernel<true, 1, false, 1>(KArgs);
 template __global__ void layer_kernel<false, 0, true, 1>(KArgs);
 template __global__ void layer_kernel<true, 0, true, 1>(KArgs);
