@@ -1369,7 +1369,15 @@ __device__ __forceinline__ void gemm1_phase(const KArgs& a, const RT& rt, char* 
   const int jblocks = I / 16;
   const int ntasks = rt.n_active * jblocks;
   const int nwg = gridDim.x;
-  const int t_begin = (int)((long)blockIdx.x * ntasks / nwg), t_end = (int)((long)(blockIdx.x + 1) * ntasks / nwg);
+  // contiguous shares of ntasks / nwg tasks, one more for ntasks % nwg workgroups; those extra
+  // tasks go to the workgroups after the first T first (the first T published the routing and
+  // start GEMM1 late), so that no share grows
+  const int base = ntasks / nwg, rem = ntasks % nwg, npub = min(T, nwg);
+  const int rem_o = min(rem, nwg - npub), rem_p = rem - rem_o;
+  auto share_start = [&](int w) {
+    return w * base + (w < npub ? min(w, rem_p) : rem_p + min(w - npub, rem_o));
+  };
+  const int t_begin = share_start(blockIdx.x), t_end = share_start(blockIdx.x + 1);
   if (t_begin >= t_end) return;                 // uniform over the workgroup
   const int nh = g1_pieces(P);                                   // pieces per unit
   const int hsteps = g1_hsteps(P);                               // load steps per piece (<= 8)
